@@ -1,0 +1,174 @@
+"""The channel-selection reader, step by step, in float64.  (Oracle.)
+
+Load time, once per layer ([zh §方法步骤详情] load steps (1)-(4)):
+  (1) rotate every gate/up row per 128-block and store ternary codes, an FP16
+      scale and rho per (row, block)                      -> rotation, sketch
+  (2) precompute each down column's norm ||d_j||          -> norms
+  (3) stack the layer's down columns, keep the top-32 left singular vectors
+      U and store b_j = U^T d_j                           -> lowrank
+  (4) transpose D so a kept channel's down weights are contiguous (a layout
+      only: the oracle indexes D directly).
+Decode, per token and layer ([zh §方法步骤详情] decode steps (1)-(4);
+[zh §核心方法]; [ko §어떻게 쓰나]):
+  (1) rotate x once; per block keep the n_screen (= 80) coordinates of largest
+      |R x| and read only their codes (partial screen); estimate
+      g_hat_j ~= g_j^T x and v_hat_j ~= v_j^T x from codes and scales;
+  (2) score every candidate channel of the routed experts in output units,
+      s_j = w_j ||d_j|| |phi(g_hat_j) v_hat_j|, and keep exactly the top k
+      across all routed experts;
+  (3) for kept channels read the native BF16 rows: a_j = phi(g_j^T x)(v_j^T x),
+      output part one = sum_K w_j a_j d_j;
+  (4) output part two = U sum_S w_j b_j p_j over the skipped channels S, with
+      p_j = phi(g_hat_j) v_hat_j reused from the screen.
+
+Readings of open points (each also listed in the design notes):
+  * score bars: s_j = w_j ||d_j|| * |phi(g_hat_j) * v_hat_j|, the absolute value
+    of the whole product ([ko §어떻게 쓰나] derives it from the output
+    contribution w_j ||d_j|| |a_j|);
+  * no rescaling of the partial screen; ties in the coordinate ranking go to
+    the lower index; the same coordinates serve gate, up and every expert;
+  * the ranking is taken on the float32 butterfly values (see rotation);
+    all arithmetic after it uses float64 R x;
+  * stored formats: scales, rho, U and b in fp16 (round to nearest even),
+    norms in fp32; the oracle computes with those stored values;
+  * the exact part multiplies native (unrotated) BF16 rows with the token x.
+
+Test-only modes (never used by the library): ``storage="fp64"`` keeps U and b
+unrounded; ``sketch="exact"`` replaces alpha*c by the true rotated row values,
+so a full screen (n_screen = 128) reproduces g^T x exactly.
+
+Pins (tests/test_oracle_reader.py): k = all channels reproduces the dense
+gated MLP; rank = H recovery equals the exact skipped contribution; full
+screen with exact sketch gives g_hat = g^T x; k = 0 gives y = U z; one expert
+may take every kept channel.  The y values at the real layer sizes have no
+printed worked example: beyond those identities they are parity unpinned.
+"""
+import numpy as np
+
+from .numerics import bf16_to_f64, f64_to_f16_bits, f16_bits_to_f64
+from .rotation import sign_vector, rotate_rows, rotate_x_f64, rotate_x_f32_unscaled
+from .sketch import ternarize_blocks, pack_units
+from .lowrank import recovery_basis
+from .dense import silu
+from .topk import topk_desc
+from .route import route as _route
+
+DEFAULT_ROT_SEED = 0x5EED_0000_CAFE_F00D
+
+
+class OracleReader:
+    def __init__(self, hidden, n_experts, inter, top, gate, up, down, router=None, *,
+                 rank=32, n_screen=80, rot_seed=DEFAULT_ROT_SEED, storage="fp16",
+                 sketch="ternary", block=128):
+        assert hidden % block == 0
+        self.H, self.E, self.I, self.top = hidden, n_experts, inter, top
+        self.rank, self.n_screen, self.block = rank, n_screen, block
+        self.nblk = hidden // block
+        self.storage, self.sketch_mode = storage, sketch
+        self.gate, self.up, self.down, self.router = gate, up, down, router
+        self.sigma = sign_vector(rot_seed, hidden)
+        nb, E, I = self.nblk, n_experts, inter
+
+        # load step (1): rotation + ternary sketch
+        self.codes = np.empty((E, 2, nb, block, I), dtype=np.int8)
+        self.alpha_bits = np.empty((E, nb, 2, I), dtype=np.uint16)
+        self.rho_bits = np.empty((E, nb, 2, I), dtype=np.uint16)
+        self.rot_rows = np.empty((E, 2, nb, block, I)) if sketch == "exact" else None
+        for e in range(E):
+            for m, w in enumerate((gate, up)):
+                u = rotate_rows(bf16_to_f64(w[e]), self.sigma, block)  # [I][nb][128]
+                c, a, r = ternarize_blocks(u)
+                self.codes[e, m] = c.transpose(1, 2, 0)
+                self.alpha_bits[e, :, m, :] = a.T
+                self.rho_bits[e, :, m, :] = r.T
+                if self.rot_rows is not None:
+                    self.rot_rows[e, m] = (u / np.sqrt(128.0)).transpose(1, 2, 0)
+        self.alpha = f16_bits_to_f64(self.alpha_bits)
+        self.units = pack_units(self.codes[:, 0], self.codes[:, 1])  # [E][nb][128][unit]
+
+        # load step (2): down-column norms, summed over h in index order
+        self.norms = np.empty((E, I), dtype=np.float32)
+        for e0 in range(0, E, 16):
+            d = bf16_to_f64(down[e0:e0 + 16])  # [e][H][I]
+            acc = np.zeros((d.shape[0], I))
+            for h in range(hidden):
+                acc = acc + d[:, h, :] * d[:, h, :]
+            self.norms[e0:e0 + 16] = np.sqrt(acc).astype(np.float32)
+
+        # load step (3): recovery basis
+        u64, b64 = recovery_basis(down, rank)
+        self.U64, self.b64 = u64, b64
+        if storage == "fp16":
+            self.U_bits, self.b_bits = f64_to_f16_bits(u64), f64_to_f16_bits(b64)
+            self.U, self.b = f16_bits_to_f64(self.U_bits), f16_bits_to_f64(self.b_bits)
+        else:
+            self.U_bits = self.b_bits = None
+            self.U, self.b = u64, b64
+
+    # -- decode -------------------------------------------------------------
+    def select(self, x):
+        """Per block, the n_screen coordinates of largest |R x| (ascending index)."""
+        v = rotate_x_f32_unscaled(x, self.sigma, self.block)  # [nb][128] float32
+        sel = np.empty((self.nblk, self.n_screen), dtype=np.int64)
+        idx = np.arange(self.block)
+        for b in range(self.nblk):
+            order = np.lexsort((idx, -np.abs(v[b])))
+            sel[b] = np.sort(order[:self.n_screen])
+        return v, sel
+
+    def screen(self, x, ids, sel):
+        xr = rotate_x_f64(np.asarray(x, dtype=np.float32).astype(np.float64), self.sigma, self.block)
+        est = np.zeros((2, self.top, self.I))
+        for s, e in enumerate(np.asarray(ids).tolist()):
+            for m in range(2):
+                acc = np.zeros(self.I)
+                for b in range(self.nblk):
+                    if self.rot_rows is not None:
+                        part = xr[b, sel[b]] @ self.rot_rows[e, m, b, sel[b], :]
+                        acc = acc + part
+                    else:
+                        part = xr[b, sel[b]] @ self.codes[e, m, b, sel[b], :].astype(np.float64)
+                        acc = acc + self.alpha[e, b, m, :] * part
+                est[m, s] = acc
+        return est[0], est[1]
+
+    def decode(self, x, ids, w, k, kept=None):
+        """One token.  Returns a dict of every intermediate and y (float64 [H])."""
+        H, I = self.H, self.I
+        ids = np.asarray(ids, dtype=np.int64)
+        w = np.asarray(w, dtype=np.float32).astype(np.float64)
+        x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+        v32, sel = self.select(x)
+        ghat, vhat = self.screen(x, ids, sel)
+        p = silu(ghat) * vhat
+        score = w[:, None] * self.norms[ids].astype(np.float64) * np.abs(p)
+        flat = score.reshape(-1)
+        kk = topk_desc(flat, k) if kept is None else np.sort(np.asarray(kept, dtype=np.int64))
+        mask = np.zeros(flat.shape[0], dtype=bool)
+        mask[kk] = True
+        slot, j = np.divmod(kk, I)
+        e = ids[slot]
+        # decode step (3): exact kept channels from native rows
+        g = bf16_to_f64(self.gate[e, j]) @ x64
+        v = bf16_to_f64(self.up[e, j]) @ x64
+        a = silu(g) * v
+        dcols = bf16_to_f64(self.down[e, :, j])  # [k][H]
+        y_exact = (w[slot] * a) @ dcols if kk.size else np.zeros(H)
+        # decode step (4): recovery of skipped channels
+        sk = np.nonzero(~mask)[0]
+        s_slot, s_j = np.divmod(sk, I)
+        coef = w[s_slot] * p.reshape(-1)[sk]
+        z = coef @ self.b[ids[s_slot], s_j] if sk.size else np.zeros(self.rank)
+        y_rec = self.U @ z
+        return {"v32": v32, "sel": sel, "ghat": ghat, "vhat": vhat, "p": p,
+                "score": score, "kept": kk, "a": a, "y_exact": y_exact, "z": z,
+                "y_rec": y_rec, "y": y_exact + y_rec}
+
+    def decode_batch(self, X, IDS, W, k, kept=None):
+        outs = [self.decode(X[t], IDS[t], W[t], k, None if kept is None else kept[t])
+                for t in range(X.shape[0])]
+        return outs
+
+    def route(self, x):
+        assert self.router is not None
+        return _route(self.router, x, self.top)
