@@ -1,0 +1,312 @@
+// C ABI entry points that touch the device: build, decode, dense baseline,
+// export, clone, status, free.  Argument rules are documented in include/cfr.h.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <memory>
+#include <new>
+#include <string>
+
+#include "kernels.h"
+
+using namespace cfr;
+
+namespace {
+
+int hipf(hipError_t e, const char* what) {
+  return fail(CFR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Makes the reader's device current for the scope of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = prev == dev || hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+template <typename T>
+T* carve(char*& p, size_t count) {
+  T* out = reinterpret_cast<T*>(p);
+  p += (sizeof(T) * count + 255) / 256 * 256;
+  return out;
+}
+
+size_t workspace_bytes(const cfr_reader& r, size_t* layout) {
+  const cfr_config& c = r.cfg;
+  const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
+  auto rnd = [](size_t n) { return (n + 255) / 256 * 256; };
+  size_t tot = 0;
+  tot += rnd(sizeof(float) * B * H);                              // xrot
+  tot += rnd(B * r.nblk * c.n_screen);                            // sel
+  tot += rnd(sizeof(float) * B * c.top * r.nblk * 2 * c.inter);   // part
+  tot += 4 * rnd(sizeof(float) * B * nc);                         // ghat vhat pact score
+  tot += rnd(sizeof(int32_t) * B * nc);                           // kept
+  tot += rnd(B * nc);                                             // keptf
+  tot += rnd(sizeof(float) * B * nc);                             // coef
+  tot += rnd(sizeof(float) * B * r.max_chunks * H);               // ypart
+  tot += rnd(sizeof(float) * B * r.max_zchunks * (c.rank > 0 ? c.rank : 1));  // zpart
+  tot += 256;                                                     // status
+  (void)layout;
+  return tot;
+}
+
+void carve_workspace(cfr_reader& r) {
+  const cfr_config& c = r.cfg;
+  const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
+  char* p = static_cast<char*>(r.ws);
+  r.xrot = carve<float>(p, B * H);
+  r.sel = carve<uint8_t>(p, B * r.nblk * c.n_screen);
+  r.part = carve<float>(p, B * c.top * r.nblk * 2 * c.inter);
+  r.ghat = carve<float>(p, B * nc);
+  r.vhat = carve<float>(p, B * nc);
+  r.pact = carve<float>(p, B * nc);
+  r.score = carve<float>(p, B * nc);
+  r.kept = carve<int32_t>(p, B * nc);
+  r.keptf = carve<uint8_t>(p, B * nc);
+  r.coef = carve<float>(p, B * nc);
+  r.ypart = carve<float>(p, B * r.max_chunks * H);
+  r.zpart = carve<float>(p, B * r.max_zchunks * (c.rank > 0 ? c.rank : 1));
+  r.status = carve<int32_t>(p, 1);
+}
+
+void free_reader(cfr_reader* r) {
+  if (!r) return;
+  void* bufs[] = {r->w3, r->codes, r->scales, r->rho, r->norms, r->u,
+                  r->b,  r->sigma, r->router, r->ws};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  delete r;
+}
+
+void init_geometry(cfr_reader& r) {
+  r.nblk = r.cfg.hidden / kBlock;
+  r.lp = half_bytes(r.cfg.inter);
+  r.unit = unit_bytes(r.cfg.inter);
+  r.ncand = r.cfg.top * r.cfg.inter;
+  r.max_chunks = (r.ncand + 31) / 32;
+  r.max_zchunks = (r.ncand + 255) / 256;
+}
+
+struct ResidentSizes {
+  size_t w3, codes, scales, norms, u, b, sigma, router;
+};
+
+ResidentSizes resident_sizes(const cfr_reader& r) {
+  const cfr_config& c = r.cfg;
+  const size_t E = c.n_experts, I = c.inter, H = c.hidden;
+  ResidentSizes s;
+  s.w3 = E * I * 3 * H * 2;
+  s.codes = E * r.nblk * kBlock * r.unit;
+  s.scales = E * r.nblk * 2 * I * 2;
+  s.norms = E * I * 4;
+  s.u = H * (size_t)c.rank * 2;
+  s.b = E * I * (size_t)c.rank * 2;
+  s.sigma = H * 4;
+  s.router = E * H * 2;
+  return s;
+}
+
+int alloc_resident(cfr_reader& r, bool with_router) {
+  ResidentSizes s = resident_sizes(r);
+  hipError_t e;
+  auto al = [&](void** p, size_t n) { return hipMalloc(p, n ? n : 256); };
+  if ((e = al((void**)&r.w3, s.w3)) != hipSuccess || (e = al((void**)&r.codes, s.codes)) != hipSuccess ||
+      (e = al((void**)&r.scales, s.scales)) != hipSuccess ||
+      (e = al((void**)&r.rho, s.scales)) != hipSuccess ||
+      (e = al((void**)&r.norms, s.norms)) != hipSuccess ||
+      (e = al((void**)&r.u, s.u)) != hipSuccess || (e = al((void**)&r.b, s.b)) != hipSuccess ||
+      (e = al((void**)&r.sigma, s.sigma)) != hipSuccess ||
+      (with_router && (e = al((void**)&r.router, s.router)) != hipSuccess))
+    return fail(CFR_ENOMEM, std::string("device allocation: ") + hipGetErrorString(e));
+  r.ws_bytes = workspace_bytes(r, nullptr);
+  if ((e = hipMalloc(&r.ws, r.ws_bytes)) != hipSuccess)
+    return fail(CFR_ENOMEM, std::string("workspace allocation: ") + hipGetErrorString(e));
+  carve_workspace(r);
+  if ((e = hipMemset(r.status, 0, sizeof(int32_t))) != hipSuccess) return hipf(e, "status init");
+  return CFR_OK;
+}
+
+template <typename T>
+std::unique_ptr<T[]> host_array(size_t n) {
+  return std::unique_ptr<T[]>(new (std::nothrow) T[n ? n : 1]);
+}
+
+int check_decode_args(cfr_reader* r, const void* x, const void* ids, const void* gw, int batch,
+                      int k, const void* y) {
+  if (!r) return fail(CFR_EINVAL, "reader is NULL");
+  if (!x || !ids || !gw || !y) return fail(CFR_EINVAL, "x, expert_ids, gate_w and y must be non-NULL");
+  if (batch < 1 || batch > r->cfg.max_batch)
+    return fail(CFR_EINVAL, "batch must be in 1..max_batch");
+  if (k < 0 || k > r->ncand) return fail(CFR_EINVAL, "k must be in 0..top*inter");
+  return CFR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t* up,
+                     const uint16_t* down, const uint16_t* router, cfr_reader** out) {
+  clear_error();
+  if (!out) return fail(CFR_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!gate || !up || !down) return fail(CFR_EINVAL, "gate, up and down must be non-NULL");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev)
+    return fail(CFR_EINVAL, "device ordinal not available");
+  DeviceGuard guard(cfg->device);
+  if (!guard.ok) return fail(CFR_EHIP, "cannot select device");
+
+  std::unique_ptr<cfr_reader, void (*)(cfr_reader*)> r(new (std::nothrow) cfr_reader(), free_reader);
+  if (!r) return fail(CFR_ENOMEM, "host allocation");
+  r->cfg = *cfg;
+  init_geometry(*r);
+  ResidentSizes s = resident_sizes(*r);
+
+  // load steps (1), (2), (4) on the host
+  auto w3 = host_array<uint16_t>(s.w3 / 2);
+  auto codes = host_array<uint8_t>(s.codes);
+  auto scales = host_array<uint16_t>(s.scales / 2);
+  auto rho = host_array<uint16_t>(s.scales / 2);
+  auto norms = host_array<float>(s.norms / 4);
+  auto sigma = host_array<float>(s.sigma / 4);
+  if (!w3 || !codes || !scales || !rho || !norms || !sigma)
+    return fail(CFR_ENOMEM, "host staging allocation");
+  rc = pack_host(*cfg, gate, up, down, codes.get(), scales.get(), rho.get(), norms.get(),
+                 w3.get(), sigma.get());
+  if (rc) return rc;
+
+  rc = alloc_resident(*r, router != nullptr);
+  if (rc) return rc;
+  hipError_t e;
+  if ((e = hipMemcpy(r->w3, w3.get(), s.w3, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->codes, codes.get(), s.codes, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->scales, scales.get(), s.scales, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->rho, rho.get(), s.scales, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->norms, norms.get(), s.norms, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->sigma, sigma.get(), s.sigma, hipMemcpyHostToDevice)) != hipSuccess ||
+      (router && (e = hipMemcpy(r->router, router, s.router, hipMemcpyHostToDevice)) != hipSuccess))
+    return hipf(e, "upload");
+  // load step (3) on the device
+  rc = device_lowrank(r.get());
+  if (rc) return rc;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "build");
+  *out = r.release();
+  return CFR_OK;
+}
+
+int cfr_reader_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                      int32_t batch, int32_t k, float* y, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, k, y);
+  if (rc) return rc;
+  DeviceGuard guard(r->cfg.device);
+  return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                            int32_t batch, int32_t k, float* y, float* xrot, uint8_t* sel,
+                            float* ghat, float* vhat, float* score, int32_t* kept, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, k, y);
+  if (rc) return rc;
+  DeviceGuard guard(r->cfg.device);
+  DebugOut dbg;
+  dbg.xrot = xrot;
+  dbg.sel = sel;
+  dbg.ghat = ghat;
+  dbg.vhat = vhat;
+  dbg.score = score;
+  dbg.kept = kept;
+  return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), &dbg);
+}
+
+int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                     int32_t batch, float* y, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, 0, y);
+  if (rc) return rc;
+  DeviceGuard guard(r->cfg.device);
+  return launch_dense(r, x, ids, gw, batch, y, static_cast<hipStream_t>(stream));
+}
+
+int cfr_reader_export(const cfr_reader* r, uint8_t* codes, uint16_t* scales, uint16_t* rho,
+                      float* norms, uint16_t* u, uint16_t* b, float* sigma) {
+  clear_error();
+  if (!r) return fail(CFR_EINVAL, "reader is NULL");
+  DeviceGuard guard(r->cfg.device);
+  ResidentSizes s = resident_sizes(*r);
+  hipError_t e;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "export sync");
+  auto dl = [&](void* dst, const void* src, size_t n) {
+    return dst && n ? hipMemcpy(dst, src, n, hipMemcpyDeviceToHost) : hipSuccess;
+  };
+  if ((e = dl(codes, r->codes, s.codes)) != hipSuccess || (e = dl(scales, r->scales, s.scales)) != hipSuccess ||
+      (e = dl(rho, r->rho, s.scales)) != hipSuccess || (e = dl(norms, r->norms, s.norms)) != hipSuccess ||
+      (e = dl(u, r->u, s.u)) != hipSuccess || (e = dl(b, r->b, s.b)) != hipSuccess ||
+      (e = dl(sigma, r->sigma, s.sigma)) != hipSuccess)
+    return hipf(e, "export");
+  return CFR_OK;
+}
+
+int cfr_reader_clone(const cfr_reader* src, cfr_reader** out) {
+  clear_error();
+  if (!src || !out) return fail(CFR_EINVAL, "src and out must be non-NULL");
+  *out = nullptr;
+  DeviceGuard guard(src->cfg.device);
+  std::unique_ptr<cfr_reader, void (*)(cfr_reader*)> r(new (std::nothrow) cfr_reader(), free_reader);
+  if (!r) return fail(CFR_ENOMEM, "host allocation");
+  r->cfg = src->cfg;
+  init_geometry(*r);
+  int rc = alloc_resident(*r, src->router != nullptr);
+  if (rc) return rc;
+  ResidentSizes s = resident_sizes(*r);
+  hipError_t e;
+  auto cp = [&](void* dst, const void* from, size_t n) {
+    return n ? hipMemcpy(dst, from, n, hipMemcpyDeviceToDevice) : hipSuccess;
+  };
+  if ((e = cp(r->w3, src->w3, s.w3)) != hipSuccess || (e = cp(r->codes, src->codes, s.codes)) != hipSuccess ||
+      (e = cp(r->scales, src->scales, s.scales)) != hipSuccess ||
+      (e = cp(r->rho, src->rho, s.scales)) != hipSuccess ||
+      (e = cp(r->norms, src->norms, s.norms)) != hipSuccess || (e = cp(r->u, src->u, s.u)) != hipSuccess ||
+      (e = cp(r->b, src->b, s.b)) != hipSuccess || (e = cp(r->sigma, src->sigma, s.sigma)) != hipSuccess ||
+      (src->router && (e = cp(r->router, src->router, s.router)) != hipSuccess))
+    return hipf(e, "clone copy");
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "clone");
+  *out = r.release();
+  return CFR_OK;
+}
+
+int cfr_reader_config(const cfr_reader* r, cfr_config* out) {
+  clear_error();
+  if (!r || !out) return fail(CFR_EINVAL, "reader and out must be non-NULL");
+  *out = r->cfg;
+  return CFR_OK;
+}
+
+int cfr_reader_status(cfr_reader* r, int32_t* flags) {
+  clear_error();
+  if (!r || !flags) return fail(CFR_EINVAL, "reader and flags must be non-NULL");
+  DeviceGuard guard(r->cfg.device);
+  hipError_t e;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "status sync");
+  if ((e = hipMemcpy(flags, r->status, sizeof(int32_t), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hipf(e, "status read");
+  if ((e = hipMemset(r->status, 0, sizeof(int32_t))) != hipSuccess) return hipf(e, "status clear");
+  return CFR_OK;
+}
+
+void cfr_reader_free(cfr_reader* r) {
+  if (!r) return;
+  DeviceGuard guard(r->cfg.device);
+  (void)hipDeviceSynchronize();
+  free_reader(r);
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <stdint.h>
+#include <stddef.h>
+
+#include <string>
+
+#include "../../include/cfr.h"
+
+namespace cfr {
+
+constexpr int kBlock = 128;                      // rotation block
+constexpr double kSqrt128 = 11.313708498984761;  // sqrt(128) rounded to the nearest double
+constexpr int kMaxInter = 4096;
+constexpr int kMaxTop = 16;
+constexpr int kMaxRank = 64;
+constexpr int kMaxBatch = 64;
+constexpr int kMaxHidden = 16384;
+
+// Error reporting (thread-local message).
+int fail(int code, const std::string& msg);
+void clear_error();
+
+// Geometry of one sketch unit for I channels: each half (gate, up) holds five
+// codes per byte, padded to a multiple of 16 bytes; the unit is padded to a
+// multiple of 32 bytes (whole sectors).
+inline int half_bytes(int inter) {
+  int lp = (inter + 4) / 5;
+  return (lp + 15) / 16 * 16;
+}
+inline int unit_bytes(int inter) { return (2 * half_bytes(inter) + 31) / 32 * 32; }
+
+int validate_config(const cfr_config* c);
+
+// Host pack (load steps 1, 2 and 4).  Writes into caller buffers; any may be null.
+//   w3: [E][I][3][H] bf16 (gate row, up row, down column) — the resident layout.
+int pack_host(const cfr_config& c, const uint16_t* gate, const uint16_t* up,
+              const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
+              float* norms, uint16_t* w3, float* sigma);
+
+void sign_vector(uint64_t seed, int hidden, float* out);
+uint16_t f64_to_f16_rne(double v);
+double f16_to_f64(uint16_t h);
+
+}  // namespace cfr
+
+// The reader object.  All pointers are device memory on cfg.device unless
+// noted.  Workspace pointers are views into one allocation.
+struct cfr_reader {
+  cfr_config cfg;
+  int nblk, lp, unit, ncand;
+  // resident state
+  uint16_t* w3 = nullptr;      // [E][I][3][H] bf16
+  uint8_t* codes = nullptr;    // [E][nblk][128][unit]
+  uint16_t* scales = nullptr;  // [E][nblk][2][I] fp16
+  uint16_t* rho = nullptr;     // [E][nblk][2][I] fp16
+  float* norms = nullptr;      // [E][I]
+  uint16_t* u = nullptr;       // [H][rank] fp16
+  uint16_t* b = nullptr;       // [E][I][rank] fp16
+  float* sigma = nullptr;      // [H] +1 / -1
+  uint16_t* router = nullptr;  // [E][H] bf16 or null
+  // workspace (sized for cfg.max_batch)
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  float* xrot = nullptr;       // [B][H]
+  uint8_t* sel = nullptr;      // [B][nblk][n_screen]
+  float* part = nullptr;       // [B][top][nblk][2][I]
+  float* ghat = nullptr;       // [B][ncand]
+  float* vhat = nullptr;       // [B][ncand]
+  float* pact = nullptr;       // [B][ncand]  p = phi(ghat) vhat
+  float* score = nullptr;      // [B][ncand]
+  int32_t* kept = nullptr;     // [B][ncand]
+  uint8_t* keptf = nullptr;    // [B][ncand]
+  float* coef = nullptr;       // [B][ncand]  w * a for kept channels
+  float* ypart = nullptr;      // [B][max_chunks][H]
+  float* zpart = nullptr;      // [B][max_zchunks][rank]
+  int32_t* status = nullptr;   // [1]
+  int max_chunks = 0, max_zchunks = 0;
+};

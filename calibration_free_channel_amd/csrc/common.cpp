@@ -1,0 +1,94 @@
+// Host-only parts of the C ABI: errors, config validation, sizes, read
+// accounting and the host pack entry point.  No HIP calls in this file.
+#include <string.h>
+
+#include <string>
+
+#include "cfr_internal.h"
+
+namespace cfr {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+int validate_config(const cfr_config* c) {
+  if (!c) return fail(CFR_EINVAL, "config is NULL");
+  if (c->hidden <= 0 || c->hidden % kBlock != 0)
+    return fail(CFR_EINVAL, "hidden must be a positive multiple of 128");
+  if (c->hidden > kMaxHidden) return fail(CFR_EUNSUPPORTED, "hidden above 16384");
+  if (c->n_experts <= 0) return fail(CFR_EINVAL, "n_experts must be positive");
+  if (c->inter <= 0) return fail(CFR_EINVAL, "inter must be positive");
+  if (c->inter > kMaxInter) return fail(CFR_EUNSUPPORTED, "inter above 4096");
+  if (c->top <= 0 || c->top > c->n_experts) return fail(CFR_EINVAL, "top must be in 1..n_experts");
+  if (c->top > kMaxTop) return fail(CFR_EUNSUPPORTED, "top above 16");
+  if (c->rank < 0 || c->rank > c->hidden) return fail(CFR_EINVAL, "rank must be in 0..hidden");
+  if (c->rank > kMaxRank) return fail(CFR_EUNSUPPORTED, "rank above 64");
+  if (c->n_screen < 1 || c->n_screen > kBlock) return fail(CFR_EINVAL, "n_screen must be in 1..128");
+  if (c->max_batch < 1) return fail(CFR_EINVAL, "max_batch must be at least 1");
+  if (c->max_batch > kMaxBatch) return fail(CFR_EUNSUPPORTED, "max_batch above 64");
+  if (c->device < 0) return fail(CFR_EINVAL, "device must be non-negative");
+  return CFR_OK;
+}
+
+static int64_t sect(int64_t nbytes) { return (nbytes + 31) / 32 * 32; }
+
+}  // namespace cfr
+
+using namespace cfr;
+
+extern "C" {
+
+const char* cfr_last_error(void) { return g_last_error.c_str(); }
+
+int cfr_sizes_of(const cfr_config* c, cfr_sizes* out) {
+  int rc = validate_config(c);
+  if (rc) return rc;
+  if (!out) return fail(CFR_EINVAL, "out is NULL");
+  const int64_t E = c->n_experts, I = c->inter, H = c->hidden, nblk = H / kBlock;
+  out->n_blocks = (int32_t)nblk;
+  out->half_bytes = half_bytes(c->inter);
+  out->unit_bytes = unit_bytes(c->inter);
+  out->n_cand = c->top * c->inter;
+  out->codes_bytes = E * nblk * kBlock * out->unit_bytes;
+  out->scales_count = E * nblk * 2 * I;
+  out->norms_count = E * I;
+  out->u_count = H * c->rank;
+  out->b_count = E * I * c->rank;
+  out->weights_bytes = E * I * 3 * H * 2;
+  return CFR_OK;
+}
+
+int cfr_read_bytes(const cfr_config* c, int32_t k, cfr_read_stats* out) {
+  int rc = validate_config(c);
+  if (rc) return rc;
+  if (!out) return fail(CFR_EINVAL, "out is NULL");
+  const int64_t I = c->inter, H = c->hidden, top = c->top, nblk = H / kBlock;
+  if (k < 0 || k > top * I) return fail(CFR_EINVAL, "k must be in 0..top*inter");
+  out->codes = top * nblk * c->n_screen * sect(unit_bytes(c->inter));
+  out->scales = top * nblk * sect(2 * I * 2);
+  out->norms = top * sect(I * 4);
+  out->exact = (int64_t)k * sect(3 * H * 2);
+  out->b = (top * I - k) * sect((int64_t)c->rank * 2);
+  out->u = sect(H * (int64_t)c->rank * 2);
+  out->total = out->codes + out->scales + out->norms + out->exact + out->b + out->u;
+  out->dense = top * 3 * I * H * 2;
+  return CFR_OK;
+}
+
+int cfr_pack_host(const cfr_config* c, const uint16_t* gate, const uint16_t* up,
+                  const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
+                  float* norms) {
+  clear_error();
+  int rc = validate_config(c);
+  if (rc) return rc;
+  if (!gate || !up || !down) return fail(CFR_EINVAL, "gate, up and down must be non-NULL");
+  return pack_host(*c, gate, up, down, codes, scales, rho, norms, nullptr, nullptr);
+}
+
+}  // extern "C"

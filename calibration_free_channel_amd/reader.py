@@ -1,0 +1,212 @@
+"""Python binding of the reader: argument marshalling around libcfr.so.
+
+Every step of the decode path runs in the library's HIP kernels; this module
+only checks shapes and dtypes, takes device pointers from torch tensors and
+passes the current HIP stream.  There is no fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _lib
+from ._lib import CfrConfig, CfrReadStats, CfrSizes, check, load
+
+DEFAULT_ROT_SEED = 0x5EED_0000_CAFE_F00D
+
+
+@dataclass(frozen=True)
+class Config:
+    hidden: int
+    n_experts: int
+    inter: int
+    top: int
+    rank: int = 32
+    n_screen: int = 80
+    max_batch: int = 1
+    device: int = 0
+    rot_seed: int = DEFAULT_ROT_SEED
+
+    def c(self) -> CfrConfig:
+        return CfrConfig(self.hidden, self.n_experts, self.inter, self.top, self.rank,
+                         self.n_screen, self.max_batch, self.device, self.rot_seed & (2 ** 64 - 1))
+
+
+def sizes(cfg: Config) -> dict:
+    s = CfrSizes()
+    check(load().cfr_sizes_of(ctypes.byref(cfg.c()), ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in CfrSizes._fields_}
+
+
+def read_bytes(cfg: Config, k: int) -> dict:
+    s = CfrReadStats()
+    check(load().cfr_read_bytes(ctypes.byref(cfg.c()), int(k), ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in CfrReadStats._fields_}
+
+
+def _u16(a, shape, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16 or a.shape != tuple(shape):
+        raise ValueError(f"{name}: expected uint16 (bf16 bits) of shape {tuple(shape)}, "
+                         f"got {a.dtype} {a.shape}")
+    return a
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def pack_host(cfg: Config, gate, up, down) -> dict:
+    """Host-only sketch pack and down norms (load steps 1 and 2), no device used."""
+    E, I, H = cfg.n_experts, cfg.inter, cfg.hidden
+    gate = _u16(gate, (E, I, H), "gate")
+    up = _u16(up, (E, I, H), "up")
+    down = _u16(down, (E, H, I), "down")
+    sz = sizes(cfg)
+    nblk = sz["n_blocks"]
+    codes = np.empty((E, nblk, 128, sz["unit_bytes"]), dtype=np.uint8)
+    scales = np.empty((E, nblk, 2, I), dtype=np.uint16)
+    rho = np.empty((E, nblk, 2, I), dtype=np.uint16)
+    norms = np.empty((E, I), dtype=np.float32)
+    check(load().cfr_pack_host(ctypes.byref(cfg.c()), _ptr(gate), _ptr(up), _ptr(down),
+                               _ptr(codes), _ptr(scales), _ptr(rho), _ptr(norms)))
+    return {"codes": codes, "scales": scales, "rho": rho, "norms": norms}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_tensor(t, dtype, shape, name, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.device.index != device:
+        raise ValueError(f"{name}: on device {t.device}, reader is on device {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Reader:
+    """One built layer.  Owns device memory until close()."""
+
+    def __init__(self, handle: ctypes.c_void_p, cfg: Config):
+        self._h = handle
+        self.cfg = cfg
+        self._sizes = sizes(cfg)
+
+    # -- construction ------------------------------------------------------
+    @classmethod
+    def build(cls, cfg: Config, gate, up, down, router=None) -> "Reader":
+        """Load-time work (rotation, ternary pack, norms, SVD, transpose) for one layer."""
+        E, I, H = cfg.n_experts, cfg.inter, cfg.hidden
+        gate = _u16(gate, (E, I, H), "gate")
+        up = _u16(up, (E, I, H), "up")
+        down = _u16(down, (E, H, I), "down")
+        if router is not None:
+            router = _u16(router, (E, H), "router")
+        h = ctypes.c_void_p()
+        check(load().cfr_build_reader(ctypes.byref(cfg.c()), _ptr(gate), _ptr(up), _ptr(down),
+                                      _ptr(router), ctypes.byref(h)))
+        return cls(h, cfg)
+
+    def clone(self) -> "Reader":
+        h = ctypes.c_void_p()
+        check(load().cfr_reader_clone(self._h, ctypes.byref(h)))
+        return Reader(h, self.cfg)
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            load().cfr_reader_free(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- decode --------------------------------------------------------------
+    def _stream(self, stream):
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream(self.cfg.device)
+        return ctypes.c_void_p(s.cuda_stream)
+
+    def _args(self, x, ids, w):
+        torch = _torch()
+        if x.dim() != 2:
+            raise ValueError("x must be [batch, hidden]")
+        B = x.shape[0]
+        c = self.cfg
+        return (B, _dev_tensor(x, torch.float32, (B, c.hidden), "x", c.device),
+                _dev_tensor(ids, torch.int32, (B, c.top), "expert_ids", c.device),
+                _dev_tensor(w, torch.float32, (B, c.top), "gate_w", c.device))
+
+    def decode(self, x, expert_ids, gate_w, k: int, out=None, stream=None):
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        if out is None:
+            out = torch.empty((B, self.cfg.hidden), dtype=torch.float32, device=x.device)
+        py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
+        check(load().cfr_reader_decode(self._h, px, pi, pw, B, int(k), py, self._stream(stream)))
+        return out
+
+    def decode_debug(self, x, expert_ids, gate_w, k: int, stream=None) -> dict:
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        c, dev = self.cfg, x.device
+        nc = c.top * c.inter
+        o = {
+            "y": torch.empty((B, c.hidden), dtype=torch.float32, device=dev),
+            "xrot": torch.empty((B, c.hidden), dtype=torch.float32, device=dev),
+            "sel": torch.empty((B, c.hidden // 128, c.n_screen), dtype=torch.uint8, device=dev),
+            "ghat": torch.empty((B, nc), dtype=torch.float32, device=dev),
+            "vhat": torch.empty((B, nc), dtype=torch.float32, device=dev),
+            "score": torch.empty((B, nc), dtype=torch.float32, device=dev),
+            "kept": torch.empty((B, max(int(k), 1)), dtype=torch.int32, device=dev),
+        }
+        p = {n: ctypes.c_void_p(t.data_ptr()) for n, t in o.items()}
+        check(load().cfr_reader_decode_debug(self._h, px, pi, pw, B, int(k), p["y"], p["xrot"],
+                                             p["sel"], p["ghat"], p["vhat"], p["score"],
+                                             p["kept"], self._stream(stream)))
+        o["kept"] = o["kept"][:, :int(k)]
+        return o
+
+    def dense(self, x, expert_ids, gate_w, out=None, stream=None):
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        if out is None:
+            out = torch.empty((B, self.cfg.hidden), dtype=torch.float32, device=x.device)
+        py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
+        check(load().cfr_dense_decode(self._h, px, pi, pw, B, py, self._stream(stream)))
+        return out
+
+    # -- state ----------------------------------------------------------------
+    def export(self) -> dict:
+        c, sz = self.cfg, self._sizes
+        E, I, H, nblk = c.n_experts, c.inter, c.hidden, sz["n_blocks"]
+        o = {
+            "codes": np.empty((E, nblk, 128, sz["unit_bytes"]), dtype=np.uint8),
+            "scales": np.empty((E, nblk, 2, I), dtype=np.uint16),
+            "rho": np.empty((E, nblk, 2, I), dtype=np.uint16),
+            "norms": np.empty((E, I), dtype=np.float32),
+            "U": np.empty((H, c.rank), dtype=np.uint16),
+            "b": np.empty((E, I, c.rank), dtype=np.uint16),
+            "sigma": np.empty((H,), dtype=np.float32),
+        }
+        check(load().cfr_reader_export(self._h, *(_ptr(o[n]) for n in
+                                                  ("codes", "scales", "rho", "norms", "U", "b",
+                                                   "sigma"))))
+        return o
+
+    def status(self) -> int:
+        f = ctypes.c_int32()
+        check(load().cfr_reader_status(self._h, ctypes.byref(f)))
+        return f.value

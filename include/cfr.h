@@ -1,0 +1,199 @@
+/*
+ * cfr.h — C ABI of the calibration-free MoE channel-selection reader for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The reader replaces the routed-expert gated-MLP block of one MoE layer at
+ * small-batch decode.  Per token it (1) rotates x by a block-128 randomized
+ * Hadamard matrix and keeps, per block, the n_screen coordinates of largest
+ * |Rx|; (2) estimates every candidate channel's gate/up activations from a
+ * packed ternary sketch of the rotated rows, read only at those coordinates;
+ * (3) scores channels in output units, s_j = w_j ||d_j|| |phi(g_hat_j) v_hat_j|,
+ * and keeps exactly the top k across all routed experts; (4) computes kept
+ * channels exactly from native BF16 rows and adds a rank-`rank` recovery term
+ * U sum_{skipped} w_j b_j p_j.
+ *
+ * Sources (cited by page title and section):
+ *   [zh §S] Chinese summary page of "Channel Selection for Mixture-of-Experts
+ *           Decoding Needs No Calibration Data" (paper.rainbus.top), section S.
+ *   [ko §S] Korean summary page of the same paper, "MoE 채널 선택은
+ *           캘리브레이션 없이 top-k로 충분하다" (onedev.kr), section S.
+ *
+ * Conventions for every call:
+ *   - Return 0 (CFR_OK) on success or a negative CFR_E* code; a thread-local
+ *     message is then available from cfr_last_error().  No C++ exception
+ *     crosses this boundary.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP
+ *     device memory on the reader's device (for example a torch tensor's
+ *     data_ptr()).  The caller owns every pointer it passes; the library
+ *     owns the reader and all memory inside it.
+ *   - Decode-time calls enqueue work on the caller's HIP stream (`stream`,
+ *     a hipStream_t; NULL = the null stream), never synchronise the host
+ *     and never allocate.  Calls that share a reader must be ordered on one
+ *     stream: the reader's workspace is reused by every call.
+ */
+#ifndef CFR_H
+#define CFR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CFR_OK 0
+#define CFR_EINVAL (-1)        /* bad argument (pointer, size, range)            */
+#define CFR_ENOMEM (-2)        /* host or device allocation failed               */
+#define CFR_EHIP (-3)          /* a HIP runtime call failed                      */
+#define CFR_EUNSUPPORTED (-4)  /* shape outside what the kernels support         */
+#define CFR_ESOLVER (-5)       /* the load-time eigensolver failed               */
+
+typedef struct cfr_reader cfr_reader; /* opaque; owned by the library */
+
+/* Layer shape and method constants, fixed at build time. */
+typedef struct cfr_config {
+  int32_t hidden;     /* H: model width, a multiple of 128, at most 16384             */
+  int32_t n_experts;  /* E: experts in the layer                                        */
+  int32_t inter;      /* I: channels per expert (expert intermediate size), 1..4096     */
+  int32_t top;        /* routed experts per token, 1..16 and <= E                       */
+  int32_t rank;       /* recovery rank, 0..64 (the pages use 32)                        */
+  int32_t n_screen;   /* coordinates screened per 128-block, 1..128 (the pages use 80) */
+  int32_t max_batch;  /* largest batch a decode call may pass, 1..64                    */
+  int32_t device;     /* HIP device ordinal the reader lives on                         */
+  uint64_t rot_seed;  /* SplitMix64 seed of the rotation's sign vector                 */
+} cfr_config;
+
+/* Buffer sizes and layout constants implied by a config (see cfr_sizes_of()). */
+typedef struct cfr_sizes {
+  int32_t n_blocks;      /* H / 128                                                    */
+  int32_t half_bytes;    /* Lp: bytes of one half (gate or up) of a sketch unit        */
+  int32_t unit_bytes;    /* bytes of one sketch unit (one expert, block, coordinate)   */
+  int32_t n_cand;        /* candidate channels per token = top * I                     */
+  int64_t codes_bytes;   /* E * n_blocks * 128 * unit_bytes                            */
+  int64_t scales_count;  /* E * n_blocks * 2 * I   (fp16 scales; rho has the same)     */
+  int64_t norms_count;   /* E * I                  (fp32)                              */
+  int64_t u_count;       /* H * rank               (fp16)                              */
+  int64_t b_count;       /* E * I * rank           (fp16)                              */
+  int64_t weights_bytes; /* E * I * 3 * H * 2      (native BF16 rows, resident)        */
+} cfr_sizes;
+
+/* Counted reads of one decode, in whole 32-byte sectors ([zh §前置知识 /
+ * 显存带宽受限的解码]: every touched sector is charged). */
+typedef struct cfr_read_stats {
+  int64_t codes;   /* sketch codes of the screened coordinates                    */
+  int64_t scales;  /* fp16 scales of the routed experts                            */
+  int64_t norms;   /* ||d_j|| of the routed experts                                */
+  int64_t exact;   /* native gate row, up row and transposed down row, k channels */
+  int64_t b;       /* recovery coefficients of the skipped channels                */
+  int64_t u;       /* the recovery basis U                                         */
+  int64_t total;   /* sum of the above                                             */
+  int64_t dense;   /* all BF16 bytes of the routed experts (the dense block)       */
+} cfr_read_stats;
+
+/* Fill *out from *cfg.  Validates cfg.  Host only; no device work. */
+int cfr_sizes_of(const cfr_config* cfg, cfr_sizes* out);
+
+/* Counted reads per token for budget k ([zh §核心方法] read composition;
+ * [zh §前置知识 / 显存带宽受限的解码]).  Host only. */
+int cfr_read_bytes(const cfr_config* cfg, int32_t k, cfr_read_stats* out);
+
+/*
+ * Load-time work for one layer ([zh §方法步骤详情] load steps (1)-(4);
+ * [ko §어떻게 쓰나]):
+ *   (1) rotate every gate/up row per 128-block and store TWN ternary codes,
+ *       an FP16 scale and the block's mean squared quantisation error rho;
+ *   (2) ||d_j|| of every down column;
+ *   (3) the top-`rank` left singular vectors U of the stacked down columns
+ *       of all experts (fp64 Gram + symmetric eigensolver on the device) and
+ *       b_j = U^T d_j;
+ *   (4) the down projection transposed, so a channel's gate row, up row and
+ *       down column sit together.
+ * Inputs (host, BF16 bit patterns, read only during the call):
+ *   gate, up: [E][I][H]   down: [E][H][I]   router: [E][H] or NULL.
+ * On success *out owns device memory for the native weights, the sketch,
+ * norms, U, b, the router and a decode workspace sized for max_batch.
+ * Errors: CFR_EINVAL (config/pointers), CFR_EUNSUPPORTED, CFR_ENOMEM,
+ * CFR_EHIP, CFR_ESOLVER.  *out is left NULL on failure.
+ */
+int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t* up,
+                     const uint16_t* down, const uint16_t* router, cfr_reader** out);
+
+/*
+ * Decode one batch ([zh §方法步骤详情] decode steps (1)-(4); [zh §核心方法];
+ * [ko §어떻게 쓰나]).  All arrays are device memory:
+ *   x          fp32  [batch][H]     token hidden states (not rotated)
+ *   expert_ids int32 [batch][top]   routed experts, distinct per token, in [0,E)
+ *   gate_w     fp32  [batch][top]   routing weight of each routed expert
+ *   y          fp32  [batch][H]     output, written (not accumulated)
+ * Each token keeps its own exact top-k over its top*I candidates
+ * (0 <= k <= top*I; k = top*I keeps all and skips recovery; k = 0 returns the
+ * recovery term alone).  Ties in any ranking go to the lower index.
+ * Out-of-range expert ids are clamped into [0,E) and recorded in the
+ * reader's status word (cfr_reader_status); ids are not otherwise checked.
+ * Errors: CFR_EINVAL (null pointer, batch outside 1..max_batch, k outside
+ * 0..top*I), CFR_EHIP (launch failure).
+ */
+int cfr_reader_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                      const float* gate_w, int32_t batch, int32_t k, float* y, void* stream);
+
+/*
+ * Same computation as cfr_reader_decode, also copying the intermediates to
+ * the caller's device buffers (any may be NULL):
+ *   xrot  fp32  [batch][H]              H_128 (sigma * x) per block, before the 1/sqrt(128)
+ *   sel   uint8 [batch][H/128][n_screen] screened coordinates per block, ascending
+ *   ghat, vhat, score  fp32 [batch][top*I]  candidate c = slot*I + j
+ *   kept  int32 [batch][k]              kept candidates, ascending
+ * For tests and measurement; not on the fast path.
+ */
+int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                            const float* gate_w, int32_t batch, int32_t k, float* y,
+                            float* xrot, uint8_t* sel, float* ghat, float* vhat,
+                            float* score, int32_t* kept, void* stream);
+
+/*
+ * The dense routed-expert gated MLP on the same resident BF16 weights
+ * ([zh §前置知识 / 门控MLP与通道]): y = sum_s w_s D_e (phi(G_e x) * V_e x).
+ * The baseline the reader is measured against.  Same argument rules as
+ * cfr_reader_decode.
+ */
+int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                     const float* gate_w, int32_t batch, float* y, void* stream);
+
+/* Copy the built state to host buffers (any may be NULL); sizes from
+ * cfr_sizes_of.  codes uint8, scales/rho/U/b fp16 bits, norms fp32,
+ * sigma fp32 (+1/-1).  Synchronises the reader's device. */
+int cfr_reader_export(const cfr_reader* r, uint8_t* codes, uint16_t* scales, uint16_t* rho,
+                      float* norms, uint16_t* u, uint16_t* b, float* sigma);
+
+/*
+ * Host-only load steps (1) and (2): the sketch (codes, scales, rho) and the
+ * down norms, exactly as cfr_build_reader computes them, into host buffers
+ * sized by cfr_sizes_of (any output may be NULL).  No device is touched, so
+ * the pack can be checked on a machine without a GPU.
+ */
+int cfr_pack_host(const cfr_config* cfg, const uint16_t* gate, const uint16_t* up,
+                  const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
+                  float* norms);
+
+/* A second reader with the same configuration and a byte-identical copy of
+ * every resident buffer at new device addresses (so benchmark loops can
+ * cycle through layers the caches have not seen).  Fresh workspace. */
+int cfr_reader_clone(const cfr_reader* src, cfr_reader** out);
+
+/* Config the reader was built with. */
+int cfr_reader_config(const cfr_reader* r, cfr_config* out);
+
+/* Read (and clear) the reader's device status word: bit 0 = an expert id
+ * was out of range and clamped.  Synchronises the reader's device. */
+int cfr_reader_status(cfr_reader* r, int32_t* flags);
+
+/* Release the reader and all its device memory.  NULL-safe. */
+void cfr_reader_free(cfr_reader* r);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* cfr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFR_H */

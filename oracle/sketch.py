@@ -83,12 +83,15 @@ def _pack_half(codes_ci: np.ndarray, lp: int) -> np.ndarray:
     """codes [..., I] in {-1,0,1} -> bytes [..., lp] (base 3, five codes per byte)."""
     inter = codes_ci.shape[-1]
     nbytes = -(-inter // 5)
-    t = np.ones(codes_ci.shape[:-1] + (nbytes * 5,), dtype=np.int64)  # code 0 -> digit 1
-    t[..., :inter] = codes_ci.astype(np.int64) + 1
+    # digits fit in uint8 and so does every byte (at most 2 * 121 = 242)
+    t = np.empty(codes_ci.shape[:-1] + (nbytes * 5,), dtype=np.uint8)
+    t[..., inter:] = 1  # code 0 -> digit 1
+    t[..., :inter] = (codes_ci + 1).astype(np.uint8)
     t = t.reshape(codes_ci.shape[:-1] + (nbytes, 5))
-    q = t[..., 0] + 3 * t[..., 1] + 9 * t[..., 2] + 27 * t[..., 3] + 81 * t[..., 4]
+    q = t[..., 0] + np.uint8(3) * t[..., 1] + np.uint8(9) * t[..., 2] + \
+        np.uint8(27) * t[..., 3] + np.uint8(81) * t[..., 4]
     out = np.zeros(codes_ci.shape[:-1] + (lp,), dtype=np.uint8)
-    out[..., :nbytes] = q.astype(np.uint8)
+    out[..., :nbytes] = q
     return out
 
 
