@@ -228,6 +228,32 @@ int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* ids, c
   return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), &dbg);
 }
 
+int cfr_reader_decode_profile(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                              int32_t batch, int32_t k, float* y, float* stage_us, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, k, y);
+  if (rc) return rc;
+  if (!stage_us) return fail(CFR_EINVAL, "stage_us is NULL");
+  DeviceGuard guard(r->cfg.device);
+  hipEvent_t ev[CFR_NUM_STAGES + 1] = {};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i <= CFR_NUM_STAGES && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (e == hipSuccess) {
+    rc = launch_decode(r, x, ids, gw, batch, k, y, st, nullptr, ev);
+    if (rc == CFR_OK) e = hipStreamSynchronize(st);
+    for (int i = 0; i < CFR_NUM_STAGES && e == hipSuccess && rc == CFR_OK; ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+      stage_us[i] = 1000.f * ms;
+    }
+  }
+  for (int i = 0; i <= CFR_NUM_STAGES; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);
+  if (rc) return rc;
+  if (e != hipSuccess) return hipf(e, "profile events");
+  return CFR_OK;
+}
+
 int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
                      int32_t batch, float* y, void* stream) {
   int rc = check_decode_args(r, x, ids, gw, batch, 0, y);

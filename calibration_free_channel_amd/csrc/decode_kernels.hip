@@ -418,7 +418,7 @@ static int hip_fail(hipError_t e, const char* what) {
 }
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
-                  int k, float* y, hipStream_t st, const DebugOut* dbg) {
+                  int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev) {
   const cfr_config& c = r->cfg;
   const int H = c.hidden, E = c.n_experts, I = c.inter, top = c.top, nblk = r->nblk;
   const int ncand = r->ncand;
@@ -428,33 +428,47 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   if (G > c.n_screen) G = c.n_screen;
   const size_t lds = (size_t)G * D * 20 * sizeof(float);
 
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], st);
+  };
+  mark(0);
   k_rotate_select<<<dim3(nblk, batch), 128, 0, st>>>(x, r->sigma, r->xrot, r->sel, H, nblk,
                                                      c.n_screen);
+  mark(1);
   k_screen<<<dim3(nblk, top, batch), G * D, lds, st>>>(r->codes, r->scales, r->xrot, r->sel, ids,
                                                        r->part, r->status, H, E, I, top, nblk,
                                                        c.n_screen, r->lp, r->unit, G);
+  mark(2);
   const int nsc = batch * ncand;
   k_score<<<(nsc + 255) / 256, 256, 0, st>>>(r->part, r->norms, ids, gw, r->ghat, r->vhat,
                                              r->pact, r->score, r->status, E, I, top, nblk, ncand,
                                              batch);
+  mark(3);
   k_topk<<<batch, 1024, 0, st>>>(r->score, r->kept, r->keptf, ncand, k);
+  mark(4);
   int nchunks = 0, nz = 0;
   if (k > 0) {
     nchunks = (k + kDownChunk - 1) / kDownChunk;
     k_exact_act<<<dim3((k + 3) / 4, batch), 256, 0, st>>>(r->w3, x, r->kept, ids, gw, r->coef,
                                                           r->status, H, E, I, top, ncand, k);
+  }
+  mark(5);
+  if (k > 0) {
     k_down_partial<<<dim3((H + kDownSlice - 1) / kDownSlice, nchunks, batch), 256, 0, st>>>(
         r->w3, r->kept, ids, r->coef, r->ypart, r->status, H, E, I, top, ncand, k, r->max_chunks);
   }
+  mark(6);
   if (k < ncand && c.rank > 0) {
     nz = (ncand + kZChunk - 1) / kZChunk;
     k_recover_partial<<<dim3(nz, batch), 256, 0, st>>>(r->b, r->keptf, r->pact, ids, gw, r->zpart,
                                                         r->status, E, I, top, ncand, c.rank,
                                                         r->max_zchunks);
   }
+  mark(7);
   k_finalize<<<dim3((H + 255) / 256, batch), 256, 0, st>>>(r->ypart, r->zpart, r->u, y, H, c.rank,
                                                            nchunks, nz, r->max_chunks,
                                                            r->max_zchunks);
+  mark(8);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (dbg) {

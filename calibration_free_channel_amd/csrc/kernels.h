@@ -18,7 +18,8 @@ struct DebugOut {
 };
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
-                  int k, float* y, hipStream_t stream, const DebugOut* dbg);
+                  int k, float* y, hipStream_t stream, const DebugOut* dbg,
+                  hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t stream);
 

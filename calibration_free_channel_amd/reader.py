@@ -179,6 +179,23 @@ class Reader:
         o["kept"] = o["kept"][:, :int(k)]
         return o
 
+    STAGES = ("rotate_select", "screen", "score", "topk", "exact_gate_up", "exact_down",
+              "recovery_z", "finalize")
+
+    def decode_profile(self, x, expert_ids, gate_w, k: int, out=None, stream=None) -> dict:
+        """Decode with an event after every stage; returns {stage: microseconds}.
+
+        Synchronises the host; for measurement only."""
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        if out is None:
+            out = torch.empty((B, self.cfg.hidden), dtype=torch.float32, device=x.device)
+        py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
+        us = (ctypes.c_float * len(self.STAGES))()
+        check(load().cfr_reader_decode_profile(self._h, px, pi, pw, B, int(k), py, us,
+                                               self._stream(stream)))
+        return dict(zip(self.STAGES, list(us)))
+
     def dense(self, x, expert_ids, gate_w, out=None, stream=None):
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)

@@ -158,6 +158,23 @@ int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* expert
 int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
                      const float* gate_w, int32_t batch, float* y, void* stream);
 
+/* Stages of the decode path, in launch order; cfr_reader_decode_profile
+ * reports one duration per stage. */
+#define CFR_NUM_STAGES 8
+/* 0 rotate+select, 1 screen, 2 score, 3 top-k, 4 exact gate/up,
+ * 5 exact down, 6 recovery z, 7 finalize (sum partials + U z) */
+
+/*
+ * Measurement entry: the same computation as cfr_reader_decode with a HIP
+ * event recorded on `stream` after every stage; waits for the stream and
+ * writes each stage's duration in microseconds to stage_us (host,
+ * CFR_NUM_STAGES floats; a stage that did not run reports 0).  Not for the
+ * fast path: it synchronises the host.
+ */
+int cfr_reader_decode_profile(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                              const float* gate_w, int32_t batch, int32_t k, float* y,
+                              float* stage_us, void* stream);
+
 /* Copy the built state to host buffers (any may be NULL); sizes from
  * cfr_sizes_of.  codes uint8, scales/rho/U/b fp16 bits, norms fp32,
  * sigma fp32 (+1/-1).  Synchronises the reader's device. */
