@@ -189,14 +189,11 @@ def main():
 
     main_r = res[k_main]
     rb = main_r["bytes"]
-    # algorithmic bytes of each stage per launch (one token)
+    # algorithmic bytes of each kernel per launch (one token)
     stage_bytes = {
-        "screen": rb["codes"] + rb["scales"],
-        "score": rb["norms"],
-        "exact_gate_up": k_main * 2 * s.hidden * 2,
-        "exact_down": k_main * s.hidden * 2,
-        "recovery_z": rb["b"],
-        "finalize": rb["u"],
+        "screen_score": rb["codes"] + rb["scales"] + rb["norms"],
+        "select_exact": k_main * 2 * s.hidden * 2 + rb["b"],
+        "down_recover": k_main * s.hidden * 2 + rb["u"],
     }
     dom = max(stage_bytes, key=lambda n: main_r["stages"].get(n, 0.0))
     dom_us = main_r["stages"][dom]

@@ -38,22 +38,18 @@ T* carve(char*& p, size_t count) {
   return out;
 }
 
-size_t workspace_bytes(const cfr_reader& r, size_t* layout) {
+size_t workspace_bytes(const cfr_reader& r) {
   const cfr_config& c = r.cfg;
   const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
   auto rnd = [](size_t n) { return (n + 255) / 256 * 256; };
   size_t tot = 0;
-  tot += rnd(sizeof(float) * B * H);                              // xrot
-  tot += rnd(B * r.nblk * c.n_screen);                            // sel
-  tot += rnd(sizeof(float) * B * c.top * r.nblk * 2 * c.inter);   // part
-  tot += 4 * rnd(sizeof(float) * B * nc);                         // ghat vhat pact score
-  tot += rnd(sizeof(int32_t) * B * nc);                           // kept
-  tot += rnd(B * nc);                                             // keptf
-  tot += rnd(sizeof(float) * B * nc);                             // coef
-  tot += rnd(sizeof(float) * B * r.max_chunks * H);               // ypart
-  tot += rnd(sizeof(float) * B * r.max_zchunks * (c.rank > 0 ? c.rank : 1));  // zpart
-  tot += 256;                                                     // status
-  (void)layout;
+  tot += rnd(sizeof(float) * B * H);                          // xrot
+  tot += rnd(B * r.nblk * c.n_screen);                        // sel
+  tot += 4 * rnd(sizeof(float) * B * nc);                     // ghat vhat pact score
+  tot += 2 * rnd(sizeof(int32_t) * B * nc);                   // kept rowidx
+  tot += rnd(sizeof(float) * B * nc);                         // coef
+  tot += rnd(sizeof(float) * r.zrows * (c.rank > 0 ? c.rank : 1));  // zpart
+  tot += 256;                                                 // status
   return tot;
 }
 
@@ -63,16 +59,14 @@ void carve_workspace(cfr_reader& r) {
   char* p = static_cast<char*>(r.ws);
   r.xrot = carve<float>(p, B * H);
   r.sel = carve<uint8_t>(p, B * r.nblk * c.n_screen);
-  r.part = carve<float>(p, B * c.top * r.nblk * 2 * c.inter);
   r.ghat = carve<float>(p, B * nc);
   r.vhat = carve<float>(p, B * nc);
   r.pact = carve<float>(p, B * nc);
   r.score = carve<float>(p, B * nc);
   r.kept = carve<int32_t>(p, B * nc);
-  r.keptf = carve<uint8_t>(p, B * nc);
+  r.rowidx = carve<int32_t>(p, B * nc);
   r.coef = carve<float>(p, B * nc);
-  r.ypart = carve<float>(p, B * r.max_chunks * H);
-  r.zpart = carve<float>(p, B * r.max_zchunks * (c.rank > 0 ? c.rank : 1));
+  r.zpart = carve<float>(p, r.zrows * (c.rank > 0 ? c.rank : 1));
   r.status = carve<int32_t>(p, 1);
 }
 
@@ -90,8 +84,7 @@ void init_geometry(cfr_reader& r) {
   r.lp = half_bytes(r.cfg.inter);
   r.unit = unit_bytes(r.cfg.inter);
   r.ncand = r.cfg.top * r.cfg.inter;
-  r.max_chunks = (r.ncand + 31) / 32;
-  r.max_zchunks = (r.ncand + 255) / 256;
+  r.zrows = zpart_rows(r.cfg);
 }
 
 struct ResidentSizes {
@@ -117,7 +110,9 @@ int alloc_resident(cfr_reader& r, bool with_router) {
   ResidentSizes s = resident_sizes(r);
   hipError_t e;
   auto al = [&](void** p, size_t n) { return hipMalloc(p, n ? n : 256); };
-  if ((e = al((void**)&r.w3, s.w3)) != hipSuccess || (e = al((void**)&r.codes, s.codes)) != hipSuccess ||
+  // the screen kernel reads whole dwords around its byte slice: up to 19
+  // bytes past the last unit, so the codes allocation carries a tail pad
+  if ((e = al((void**)&r.w3, s.w3)) != hipSuccess || (e = al((void**)&r.codes, s.codes + 64)) != hipSuccess ||
       (e = al((void**)&r.scales, s.scales)) != hipSuccess ||
       (e = al((void**)&r.rho, s.scales)) != hipSuccess ||
       (e = al((void**)&r.norms, s.norms)) != hipSuccess ||
@@ -125,7 +120,7 @@ int alloc_resident(cfr_reader& r, bool with_router) {
       (e = al((void**)&r.sigma, s.sigma)) != hipSuccess ||
       (with_router && (e = al((void**)&r.router, s.router)) != hipSuccess))
     return fail(CFR_ENOMEM, std::string("device allocation: ") + hipGetErrorString(e));
-  r.ws_bytes = workspace_bytes(r, nullptr);
+  r.ws_bytes = workspace_bytes(r);
   if ((e = hipMalloc(&r.ws, r.ws_bytes)) != hipSuccess)
     return fail(CFR_ENOMEM, std::string("workspace allocation: ") + hipGetErrorString(e));
   carve_workspace(r);
@@ -170,6 +165,8 @@ int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t
   if (!r) return fail(CFR_ENOMEM, "host allocation");
   r->cfg = *cfg;
   init_geometry(*r);
+  if (max_lds_needed(*cfg) > kMaxLds)
+    return fail(CFR_EUNSUPPORTED, "hidden, inter and top too large for one workgroup's LDS");
   ResidentSizes s = resident_sizes(*r);
 
   // load steps (1), (2), (4) on the host

@@ -63,18 +63,16 @@ struct cfr_reader {
   // workspace (sized for cfg.max_batch)
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  float* xrot = nullptr;       // [B][H]
-  uint8_t* sel = nullptr;      // [B][nblk][n_screen]
-  float* part = nullptr;       // [B][top][nblk][2][I]
+  float* xrot = nullptr;       // [B][H]   H_128 (sigma x) per block (debug copy only)
+  uint8_t* sel = nullptr;      // [B][nblk][n_screen] (debug copy only)
   float* ghat = nullptr;       // [B][ncand]
   float* vhat = nullptr;       // [B][ncand]
   float* pact = nullptr;       // [B][ncand]  p = phi(ghat) vhat
   float* score = nullptr;      // [B][ncand]
-  int32_t* kept = nullptr;     // [B][ncand]
-  uint8_t* keptf = nullptr;    // [B][ncand]
-  float* coef = nullptr;       // [B][ncand]  w * a for kept channels
-  float* ypart = nullptr;      // [B][max_chunks][H]
-  float* zpart = nullptr;      // [B][max_zchunks][rank]
+  int32_t* kept = nullptr;     // [B][ncand]  kept candidates by rank
+  int32_t* rowidx = nullptr;   // [B][ncand]  e*I + j of each kept rank
+  float* coef = nullptr;       // [B][ncand]  w * a of each kept rank
+  float* zpart = nullptr;      // [zrows][rank]  partial recovery vectors
   int32_t* status = nullptr;   // [1]
-  int max_chunks = 0, max_zchunks = 0;
+  size_t zrows = 0;
 };

@@ -2,21 +2,36 @@
 //
 // Per token and layer ([zh §方法步骤详情] decode steps (1)-(4); [zh §核心方法];
 // [ko §어떻게 쓰나]; zh/ko = the Chinese/Korean summary pages of "Channel
-// Selection for Mixture-of-Experts Decoding Needs No Calibration Data"):
-//   k_rotate_select   v = H_128 (sigma * x) per block (float32 butterfly) and
-//                     the n_screen coordinates of largest |v| per block
-//   k_screen          per (token, routed slot, block): sum over screened
-//                     coordinates of code * v, times the block's fp16 scale
-//   k_score           g_hat, v_hat (sum over blocks, / sqrt 128), p = silu(g_hat) v_hat,
-//                     s = w ||d|| |p|
-//   k_topk            exact top-k per token: radix select on the score bits,
-//                     ties to the lower candidate index, ascending compaction
-//   k_exact_act       kept channels: a = silu(g.x) (v.x) from native BF16 rows
-//   k_down_partial    partial y over chunks of kept channels (transposed down rows)
-//   k_recover_partial partial z = sum over skipped of w p b
-//   k_finalize        y = sum of partials + U z
-// The whole path is HBM-bandwidth bound at batch 1 (about 2 flops per byte),
-// so it uses vector ALU and wave reductions, not matrix cores.
+// Selection for Mixture-of-Experts Decoding Needs No Calibration Data"), three
+// kernels separated by the only two global dependencies of the method:
+//
+//   A  k_screen_score   rotate x (float32 butterfly, H_128 sigma x per block),
+//                       pick the n_screen coordinates of largest |v| per block
+//                       (LDS radix select), read the codes of those coordinates
+//                       for a slice of channels of one routed expert, and emit
+//                       g_hat, v_hat, p = silu(g_hat) v_hat and the output-unit
+//                       score s = w ||d|| |p| of every channel in the slice.
+//   B  k_select_exact   every workgroup finds the exact top-k threshold of its
+//                       token from all scores (radix select, ties to the lower
+//                       candidate index), takes its share of the kept channels,
+//                       computes a_j = silu(g_j.x)(v_j.x) from the native BF16
+//                       rows and w a_j, and a partial recovery vector
+//                       z = sum over its skipped candidates of w p b.
+//   C  k_down_recover   per hidden slice: y = sum over kept of (w a_j) d_j
+//                       (transposed down rows) + U z.
+//
+// Each workgroup of A owns whole channels (all blocks, all screened
+// coordinates), so no partial sums cross workgroups before the top-k.
+// Cross-workgroup handoff goes through kernel boundaries: on MI355X a kernel
+// boundary costs less than an in-kernel grid barrier, whose agent-scope
+// release has to write back every XCD's L2.
+//
+// Workgroups are mapped XCD-aware: dispatch places workgroup i on XCD i % 8,
+// so work item (i % 8) * per_xcd + i / 8 gives each XCD a contiguous range of
+// items.  In A that puts all slices of one routed expert on one XCD (its L2
+// then fetches each 32-byte sector of a sketch unit once); in C adjacent
+// hidden slices of a row land in the same L2.  The mapping only affects
+// performance, never correctness.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -26,11 +41,8 @@ namespace cfr {
 namespace {
 
 constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
-constexpr int kDownChunk = 32;    // kept channels per down-projection work item
-constexpr int kDownSlice = 512;   // hidden units per down-projection work item
-constexpr int kZChunk = 256;      // candidates per recovery work item
-
-__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+constexpr int kThreads = 256;
+constexpr int kMaxS = 13;  // bytes per half handled by one screen workgroup
 
 __device__ __forceinline__ float f16f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -47,431 +59,674 @@ __device__ __forceinline__ int clamp_expert(int e, int E, int32_t* status) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-// Inclusive scan of one int per thread over a 1024-thread block (16 waves).
-__device__ int block_scan_1024(int v, int* sh /* >= 16 ints */) {
+// Inclusive prefix sum over a 256-thread block (4 waves); sh >= 4 ints.
+__device__ __forceinline__ int block_scan_256(int v, int* sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     int o = __shfl_up(v, off, 64);
     if (lane >= off) v += o;
   }
   if (lane == 63) sh[w] = v;
   __syncthreads();
-  if (w == 0) {
-    int t = lane < 16 ? sh[lane] : 0;
-    for (int off = 1; off < 16; off <<= 1) {
-      int o = __shfl_up(t, off, 64);
-      if (lane >= off) t += o;
-    }
-    if (lane < 16) sh[lane] = t;
-  }
-  __syncthreads();
-  int add = w > 0 ? sh[w - 1] : 0;
+  int add = 0;
+  for (int q = 0; q < w; ++q) add += sh[q];
   __syncthreads();
   return v + add;
 }
 
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// decode step (1a): rotate and select.  grid (nblk, B), 128 threads.
-__global__ __launch_bounds__(128) void k_rotate_select(const float* __restrict__ x,
-                                                       const float* __restrict__ sigma,
-                                                       float* __restrict__ xrot,
-                                                       uint8_t* __restrict__ sel, int H, int nblk,
-                                                       int n_screen) {
-  const int b = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
-  __shared__ float s[128];
-  __shared__ unsigned long long bal[2];
-  const size_t off = (size_t)t * H + (size_t)b * 128 + tid;
-  float v = x[off] * sigma[b * 128 + tid];
-  for (int h = 1; h < 128; h <<= 1) {
-    s[tid] = v;
-    __syncthreads();
-    float o = s[tid ^ h];
-    v = (tid & h) ? (o - v) : (v + o);
-    __syncthreads();
-  }
-  xrot[off] = v;
-  const float a = fabsf(v);
-  s[tid] = a;
-  __syncthreads();
-  int rank = 0;
-  for (int j = 0; j < 128; ++j) {
-    float aj = s[j];
-    rank += (aj > a) || (aj == a && j < tid);
-  }
-  const bool on = rank < n_screen;
-  const unsigned long long m = __ballot(on);
-  const int lane = tid & 63, w = tid >> 6;
-  if (lane == 0) bal[w] = m;
-  __syncthreads();
-  const int pos = __popcll(m & ((1ull << lane) - 1ull)) + (w ? __popcll(bal[0]) : 0);
-  // ranks form a permutation for finite inputs; the bound keeps NaN inputs in range
-  if (on && pos < n_screen) sel[((size_t)t * nblk + b) * n_screen + pos] = (uint8_t)tid;
+__device__ __forceinline__ int xcd_item(int id, int per_xcd) {
+  return (id & 7) * per_xcd + (id >> 3);
 }
 
-// ---------------------------------------------------------------------------
-// decode step (1b): partial screen.  grid (nblk, top, B), G*D threads where
-// D = unit/4 dwords per unit and G coordinate groups.  Each thread owns one
-// dword (four bytes = twenty channel codes) of the unit and accumulates over
-// its group's screened coordinates; groups are then summed through LDS and
-// scaled by the block's fp16 scale.
-__global__ __launch_bounds__(512) void k_screen(const uint8_t* __restrict__ codes,
-                                                const uint16_t* __restrict__ scales,
-                                                const float* __restrict__ xrot,
-                                                const uint8_t* __restrict__ sel,
-                                                const int32_t* __restrict__ ids,
-                                                float* __restrict__ part, int32_t* status, int H,
-                                                int E, int I, int top, int nblk, int n_screen,
-                                                int lp, int unit, int G) {
-  extern __shared__ float red[];  // [G][D*20]
-  const int b = blockIdx.x, s = blockIdx.y, t = blockIdx.z;
-  const int D = unit >> 2;
-  const int tid = threadIdx.x, d = tid % D, g = tid / D;
-  const int e = clamp_expert(ids[t * top + s], E, status);
-  float acc[20];
+}  // namespace
+
+// ===========================================================================
+// A: rotate + select + screen + score
+// ===========================================================================
+struct ScreenArgs {
+  const float* x;
+  const int32_t* ids;
+  const float* gw;
+  const float* sigma;
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const float* norms;
+  float* xrot;
+  uint8_t* sel;
+  float* ghat;
+  float* vhat;
+  float* pact;
+  float* score;
+  int32_t* status;
+  int H, E, I, top, nblk, n_screen, lp, unit, n_slices, items, per_xcd, CH, dbg;
+};
+
+template <int S>
+__global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int item = xcd_item(blockIdx.x, a.per_xcd);
+  if (item >= a.items) return;
+  const int c = item % a.n_slices;
+  const int ts = item / a.n_slices;
+  const int s = ts % a.top, t = ts / a.top;
+  const int tid = threadIdx.x;
+  const int H = a.H, I = a.I, nblk = a.nblk, NS = a.n_screen;
+  constexpr int NCH = 5 * S;  // channels per half in this slice
+  const ScreenLds L(H, nblk, NS, S, a.CH);
+  float* xs = reinterpret_cast<float*>(smem + L.xs);
+  int* hist = reinterpret_cast<int*>(smem + L.uni);
+  float* red = reinterpret_cast<float*>(smem + L.uni);
+  uint32_t* st_pref = reinterpret_cast<uint32_t*>(smem + L.st);
+  uint32_t* st_msk = st_pref + nblk;
+  int* st_need = reinterpret_cast<int*>(st_msk + nblk);
+  int* st_done = st_need + nblk;
+  uint8_t* sl = smem + L.sl;
+  float* xsel = reinterpret_cast<float*>(smem + L.xsel);
+  float* sc = reinterpret_cast<float*>(smem + L.sc);
+
+  const int e = clamp_expert(a.ids[t * a.top + s], a.E, a.status);
+  const float wgt = a.gw[t * a.top + s];
+  const int b0 = c * S;   // first byte of the slice inside each half
+  const int j0 = 5 * b0;  // first channel of the slice
+
+  // scales of the slice for every block and half, and the slice's norms
+  for (int q = tid; q < nblk * 2 * NCH; q += kThreads) {
+    const int jj = q % NCH, bm = q / NCH;  // bm = block * 2 + half
+    const int j = j0 + jj;
+    sc[q] = j < I ? f16f(a.scales[((size_t)e * nblk + (bm >> 1)) * 2 * I + (bm & 1) * I + j]) : 0.f;
+  }
+  float nrm = 0.f;
+  if (tid < NCH && j0 + tid < I) nrm = a.norms[(size_t)e * I + j0 + tid];
+
+  // ---- decode step (1): rotation, float32 butterfly per 128-block ----
+  const float* xt = a.x + (size_t)t * H;
+  for (int q = tid * 4; q < H; q += kThreads * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xt + q);
+    const float4 g = *reinterpret_cast<const float4*>(a.sigma + q);
+    xs[q] = v.x * g.x;
+    xs[q + 1] = v.y * g.y;
+    xs[q + 2] = v.z * g.z;
+    xs[q + 3] = v.w * g.w;
+  }
+  for (int h = 1; h < 128; h <<= 1) {
+    __syncthreads();
+    for (int p = tid; p < H / 2; p += kThreads) {
+      const int blk = p >> 6, r = p & 63;
+      const int i = blk * 128 + (r / h) * 2 * h + (r % h);
+      const float u = xs[i], v = xs[i + h];
+      xs[i] = u + v;
+      xs[i + h] = u - v;
+    }
+  }
+  __syncthreads();
+  const bool writer = a.dbg && c == 0 && s == 0;
+  if (writer)
+    for (int q = tid; q < H; q += kThreads) a.xrot[(size_t)t * H + q] = xs[q];
+
+  // ---- partial screen: per block, the NS coordinates of largest |v| ----
+  // radix select on the 31 magnitude bits, MSB first, ties to the lower index
+  const int CH = a.CH, tpb = kThreads / CH, ept = 128 / tpb;
+  const int bl = tid / tpb, ln = tid % tpb;
+  const int nbt = 256 / tpb;
+  for (int cb0 = 0; cb0 < nblk; cb0 += CH) {
+    const int b = cb0 + bl;
+    const bool act = b < nblk;
+    if (act && ln == 0) {
+      st_pref[b] = 0u;
+      st_msk[b] = 0u;
+      st_need[b] = NS;
+      st_done[b] = 0;
+    }
+    uint32_t key[16];
 #pragma unroll
-  for (int q = 0; q < 20; ++q) acc[q] = 0.f;
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(codes + ((size_t)e * nblk + b) * 128 * unit);
-  const uint8_t* selp = sel + ((size_t)t * nblk + b) * n_screen;
-  const float* xr = xrot + (size_t)t * H + (size_t)b * 128;
-  if (g < G) {
-    for (int i = g; i < n_screen; i += G) {
-      const int c = selp[i] & 127;
-      const float xv = xr[c];
-      uint32_t w = base[(size_t)c * D + d];
+    for (int q = 0; q < 16; ++q)
+      key[q] = (act && q < ept) ? (__float_as_uint(xs[b * 128 + ln * ept + q]) & 0x7FFFFFFFu) : 0u;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+      const uint32_t dm = pass == 3 ? 0x7Fu : 0xFFu;
+      __syncthreads();
+      for (int q = tid; q < CH * 256; q += kThreads) hist[q] = 0;
+      __syncthreads();
+      const bool work = act && !st_done[b];
+      if (work) {
+        const uint32_t pf = st_pref[b], mk = st_msk[b];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        uint32_t q = (w >> (8 * kb)) & 255u;
-#pragma unroll
-        for (int dd = 0; dd < 5; ++dd) {
-          const uint32_t r = q % 3u;
-          q /= 3u;
-          acc[kb * 5 + dd] += (r == 2u) ? xv : ((r == 0u) ? -xv : 0.f);
+        for (int q = 0; q < 16; ++q)
+          if (q < ept && (key[q] & mk) == pf)
+            atomicAdd(&hist[bl * 256 + ((key[q] >> shift) & dm)], 1);
+      }
+      __syncthreads();
+      int loc = 0;
+      if (work)
+        for (int d = 0; d < nbt; ++d) loc += hist[bl * 256 + ln * nbt + d];
+      int suf = loc;  // inclusive suffix sum over the tpb lanes of this block
+      for (int off = 1; off < tpb; off <<= 1) {
+        const int o = __shfl_down(suf, off, tpb);
+        if (ln + off < tpb) suf += o;
+      }
+      if (work) {
+        const int need = st_need[b];
+        const int above = suf - loc;
+        if (above < need && suf >= need) {
+          int cum = above;
+          for (int d = ln * nbt + nbt - 1; d >= ln * nbt; --d) {
+            const int hc = hist[bl * 256 + d];
+            if (cum + hc >= need) {
+              st_pref[b] |= (uint32_t)d << shift;
+              st_msk[b] |= dm << shift;
+              st_need[b] = need - cum;
+              if (hc == need - cum) st_done[b] = 1;
+              break;
+            }
+            cum += hc;
+          }
         }
       }
     }
-    float* my = red + (size_t)g * D * 20 + d * 20;
+    __syncthreads();
+    // final rule and ascending compaction
+    {
+      const uint32_t pf = act ? st_pref[b] : 0u, mk = act ? st_msk[b] : 0u;
+      const int need = act ? st_need[b] : 0;
+      int neq = 0;
 #pragma unroll
-    for (int q = 0; q < 20; ++q) my[q] = acc[q];
+      for (int q = 0; q < 16; ++q)
+        if (act && q < ept) neq += (key[q] & mk) == pf;
+      int eqb = neq;  // prefix of equal keys over lanes
+      for (int off = 1; off < tpb; off <<= 1) {
+        const int o = __shfl_up(eqb, off, tpb);
+        if (ln >= off) eqb += o;
+      }
+      eqb -= neq;
+      uint32_t selmask = 0;
+      int nsel = 0, er = eqb;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (act && q < ept) {
+          const uint32_t km = key[q] & mk;
+          bool on = km > pf;
+          if (km == pf) {
+            on = er < need;
+            ++er;
+          }
+          if (on) {
+            selmask |= 1u << q;
+            ++nsel;
+          }
+        }
+      int pos = nsel;
+      for (int off = 1; off < tpb; off <<= 1) {
+        const int o = __shfl_up(pos, off, tpb);
+        if (ln >= off) pos += o;
+      }
+      pos -= nsel;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if ((selmask >> q) & 1u) {
+          if (pos < NS) {
+            const int i = ln * ept + q;
+            sl[b * NS + pos] = (uint8_t)i;
+            xsel[b * NS + pos] = xs[b * 128 + i];
+          }
+          ++pos;
+        }
+    }
   }
   __syncthreads();
-  const int nout = D * 20;
-  float* out = part + (((size_t)t * top + s) * nblk + b) * 2 * I;
-  const uint16_t* sc = scales + ((size_t)e * nblk + b) * 2 * I;
-  for (int o = tid; o < nout; o += blockDim.x) {
-    const int p = o / 5, digit = o % 5;
-    const int half = p / lp;
-    if (half >= 2) continue;
-    const int ch = 5 * (p % lp) + digit;
-    if (ch >= I) continue;
-    float v = 0.f;
-    for (int gg = 0; gg < G; ++gg) v += red[(size_t)gg * nout + o];
-    out[half * I + ch] = v * f16f(sc[half * I + ch]);
+  if (writer)
+    for (int q = tid; q < nblk * NS; q += kThreads) a.sel[(size_t)t * nblk * NS + q] = sl[q];
+
+  // ---- screen: codes of the slice at the screened coordinates ----
+  // group g = (block, half) with tpg threads; each thread takes every
+  // tpg-th screened coordinate of its block.
+  const int groups = 2 * nblk;
+  int tpg = 1;
+  while (tpg * 2 * groups <= kThreads) tpg *= 2;
+  const int g = tid / tpg, lg = tid % tpg;
+  float acc[NCH];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) acc[q] = 0.f;
+  const int nbytes = (I + 4) / 5;
+  const int nb_slice = min(S, nbytes - b0);  // bytes of this slice inside a half
+  if (g < groups) {
+    const int b = g >> 1, m = g & 1;
+    const uint8_t* ubase = a.codes + ((size_t)e * nblk + b) * 128 * a.unit + m * a.lp + (b0 & ~3);
+    const int sh = (b0 & 3) * 8;
+    for (int q = lg; q < NS; q += tpg) {
+      const int ci = sl[b * NS + q];
+      const float xv = xsel[b * NS + q];
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + (size_t)ci * a.unit);
+      constexpr int ND = (S + 6) / 4;  // dwords covering S bytes at any 4-byte phase
+      uint32_t w[ND];
+#pragma unroll
+      for (int d = 0; d < ND; ++d) w[d] = wp[d];
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        const int bit = sh + 8 * k;
+        const int wi = bit >> 5, bo = bit & 31;
+        uint32_t byte = wi < ND ? (w[wi < ND ? wi : 0] >> bo) & 0xFFu : 0u;
+        if (k < nb_slice) {
+#pragma unroll
+          for (int d = 0; d < 5; ++d) {
+            const uint32_t dig = byte % 3u;
+            byte /= 3u;
+            acc[5 * k + d] = fmaf((float)((int)dig - 1), xv, acc[5 * k + d]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // the select histogram space becomes the reduction space
+  if (g < groups) {
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) red[(size_t)tid * NCH + q] = acc[q];
+  }
+  __syncthreads();
+  if (g < groups)
+    for (int jj = lg; jj < NCH; jj += tpg) {
+      float v = 0.f;
+      for (int l = 0; l < tpg; ++l) v += red[(size_t)(g * tpg + l) * NCH + jj];
+      sc[g * NCH + jj] *= v;  // alpha_b * sum over screened coordinates
+    }
+  __syncthreads();
+  if (tid < NCH && j0 + tid < I) {
+    float gs = 0.f, vs = 0.f;
+    for (int b = 0; b < nblk; ++b) {
+      gs += sc[(2 * b) * NCH + tid];
+      vs += sc[(2 * b + 1) * NCH + tid];
+    }
+    gs *= kInvSqrt128f;
+    vs *= kInvSqrt128f;
+    const float p = silu(gs) * vs;
+    const size_t o = (size_t)t * a.top * I + (size_t)s * I + j0 + tid;
+    a.ghat[o] = gs;
+    a.vhat[o] = vs;
+    a.pact[o] = p;
+    a.score[o] = wgt * nrm * fabsf(p);
   }
 }
 
-// ---------------------------------------------------------------------------
-// decode step (2a): estimates and scores.  One thread per (token, candidate).
-__global__ __launch_bounds__(256) void k_score(const float* __restrict__ part,
-                                               const float* __restrict__ norms,
-                                               const int32_t* __restrict__ ids,
-                                               const float* __restrict__ gw,
-                                               float* __restrict__ ghat, float* __restrict__ vhat,
-                                               float* __restrict__ pact,
-                                               float* __restrict__ score, int32_t* status, int E,
-                                               int I, int top, int nblk, int ncand, int batch) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= batch * ncand) return;
-  const int t = idx / ncand, c = idx % ncand, s = c / I, j = c % I;
-  const int e = clamp_expert(ids[t * top + s], E, status);
-  const float* pp = part + ((size_t)t * top + s) * nblk * 2 * I;
-  float g = 0.f, v = 0.f;
-  for (int b = 0; b < nblk; ++b) {
-    g += pp[(size_t)b * 2 * I + j];
-    v += pp[(size_t)b * 2 * I + I + j];
+// ===========================================================================
+// B: exact top-k (redundant per workgroup) + exact kept channels + recovery z
+// ===========================================================================
+struct SelectArgs {
+  const float* x;
+  const int32_t* ids;
+  const float* gw;
+  const uint16_t* w3;
+  const uint16_t* bmat;
+  const float* score;
+  const float* pact;
+  int32_t* kept;
+  int32_t* rowidx;
+  float* coef;
+  float* zpart;
+  int32_t* status;
+  int H, E, I, top, ncand, k, rank, G, share_max;
+  int dense;  // 1: every candidate is kept (the dense baseline); scores unused
+};
+
+__global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int t = blockIdx.x / a.G, w = blockIdx.x % a.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I, nc = a.ncand, k = a.k;
+  const SelectLds L(H, nc, a.share_max, a.rank);
+  float* xs = reinterpret_cast<float*>(smem + L.xs);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + L.keys);
+  uint8_t* flags = smem + L.flags;
+  int* list = reinterpret_cast<int*>(smem + L.list);
+  float* zred = reinterpret_cast<float*>(smem + L.zred);
+  int* hist = reinterpret_cast<int*>(smem + L.misc);
+  int* misc = hist + 256;  // [0..3] scan scratch, [8] digit, [9] need, [10] done, [11] bin count
+
+  const float* xt = a.x + (size_t)t * H;
+  for (int q = tid * 4; q < H; q += kThreads * 4)
+    *reinterpret_cast<float4*>(xs + q) = *reinterpret_cast<const float4*>(xt + q);
+  const bool partial = !a.dense && k > 0 && k < nc;
+  if (partial) {
+    const float* sct = a.score + (size_t)t * nc;
+    for (int q = tid; q < nc; q += kThreads) keys[q] = __float_as_uint(sct[q]);
   }
-  g *= kInvSqrt128f;
-  v *= kInvSqrt128f;
-  const float p = silu(g) * v;
-  ghat[idx] = g;
-  vhat[idx] = v;
-  pact[idx] = p;
-  score[idx] = gw[t * top + s] * norms[(size_t)e * I + j] * fabsf(p);
-}
-
-// ---------------------------------------------------------------------------
-// decode step (2b): exact top-k per token.  grid (B), 1024 threads.
-// Scores are non-negative floats, so their bit patterns order like their
-// values; a 4-pass MSB-first radix select finds the k-th largest key T and
-// how many keys equal to T are kept (lowest indices first).
-__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ score,
-                                               int32_t* __restrict__ kept,
-                                               uint8_t* __restrict__ keptf, int ncand, int k) {
-  __shared__ int hist[256];
-  __shared__ int scan_sh[16];
-  __shared__ int sel_digit, sel_kk;
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const uint32_t* key = reinterpret_cast<const uint32_t*>(score + (size_t)t * ncand);
-  int32_t* kout = kept + (size_t)t * ncand;
-  uint8_t* fout = keptf + (size_t)t * ncand;
-  const int per = (ncand + 1023) / 1024;
-  const int lo = min(tid * per, ncand), hi = min(lo + per, ncand);
-
+  // each thread owns a contiguous chunk of candidates
+  const int per = (nc + kThreads - 1) / kThreads;
+  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
   uint32_t prefix = 0, mask = 0;
-  int kk = k;
-  if (k > 0 && k < ncand) {
+  int need = k;
+  if (tid == 0) misc[10] = 0;
+  __syncthreads();
+  if (partial) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
+      hist[tid] = 0;
       __syncthreads();
-      for (int i = lo; i < hi; ++i) {
-        uint32_t kv = key[i];
-        if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1);
+      const int done = misc[10];
+      if (!done)
+        for (int i = lo; i < hi; ++i) {
+          const uint32_t kv = keys[i];
+          if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1);
+        }
+      __syncthreads();
+      const int own = hist[255 - tid];
+      const int incl = block_scan_256(own, misc);  // count of digits >= 255 - tid
+      if (!done && incl >= need && incl - own < need) {
+        misc[8] = 255 - tid;
+        misc[9] = need - (incl - own);
+        misc[11] = own;
       }
       __syncthreads();
-      // suffix counts: thread d holds count of digits >= 255 - d
-      int own = tid < 256 ? hist[255 - tid] : 0;
-      int incl = block_scan_1024(own, scan_sh);
-      if (tid < 256 && incl >= kk && incl - own < kk) {
-        sel_digit = 255 - tid;
-        sel_kk = kk - (incl - own);
+      if (!done) {
+        prefix |= (uint32_t)misc[8] << shift;
+        mask |= 255u << shift;
+        need = misc[9];
       }
       __syncthreads();
-      prefix |= (uint32_t)sel_digit << shift;
-      mask |= 255u << shift;
-      kk = sel_kk;
+      if (tid == 0 && !done && misc[11] == need) misc[10] = 1;  // every key of the bin is kept
       __syncthreads();
     }
   }
-  // count per thread, then scan for equal keys and for output positions
+  // kept flags and ranks in ascending candidate order
   int ngt = 0, neq = 0;
-  if (k == ncand) {
-    ngt = hi - lo;
-  } else if (k > 0) {
+  if (partial)
     for (int i = lo; i < hi; ++i) {
-      uint32_t kv = key[i];
+      const uint32_t kv = keys[i] & mask;
       ngt += kv > prefix;
       neq += kv == prefix;
     }
-  }
-  const int eq_incl = block_scan_1024(neq, scan_sh);
-  int eq_before = eq_incl - neq;
+  const int eq_incl = block_scan_256(neq, misc);
+  const int eq_before = eq_incl - neq;
   int take_eq = 0;
-  if (k > 0 && k < ncand) take_eq = max(0, min(neq, kk - eq_before));
-  const int mine = ngt + take_eq;
-  const int pos_incl = block_scan_1024(mine, scan_sh);
-  int pos = pos_incl - mine;
+  if (partial) take_eq = max(0, min(neq, need - eq_before));
+  const bool all = a.dense || k == nc;
+  const int mine = partial ? ngt + take_eq : (all ? hi - lo : 0);
+  const int pos_incl = block_scan_256(mine, misc);
+  int rnk = pos_incl - mine;
+  const int share = (k + a.G - 1) / a.G;
+  const int r0 = min(w * share, k), r1 = min(r0 + share, k);
   int eq_seen = 0;
   for (int i = lo; i < hi; ++i) {
-    bool on;
-    if (k == ncand) {
-      on = true;
-    } else if (k == 0) {
-      on = false;
-    } else {
-      uint32_t kv = key[i];
+    bool on = all;
+    if (partial) {
+      const uint32_t kv = keys[i] & mask;
       on = kv > prefix;
       if (kv == prefix) {
         on = eq_seen < take_eq;
         ++eq_seen;
       }
     }
-    fout[i] = on ? 1 : 0;
-    if (on) kout[pos++] = i;
+    flags[i] = on ? 1 : 0;
+    if (on) {
+      if (rnk >= r0 && rnk < r1) list[rnk - r0] = i;
+      ++rnk;
+    }
   }
-}
+  __syncthreads();
 
-// ---------------------------------------------------------------------------
-// decode step (3a): exact activations of kept channels from native rows.
-// grid (ceil(k/4), B), 256 threads = 4 waves, one kept channel per wave.
-// kept == nullptr means candidate idx itself (the dense baseline).
-__global__ __launch_bounds__(256) void k_exact_act(const uint16_t* __restrict__ w3,
-                                                   const float* __restrict__ x,
-                                                   const int32_t* __restrict__ kept,
-                                                   const int32_t* __restrict__ ids,
-                                                   const float* __restrict__ gw,
-                                                   float* __restrict__ coef, int32_t* status,
-                                                   int H, int E, int I, int top, int ncand, int k) {
-  const int t = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * 4 + wave;
-  if (idx >= k) return;
-  const int c = kept ? kept[(size_t)t * ncand + idx] : idx;
-  const int s = c / I, j = c % I;
-  const int e = clamp_expert(ids[t * top + s], E, status);
-  const uint16_t* row = w3 + ((size_t)e * I + j) * 3 * H;
-  const float* xt = x + (size_t)t * H;
-  float g = 0.f, v = 0.f;
-  for (int h = lane * 8; h < H; h += 512) {
-    const uint4 gq = *reinterpret_cast<const uint4*>(row + h);
-    const uint4 vq = *reinterpret_cast<const uint4*>(row + H + h);
-    const float4 x0 = *reinterpret_cast<const float4*>(xt + h);
-    const float4 x1 = *reinterpret_cast<const float4*>(xt + h + 4);
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    const uint32_t gw4[4] = {gq.x, gq.y, gq.z, gq.w};
-    const uint32_t vw4[4] = {vq.x, vq.y, vq.z, vq.w};
+  // ---- decode step (3): exact kept channels from native BF16 rows ----
+  for (int q = wave; q < r1 - r0; q += 4) {
+    const int cnd = list[q];
+    const int sl = cnd / I, j = cnd % I;
+    const int e = clamp_expert(a.ids[t * a.top + sl], a.E, a.status);
+    const size_t row = (size_t)e * I + j;
+    const uint16_t* gr = a.w3 + row * 3 * H;
+    float gsum = 0.f, vsum = 0.f;
+    for (int h = lane * 8; h < H; h += 512) {
+      const uint4 gq = *reinterpret_cast<const uint4*>(gr + h);
+      const uint4 vq = *reinterpret_cast<const uint4*>(gr + H + h);
+      const float4 x0 = *reinterpret_cast<const float4*>(xs + h);
+      const float4 x1 = *reinterpret_cast<const float4*>(xs + h + 4);
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const uint32_t gu[4] = {gq.x, gq.y, gq.z, gq.w};
+      const uint32_t vu[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      g += __uint_as_float(gw4[q] << 16) * xs[2 * q] + __uint_as_float(gw4[q] & 0xFFFF0000u) * xs[2 * q + 1];
-      v += __uint_as_float(vw4[q] << 16) * xs[2 * q] + __uint_as_float(vw4[q] & 0xFFFF0000u) * xs[2 * q + 1];
+      for (int d = 0; d < 4; ++d) {
+        gsum = fmaf(__uint_as_float(gu[d] << 16), xv[2 * d], gsum);
+        gsum = fmaf(__uint_as_float(gu[d] & 0xFFFF0000u), xv[2 * d + 1], gsum);
+        vsum = fmaf(__uint_as_float(vu[d] << 16), xv[2 * d], vsum);
+        vsum = fmaf(__uint_as_float(vu[d] & 0xFFFF0000u), xv[2 * d + 1], vsum);
+      }
+    }
+    gsum = wave_sum(gsum);
+    vsum = wave_sum(vsum);
+    if (lane == 0) {
+      const size_t o = (size_t)t * nc + r0 + q;
+      a.coef[o] = a.gw[t * a.top + sl] * silu(gsum) * vsum;
+      a.rowidx[o] = (int32_t)row;
+      a.kept[o] = cnd;
     }
   }
-  g = wave_sum(g);
-  v = wave_sum(v);
-  if (lane == 0) coef[(size_t)t * ncand + idx] = gw[t * top + s] * silu(g) * v;
-}
 
-// ---------------------------------------------------------------------------
-// decode step (3b): partial y over a chunk of kept channels.
-// grid (ceil(H/512), nchunks, B), 256 threads, two hidden units per thread.
-__global__ __launch_bounds__(256) void k_down_partial(const uint16_t* __restrict__ w3,
-                                                      const int32_t* __restrict__ kept,
-                                                      const int32_t* __restrict__ ids,
-                                                      const float* __restrict__ coef,
-                                                      float* __restrict__ ypart, int32_t* status,
-                                                      int H, int E, int I, int top, int ncand,
-                                                      int k, int max_chunks) {
-  const int t = blockIdx.z, ch = blockIdx.y;
-  const int h0 = blockIdx.x * kDownSlice + threadIdx.x * 2;
-  const int i0 = ch * kDownChunk, i1 = min(k, i0 + kDownChunk);
-  float a0 = 0.f, a1 = 0.f;
-  if (h0 < H) {
-    for (int idx = i0; idx < i1; ++idx) {
-      const int c = kept ? kept[(size_t)t * ncand + idx] : idx;
-      const int s = c / I, j = c % I;
-      const int e = clamp_expert(ids[t * top + s], E, status);
-      const float cf = coef[(size_t)t * ncand + idx];
-      const uint32_t dq = *reinterpret_cast<const uint32_t*>(w3 + (((size_t)e * I + j) * 3 + 2) * H + h0);
-      a0 += cf * __uint_as_float(dq << 16);
-      a1 += cf * __uint_as_float(dq & 0xFFFF0000u);
+  // ---- decode step (4), first half: z over this workgroup's skipped candidates ----
+  if (a.rank > 0 && !all) {
+    const int zper = (nc + a.G - 1) / a.G;
+    const int c0 = min(w * zper, nc), c1 = min(c0 + zper, nc);
+    const int R = a.rank;
+    const int rl = tid % R, grp = tid / R, ngrp = kThreads / R;
+    float zacc = 0.f;
+    if (grp < ngrp)
+      for (int cnd = c0 + grp; cnd < c1; cnd += ngrp) {
+        if (flags[cnd]) continue;
+        const int sl = cnd / I, j = cnd % I;
+        const int e = clamp_expert(a.ids[t * a.top + sl], a.E, a.status);
+        const float cf = a.gw[t * a.top + sl] * a.pact[(size_t)t * nc + cnd];
+        zacc = fmaf(cf, f16f(a.bmat[((size_t)e * I + j) * R + rl]), zacc);
+      }
+    if (grp < 8 && grp < ngrp) zred[grp * R + rl] = zacc;
+    __syncthreads();
+    for (int g2 = 8; g2 < ngrp; ++g2) {  // only when rank < 32
+      if (grp == g2) zred[rl] += zacc;
+      __syncthreads();
     }
-    float* yp = ypart + ((size_t)t * max_chunks + ch) * H + h0;
-    yp[0] = a0;
-    yp[1] = a1;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// decode step (4a): partial recovery vector z over a chunk of candidates.
-// grid (nz, B), 256 threads = 4 candidate groups x 64 rank lanes.
-__global__ __launch_bounds__(256) void k_recover_partial(const uint16_t* __restrict__ bmat,
-                                                         const uint8_t* __restrict__ keptf,
-                                                         const float* __restrict__ pact,
-                                                         const int32_t* __restrict__ ids,
-                                                         const float* __restrict__ gw,
-                                                         float* __restrict__ zpart,
-                                                         int32_t* status, int E, int I, int top,
-                                                         int ncand, int rank, int max_zchunks) {
-  __shared__ float red[4][64];
-  const int t = blockIdx.y, zc = blockIdx.x;
-  const int r = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int c0 = zc * kZChunk, c1 = min(ncand, c0 + kZChunk);
-  float acc = 0.f;
-  if (r < rank) {
-    for (int c = c0 + grp; c < c1; c += 4) {
-      if (keptf[(size_t)t * ncand + c]) continue;
-      const int s = c / I, j = c % I;
-      const int e = clamp_expert(ids[t * top + s], E, status);
-      const float cf = gw[t * top + s] * pact[(size_t)t * ncand + c];
-      acc += cf * f16f(bmat[((size_t)e * I + j) * rank + r]);
+    if (tid < R) {
+      float z = 0.f;
+      for (int g2 = 0; g2 < min(8, ngrp); ++g2) z += zred[g2 * R + tid];
+      a.zpart[((size_t)t * a.G + w) * R + tid] = z;
     }
   }
-  red[grp][r] = acc;
-  __syncthreads();
-  if (grp == 0 && r < rank)
-    zpart[((size_t)t * max_zchunks + zc) * rank + r] = red[0][r] + red[1][r] + red[2][r] + red[3][r];
 }
 
-// ---------------------------------------------------------------------------
-// y = sum of partial y + U z.  grid (ceil(H/256), B), 256 threads.
-__global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ ypart,
-                                                  const float* __restrict__ zpart,
-                                                  const uint16_t* __restrict__ U,
-                                                  float* __restrict__ y, int H, int rank,
-                                                  int nchunks, int nz, int max_chunks,
-                                                  int max_zchunks) {
-  __shared__ float z[64];
-  const int t = blockIdx.y, tid = threadIdx.x;
+// ===========================================================================
+// C: y = sum over kept of (w a_j) d_j + U z, per hidden slice
+// ===========================================================================
+struct DownArgs {
+  const uint16_t* w3;
+  const uint16_t* U;
+  const int32_t* rowidx;
+  const float* coef;
+  const float* zpart;
+  float* y;
+  int H, ncand, k, rank, G, nz, nhs, items, per_xcd;
+};
+
+template <int HS>
+__global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
+  __shared__ float zs[64];
+  __shared__ float part[4][HS];
+  const int item = xcd_item(blockIdx.x, a.per_xcd);
+  if (item >= a.items) return;
+  const int t = item / a.nhs, hs = item % a.nhs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, h0 = hs * HS;
   if (tid < 64) {
-    float a = 0.f;
-    if (tid < rank)
-      for (int q = 0; q < nz; ++q) a += zpart[((size_t)t * max_zchunks + q) * rank + tid];
-    z[tid] = a;
+    float z = 0.f;
+    if (tid < a.rank)
+      for (int q = 0; q < a.nz; ++q) z += a.zpart[((size_t)t * a.G + q) * a.rank + tid];
+    zs[tid] = z;
   }
+  float acc[HS];
+#pragma unroll
+  for (int q = 0; q < HS; ++q) acc[q] = 0.f;
+  const int32_t* ri = a.rowidx + (size_t)t * a.ncand;
+  const float* cf = a.coef + (size_t)t * a.ncand;
+  for (int r = tid; r < a.k; r += kThreads) {
+    const float c = cf[r];
+    const uint16_t* d = a.w3 + ((size_t)ri[r] * 3 + 2) * H + h0;
+#pragma unroll
+    for (int q = 0; q < HS; q += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(d + q);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        acc[q + 2 * p] = fmaf(c, __uint_as_float(u[p] << 16), acc[q + 2 * p]);
+        acc[q + 2 * p + 1] = fmaf(c, __uint_as_float(u[p] & 0xFFFF0000u), acc[q + 2 * p + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < HS; ++q) acc[q] = wave_sum(acc[q]);
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < HS; ++q) part[wave][q] = acc[q];
   __syncthreads();
-  const int h = blockIdx.x * 256 + tid;
-  if (h >= H) return;
-  float acc = 0.f;
-  for (int q = 0; q < nchunks; ++q) acc += ypart[((size_t)t * max_chunks + q) * H + h];
-  if (nz > 0)
-    for (int rr = 0; rr < rank; ++rr) acc += f16f(U[(size_t)h * rank + rr]) * z[rr];
-  y[(size_t)t * H + h] = acc;
+  if (tid < HS) {
+    const int h = h0 + tid;
+    float v = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    if (a.nz > 0)
+      for (int r = 0; r < a.rank; ++r) v = fmaf(f16f(a.U[(size_t)h * a.rank + r]), zs[r], v);
+    a.y[(size_t)t * H + h] = v;
+  }
 }
 
-// ---------------------------------------------------------------------------
+// ===========================================================================
+// host side
+// ===========================================================================
 static int hip_fail(hipError_t e, const char* what) {
   return fail(CFR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+Plan make_plan(const cfr_config& c, int batch, int k) {
+  Plan p;
+  const int nblk = c.hidden / kBlock, nbytes = (c.inter + 4) / 5, nc = c.top * c.inter;
+  // A: about 32 slices per routed expert, i.e. one workgroup per CU at batch 1
+  p.S = (nbytes + 31) / 32;
+  if (p.S < 1) p.S = 1;
+  if (p.S > kMaxS) p.S = kMaxS;
+  p.n_slices = (nbytes + p.S - 1) / p.S;
+  p.itemsA = batch * c.top * p.n_slices;
+  p.per_xcdA = (p.itemsA + 7) / 8;
+  int ch = 4;
+  while (ch < nblk && ch < 32) ch *= 2;
+  p.CH = ch;
+  p.ldsA = ScreenLds(c.hidden, nblk, c.n_screen, p.S, p.CH).total;
+  // B: workgroups per token; about one kept channel per wave at batch 1
+  int g = 256 / batch;
+  if (g < 4) g = 4;
+  const int per4 = ((k > 0 ? k : 1) + 3) / 4;
+  if (g > per4) g = per4 < 4 ? 4 : per4;
+  p.G = g;
+  p.share_max = (k + g - 1) / g;
+  p.ldsB = SelectLds(c.hidden, nc, p.share_max, c.rank).total;
+  // C: hidden slices per token (8..64 hidden units each)
+  int hsl = 8;
+  while ((long)batch * (c.hidden / hsl) > 512 && hsl < 64) hsl *= 2;
+  p.HS = hsl;
+  p.nhs = c.hidden / hsl;
+  p.itemsC = batch * p.nhs;
+  p.per_xcdC = (p.itemsC + 7) / 8;
+  return p;
+}
+
+size_t max_lds_needed(const cfr_config& c) {
+  size_t m = 0;
+  for (int b = 1; b <= c.max_batch; ++b) {
+    const Plan p = make_plan(c, b, c.top * c.inter);
+    if (p.ldsA > m) m = p.ldsA;
+    if (p.ldsB > m) m = p.ldsB;
+  }
+  return m;
+}
+
+size_t zpart_rows(const cfr_config& c) {
+  size_t m = 0;
+  for (int b = 1; b <= c.max_batch; ++b) {
+    const int g = 256 / b < 4 ? 4 : 256 / b;  // the largest G make_plan can pick at batch b
+    if ((size_t)b * g > m) m = (size_t)b * g;
+  }
+  return m;
+}
+
+template <int S>
+static hipError_t launch_A(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_screen_score<S>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    attr = true;
+  }
+  k_screen_score<S><<<8 * p.per_xcdA, kThreads, p.ldsA, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int HS>
+static hipError_t launch_C(const DownArgs& a, const Plan& p, hipStream_t st) {
+  k_down_recover<HS><<<8 * p.per_xcdC, kThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_C_any(const DownArgs& a, const Plan& p, hipStream_t st) {
+  switch (p.HS) {
+    case 8: return launch_C<8>(a, p, st);
+    case 16: return launch_C<16>(a, p, st);
+    case 32: return launch_C<32>(a, p, st);
+    default: return launch_C<64>(a, p, st);
+  }
+}
+
+static hipError_t launch_B(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_select_exact,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    attr = true;
+  }
+  k_select_exact<<<batch * p.G, kThreads, p.ldsB, st>>>(a);
+  return hipGetLastError();
 }
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev) {
   const cfr_config& c = r->cfg;
-  const int H = c.hidden, E = c.n_experts, I = c.inter, top = c.top, nblk = r->nblk;
-  const int ncand = r->ncand;
-  const int D = r->unit / 4;
-  int G = 512 / D;
-  if (G < 1) G = 1;
-  if (G > c.n_screen) G = c.n_screen;
-  const size_t lds = (size_t)G * D * 20 * sizeof(float);
-
+  const Plan p = make_plan(c, batch, k);
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], st);
   };
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->xrot, r->sel, r->ghat,
+               r->vhat, r->pact, r->score, r->status, c.hidden, c.n_experts, c.inter, c.top,
+               r->nblk, c.n_screen, r->lp, r->unit, p.n_slices, p.itemsA, p.per_xcdA, p.CH,
+               dbg != nullptr};
+  hipError_t e = hipSuccess;
   mark(0);
-  k_rotate_select<<<dim3(nblk, batch), 128, 0, st>>>(x, r->sigma, r->xrot, r->sel, H, nblk,
-                                                     c.n_screen);
+  switch (p.S) {
+#define CFR_CASE(v) \
+  case v:           \
+    e = launch_A<v>(A, p, st); \
+    break;
+    CFR_CASE(1) CFR_CASE(2) CFR_CASE(3) CFR_CASE(4) CFR_CASE(5) CFR_CASE(6) CFR_CASE(7)
+    CFR_CASE(8) CFR_CASE(9) CFR_CASE(10) CFR_CASE(11) CFR_CASE(12) CFR_CASE(13)
+#undef CFR_CASE
+    default:
+      return fail(CFR_EUNSUPPORTED, "screen slice width");
+  }
+  if (e != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
-  k_screen<<<dim3(nblk, top, batch), G * D, lds, st>>>(r->codes, r->scales, r->xrot, r->sel, ids,
-                                                       r->part, r->status, H, E, I, top, nblk,
-                                                       c.n_screen, r->lp, r->unit, G);
+  SelectArgs B{x, ids, gw, r->w3, r->b, r->score, r->pact, r->kept, r->rowidx, r->coef,
+               r->zpart, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand, k,
+               c.rank, p.G, p.share_max, 0};
+  if ((e = launch_B(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
-  const int nsc = batch * ncand;
-  k_score<<<(nsc + 255) / 256, 256, 0, st>>>(r->part, r->norms, ids, gw, r->ghat, r->vhat,
-                                             r->pact, r->score, r->status, E, I, top, nblk, ncand,
-                                             batch);
+  const int nz = (c.rank > 0 && k < r->ncand) ? p.G : 0;
+  DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, r->ncand, k,
+             c.rank, p.G, nz, p.nhs, p.itemsC, p.per_xcdC};
+  if ((e = launch_C_any(C, p, st)) != hipSuccess) return hip_fail(e, "down launch");
   mark(3);
-  k_topk<<<batch, 1024, 0, st>>>(r->score, r->kept, r->keptf, ncand, k);
-  mark(4);
-  int nchunks = 0, nz = 0;
-  if (k > 0) {
-    nchunks = (k + kDownChunk - 1) / kDownChunk;
-    k_exact_act<<<dim3((k + 3) / 4, batch), 256, 0, st>>>(r->w3, x, r->kept, ids, gw, r->coef,
-                                                          r->status, H, E, I, top, ncand, k);
-  }
-  mark(5);
-  if (k > 0) {
-    k_down_partial<<<dim3((H + kDownSlice - 1) / kDownSlice, nchunks, batch), 256, 0, st>>>(
-        r->w3, r->kept, ids, r->coef, r->ypart, r->status, H, E, I, top, ncand, k, r->max_chunks);
-  }
-  mark(6);
-  if (k < ncand && c.rank > 0) {
-    nz = (ncand + kZChunk - 1) / kZChunk;
-    k_recover_partial<<<dim3(nz, batch), 256, 0, st>>>(r->b, r->keptf, r->pact, ids, gw, r->zpart,
-                                                        r->status, E, I, top, ncand, c.rank,
-                                                        r->max_zchunks);
-  }
-  mark(7);
-  k_finalize<<<dim3((H + 255) / 256, batch), 256, 0, st>>>(r->ypart, r->zpart, r->u, y, H, c.rank,
-                                                           nchunks, nz, r->max_chunks,
-                                                           r->max_zchunks);
-  mark(8);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (dbg) {
+    const int H = c.hidden, nblk = r->nblk, nsc = batch * r->ncand;
     auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
       return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
     };
@@ -482,7 +737,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
         (e = cp(dbg->score, r->score, sizeof(float) * nsc)) != hipSuccess)
       return hip_fail(e, "debug copy");
     if (dbg->kept && k > 0) {
-      e = hipMemcpy2DAsync(dbg->kept, sizeof(int32_t) * k, r->kept, sizeof(int32_t) * ncand,
+      e = hipMemcpy2DAsync(dbg->kept, sizeof(int32_t) * k, r->kept, sizeof(int32_t) * r->ncand,
                            sizeof(int32_t) * k, batch, hipMemcpyDeviceToDevice, st);
       if (e != hipSuccess) return hip_fail(e, "debug copy kept");
     }
@@ -493,17 +748,20 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t st) {
   const cfr_config& c = r->cfg;
-  const int H = c.hidden, E = c.n_experts, I = c.inter, top = c.top, ncand = r->ncand;
-  const int k = ncand, nchunks = (k + kDownChunk - 1) / kDownChunk;
-  k_exact_act<<<dim3((k + 3) / 4, batch), 256, 0, st>>>(r->w3, x, nullptr, ids, gw, r->coef,
-                                                        r->status, H, E, I, top, ncand, k);
-  k_down_partial<<<dim3((H + kDownSlice - 1) / kDownSlice, nchunks, batch), 256, 0, st>>>(
-      r->w3, nullptr, ids, r->coef, r->ypart, r->status, H, E, I, top, ncand, k, r->max_chunks);
-  k_finalize<<<dim3((H + 255) / 256, batch), 256, 0, st>>>(r->ypart, r->zpart, r->u, y, H, c.rank,
-                                                           nchunks, 0, r->max_chunks,
-                                                           r->max_zchunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "dense launch");
+  const int nc = r->ncand;
+  Plan p = make_plan(c, batch, nc);
+  // the dense block keeps every candidate: one wave per channel
+  p.G = (nc + 3) / 4;
+  p.share_max = 4;
+  p.ldsB = SelectLds(c.hidden, nc, p.share_max, 0).total;
+  SelectArgs B{x, ids, gw, r->w3, r->b, r->score, r->pact, r->kept, r->rowidx, r->coef,
+               r->zpart, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, nc, 0, p.G,
+               p.share_max, 1};
+  hipError_t e;
+  if ((e = launch_B(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
+  DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, nc, nc, 0, p.G, 0,
+             p.nhs, p.itemsC, p.per_xcdC};
+  if ((e = launch_C_any(C, p, st)) != hipSuccess) return hip_fail(e, "dense down launch");
   return CFR_OK;
 }
 

@@ -7,6 +7,64 @@
 
 namespace cfr {
 
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
+__host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 16; }
+
+// LDS layout of the screen kernel (bytes); host and device share it.
+struct ScreenLds {
+  size_t xs, uni, st, sl, xsel, sc, total;
+  __host__ __device__ ScreenLds(int H, int nblk, int n_screen, int S, int CH) {
+    size_t o = 0;
+    xs = o;
+    o += lds_align((size_t)H * 4);
+    uni = o;  // radix-select histograms, later the screen reduction
+    const size_t hist = (size_t)CH * 256 * 4, red = (size_t)256 * 5 * S * 4;
+    o += lds_align(hist > red ? hist : red);
+    st = o;
+    o += lds_align((size_t)nblk * 4 * 4);
+    sl = o;
+    o += lds_align((size_t)nblk * n_screen);
+    xsel = o;
+    o += lds_align((size_t)nblk * n_screen * 4);
+    sc = o;
+    o += lds_align((size_t)nblk * 2 * 5 * S * 4);
+    total = o;
+  }
+};
+
+// LDS layout of the select/exact kernel (bytes).
+struct SelectLds {
+  size_t xs, keys, flags, list, zred, misc, total;
+  __host__ __device__ SelectLds(int H, int ncand, int share_max, int rank) {
+    size_t o = 0;
+    xs = o;
+    o += lds_align((size_t)H * 4);
+    keys = o;
+    o += lds_align((size_t)ncand * 4);
+    flags = o;
+    o += lds_align((size_t)ncand);
+    list = o;
+    o += lds_align((size_t)(share_max > 0 ? share_max : 1) * 4);
+    zred = o;
+    o += lds_align((size_t)8 * (rank > 0 ? rank : 1) * 4);
+    misc = o;
+    o += lds_align((256 + 32) * 4);
+    total = o;
+  }
+};
+
+// Launch geometry of one decode call.
+struct Plan {
+  int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0, CH = 4;  // screen
+  int G = 4, share_max = 0;                                  // select/exact
+  int HS = 8, nhs = 0, itemsC = 0, per_xcdC = 0;             // down/recover
+  size_t ldsA = 0, ldsB = 0;
+};
+Plan make_plan(const cfr_config& c, int batch, int k);
+size_t max_lds_needed(const cfr_config& c);  // over every batch and k the config allows
+size_t zpart_rows(const cfr_config& c);      // rows of the recovery partial buffer
+
 // Intermediates copied out by the debug entry point (any may be null).
 struct DebugOut {
   float* xrot = nullptr;

@@ -179,8 +179,7 @@ class Reader:
         o["kept"] = o["kept"][:, :int(k)]
         return o
 
-    STAGES = ("rotate_select", "screen", "score", "topk", "exact_gate_up", "exact_down",
-              "recovery_z", "finalize")
+    STAGES = ("screen_score", "select_exact", "down_recover")
 
     def decode_profile(self, x, expert_ids, gate_w, k: int, out=None, stream=None) -> dict:
         """Decode with an event after every stage; returns {stage: microseconds}.

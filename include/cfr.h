@@ -160,9 +160,9 @@ int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
 
 /* Stages of the decode path, in launch order; cfr_reader_decode_profile
  * reports one duration per stage. */
-#define CFR_NUM_STAGES 8
-/* 0 rotate+select, 1 screen, 2 score, 3 top-k, 4 exact gate/up,
- * 5 exact down, 6 recovery z, 7 finalize (sum partials + U z) */
+#define CFR_NUM_STAGES 3
+/* 0 rotate + select + screen + score, 1 top-k + exact gate/up + recovery z,
+ * 2 down projection of kept channels + U z */
 
 /*
  * Measurement entry: the same computation as cfr_reader_decode with a HIP
