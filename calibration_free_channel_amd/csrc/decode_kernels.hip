@@ -130,23 +130,56 @@ __global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
   float* xsel = reinterpret_cast<float*>(smem + L.xsel);
   float* sc = reinterpret_cast<float*>(smem + L.sc);
 
+  // issue the token and sign loads first; they do not depend on the routing
+  const float* xt = a.x + (size_t)t * H;
+  float4 xr[4], sg[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = (tid + u * kThreads) * 4;
+    if (q < H) {
+      xr[u] = *reinterpret_cast<const float4*>(xt + q);
+      sg[u] = *reinterpret_cast<const float4*>(a.sigma + q);
+    }
+  }
   const int e = clamp_expert(a.ids[t * a.top + s], a.E, a.status);
   const float wgt = a.gw[t * a.top + s];
   const int b0 = c * S;   // first byte of the slice inside each half
   const int j0 = 5 * b0;  // first channel of the slice
 
   // scales of the slice for every block and half, and the slice's norms
-  for (int q = tid; q < nblk * 2 * NCH; q += kThreads) {
-    const int jj = q % NCH, bm = q / NCH;  // bm = block * 2 + half
-    const int j = j0 + jj;
-    sc[q] = j < I ? f16f(a.scales[((size_t)e * nblk + (bm >> 1)) * 2 * I + (bm & 1) * I + j]) : 0.f;
+  const int nsc = nblk * 2 * NCH;
+  for (int q0 = 0; q0 < nsc; q0 += kThreads * 8) {
+    uint16_t hv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + tid + u * kThreads;
+      const int jj = q % NCH, bm = q / NCH;  // bm = block * 2 + half
+      const int j = j0 + jj;
+      hv[u] = (q < nsc && j < I)
+                  ? a.scales[((size_t)e * nblk + (bm >> 1)) * 2 * I + (bm & 1) * I + j]
+                  : (uint16_t)0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + tid + u * kThreads;
+      if (q < nsc) sc[q] = f16f(hv[u]);
+    }
   }
   float nrm = 0.f;
   if (tid < NCH && j0 + tid < I) nrm = a.norms[(size_t)e * I + j0 + tid];
 
   // ---- decode step (1): rotation, float32 butterfly per 128-block ----
-  const float* xt = a.x + (size_t)t * H;
-  for (int q = tid * 4; q < H; q += kThreads * 4) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = (tid + u * kThreads) * 4;
+    if (q < H) {
+      xs[q] = xr[u].x * sg[u].x;
+      xs[q + 1] = xr[u].y * sg[u].y;
+      xs[q + 2] = xr[u].z * sg[u].z;
+      xs[q + 3] = xr[u].w * sg[u].w;
+    }
+  }
+  for (int q = (tid + 4 * kThreads) * 4; q < H; q += kThreads * 4) {  // hidden above 4096
     const float4 v = *reinterpret_cast<const float4*>(xt + q);
     const float4 g = *reinterpret_cast<const float4*>(a.sigma + q);
     xs[q] = v.x * g.x;
@@ -298,25 +331,40 @@ __global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
     const int b = g >> 1, m = g & 1;
     const uint8_t* ubase = a.codes + ((size_t)e * nblk + b) * 128 * a.unit + m * a.lp + (b0 & ~3);
     const int sh = (b0 & 3) * 8;
-    for (int q = lg; q < NS; q += tpg) {
-      const int ci = sl[b * NS + q];
-      const float xv = xsel[b * NS + q];
-      const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + (size_t)ci * a.unit);
-      constexpr int ND = (S + 6) / 4;  // dwords covering S bytes at any 4-byte phase
-      uint32_t w[ND];
+    constexpr int ND = (S + 6) / 4;  // dwords covering S bytes at any 4-byte phase
+    constexpr int CB = 8;            // coordinates whose codes are in flight together
+    for (int q0 = lg; q0 < NS; q0 += tpg * CB) {
+      uint32_t w[CB][ND];
+      float xv[CB];
 #pragma unroll
-      for (int d = 0; d < ND; ++d) w[d] = wp[d];
+      for (int u = 0; u < CB; ++u) {
+        const int q = q0 + u * tpg;
+        if (q < NS) {
+          const int ci = sl[b * NS + q];
+          xv[u] = xsel[b * NS + q];
+          const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + (size_t)ci * a.unit);
 #pragma unroll
-      for (int k = 0; k < S; ++k) {
-        const int bit = sh + 8 * k;
-        const int wi = bit >> 5, bo = bit & 31;
-        uint32_t byte = wi < ND ? (w[wi < ND ? wi : 0] >> bo) & 0xFFu : 0u;
-        if (k < nb_slice) {
+          for (int d = 0; d < ND; ++d) w[u][d] = wp[d];
+        } else {
+          xv[u] = 0.f;
 #pragma unroll
-          for (int d = 0; d < 5; ++d) {
-            const uint32_t dig = byte % 3u;
-            byte /= 3u;
-            acc[5 * k + d] = fmaf((float)((int)dig - 1), xv, acc[5 * k + d]);
+          for (int d = 0; d < ND; ++d) w[u][d] = 0u;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+          const int bit = sh + 8 * k;
+          const int wi = bit >> 5, bo = bit & 31;
+          uint32_t byte = wi < ND ? (w[u][wi < ND ? wi : 0] >> bo) & 0xFFu : 0u;
+          if (k < nb_slice) {
+#pragma unroll
+            for (int d = 0; d < 5; ++d) {
+              const uint32_t dig = byte % 3u;
+              byte /= 3u;
+              acc[5 * k + d] = fmaf((float)((int)dig - 1), xv[u], acc[5 * k + d]);
+            }
           }
         }
       }
@@ -368,7 +416,7 @@ struct SelectArgs {
   float* coef;
   float* zpart;
   int32_t* status;
-  int H, E, I, top, ncand, k, rank, G, share_max;
+  int H, E, I, top, ncand, k, rank, G, share_max, ZW;
   int dense;  // 1: every candidate is kept (the dense baseline); scores unused
 };
 
@@ -385,14 +433,47 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   float* zred = reinterpret_cast<float*>(smem + L.zred);
   int* hist = reinterpret_cast<int*>(smem + L.misc);
   int* misc = hist + 256;  // [0..3] scan scratch, [8] digit, [9] need, [10] done, [11] bin count
+  int* sl_e = misc + 12;   // routed expert of each slot (16)
+  float* sl_w = reinterpret_cast<float*>(misc + 28);  // its routing weight (16)
 
-  const float* xt = a.x + (size_t)t * H;
-  for (int q = tid * 4; q < H; q += kThreads * 4)
-    *reinterpret_cast<float4*>(xs + q) = *reinterpret_cast<const float4*>(xt + q);
   const bool partial = !a.dense && k > 0 && k < nc;
-  if (partial) {
-    const float* sct = a.score + (size_t)t * nc;
-    for (int q = tid; q < nc; q += kThreads) keys[q] = __float_as_uint(sct[q]);
+  const bool all = a.dense || k == nc;
+  // loads first: routing of the token, the token itself, its scores
+  if (tid < a.top) {
+    sl_e[tid] = clamp_expert(a.ids[t * a.top + tid], a.E, a.status);
+    sl_w[tid] = a.gw[t * a.top + tid];
+  }
+  const float* xt = a.x + (size_t)t * H;
+  {
+    float4 xr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = (tid + u * kThreads) * 4;
+      if (q < H) xr[u] = *reinterpret_cast<const float4*>(xt + q);
+    }
+    if (partial) {
+      const float* sct = a.score + (size_t)t * nc;
+      for (int q0 = 0; q0 < nc; q0 += kThreads * 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int q = q0 + tid + u * kThreads;
+          v[u] = q < nc ? sct[q] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int q = q0 + tid + u * kThreads;
+          if (q < nc) keys[q] = __float_as_uint(v[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = (tid + u * kThreads) * 4;
+      if (q < H) *reinterpret_cast<float4*>(xs + q) = xr[u];
+    }
+    for (int q = (tid + 4 * kThreads) * 4; q < H; q += kThreads * 4)  // hidden above 4096
+      *reinterpret_cast<float4*>(xs + q) = *reinterpret_cast<const float4*>(xt + q);
   }
   // each thread owns a contiguous chunk of candidates
   const int per = (nc + kThreads - 1) / kThreads;
@@ -443,7 +524,6 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   const int eq_before = eq_incl - neq;
   int take_eq = 0;
   if (partial) take_eq = max(0, min(neq, need - eq_before));
-  const bool all = a.dense || k == nc;
   const int mine = partial ? ngt + take_eq : (all ? hi - lo : 0);
   const int pos_incl = block_scan_256(mine, misc);
   int rnk = pos_incl - mine;
@@ -469,65 +549,105 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   __syncthreads();
 
   // ---- decode step (3): exact kept channels from native BF16 rows ----
+  // one kept channel per wave; all of its gate and up loads in flight together
   for (int q = wave; q < r1 - r0; q += 4) {
     const int cnd = list[q];
     const int sl = cnd / I, j = cnd % I;
-    const int e = clamp_expert(a.ids[t * a.top + sl], a.E, a.status);
-    const size_t row = (size_t)e * I + j;
+    const size_t row = (size_t)sl_e[sl] * I + j;
     const uint16_t* gr = a.w3 + row * 3 * H;
     float gsum = 0.f, vsum = 0.f;
-    for (int h = lane * 8; h < H; h += 512) {
-      const uint4 gq = *reinterpret_cast<const uint4*>(gr + h);
-      const uint4 vq = *reinterpret_cast<const uint4*>(gr + H + h);
-      const float4 x0 = *reinterpret_cast<const float4*>(xs + h);
-      const float4 x1 = *reinterpret_cast<const float4*>(xs + h + 4);
-      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      const uint32_t gu[4] = {gq.x, gq.y, gq.z, gq.w};
-      const uint32_t vu[4] = {vq.x, vq.y, vq.z, vq.w};
+    for (int hb = 0; hb < H; hb += 512 * 8) {
+      uint4 gq[8], vq[8];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        gsum = fmaf(__uint_as_float(gu[d] << 16), xv[2 * d], gsum);
-        gsum = fmaf(__uint_as_float(gu[d] & 0xFFFF0000u), xv[2 * d + 1], gsum);
-        vsum = fmaf(__uint_as_float(vu[d] << 16), xv[2 * d], vsum);
-        vsum = fmaf(__uint_as_float(vu[d] & 0xFFFF0000u), xv[2 * d + 1], vsum);
+      for (int u = 0; u < 8; ++u) {
+        const int h = hb + u * 512 + lane * 8;
+        if (h < H) {
+          gq[u] = *reinterpret_cast<const uint4*>(gr + h);
+          vq[u] = *reinterpret_cast<const uint4*>(gr + H + h);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int h = hb + u * 512 + lane * 8;
+        if (h < H) {
+          const float4 x0 = *reinterpret_cast<const float4*>(xs + h);
+          const float4 x1 = *reinterpret_cast<const float4*>(xs + h + 4);
+          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          const uint32_t gu[4] = {gq[u].x, gq[u].y, gq[u].z, gq[u].w};
+          const uint32_t vu[4] = {vq[u].x, vq[u].y, vq[u].z, vq[u].w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            gsum = fmaf(__uint_as_float(gu[d] << 16), xv[2 * d], gsum);
+            gsum = fmaf(__uint_as_float(gu[d] & 0xFFFF0000u), xv[2 * d + 1], gsum);
+            vsum = fmaf(__uint_as_float(vu[d] << 16), xv[2 * d], vsum);
+            vsum = fmaf(__uint_as_float(vu[d] & 0xFFFF0000u), xv[2 * d + 1], vsum);
+          }
+        }
       }
     }
     gsum = wave_sum(gsum);
     vsum = wave_sum(vsum);
     if (lane == 0) {
       const size_t o = (size_t)t * nc + r0 + q;
-      a.coef[o] = a.gw[t * a.top + sl] * silu(gsum) * vsum;
+      a.coef[o] = sl_w[sl] * silu(gsum) * vsum;
       a.rowidx[o] = (int32_t)row;
       a.kept[o] = cnd;
     }
   }
 
-  // ---- decode step (4), first half: z over this workgroup's skipped candidates ----
-  if (a.rank > 0 && !all) {
-    const int zper = (nc + a.G - 1) / a.G;
+  // ---- decode step (4), first half: z over a range of skipped candidates ----
+  // the first ZW workgroups of the token each take nc/ZW candidates, one per
+  // thread at a time, with all R coefficients of a candidate loaded at once
+  if (a.rank > 0 && !all && w < a.ZW) {
+    const int R = a.rank, R8 = R / 8;
+    const int zper = (nc + a.ZW - 1) / a.ZW;
     const int c0 = min(w * zper, nc), c1 = min(c0 + zper, nc);
-    const int R = a.rank;
-    const int rl = tid % R, grp = tid / R, ngrp = kThreads / R;
-    float zacc = 0.f;
-    if (grp < ngrp)
-      for (int cnd = c0 + grp; cnd < c1; cnd += ngrp) {
-        if (flags[cnd]) continue;
-        const int sl = cnd / I, j = cnd % I;
-        const int e = clamp_expert(a.ids[t * a.top + sl], a.E, a.status);
-        const float cf = a.gw[t * a.top + sl] * a.pact[(size_t)t * nc + cnd];
-        zacc = fmaf(cf, f16f(a.bmat[((size_t)e * I + j) * R + rl]), zacc);
+    float zacc[64];
+#pragma unroll
+    for (int r = 0; r < 64; ++r) zacc[r] = 0.f;
+    for (int cb = c0; cb < c1; cb += kThreads * 2) {
+      float cf[2];
+      uint4 bq[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int cnd = cb + tid + u * kThreads;
+        cf[u] = 0.f;
+        if (cnd < c1 && !flags[cnd]) {
+          const int sl = cnd / I, j = cnd % I;
+          cf[u] = sl_w[sl] * a.pact[(size_t)t * nc + cnd];
+          const uint4* bp = reinterpret_cast<const uint4*>(a.bmat + ((size_t)sl_e[sl] * I + j) * R);
+#pragma unroll
+          for (int r8 = 0; r8 < 8; ++r8)
+            if (r8 < R8) bq[u][r8] = bp[r8];
+        } else {
+#pragma unroll
+          for (int r8 = 0; r8 < 8; ++r8) bq[u][r8] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
-    if (grp < 8 && grp < ngrp) zred[grp * R + rl] = zacc;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8)
+          if (r8 < R8) {
+            const uint32_t bw[4] = {bq[u][r8].x, bq[u][r8].y, bq[u][r8].z, bq[u][r8].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              zacc[8 * r8 + 2 * d] = fmaf(cf[u], f16f((uint16_t)(bw[d] & 0xFFFFu)), zacc[8 * r8 + 2 * d]);
+              zacc[8 * r8 + 2 * d + 1] = fmaf(cf[u], f16f((uint16_t)(bw[d] >> 16)), zacc[8 * r8 + 2 * d + 1]);
+            }
+          }
+    }
+    // reduce the R sums over the workgroup: waves, then LDS across 4 waves
+#pragma unroll
+    for (int r = 0; r < 64; ++r)
+      if (r < R) {
+        const float v = wave_sum(zacc[r]);
+        if (lane == 0) zred[wave * R + r] = v;
+      }
     __syncthreads();
-    for (int g2 = 8; g2 < ngrp; ++g2) {  // only when rank < 32
-      if (grp == g2) zred[rl] += zacc;
-      __syncthreads();
-    }
-    if (tid < R) {
-      float z = 0.f;
-      for (int g2 = 0; g2 < min(8, ngrp); ++g2) z += zred[g2 * R + tid];
-      a.zpart[((size_t)t * a.G + w) * R + tid] = z;
-    }
+    if (tid < R)
+      a.zpart[((size_t)t * a.ZW + w) * R + tid] =
+          zred[tid] + zred[R + tid] + zred[2 * R + tid] + zred[3 * R + tid];
   }
 }
 
@@ -541,11 +661,12 @@ struct DownArgs {
   const float* coef;
   const float* zpart;
   float* y;
-  int H, ncand, k, rank, G, nz, nhs, items, per_xcd;
+  int H, ncand, k, rank, nz, nhs, items, per_xcd;
 };
 
 template <int HS>
 __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
+  __shared__ float zl[16 * 64];
   __shared__ float zs[64];
   __shared__ float part[4][HS];
   const int item = xcd_item(blockIdx.x, a.per_xcd);
@@ -553,36 +674,67 @@ __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
   const int t = item / a.nhs, hs = item % a.nhs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, h0 = hs * HS;
-  if (tid < 64) {
-    float z = 0.f;
-    if (tid < a.rank)
-      for (int q = 0; q < a.nz; ++q) z += a.zpart[((size_t)t * a.G + q) * a.rank + tid];
-    zs[tid] = z;
+  const int nzv = a.nz * a.rank;  // at most 16 * 64 partial values
+  {
+    float zv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + u * kThreads;
+      zv[u] = q < nzv ? a.zpart[(size_t)t * nzv + q] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = tid + u * kThreads;
+      if (q < nzv) zl[q] = zv[u];
+    }
   }
+  constexpr int RB = HS >= 64 ? 1 : 64 / HS;  // kept rows in flight per thread
   float acc[HS];
 #pragma unroll
   for (int q = 0; q < HS; ++q) acc[q] = 0.f;
   const int32_t* ri = a.rowidx + (size_t)t * a.ncand;
-  const float* cf = a.coef + (size_t)t * a.ncand;
-  for (int r = tid; r < a.k; r += kThreads) {
-    const float c = cf[r];
-    const uint16_t* d = a.w3 + ((size_t)ri[r] * 3 + 2) * H + h0;
+  const float* cfp = a.coef + (size_t)t * a.ncand;
+  for (int rb = tid; rb < a.k; rb += kThreads * RB) {
+    int rows[RB];
+    float cf[RB];
 #pragma unroll
-    for (int q = 0; q < HS; q += 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(d + q);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        acc[q + 2 * p] = fmaf(c, __uint_as_float(u[p] << 16), acc[q + 2 * p]);
-        acc[q + 2 * p + 1] = fmaf(c, __uint_as_float(u[p] & 0xFFFF0000u), acc[q + 2 * p + 1]);
-      }
+    for (int u = 0; u < RB; ++u) {
+      const int r = rb + u * kThreads;
+      rows[u] = r < a.k ? ri[r] : -1;
+      cf[u] = r < a.k ? cfp[r] : 0.f;
     }
+    uint4 dv[RB][HS / 8];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const uint16_t* d = a.w3 + ((size_t)(rows[u] < 0 ? 0 : rows[u]) * 3 + 2) * H + h0;
+#pragma unroll
+      for (int q = 0; q < HS / 8; ++q)
+        dv[u][q] = rows[u] >= 0 ? *reinterpret_cast<const uint4*>(d + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int q = 0; q < HS / 8; ++q) {
+        const uint32_t dw[4] = {dv[u][q].x, dv[u][q].y, dv[u][q].z, dv[u][q].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          acc[8 * q + 2 * p] = fmaf(cf[u], __uint_as_float(dw[p] << 16), acc[8 * q + 2 * p]);
+          acc[8 * q + 2 * p + 1] = fmaf(cf[u], __uint_as_float(dw[p] & 0xFFFF0000u), acc[8 * q + 2 * p + 1]);
+        }
+      }
   }
 #pragma unroll
   for (int q = 0; q < HS; ++q) acc[q] = wave_sum(acc[q]);
   if (lane == 0)
 #pragma unroll
     for (int q = 0; q < HS; ++q) part[wave][q] = acc[q];
+  __syncthreads();
+  if (tid < 64) {
+    float z = 0.f;
+    if (tid < a.rank)
+      for (int q = 0; q < a.nz; ++q) z += zl[q * a.rank + tid];
+    zs[tid] = z;
+  }
   __syncthreads();
   if (tid < HS) {
     const int h = h0 + tid;
@@ -621,6 +773,7 @@ Plan make_plan(const cfr_config& c, int batch, int k) {
   if (g > per4) g = per4 < 4 ? 4 : per4;
   p.G = g;
   p.share_max = (k + g - 1) / g;
+  p.ZW = g < 16 ? g : 16;
   p.ldsB = SelectLds(c.hidden, nc, p.share_max, c.rank).total;
   // C: hidden slices per token (8..64 hidden units each)
   int hsl = 8;
@@ -642,14 +795,7 @@ size_t max_lds_needed(const cfr_config& c) {
   return m;
 }
 
-size_t zpart_rows(const cfr_config& c) {
-  size_t m = 0;
-  for (int b = 1; b <= c.max_batch; ++b) {
-    const int g = 256 / b < 4 ? 4 : 256 / b;  // the largest G make_plan can pick at batch b
-    if ((size_t)b * g > m) m = (size_t)b * g;
-  }
-  return m;
-}
+size_t zpart_rows(const cfr_config& c) { return (size_t)c.max_batch * 16; }
 
 template <int S>
 static hipError_t launch_A(const ScreenArgs& a, const Plan& p, hipStream_t st) {
@@ -717,12 +863,12 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   mark(1);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->score, r->pact, r->kept, r->rowidx, r->coef,
                r->zpart, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand, k,
-               c.rank, p.G, p.share_max, 0};
+               c.rank, p.G, p.share_max, p.ZW, 0};
   if ((e = launch_B(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
-  const int nz = (c.rank > 0 && k < r->ncand) ? p.G : 0;
+  const int nz = (c.rank > 0 && k < r->ncand) ? p.ZW : 0;
   DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, r->ncand, k,
-             c.rank, p.G, nz, p.nhs, p.itemsC, p.per_xcdC};
+             c.rank, nz, p.nhs, p.itemsC, p.per_xcdC};
   if ((e = launch_C_any(C, p, st)) != hipSuccess) return hip_fail(e, "down launch");
   mark(3);
   if (dbg) {
@@ -756,10 +902,10 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   p.ldsB = SelectLds(c.hidden, nc, p.share_max, 0).total;
   SelectArgs B{x, ids, gw, r->w3, r->b, r->score, r->pact, r->kept, r->rowidx, r->coef,
                r->zpart, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, nc, 0, p.G,
-               p.share_max, 1};
+               p.share_max, 0, 1};
   hipError_t e;
   if ((e = launch_B(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
-  DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, nc, nc, 0, p.G, 0,
+  DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, nc, nc, 0, 0,
              p.nhs, p.itemsC, p.per_xcdC};
   if ((e = launch_C_any(C, p, st)) != hipSuccess) return hip_fail(e, "dense down launch");
   return CFR_OK;

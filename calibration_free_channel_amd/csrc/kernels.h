@@ -47,9 +47,9 @@ struct SelectLds {
     list = o;
     o += lds_align((size_t)(share_max > 0 ? share_max : 1) * 4);
     zred = o;
-    o += lds_align((size_t)8 * (rank > 0 ? rank : 1) * 4);
+    o += lds_align((size_t)4 * (rank > 0 ? rank : 1) * 4);
     misc = o;
-    o += lds_align((256 + 32) * 4);
+    o += lds_align((256 + 48) * 4);
     total = o;
   }
 };
@@ -57,7 +57,7 @@ struct SelectLds {
 // Launch geometry of one decode call.
 struct Plan {
   int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0, CH = 4;  // screen
-  int G = 4, share_max = 0;                                  // select/exact
+  int G = 4, share_max = 0, ZW = 4;                          // select/exact
   int HS = 8, nhs = 0, itemsC = 0, per_xcdC = 0;             // down/recover
   size_t ldsA = 0, ldsB = 0;
 };

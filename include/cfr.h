@@ -55,7 +55,7 @@ typedef struct cfr_config {
   int32_t n_experts;  /* E: experts in the layer                                        */
   int32_t inter;      /* I: channels per expert (expert intermediate size), 1..4096     */
   int32_t top;        /* routed experts per token, 1..16 and <= E                       */
-  int32_t rank;       /* recovery rank, 0..64 (the pages use 32)                        */
+  int32_t rank;       /* recovery rank, 0..64, a multiple of 8 (the pages use 32)       */
   int32_t n_screen;   /* coordinates screened per 128-block, 1..128 (the pages use 80) */
   int32_t max_batch;  /* largest batch a decode call may pass, 1..64                    */
   int32_t device;     /* HIP device ordinal the reader lives on                         */

@@ -56,7 +56,7 @@ def test_read_bytes_match_oracle_accounting(k):
 
 
 @pytest.mark.parametrize("bad", [dict(hidden=200), dict(hidden=0), dict(top=0), dict(top=17),
-                                 dict(n_screen=0), dict(n_screen=129), dict(rank=65),
+                                 dict(n_screen=0), dict(n_screen=129), dict(rank=65), dict(rank=12),
                                  dict(max_batch=0), dict(inter=0), dict(inter=5000),
                                  dict(n_experts=1, top=2)])
 def test_invalid_configs_rejected(bad):
