@@ -30,6 +30,8 @@ int validate_config(const cfr_config* c) {
   if (c->rank < 0 || c->rank > c->hidden) return fail(CFR_EINVAL, "rank must be in 0..hidden");
   if (c->rank > kMaxRank) return fail(CFR_EUNSUPPORTED, "rank above 64");
   if (c->rank % 8 != 0) return fail(CFR_EUNSUPPORTED, "rank must be a multiple of 8");
+  if ((int64_t)c->top * c->inter > 16384)
+    return fail(CFR_EUNSUPPORTED, "top * inter above 16384 candidates per token");
   if (c->n_screen < 1 || c->n_screen > kBlock) return fail(CFR_EINVAL, "n_screen must be in 1..128");
   if (c->max_batch < 1) return fail(CFR_EINVAL, "max_batch must be at least 1");
   if (c->max_batch > kMaxBatch) return fail(CFR_EUNSUPPORTED, "max_batch above 64");

@@ -42,6 +42,7 @@ namespace {
 
 constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
 constexpr int kThreads = 256;
+constexpr int kScreenThreads = 512;
 constexpr int kMaxS = 13;  // bytes per half handled by one screen workgroup
 
 __device__ __forceinline__ float f16f(uint16_t h) {
@@ -104,42 +105,100 @@ struct ScreenArgs {
   float* pact;
   float* score;
   int32_t* status;
-  int H, E, I, top, nblk, n_screen, lp, unit, n_slices, items, per_xcd, CH, dbg;
+  int H, E, I, top, nblk, n_screen, lp, unit, n_slices, items, per_xcd, dbg;
 };
 
+// One wave rotates and screens one 128-block held as two values per lane
+// (lane l holds coordinates l and l + 64).  The float32 butterfly runs the
+// stages h = 1 .. 32 across lanes and h = 64 inside the lane, in that order,
+// with the lower element of each pair taking a + b and the upper a - b.
+// The n_screen largest |v| (ties to the lower index) are found by a
+// bit-by-bit search of the n_screen-th largest magnitude over wave ballots,
+// then compacted in ascending coordinate order.
+__device__ __forceinline__ void rotate_select_block(float v0, float v1, int b, int NS,
+                                                    uint8_t* sl, float* xsel, float* xrot_out) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const float o0 = __shfl_xor(v0, h, 64);
+    const float o1 = __shfl_xor(v1, h, 64);
+    if (lane & h) {
+      v0 = o0 - v0;
+      v1 = o1 - v1;
+    } else {
+      v0 = v0 + o0;
+      v1 = v1 + o1;
+    }
+  }
+  {
+    const float u = v0;
+    v0 = u + v1;
+    v1 = u - v1;
+  }
+  if (xrot_out) {
+    xrot_out[lane] = v0;
+    xrot_out[lane + 64] = v1;
+  }
+  const uint32_t k0 = __float_as_uint(v0) & 0x7FFFFFFFu;
+  const uint32_t k1 = __float_as_uint(v1) & 0x7FFFFFFFu;
+  uint32_t T = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
+    if (cnt >= NS) T = cand;
+  }
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const unsigned long long gt0 = __ballot(k0 > T), gt1 = __ballot(k1 > T);
+  const unsigned long long eq0 = __ballot(k0 == T), eq1 = __ballot(k1 == T);
+  const int need = NS - __popcll(gt0) - __popcll(gt1);
+  const bool s0 = k0 > T || (k0 == T && __popcll(eq0 & lt) < need);
+  const bool s1 = k1 > T || (k1 == T && __popcll(eq0) + __popcll(eq1 & lt) < need);
+  const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+  if (s0) {
+    const int pos = __popcll(m0 & lt);
+    if (pos < NS) {
+      sl[b * NS + pos] = (uint8_t)lane;
+      xsel[b * NS + pos] = v0;
+    }
+  }
+  if (s1) {
+    const int pos = __popcll(m0) + __popcll(m1 & lt);
+    if (pos < NS) {
+      sl[b * NS + pos] = (uint8_t)(lane + 64);
+      xsel[b * NS + pos] = v1;
+    }
+  }
+}
+
 template <int S>
-__global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
+__global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
   const int c = item % a.n_slices;
   const int ts = item / a.n_slices;
   const int s = ts % a.top, t = ts / a.top;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = kScreenThreads / 64;
   const int H = a.H, I = a.I, nblk = a.nblk, NS = a.n_screen;
   constexpr int NCH = 5 * S;  // channels per half in this slice
-  const ScreenLds L(H, nblk, NS, S, a.CH);
-  float* xs = reinterpret_cast<float*>(smem + L.xs);
-  int* hist = reinterpret_cast<int*>(smem + L.uni);
-  float* red = reinterpret_cast<float*>(smem + L.uni);
-  uint32_t* st_pref = reinterpret_cast<uint32_t*>(smem + L.st);
-  uint32_t* st_msk = st_pref + nblk;
-  int* st_need = reinterpret_cast<int*>(st_msk + nblk);
-  int* st_done = st_need + nblk;
+  const ScreenLds L(nblk, NS, S);
+  uint4* lut = reinterpret_cast<uint4*>(smem + L.lut);
   uint8_t* sl = smem + L.sl;
   float* xsel = reinterpret_cast<float*>(smem + L.xsel);
   float* sc = reinterpret_cast<float*>(smem + L.sc);
+  float* red = reinterpret_cast<float*>(smem + L.red);
 
-  // issue the token and sign loads first; they do not depend on the routing
+  // token and signs of this wave's first blocks: independent of the routing
   const float* xt = a.x + (size_t)t * H;
-  float4 xr[4], sg[4];
+  float xv0[4], xv1[4], sg0[4], sg1[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = (tid + u * kThreads) * 4;
-    if (q < H) {
-      xr[u] = *reinterpret_cast<const float4*>(xt + q);
-      sg[u] = *reinterpret_cast<const float4*>(a.sigma + q);
-    }
+  for (int u = 0; u < 4; ++u) {  // clamped addresses: every load is issued, none waits
+    const int b = min(wave + u * NW, nblk - 1);
+    xv0[u] = xt[b * 128 + lane];
+    xv1[u] = xt[b * 128 + 64 + lane];
+    sg0[u] = a.sigma[b * 128 + lane];
+    sg1[u] = a.sigma[b * 128 + 64 + lane];
   }
   const int e = clamp_expert(a.ids[t * a.top + s], a.E, a.status);
   const float wgt = a.gw[t * a.top + s];
@@ -148,179 +207,67 @@ __global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
 
   // scales of the slice for every block and half, and the slice's norms
   const int nsc = nblk * 2 * NCH;
-  for (int q0 = 0; q0 < nsc; q0 += kThreads * 8) {
-    uint16_t hv[8];
+  for (int q0 = 0; q0 < nsc; q0 += kScreenThreads * 4) {
+    uint16_t hv[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int q = q0 + tid + u * kThreads;
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + tid + u * kScreenThreads;
       const int jj = q % NCH, bm = q / NCH;  // bm = block * 2 + half
       const int j = j0 + jj;
-      hv[u] = (q < nsc && j < I)
-                  ? a.scales[((size_t)e * nblk + (bm >> 1)) * 2 * I + (bm & 1) * I + j]
-                  : (uint16_t)0;
+      const bool ok = q < nsc && j < I;
+      const size_t ix = ok ? ((size_t)e * nblk + (bm >> 1)) * 2 * I + (bm & 1) * I + j : 0;
+      hv[u] = a.scales[ix];
+      hv[u] = ok ? hv[u] : (uint16_t)0;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int q = q0 + tid + u * kThreads;
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + tid + u * kScreenThreads;
       if (q < nsc) sc[q] = f16f(hv[u]);
     }
   }
   float nrm = 0.f;
   if (tid < NCH && j0 + tid < I) nrm = a.norms[(size_t)e * I + j0 + tid];
 
-  // ---- decode step (1): rotation, float32 butterfly per 128-block ----
+  // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
+  // 243..255 never occur in a packed unit and decode to zero)
+  if (tid < 256) {
+    uint32_t h[5] = {0u, 0u, 0u, 0u, 0u};
+    if (tid < 243) {
+      int q = tid;
+#pragma unroll
+      for (int d = 0; d < 5; ++d) {
+        const int dig = q % 3;
+        q /= 3;
+        h[d] = dig == 0 ? 0xBC00u : (dig == 2 ? 0x3C00u : 0u);
+      }
+    }
+    lut[tid] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u);
+  }
+
+  // ---- decode step (1): rotation and the partial-screen coordinates ----
+  const bool writer = a.dbg && c == 0 && s == 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int q = (tid + u * kThreads) * 4;
-    if (q < H) {
-      xs[q] = xr[u].x * sg[u].x;
-      xs[q + 1] = xr[u].y * sg[u].y;
-      xs[q + 2] = xr[u].z * sg[u].z;
-      xs[q + 3] = xr[u].w * sg[u].w;
-    }
+    const int b = wave + u * NW;
+    if (b < nblk)
+      rotate_select_block(xv0[u] * sg0[u], xv1[u] * sg1[u], b, NS, sl, xsel,
+                          writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
   }
-  for (int q = (tid + 4 * kThreads) * 4; q < H; q += kThreads * 4) {  // hidden above 4096
-    const float4 v = *reinterpret_cast<const float4*>(xt + q);
-    const float4 g = *reinterpret_cast<const float4*>(a.sigma + q);
-    xs[q] = v.x * g.x;
-    xs[q + 1] = v.y * g.y;
-    xs[q + 2] = v.z * g.z;
-    xs[q + 3] = v.w * g.w;
-  }
-  for (int h = 1; h < 128; h <<= 1) {
-    __syncthreads();
-    for (int p = tid; p < H / 2; p += kThreads) {
-      const int blk = p >> 6, r = p & 63;
-      const int i = blk * 128 + (r / h) * 2 * h + (r % h);
-      const float u = xs[i], v = xs[i + h];
-      xs[i] = u + v;
-      xs[i + h] = u - v;
-    }
-  }
-  __syncthreads();
-  const bool writer = a.dbg && c == 0 && s == 0;
-  if (writer)
-    for (int q = tid; q < H; q += kThreads) a.xrot[(size_t)t * H + q] = xs[q];
-
-  // ---- partial screen: per block, the NS coordinates of largest |v| ----
-  // radix select on the 31 magnitude bits, MSB first, ties to the lower index
-  const int CH = a.CH, tpb = kThreads / CH, ept = 128 / tpb;
-  const int bl = tid / tpb, ln = tid % tpb;
-  const int nbt = 256 / tpb;
-  for (int cb0 = 0; cb0 < nblk; cb0 += CH) {
-    const int b = cb0 + bl;
-    const bool act = b < nblk;
-    if (act && ln == 0) {
-      st_pref[b] = 0u;
-      st_msk[b] = 0u;
-      st_need[b] = NS;
-      st_done[b] = 0;
-    }
-    uint32_t key[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      key[q] = (act && q < ept) ? (__float_as_uint(xs[b * 128 + ln * ept + q]) & 0x7FFFFFFFu) : 0u;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
-      const uint32_t dm = pass == 3 ? 0x7Fu : 0xFFu;
-      __syncthreads();
-      for (int q = tid; q < CH * 256; q += kThreads) hist[q] = 0;
-      __syncthreads();
-      const bool work = act && !st_done[b];
-      if (work) {
-        const uint32_t pf = st_pref[b], mk = st_msk[b];
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (q < ept && (key[q] & mk) == pf)
-            atomicAdd(&hist[bl * 256 + ((key[q] >> shift) & dm)], 1);
-      }
-      __syncthreads();
-      int loc = 0;
-      if (work)
-        for (int d = 0; d < nbt; ++d) loc += hist[bl * 256 + ln * nbt + d];
-      int suf = loc;  // inclusive suffix sum over the tpb lanes of this block
-      for (int off = 1; off < tpb; off <<= 1) {
-        const int o = __shfl_down(suf, off, tpb);
-        if (ln + off < tpb) suf += o;
-      }
-      if (work) {
-        const int need = st_need[b];
-        const int above = suf - loc;
-        if (above < need && suf >= need) {
-          int cum = above;
-          for (int d = ln * nbt + nbt - 1; d >= ln * nbt; --d) {
-            const int hc = hist[bl * 256 + d];
-            if (cum + hc >= need) {
-              st_pref[b] |= (uint32_t)d << shift;
-              st_msk[b] |= dm << shift;
-              st_need[b] = need - cum;
-              if (hc == need - cum) st_done[b] = 1;
-              break;
-            }
-            cum += hc;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // final rule and ascending compaction
-    {
-      const uint32_t pf = act ? st_pref[b] : 0u, mk = act ? st_msk[b] : 0u;
-      const int need = act ? st_need[b] : 0;
-      int neq = 0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (act && q < ept) neq += (key[q] & mk) == pf;
-      int eqb = neq;  // prefix of equal keys over lanes
-      for (int off = 1; off < tpb; off <<= 1) {
-        const int o = __shfl_up(eqb, off, tpb);
-        if (ln >= off) eqb += o;
-      }
-      eqb -= neq;
-      uint32_t selmask = 0;
-      int nsel = 0, er = eqb;
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (act && q < ept) {
-          const uint32_t km = key[q] & mk;
-          bool on = km > pf;
-          if (km == pf) {
-            on = er < need;
-            ++er;
-          }
-          if (on) {
-            selmask |= 1u << q;
-            ++nsel;
-          }
-        }
-      int pos = nsel;
-      for (int off = 1; off < tpb; off <<= 1) {
-        const int o = __shfl_up(pos, off, tpb);
-        if (ln >= off) pos += o;
-      }
-      pos -= nsel;
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if ((selmask >> q) & 1u) {
-          if (pos < NS) {
-            const int i = ln * ept + q;
-            sl[b * NS + pos] = (uint8_t)i;
-            xsel[b * NS + pos] = xs[b * 128 + i];
-          }
-          ++pos;
-        }
-    }
+  for (int b = wave + 4 * NW; b < nblk; b += NW) {  // hidden above 4096
+    const float v0 = xt[b * 128 + lane] * a.sigma[b * 128 + lane];
+    const float v1 = xt[b * 128 + 64 + lane] * a.sigma[b * 128 + 64 + lane];
+    rotate_select_block(v0, v1, b, NS, sl, xsel, writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
   }
   __syncthreads();
   if (writer)
-    for (int q = tid; q < nblk * NS; q += kThreads) a.sel[(size_t)t * nblk * NS + q] = sl[q];
+    for (int q = tid; q < nblk * NS; q += kScreenThreads) a.sel[(size_t)t * nblk * NS + q] = sl[q];
 
   // ---- screen: codes of the slice at the screened coordinates ----
   // group g = (block, half) with tpg threads; each thread takes every
   // tpg-th screened coordinate of its block.
   const int groups = 2 * nblk;
   int tpg = 1;
-  while (tpg * 2 * groups <= kThreads) tpg *= 2;
+  while (tpg * 2 * groups <= kScreenThreads) tpg *= 2;
   const int g = tid / tpg, lg = tid % tpg;
   float acc[NCH];
 #pragma unroll
@@ -338,18 +285,15 @@ __global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
       float xv[CB];
 #pragma unroll
       for (int u = 0; u < CB; ++u) {
+        // clamped index: the load is always issued; a coordinate past the
+        // list contributes x = 0
         const int q = q0 + u * tpg;
-        if (q < NS) {
-          const int ci = sl[b * NS + q];
-          xv[u] = xsel[b * NS + q];
-          const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + (size_t)ci * a.unit);
+        const int qc = q < NS ? q : NS - 1;
+        const int ci = sl[b * NS + qc];
+        xv[u] = q < NS ? xsel[b * NS + qc] : 0.f;
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + (size_t)ci * a.unit);
 #pragma unroll
-          for (int d = 0; d < ND; ++d) w[u][d] = wp[d];
-        } else {
-          xv[u] = 0.f;
-#pragma unroll
-          for (int d = 0; d < ND; ++d) w[u][d] = 0u;
-        }
+        for (int d = 0; d < ND; ++d) w[u][d] = wp[d];
       }
 #pragma unroll
       for (int u = 0; u < CB; ++u) {
@@ -357,20 +301,20 @@ __global__ __launch_bounds__(kThreads) void k_screen_score(ScreenArgs a) {
         for (int k = 0; k < S; ++k) {
           const int bit = sh + 8 * k;
           const int wi = bit >> 5, bo = bit & 31;
-          uint32_t byte = wi < ND ? (w[u][wi < ND ? wi : 0] >> bo) & 0xFFu : 0u;
+          const uint32_t byte = wi < ND ? (w[u][wi < ND ? wi : 0] >> bo) & 0xFFu : 121u;
           if (k < nb_slice) {
+            const uint4 cw = lut[byte];
+            const uint32_t hw[3] = {cw.x, cw.y, cw.z};
 #pragma unroll
             for (int d = 0; d < 5; ++d) {
-              const uint32_t dig = byte % 3u;
-              byte /= 3u;
-              acc[5 * k + d] = fmaf((float)((int)dig - 1), xv[u], acc[5 * k + d]);
+              const uint16_t hb = (uint16_t)(hw[d >> 1] >> ((d & 1) * 16));
+              acc[5 * k + d] = fmaf((float)__builtin_bit_cast(_Float16, hb), xv[u], acc[5 * k + d]);
             }
           }
         }
       }
     }
   }
-  __syncthreads();  // the select histogram space becomes the reduction space
   if (g < groups) {
 #pragma unroll
     for (int q = 0; q < NCH; ++q) red[(size_t)tid * NCH + q] = acc[q];
@@ -420,6 +364,7 @@ struct SelectArgs {
   int dense;  // 1: every candidate is kept (the dense baseline); scores unused
 };
 
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int t = blockIdx.x / a.G, w = blockIdx.x % a.G;
@@ -431,9 +376,9 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   uint8_t* flags = smem + L.flags;
   int* list = reinterpret_cast<int*>(smem + L.list);
   float* zred = reinterpret_cast<float*>(smem + L.zred);
-  int* hist = reinterpret_cast<int*>(smem + L.misc);
-  int* misc = hist + 256;  // [0..3] scan scratch, [8] digit, [9] need, [10] done, [11] bin count
-  int* sl_e = misc + 12;   // routed expert of each slot (16)
+  int* hist = reinterpret_cast<int*>(smem + L.hist);  // 2048 bins
+  int* misc = reinterpret_cast<int*>(smem + L.misc);  // [0..3] scan, [8] digit, [9] need, [10] done, [11] bin count
+  int* sl_e = misc + 12;                              // routed expert of each slot (16)
   float* sl_w = reinterpret_cast<float*>(misc + 28);  // its routing weight (16)
 
   const bool partial = !a.dense && k > 0 && k < nc;
@@ -448,8 +393,13 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
     float4 xr[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const int q = min((tid + u * kThreads) * 4, H - 4);
+      xr[u] = *reinterpret_cast<const float4*>(xt + q);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       const int q = (tid + u * kThreads) * 4;
-      if (q < H) xr[u] = *reinterpret_cast<const float4*>(xt + q);
+      if (q < H) *reinterpret_cast<float4*>(xs + q) = xr[u];
     }
     if (partial) {
       const float* sct = a.score + (size_t)t * nc;
@@ -458,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int q = q0 + tid + u * kThreads;
-          v[u] = q < nc ? sct[q] : 0.f;
+          v[u] = sct[q < nc ? q : nc - 1];
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -467,59 +417,72 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = (tid + u * kThreads) * 4;
-      if (q < H) *reinterpret_cast<float4*>(xs + q) = xr[u];
-    }
     for (int q = (tid + 4 * kThreads) * 4; q < H; q += kThreads * 4)  // hidden above 4096
       *reinterpret_cast<float4*>(xs + q) = *reinterpret_cast<const float4*>(xt + q);
   }
-  // each thread owns a contiguous chunk of candidates
-  const int per = (nc + kThreads - 1) / kThreads;
-  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
-  uint32_t prefix = 0, mask = 0;
-  int need = k;
   if (tid == 0) misc[10] = 0;
   __syncthreads();
+  // each thread owns a contiguous chunk of at most KPT candidates, in registers
+  const int per = (nc + kThreads - 1) / kThreads;
+  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) kr[q] = (partial && lo + q < hi) ? keys[lo + q] : 0u;
+  uint32_t prefix = 0, mask = 0;
+  int need = k;
   if (partial) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
+    // exact k-th largest key: MSB-first radix select, 11 + 11 + 10 bits
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dm = pass == 2 ? 0x3FFu : 0x7FFu;
       const int done = misc[10];
-      if (!done)
-        for (int i = lo; i < hi; ++i) {
-          const uint32_t kv = keys[i];
-          if ((kv & mask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1);
+      if (done) break;  // uniform: read after a barrier
+#pragma unroll
+      for (int q = 0; q < 8; ++q) hist[tid * 8 + q] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < KPT; ++q)
+        if (lo + q < hi && (kr[q] & mask) == prefix) atomicAdd(&hist[(kr[q] >> shift) & dm], 1);
+      __syncthreads();
+      // thread tid holds the 8 bins [8(255 - tid), 8(255 - tid) + 8): descending digits
+      const int base = 8 * (255 - tid);
+      int bins[8], own = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        bins[q] = hist[base + q];
+        own += bins[q];
+      }
+      const int incl = block_scan_256(own, misc);  // keys with digit >= base
+      if (incl >= need && incl - own < need) {
+        int cum = incl - own;
+#pragma unroll
+        for (int q = 7; q >= 0; --q) {
+          if (cum < need && cum + bins[q] >= need) {
+            misc[8] = base + q;
+            misc[9] = need - cum;
+            misc[11] = bins[q];
+          }
+          cum += bins[q];
         }
-      __syncthreads();
-      const int own = hist[255 - tid];
-      const int incl = block_scan_256(own, misc);  // count of digits >= 255 - tid
-      if (!done && incl >= need && incl - own < need) {
-        misc[8] = 255 - tid;
-        misc[9] = need - (incl - own);
-        misc[11] = own;
       }
       __syncthreads();
-      if (!done) {
-        prefix |= (uint32_t)misc[8] << shift;
-        mask |= 255u << shift;
-        need = misc[9];
-      }
-      __syncthreads();
-      if (tid == 0 && !done && misc[11] == need) misc[10] = 1;  // every key of the bin is kept
+      prefix |= (uint32_t)misc[8] << shift;
+      mask |= dm << shift;
+      need = misc[9];
+      if (tid == 0 && misc[11] == need) misc[10] = 1;  // every key of that bin is kept
       __syncthreads();
     }
   }
   // kept flags and ranks in ascending candidate order
   int ngt = 0, neq = 0;
   if (partial)
-    for (int i = lo; i < hi; ++i) {
-      const uint32_t kv = keys[i] & mask;
-      ngt += kv > prefix;
-      neq += kv == prefix;
-    }
+#pragma unroll
+    for (int q = 0; q < KPT; ++q)
+      if (lo + q < hi) {
+        const uint32_t kv = kr[q] & mask;
+        ngt += kv > prefix;
+        neq += kv == prefix;
+      }
   const int eq_incl = block_scan_256(neq, misc);
   const int eq_before = eq_incl - neq;
   int take_eq = 0;
@@ -529,21 +492,30 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   int rnk = pos_incl - mine;
   const int share = (k + a.G - 1) / a.G;
   const int r0 = min(w * share, k), r1 = min(r0 + share, k);
-  int eq_seen = 0;
-  for (int i = lo; i < hi; ++i) {
-    bool on = all;
-    if (partial) {
-      const uint32_t kv = keys[i] & mask;
-      on = kv > prefix;
-      if (kv == prefix) {
-        on = eq_seen < take_eq;
-        ++eq_seen;
+  if (partial) {
+    int eq_seen = 0;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q)
+      if (lo + q < hi) {
+        const uint32_t kv = kr[q] & mask;
+        bool on = kv > prefix;
+        if (kv == prefix) {
+          on = eq_seen < take_eq;
+          ++eq_seen;
+        }
+        flags[lo + q] = on ? 1 : 0;
+        if (on) {
+          if (rnk >= r0 && rnk < r1) list[rnk - r0] = lo + q;
+          ++rnk;
+        }
       }
-    }
-    flags[i] = on ? 1 : 0;
-    if (on) {
-      if (rnk >= r0 && rnk < r1) list[rnk - r0] = i;
-      ++rnk;
+  } else {
+    for (int i = lo; i < hi; ++i) {
+      flags[i] = all ? 1 : 0;
+      if (all) {
+        if (rnk >= r0 && rnk < r1) list[rnk - r0] = i;
+        ++rnk;
+      }
     }
   }
   __syncthreads();
@@ -560,11 +532,9 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
       uint4 gq[8], vq[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int h = hb + u * 512 + lane * 8;
-        if (h < H) {
-          gq[u] = *reinterpret_cast<const uint4*>(gr + h);
-          vq[u] = *reinterpret_cast<const uint4*>(gr + H + h);
-        }
+        const int h = min(hb + u * 512 + lane * 8, H - 8);  // clamped; the tail is skipped below
+        gq[u] = *reinterpret_cast<const uint4*>(gr + h);
+        vq[u] = *reinterpret_cast<const uint4*>(gr + H + h);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -572,16 +542,22 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
         if (h < H) {
           const float4 x0 = *reinterpret_cast<const float4*>(xs + h);
           const float4 x1 = *reinterpret_cast<const float4*>(xs + h + 4);
-          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          const uint32_t gu[4] = {gq[u].x, gq[u].y, gq[u].z, gq[u].w};
-          const uint32_t vu[4] = {vq[u].x, vq[u].y, vq[u].z, vq[u].w};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            gsum = fmaf(__uint_as_float(gu[d] << 16), xv[2 * d], gsum);
-            gsum = fmaf(__uint_as_float(gu[d] & 0xFFFF0000u), xv[2 * d + 1], gsum);
-            vsum = fmaf(__uint_as_float(vu[d] << 16), xv[2 * d], vsum);
-            vsum = fmaf(__uint_as_float(vu[d] & 0xFFFF0000u), xv[2 * d + 1], vsum);
-          }
+          gsum = fmaf(__uint_as_float(gq[u].x << 16), x0.x, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].x & 0xFFFF0000u), x0.y, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].y << 16), x0.z, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].y & 0xFFFF0000u), x0.w, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].z << 16), x1.x, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].z & 0xFFFF0000u), x1.y, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].w << 16), x1.z, gsum);
+          gsum = fmaf(__uint_as_float(gq[u].w & 0xFFFF0000u), x1.w, gsum);
+          vsum = fmaf(__uint_as_float(vq[u].x << 16), x0.x, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].x & 0xFFFF0000u), x0.y, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].y << 16), x0.z, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].y & 0xFFFF0000u), x0.w, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].z << 16), x1.x, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].z & 0xFFFF0000u), x1.y, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].w << 16), x1.z, vsum);
+          vsum = fmaf(__uint_as_float(vq[u].w & 0xFFFF0000u), x1.w, vsum);
         }
       }
     }
@@ -596,58 +572,66 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   }
 
   // ---- decode step (4), first half: z over a range of skipped candidates ----
-  // the first ZW workgroups of the token each take nc/ZW candidates, one per
-  // thread at a time, with all R coefficients of a candidate loaded at once
+  // the first ZW workgroups of the token each take nc/ZW candidates; a
+  // thread handles 8 coefficients (one uint4) of one candidate at a time
   if (a.rank > 0 && !all && w < a.ZW) {
     const int R = a.rank, R8 = R / 8;
     const int zper = (nc + a.ZW - 1) / a.ZW;
     const int c0 = min(w * zper, nc), c1 = min(c0 + zper, nc);
-    float zacc[64];
+    const int cpp = kThreads / R8;  // candidates per pass
+    const int cl = tid / R8, r8 = tid % R8;
+    float zacc[8];
 #pragma unroll
-    for (int r = 0; r < 64; ++r) zacc[r] = 0.f;
-    for (int cb = c0; cb < c1; cb += kThreads * 2) {
-      float cf[2];
-      uint4 bq[2][8];
+    for (int d = 0; d < 8; ++d) zacc[d] = 0.f;
+    if (cl < cpp)
+      for (int cb = c0 + cl; cb < c1; cb += cpp * 4) {
+        float cf[4];
+        uint4 bq[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int cnd = cb + tid + u * kThreads;
-        cf[u] = 0.f;
-        if (cnd < c1 && !flags[cnd]) {
-          const int sl = cnd / I, j = cnd % I;
-          cf[u] = sl_w[sl] * a.pact[(size_t)t * nc + cnd];
-          const uint4* bp = reinterpret_cast<const uint4*>(a.bmat + ((size_t)sl_e[sl] * I + j) * R);
+        for (int u = 0; u < 4; ++u) {
+          const int cnd = cb + u * cpp;
+          const int cc = cnd < c1 ? cnd : c1 - 1;  // clamped: loads always issued
+          const int sl = cc / I, j = cc % I;
+          const float pv = a.pact[(size_t)t * nc + cc];
+          bq[u] = reinterpret_cast<const uint4*>(a.bmat + ((size_t)sl_e[sl] * I + j) * R)[r8];
+          cf[u] = (cnd < c1 && !flags[cc]) ? sl_w[sl] * pv : 0.f;
+        }
 #pragma unroll
-          for (int r8 = 0; r8 < 8; ++r8)
-            if (r8 < R8) bq[u][r8] = bp[r8];
-        } else {
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t bw[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
 #pragma unroll
-          for (int r8 = 0; r8 < 8; ++r8) bq[u][r8] = make_uint4(0u, 0u, 0u, 0u);
+          for (int d = 0; d < 4; ++d) {
+            zacc[2 * d] = fmaf(cf[u], f16f((uint16_t)(bw[d] & 0xFFFFu)), zacc[2 * d]);
+            zacc[2 * d + 1] = fmaf(cf[u], f16f((uint16_t)(bw[d] >> 16)), zacc[2 * d + 1]);
+          }
         }
       }
+    // reduce over candidates: lanes with equal r8 inside a wave, then waves
+    for (int q = 0; q < R * 4; q += kThreads)
+      if (q + tid < R * 4) zred[q + tid] = 0.f;
+    __syncthreads();
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8)
-          if (r8 < R8) {
-            const uint32_t bw[4] = {bq[u][r8].x, bq[u][r8].y, bq[u][r8].z, bq[u][r8].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              zacc[8 * r8 + 2 * d] = fmaf(cf[u], f16f((uint16_t)(bw[d] & 0xFFFFu)), zacc[8 * r8 + 2 * d]);
-              zacc[8 * r8 + 2 * d + 1] = fmaf(cf[u], f16f((uint16_t)(bw[d] >> 16)), zacc[8 * r8 + 2 * d + 1]);
-            }
-          }
+    for (int d = 0; d < 8; ++d) {
+      float v = zacc[d];
+      for (int off = R8; off < 64; off <<= 1)
+        if ((off / R8) * R8 == off) v += __shfl_xor(v, off, 64);
+      zacc[d] = v;
     }
-    // reduce the R sums over the workgroup: waves, then LDS across 4 waves
+    // lanes 0..R8-1 of each wave hold its sums when R8 is a power of two;
+    // otherwise fall back to shared-memory atomics
+    const bool pow2 = (R8 & (R8 - 1)) == 0;
+    if (pow2) {
+      if (lane < R8 && cl < cpp)
 #pragma unroll
-    for (int r = 0; r < 64; ++r)
-      if (r < R) {
-        const float v = wave_sum(zacc[r]);
-        if (lane == 0) zred[wave * R + r] = v;
-      }
+        for (int d = 0; d < 8; ++d) zred[wave * R + r8 * 8 + d] = zacc[d];
+    } else if (cl < cpp) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) atomicAdd(&zred[r8 * 8 + d], zacc[d]);
+    }
     __syncthreads();
     if (tid < R)
       a.zpart[((size_t)t * a.ZW + w) * R + tid] =
-          zred[tid] + zred[R + tid] + zred[2 * R + tid] + zred[3 * R + tid];
+          pow2 ? zred[tid] + zred[R + tid] + zred[2 * R + tid] + zred[3 * R + tid] : zred[tid];
   }
 }
 
@@ -680,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int q = tid + u * kThreads;
-      zv[u] = q < nzv ? a.zpart[(size_t)t * nzv + q] : 0.f;
+      zv[u] = nzv > 0 ? a.zpart[(size_t)t * nzv + (q < nzv ? q : nzv - 1)] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -698,18 +682,19 @@ __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
     int rows[RB];
     float cf[RB];
 #pragma unroll
-    for (int u = 0; u < RB; ++u) {
+    for (int u = 0; u < RB; ++u) {  // clamped: every load is issued; extra ranks get weight 0
       const int r = rb + u * kThreads;
-      rows[u] = r < a.k ? ri[r] : -1;
-      cf[u] = r < a.k ? cfp[r] : 0.f;
+      const int rc = r < a.k ? r : a.k - 1;
+      rows[u] = ri[rc];
+      cf[u] = cfp[rc];
+      cf[u] = r < a.k ? cf[u] : 0.f;
     }
     uint4 dv[RB][HS / 8];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const uint16_t* d = a.w3 + ((size_t)(rows[u] < 0 ? 0 : rows[u]) * 3 + 2) * H + h0;
+      const uint16_t* d = a.w3 + ((size_t)rows[u] * 3 + 2) * H + h0;
 #pragma unroll
-      for (int q = 0; q < HS / 8; ++q)
-        dv[u][q] = rows[u] >= 0 ? *reinterpret_cast<const uint4*>(d + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+      for (int q = 0; q < HS / 8; ++q) dv[u][q] = *reinterpret_cast<const uint4*>(d + 8 * q);
     }
 #pragma unroll
     for (int u = 0; u < RB; ++u)
@@ -739,8 +724,23 @@ __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
   if (tid < HS) {
     const int h = h0 + tid;
     float v = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
-    if (a.nz > 0)
-      for (int r = 0; r < a.rank; ++r) v = fmaf(f16f(a.U[(size_t)h * a.rank + r]), zs[r], v);
+    if (a.nz > 0) {
+      const uint4* up = reinterpret_cast<const uint4*>(a.U + (size_t)h * a.rank);
+      uint4 uq[8];
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)
+        if (r8 * 8 < a.rank) uq[r8] = up[r8];
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)
+        if (r8 * 8 < a.rank) {
+          const uint32_t uw[4] = {uq[r8].x, uq[r8].y, uq[r8].z, uq[r8].w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            v = fmaf(f16f((uint16_t)(uw[d] & 0xFFFFu)), zs[r8 * 8 + 2 * d], v);
+            v = fmaf(f16f((uint16_t)(uw[d] >> 16)), zs[r8 * 8 + 2 * d + 1], v);
+          }
+        }
+    }
     a.y[(size_t)t * H + h] = v;
   }
 }
@@ -762,10 +762,7 @@ Plan make_plan(const cfr_config& c, int batch, int k) {
   p.n_slices = (nbytes + p.S - 1) / p.S;
   p.itemsA = batch * c.top * p.n_slices;
   p.per_xcdA = (p.itemsA + 7) / 8;
-  int ch = 4;
-  while (ch < nblk && ch < 32) ch *= 2;
-  p.CH = ch;
-  p.ldsA = ScreenLds(c.hidden, nblk, c.n_screen, p.S, p.CH).total;
+  p.ldsA = ScreenLds(nblk, c.n_screen, p.S).total;
   // B: workgroups per token; about one kept channel per wave at batch 1
   int g = 256 / batch;
   if (g < 4) g = 4;
@@ -805,7 +802,7 @@ static hipError_t launch_A(const ScreenArgs& a, const Plan& p, hipStream_t st) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     attr = true;
   }
-  k_screen_score<S><<<8 * p.per_xcdA, kThreads, p.ldsA, st>>>(a);
+  k_screen_score<S><<<8 * p.per_xcdA, kScreenThreads, p.ldsA, st>>>(a);
   return hipGetLastError();
 }
 
@@ -824,15 +821,25 @@ static hipError_t launch_C_any(const DownArgs& a, const Plan& p, hipStream_t st)
   }
 }
 
-static hipError_t launch_B(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+template <int KPT>
+static hipError_t launch_B_k(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_select_exact,
+    (void)hipFuncSetAttribute((const void*)k_select_exact<KPT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     attr = true;
   }
-  k_select_exact<<<batch * p.G, kThreads, p.ldsB, st>>>(a);
+  k_select_exact<KPT><<<batch * p.G, kThreads, p.ldsB, st>>>(a);
   return hipGetLastError();
+}
+
+static hipError_t launch_B(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+  const int per = a.dense ? 1 : (a.ncand + kThreads - 1) / kThreads;
+  if (per <= 1) return launch_B_k<1>(a, p, batch, st);
+  if (per <= 4) return launch_B_k<4>(a, p, batch, st);
+  if (per <= 16) return launch_B_k<16>(a, p, batch, st);
+  if (per <= 32) return launch_B_k<32>(a, p, batch, st);
+  return launch_B_k<64>(a, p, batch, st);
 }
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
@@ -844,7 +851,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   };
   ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->xrot, r->sel, r->ghat,
                r->vhat, r->pact, r->score, r->status, c.hidden, c.n_experts, c.inter, c.top,
-               r->nblk, c.n_screen, r->lp, r->unit, p.n_slices, p.itemsA, p.per_xcdA, p.CH,
+               r->nblk, c.n_screen, r->lp, r->unit, p.n_slices, p.itemsA, p.per_xcdA,
                dbg != nullptr};
   hipError_t e = hipSuccess;
   mark(0);

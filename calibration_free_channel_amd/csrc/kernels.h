@@ -13,29 +13,26 @@ __host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 1
 
 // LDS layout of the screen kernel (bytes); host and device share it.
 struct ScreenLds {
-  size_t xs, uni, st, sl, xsel, sc, total;
-  __host__ __device__ ScreenLds(int H, int nblk, int n_screen, int S, int CH) {
+  size_t lut, sl, xsel, sc, red, total;
+  __host__ __device__ ScreenLds(int nblk, int n_screen, int S) {
     size_t o = 0;
-    xs = o;
-    o += lds_align((size_t)H * 4);
-    uni = o;  // radix-select histograms, later the screen reduction
-    const size_t hist = (size_t)CH * 256 * 4, red = (size_t)256 * 5 * S * 4;
-    o += lds_align(hist > red ? hist : red);
-    st = o;
-    o += lds_align((size_t)nblk * 4 * 4);
+    lut = o;  // 256 entries of five fp16 codes
+    o += 256 * 16;
     sl = o;
     o += lds_align((size_t)nblk * n_screen);
     xsel = o;
     o += lds_align((size_t)nblk * n_screen * 4);
     sc = o;
     o += lds_align((size_t)nblk * 2 * 5 * S * 4);
+    red = o;
+    o += lds_align((size_t)512 * 5 * S * 4);
     total = o;
   }
 };
 
 // LDS layout of the select/exact kernel (bytes).
 struct SelectLds {
-  size_t xs, keys, flags, list, zred, misc, total;
+  size_t xs, keys, flags, list, zred, hist, misc, total;
   __host__ __device__ SelectLds(int H, int ncand, int share_max, int rank) {
     size_t o = 0;
     xs = o;
@@ -48,15 +45,17 @@ struct SelectLds {
     o += lds_align((size_t)(share_max > 0 ? share_max : 1) * 4);
     zred = o;
     o += lds_align((size_t)4 * (rank > 0 ? rank : 1) * 4);
+    hist = o;
+    o += 2048 * 4;
     misc = o;
-    o += lds_align((256 + 48) * 4);
+    o += lds_align(48 * 4);
     total = o;
   }
 };
 
 // Launch geometry of one decode call.
 struct Plan {
-  int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0, CH = 4;  // screen
+  int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0;          // screen
   int G = 4, share_max = 0, ZW = 4;                          // select/exact
   int HS = 8, nhs = 0, itemsC = 0, per_xcdC = 0;             // down/recover
   size_t ldsA = 0, ldsB = 0;
