@@ -124,7 +124,8 @@ int alloc_resident(cfr_reader& r, bool with_router) {
   if ((e = hipMalloc(&r.ws, r.ws_bytes)) != hipSuccess)
     return fail(CFR_ENOMEM, std::string("workspace allocation: ") + hipGetErrorString(e));
   carve_workspace(r);
-  if ((e = hipMemset(r.status, 0, sizeof(int32_t))) != hipSuccess) return hipf(e, "status init");
+  // zeroed once: every index a kernel can read from the workspace is then valid
+  if ((e = hipMemset(r.ws, 0, r.ws_bytes)) != hipSuccess) return hipf(e, "workspace init");
   return CFR_OK;
 }
 

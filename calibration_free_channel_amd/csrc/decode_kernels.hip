@@ -42,7 +42,7 @@ namespace {
 
 constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
 constexpr int kThreads = 256;
-constexpr int kScreenThreads = 512;
+constexpr int kMaxS1024 = 8;  // widest slice that still fits 128 VGPRs at 1024 threads
 constexpr int kMaxS = 13;  // bytes per half handled by one screen workgroup
 
 __device__ __forceinline__ float f16f(uint16_t h) {
@@ -59,25 +59,65 @@ __device__ __forceinline__ int clamp_expert(int e, int E, int32_t* status) {
   return e;
 }
 
+// Value of lane (lane ^ H) in a wave64, through register-level exchanges:
+// DPP quad permutes for H = 1, 2, DPP row shifts for H = 4, 8 and the gfx950
+// permlane swaps for H = 16, 32 (no trip through the LDS crossbar).
+template <int H>
+__device__ __forceinline__ int xor_lane(int v) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (H == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (H == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (H == 4 || H == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x100 + H, 0xF, 0xF, false);  // row_shl:H
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x110 + H, 0xF, 0xF, false);  // row_shr:H
+    return (lane & H) ? dn : up;
+  } else if constexpr (H == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+template <int H>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  return __int_as_float(xor_lane<H>(__float_as_int(v)));
+}
+
+// Butterfly sum over the wave; every lane ends with the same total.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  v += xor_lane_f<1>(v);
+  v += xor_lane_f<2>(v);
+  v += xor_lane_f<4>(v);
+  v += xor_lane_f<8>(v);
+  v += xor_lane_f<16>(v);
+  v += xor_lane_f<32>(v);
   return v;
 }
 
-// Inclusive prefix sum over a 256-thread block (4 waves); sh >= 4 ints.
+// Inclusive prefix sum over a wave64 (DPP row shifts and row broadcasts).
+__device__ __forceinline__ int wave_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Inclusive prefix sum over a 256-thread block (4 waves) with one barrier;
+// sh (4 ints) must not be written again before the caller's next barrier.
 __device__ __forceinline__ int block_scan_256(int v, int* sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  v = wave_scan(v);
   if (lane == 63) sh[w] = v;
   __syncthreads();
   int add = 0;
   for (int q = 0; q < w; ++q) add += sh[q];
-  __syncthreads();
   return v + add;
 }
 
@@ -116,12 +156,10 @@ struct ScreenArgs {
 // bit-by-bit search of the n_screen-th largest magnitude over wave ballots,
 // then compacted in ascending coordinate order.
 __device__ __forceinline__ void rotate_select_block(float v0, float v1, int b, int NS,
-                                                    uint8_t* sl, float* xsel, float* xrot_out) {
+                                                    uint8_t* sl, int2* rec, int unit,
+                                                    float* xrot_out) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float o0 = __shfl_xor(v0, h, 64);
-    const float o1 = __shfl_xor(v1, h, 64);
+  auto stage = [&](float o0, float o1, int h) {
     if (lane & h) {
       v0 = o0 - v0;
       v1 = o1 - v1;
@@ -129,7 +167,13 @@ __device__ __forceinline__ void rotate_select_block(float v0, float v1, int b, i
       v0 = v0 + o0;
       v1 = v1 + o1;
     }
-  }
+  };
+  stage(xor_lane_f<1>(v0), xor_lane_f<1>(v1), 1);
+  stage(xor_lane_f<2>(v0), xor_lane_f<2>(v1), 2);
+  stage(xor_lane_f<4>(v0), xor_lane_f<4>(v1), 4);
+  stage(xor_lane_f<8>(v0), xor_lane_f<8>(v1), 8);
+  stage(xor_lane_f<16>(v0), xor_lane_f<16>(v1), 16);
+  stage(xor_lane_f<32>(v0), xor_lane_f<32>(v1), 32);
   {
     const float u = v0;
     v0 = u + v1;
@@ -158,20 +202,20 @@ __device__ __forceinline__ void rotate_select_block(float v0, float v1, int b, i
     const int pos = __popcll(m0 & lt);
     if (pos < NS) {
       sl[b * NS + pos] = (uint8_t)lane;
-      xsel[b * NS + pos] = v0;
+      rec[b * NS + pos] = make_int2(lane * unit, __float_as_int(v0));
     }
   }
   if (s1) {
     const int pos = __popcll(m0) + __popcll(m1 & lt);
     if (pos < NS) {
       sl[b * NS + pos] = (uint8_t)(lane + 64);
-      xsel[b * NS + pos] = v1;
+      rec[b * NS + pos] = make_int2((lane + 64) * unit, __float_as_int(v1));
     }
   }
 }
 
-template <int S>
-__global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
+template <int S, int NT>
+__global__ __launch_bounds__(NT) void k_screen_score(ScreenArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
@@ -179,13 +223,13 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
   const int ts = item / a.n_slices;
   const int s = ts % a.top, t = ts / a.top;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NW = kScreenThreads / 64;
+  constexpr int NW = NT / 64;
   const int H = a.H, I = a.I, nblk = a.nblk, NS = a.n_screen;
   constexpr int NCH = 5 * S;  // channels per half in this slice
-  const ScreenLds L(nblk, NS, S);
+  const ScreenLds L(nblk, NS, S, NT);
   uint4* lut = reinterpret_cast<uint4*>(smem + L.lut);
   uint8_t* sl = smem + L.sl;
-  float* xsel = reinterpret_cast<float*>(smem + L.xsel);
+  int2* rec = reinterpret_cast<int2*>(smem + L.rec);  // (unit byte offset, x bits) per screened coordinate
   float* sc = reinterpret_cast<float*>(smem + L.sc);
   float* red = reinterpret_cast<float*>(smem + L.red);
 
@@ -205,13 +249,14 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
   const int b0 = c * S;   // first byte of the slice inside each half
   const int j0 = 5 * b0;  // first channel of the slice
 
-  // scales of the slice for every block and half, and the slice's norms
+  // scales of the slice for every block and half: the first batch is
+  // loaded now and stored after the rotation, so its latency hides there
   const int nsc = nblk * 2 * NCH;
-  for (int q0 = 0; q0 < nsc; q0 += kScreenThreads * 4) {
-    uint16_t hv[4];
+  uint16_t hv[4];
+  auto load_scales = [&](int q0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int q = q0 + tid + u * kScreenThreads;
+      const int q = q0 + tid + u * NT;
       const int jj = q % NCH, bm = q / NCH;  // bm = block * 2 + half
       const int j = j0 + jj;
       const bool ok = q < nsc && j < I;
@@ -219,18 +264,21 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
       hv[u] = a.scales[ix];
       hv[u] = ok ? hv[u] : (uint16_t)0;
     }
+  };
+  auto store_scales = [&](int q0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int q = q0 + tid + u * kScreenThreads;
+      const int q = q0 + tid + u * NT;
       if (q < nsc) sc[q] = f16f(hv[u]);
     }
-  }
+  };
+  load_scales(0);
   float nrm = 0.f;
   if (tid < NCH && j0 + tid < I) nrm = a.norms[(size_t)e * I + j0 + tid];
 
   // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
   // 243..255 never occur in a packed unit and decode to zero)
-  if (tid < 256) {
+  if (tid < 256) {  // NT >= 512
     uint32_t h[5] = {0u, 0u, 0u, 0u, 0u};
     if (tid < 243) {
       int q = tid;
@@ -250,24 +298,31 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
   for (int u = 0; u < 4; ++u) {
     const int b = wave + u * NW;
     if (b < nblk)
-      rotate_select_block(xv0[u] * sg0[u], xv1[u] * sg1[u], b, NS, sl, xsel,
+      rotate_select_block(xv0[u] * sg0[u], xv1[u] * sg1[u], b, NS, sl, rec, a.unit,
                           writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
   }
   for (int b = wave + 4 * NW; b < nblk; b += NW) {  // hidden above 4096
     const float v0 = xt[b * 128 + lane] * a.sigma[b * 128 + lane];
     const float v1 = xt[b * 128 + 64 + lane] * a.sigma[b * 128 + 64 + lane];
-    rotate_select_block(v0, v1, b, NS, sl, xsel, writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
+    rotate_select_block(v0, v1, b, NS, sl, rec, a.unit,
+                        writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
+  }
+  __syncthreads();
+  store_scales(0);
+  for (int q0 = NT * 4; q0 < nsc; q0 += NT * 4) {  // large layers only
+    load_scales(q0);
+    store_scales(q0);
   }
   __syncthreads();
   if (writer)
-    for (int q = tid; q < nblk * NS; q += kScreenThreads) a.sel[(size_t)t * nblk * NS + q] = sl[q];
+    for (int q = tid; q < nblk * NS; q += NT) a.sel[(size_t)t * nblk * NS + q] = sl[q];
 
   // ---- screen: codes of the slice at the screened coordinates ----
   // group g = (block, half) with tpg threads; each thread takes every
   // tpg-th screened coordinate of its block.
   const int groups = 2 * nblk;
   int tpg = 1;
-  while (tpg * 2 * groups <= kScreenThreads) tpg *= 2;
+  while (tpg * 2 * groups <= NT) tpg *= 2;
   const int g = tid / tpg, lg = tid % tpg;
   float acc[NCH];
 #pragma unroll
@@ -279,21 +334,23 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
     const uint8_t* ubase = a.codes + ((size_t)e * nblk + b) * 128 * a.unit + m * a.lp + (b0 & ~3);
     const int sh = (b0 & 3) * 8;
     constexpr int ND = (S + 6) / 4;  // dwords covering S bytes at any 4-byte phase
-    constexpr int CB = 8;            // coordinates whose codes are in flight together
+    constexpr int CB = 5;            // coordinates whose codes are in flight together
     for (int q0 = lg; q0 < NS; q0 += tpg * CB) {
+      // all records first, then all code loads: one LDS and one memory latency per batch
+      int2 rc[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int q = q0 + u * tpg;
+        rc[u] = rec[b * NS + (q < NS ? q : NS - 1)];
+      }
       uint32_t w[CB][ND];
       float xv[CB];
 #pragma unroll
       for (int u = 0; u < CB; ++u) {
-        // clamped index: the load is always issued; a coordinate past the
-        // list contributes x = 0
-        const int q = q0 + u * tpg;
-        const int qc = q < NS ? q : NS - 1;
-        const int ci = sl[b * NS + qc];
-        xv[u] = q < NS ? xsel[b * NS + qc] : 0.f;
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + (size_t)ci * a.unit);
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + rc[u].x);
 #pragma unroll
         for (int d = 0; d < ND; ++d) w[u][d] = wp[d];
+        xv[u] = q0 + u * tpg < NS ? __int_as_float(rc[u].y) : 0.f;  // past the list: x = 0
       }
 #pragma unroll
       for (int u = 0; u < CB; ++u) {
@@ -340,7 +397,7 @@ __global__ __launch_bounds__(kScreenThreads) void k_screen_score(ScreenArgs a) {
     a.ghat[o] = gs;
     a.vhat[o] = vs;
     a.pact[o] = p;
-    a.score[o] = wgt * nrm * fabsf(p);
+    a.score[o] = fabsf(wgt) * nrm * fabsf(p);  // routing weights are non-negative; |w| keeps the sign bit clear
   }
 }
 
@@ -376,101 +433,179 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   uint8_t* flags = smem + L.flags;
   int* list = reinterpret_cast<int*>(smem + L.list);
   float* zred = reinterpret_cast<float*>(smem + L.zred);
-  int* hist = reinterpret_cast<int*>(smem + L.hist);  // 2048 bins
-  int* misc = reinterpret_cast<int*>(smem + L.misc);  // [0..3] scan, [8] digit, [9] need, [10] done, [11] bin count
-  int* sl_e = misc + 12;                              // routed expert of each slot (16)
-  float* sl_w = reinterpret_cast<float*>(misc + 28);  // its routing weight (16)
+  int* hist = reinterpret_cast<int*>(smem + L.hist);  // 4096 bins, then 2 x 1024 bins
+  int* hist1 = hist + 4096;
+  int* hist2 = hist1 + 1024;
+  int* misc = reinterpret_cast<int*>(smem + L.misc);
+  // misc: [0..3] [4..7] [12..15] scan scratch, [8] digit [9] need [10] bin count,
+  // [11] gather slot, [16] [17] boundary key and count, [20..35] routed expert
+  // of each slot, [36..51] its weight; bkey/bidx: the boundary bin's elements
+  int* sl_e = misc + 20;
+  float* sl_w = reinterpret_cast<float*>(misc + 36);
+  uint32_t* bkey = reinterpret_cast<uint32_t*>(misc + 64);
+  int* bidx = misc + 128;
 
   const bool partial = !a.dense && k > 0 && k < nc;
   const bool all = a.dense || k == nc;
-  // loads first: routing of the token, the token itself, its scores
-  if (tid < a.top) {
-    sl_e[tid] = clamp_expert(a.ids[t * a.top + tid], a.E, a.status);
-    sl_w[tid] = a.gw[t * a.top + tid];
-  }
+  const int per = (nc + kThreads - 1) / kThreads;  // candidates per thread (uniform)
+  // loads first, all issued before any is consumed: routing of the token,
+  // the token itself, its scores
+  const int tsl = min(tid, a.top - 1);
+  const int id_raw = a.ids[t * a.top + tsl];
+  const float gw_raw = a.gw[t * a.top + tsl];
   const float* xt = a.x + (size_t)t * H;
   {
-    float4 xr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = min((tid + u * kThreads) * 4, H - 4);
-      xr[u] = *reinterpret_cast<const float4*>(xt + q);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = (tid + u * kThreads) * 4;
-      if (q < H) *reinterpret_cast<float4*>(xs + q) = xr[u];
-    }
+    // four named registers rather than an array: the array form ends up on
+    // the stack once its stores sit below the score loads
+    const int xq0 = min(tid * 4, H - 4), xq1 = min((tid + kThreads) * 4, H - 4);
+    const int xq2 = min((tid + 2 * kThreads) * 4, H - 4), xq3 = min((tid + 3 * kThreads) * 4, H - 4);
+    const float4 xr0 = *reinterpret_cast<const float4*>(xt + xq0);
+    const float4 xr1 = *reinterpret_cast<const float4*>(xt + xq1);
+    const float4 xr2 = *reinterpret_cast<const float4*>(xt + xq2);
+    const float4 xr3 = *reinterpret_cast<const float4*>(xt + xq3);
+    // all KPT score loads are issued unguarded (clamped addresses) and only
+    // consumed after the token's stores, so one memory latency covers them
+    float v[KPT];
     if (partial) {
       const float* sct = a.score + (size_t)t * nc;
-      for (int q0 = 0; q0 < nc; q0 += kThreads * 16) {
-        float v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int q = q0 + tid + u * kThreads;
-          v[u] = sct[q < nc ? q : nc - 1];
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int q = q0 + tid + u * kThreads;
-          if (q < nc) keys[q] = __float_as_uint(v[u]);
-        }
-      }
+      for (int u = 0; u < KPT; ++u) v[u] = sct[min(tid + u * kThreads, nc - 1)];
     }
+    if (tid < a.top) {
+      sl_e[tid] = clamp_expert(id_raw, a.E, a.status);
+      sl_w[tid] = gw_raw;
+    }
+    // clamped like the loads: duplicate addresses store equal values
+    *reinterpret_cast<float4*>(xs + xq0) = xr0;
+    *reinterpret_cast<float4*>(xs + xq1) = xr1;
+    *reinterpret_cast<float4*>(xs + xq2) = xr2;
+    *reinterpret_cast<float4*>(xs + xq3) = xr3;
     for (int q = (tid + 4 * kThreads) * 4; q < H; q += kThreads * 4)  // hidden above 4096
       *reinterpret_cast<float4*>(xs + q) = *reinterpret_cast<const float4*>(xt + q);
+    if (partial) {
+      // keys padded to 256 * per entries; padding keys are 0, the smallest key,
+      // and sit at the highest indices, so the tie rule never keeps them
+#pragma unroll
+      for (int u = 0; u < KPT; ++u)
+        if (u < per) keys[tid + u * kThreads] = tid + u * kThreads < nc ? __float_as_uint(v[u]) : 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) hist[tid * 16 + q] = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) hist1[tid * 8 + q] = 0;  // both 1024-bin histograms
+      if (tid == 0) misc[11] = 0;
+    }
   }
-  if (tid == 0) misc[10] = 0;
   __syncthreads();
-  // each thread owns a contiguous chunk of at most KPT candidates, in registers
-  const int per = (nc + kThreads - 1) / kThreads;
-  const int lo = min(tid * per, nc), hi = min(lo + per, nc);
+  // each thread owns a contiguous chunk of `per` (<= KPT) candidates, in
+  // registers; `per` is uniform, so every guard below is a scalar branch
+  const int lo = tid * per;
+  const int nreal = max(0, min(per, nc - lo));  // real candidates of this chunk
   uint32_t kr[KPT];
 #pragma unroll
-  for (int q = 0; q < KPT; ++q) kr[q] = (partial && lo + q < hi) ? keys[lo + q] : 0u;
+  for (int q = 0; q < KPT; ++q) kr[q] = (partial && q < per) ? keys[lo + q] : 0u;
   uint32_t prefix = 0, mask = 0;
   int need = k;
   if (partial) {
-    // exact k-th largest key: MSB-first radix select, 11 + 11 + 10 bits
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dm = pass == 2 ? 0x3FFu : 0x7FFu;
-      const int done = misc[10];
-      if (done) break;  // uniform: read after a barrier
+    // exact k-th largest key.  Scores are non-negative, so bits 30..19
+    // (exponent and 4 mantissa bits) order them; one pass over those 12 bits
+    // finds the boundary bin; a bin of at most 64 keys is then ranked
+    // directly, a larger one (many near-equal scores) is refined by two more
+    // passes over bits 18..9 and 8..0.
 #pragma unroll
-      for (int q = 0; q < 8; ++q) hist[tid * 8 + q] = 0;
-      __syncthreads();
+    for (int q = 0; q < KPT; ++q)
+      if (q < per) atomicAdd(&hist[(kr[q] >> 19) & 0xFFFu], 1);
+    __syncthreads();
+    {
+      const int base = 16 * (255 - tid);  // thread tid holds bins [base, base + 16), descending digits
+      int bins[16], own = 0;
 #pragma unroll
-      for (int q = 0; q < KPT; ++q)
-        if (lo + q < hi && (kr[q] & mask) == prefix) atomicAdd(&hist[(kr[q] >> shift) & dm], 1);
-      __syncthreads();
-      // thread tid holds the 8 bins [8(255 - tid), 8(255 - tid) + 8): descending digits
-      const int base = 8 * (255 - tid);
-      int bins[8], own = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        bins[q] = hist[base + q];
-        own += bins[q];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint4 hq = *reinterpret_cast<const uint4*>(hist + base + 4 * q4);
+        bins[4 * q4] = (int)hq.x;
+        bins[4 * q4 + 1] = (int)hq.y;
+        bins[4 * q4 + 2] = (int)hq.z;
+        bins[4 * q4 + 3] = (int)hq.w;
+        own += (int)(hq.x + hq.y + hq.z + hq.w);
       }
-      const int incl = block_scan_256(own, misc);  // keys with digit >= base
+      const int incl = block_scan_256(own, misc);
       if (incl >= need && incl - own < need) {
         int cum = incl - own;
 #pragma unroll
-        for (int q = 7; q >= 0; --q) {
+        for (int q = 15; q >= 0; --q) {
           if (cum < need && cum + bins[q] >= need) {
             misc[8] = base + q;
             misc[9] = need - cum;
-            misc[11] = bins[q];
+            misc[10] = bins[q];
           }
           cum += bins[q];
         }
       }
+    }
+    __syncthreads();
+    prefix = (uint32_t)misc[8] << 19;
+    mask = 0x7FF80000u;
+    need = misc[9];
+    const int cb = misc[10];
+    if (cb != need && cb <= 64) {
+      // rank the boundary bin's keys directly (key descending, index ascending)
+#pragma unroll
+      for (int q = 0; q < KPT; ++q)
+        if (q < per && (kr[q] & mask) == prefix) {
+          const int slot = atomicAdd(&misc[11], 1);
+          bkey[slot] = kr[q];
+          bidx[slot] = lo + q;
+        }
       __syncthreads();
-      prefix |= (uint32_t)misc[8] << shift;
-      mask |= dm << shift;
-      need = misc[9];
-      if (tid == 0 && misc[11] == need) misc[10] = 1;  // every key of that bin is kept
+      if (tid < cb) {
+        const uint32_t ki = bkey[tid];
+        const int ii = bidx[tid];
+        int gt = 0, eqb = 0;
+        for (int jx = 0; jx < cb; ++jx) {
+          const uint32_t kj = bkey[jx];
+          gt += kj > ki;
+          eqb += kj == ki && bidx[jx] < ii;
+        }
+        if (gt + eqb == need - 1) {
+          misc[16] = (int)ki;
+          misc[17] = need - gt;
+        }
+      }
       __syncthreads();
+      prefix = (uint32_t)misc[16];
+      mask = 0xFFFFFFFFu;
+      need = misc[17];
+    } else if (cb != need) {
+      for (int pass = 1; pass < 3; ++pass) {  // bits 18..9, then 8..0
+        const int shift = pass == 1 ? 9 : 0;
+        const uint32_t dm = pass == 1 ? 0x3FFu : 0x1FFu;
+        int* hcur = pass == 1 ? hist1 : hist2;
+#pragma unroll
+        for (int q = 0; q < KPT; ++q)
+          if (q < per && (kr[q] & mask) == prefix) atomicAdd(&hcur[(kr[q] >> shift) & dm], 1);
+        __syncthreads();
+        const int base = 4 * (255 - tid);
+        const uint4 hq = *reinterpret_cast<const uint4*>(hcur + base);
+        const int bins[4] = {(int)hq.x, (int)hq.y, (int)hq.z, (int)hq.w};
+        const int own = bins[0] + bins[1] + bins[2] + bins[3];
+        const int incl = block_scan_256(own, misc + (pass == 1 ? 4 : 12));
+        if (incl >= need && incl - own < need) {
+          int cum = incl - own;
+#pragma unroll
+          for (int q = 3; q >= 0; --q) {
+            if (cum < need && cum + bins[q] >= need) {
+              misc[8] = base + q;
+              misc[9] = need - cum;
+            }
+            cum += bins[q];
+          }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)misc[8] << shift;
+        mask |= dm << shift;
+        need = misc[9];
+        __syncthreads();
+      }
+      mask = 0xFFFFFFFFu;  // bit 31 is clear in every key
     }
   }
   // kept flags and ranks in ascending candidate order
@@ -478,17 +613,18 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
   if (partial)
 #pragma unroll
     for (int q = 0; q < KPT; ++q)
-      if (lo + q < hi) {
+      if (q < per) {
         const uint32_t kv = kr[q] & mask;
         ngt += kv > prefix;
         neq += kv == prefix;
       }
-  const int eq_incl = block_scan_256(neq, misc);
+  __syncthreads();
+  const int eq_incl = block_scan_256(neq, misc);  // scratch [0..3]
   const int eq_before = eq_incl - neq;
   int take_eq = 0;
   if (partial) take_eq = max(0, min(neq, need - eq_before));
-  const int mine = partial ? ngt + take_eq : (all ? hi - lo : 0);
-  const int pos_incl = block_scan_256(mine, misc);
+  const int mine = partial ? ngt + take_eq : (all ? nreal : 0);
+  const int pos_incl = block_scan_256(mine, misc + 4);  // scratch [4..7]
   int rnk = pos_incl - mine;
   const int share = (k + a.G - 1) / a.G;
   const int r0 = min(w * share, k), r1 = min(r0 + share, k);
@@ -496,26 +632,21 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
     int eq_seen = 0;
 #pragma unroll
     for (int q = 0; q < KPT; ++q)
-      if (lo + q < hi) {
+      if (q < per) {
         const uint32_t kv = kr[q] & mask;
-        bool on = kv > prefix;
-        if (kv == prefix) {
-          on = eq_seen < take_eq;
-          ++eq_seen;
-        }
-        flags[lo + q] = on ? 1 : 0;
-        if (on) {
-          if (rnk >= r0 && rnk < r1) list[rnk - r0] = lo + q;
-          ++rnk;
-        }
+        const bool eq = kv == prefix;
+        const bool on = kv > prefix || (eq && eq_seen < take_eq);
+        eq_seen += eq;
+        flags[lo + q] = on;
+        if (on && rnk >= r0 && rnk < r1) list[rnk - r0] = lo + q;
+        rnk += on;
       }
   } else {
-    for (int i = lo; i < hi; ++i) {
-      flags[i] = all ? 1 : 0;
-      if (all) {
-        if (rnk >= r0 && rnk < r1) list[rnk - r0] = i;
-        ++rnk;
-      }
+    for (int q = 0; q < per; ++q) {
+      const bool on = all && q < nreal;
+      flags[lo + q] = on;
+      if (on && rnk >= r0 && rnk < r1) list[rnk - r0] = lo + q;
+      rnk += on;
     }
   }
   __syncthreads();
@@ -610,17 +741,21 @@ __global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
     for (int q = 0; q < R * 4; q += kThreads)
       if (q + tid < R * 4) zred[q + tid] = 0.f;
     __syncthreads();
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      float v = zacc[d];
-      for (int off = R8; off < 64; off <<= 1)
-        if ((off / R8) * R8 == off) v += __shfl_xor(v, off, 64);
-      zacc[d] = v;
-    }
-    // lanes 0..R8-1 of each wave hold its sums when R8 is a power of two;
+    // lanes 0..R8-1 of each wave end with its sums when R8 is a power of two;
     // otherwise fall back to shared-memory atomics
     const bool pow2 = (R8 & (R8 - 1)) == 0;
     if (pow2) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {  // butterfly over lanes of equal r8
+        float v = zacc[d];
+        if (R8 <= 1) v += xor_lane_f<1>(v);
+        if (R8 <= 2) v += xor_lane_f<2>(v);
+        if (R8 <= 4) v += xor_lane_f<4>(v);
+        if (R8 <= 8) v += xor_lane_f<8>(v);
+        v += xor_lane_f<16>(v);
+        v += xor_lane_f<32>(v);
+        zacc[d] = v;
+      }
       if (lane < R8 && cl < cpp)
 #pragma unroll
         for (int d = 0; d < 8; ++d) zred[wave * R + r8 * 8 + d] = zacc[d];
@@ -658,6 +793,13 @@ __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
   const int t = item / a.nhs, hs = item % a.nhs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, h0 = hs * HS;
+  // this slice's rows of U, needed last, loaded first (thread tid < HS owns hidden h0 + tid)
+  uint4 uq[8];
+  if (a.nz > 0) {
+    const uint4* up = reinterpret_cast<const uint4*>(a.U + (size_t)(h0 + (tid < HS ? tid : 0)) * a.rank);
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) uq[r8] = up[r8 * 8 < a.rank ? r8 : 0];
+  }
   const int nzv = a.nz * a.rank;  // at most 16 * 64 partial values
   {
     float zv[4];
@@ -725,11 +867,6 @@ __global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
     const int h = h0 + tid;
     float v = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
     if (a.nz > 0) {
-      const uint4* up = reinterpret_cast<const uint4*>(a.U + (size_t)h * a.rank);
-      uint4 uq[8];
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8)
-        if (r8 * 8 < a.rank) uq[r8] = up[r8];
 #pragma unroll
       for (int r8 = 0; r8 < 8; ++r8)
         if (r8 * 8 < a.rank) {
@@ -762,7 +899,12 @@ Plan make_plan(const cfr_config& c, int batch, int k) {
   p.n_slices = (nbytes + p.S - 1) / p.S;
   p.itemsA = batch * c.top * p.n_slices;
   p.per_xcdA = (p.itemsA + 7) / 8;
-  p.ldsA = ScreenLds(nblk, c.n_screen, p.S).total;
+  p.ntA = 1024;
+  p.ldsA = ScreenLds(nblk, c.n_screen, p.S, 1024).total;
+  if (p.S > kMaxS1024 || p.ldsA > kMaxLds) {
+    p.ntA = 512;
+    p.ldsA = ScreenLds(nblk, c.n_screen, p.S, 512).total;
+  }
   // B: workgroups per token; about one kept channel per wave at batch 1
   int g = 256 / batch;
   if (g < 4) g = 4;
@@ -794,16 +936,24 @@ size_t max_lds_needed(const cfr_config& c) {
 
 size_t zpart_rows(const cfr_config& c) { return (size_t)c.max_batch * 16; }
 
-template <int S>
-static hipError_t launch_A(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+template <int S, int NT>
+static hipError_t launch_A_nt(const ScreenArgs& a, const Plan& p, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_screen_score<S>,
+    (void)hipFuncSetAttribute((const void*)k_screen_score<S, NT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     attr = true;
   }
-  k_screen_score<S><<<8 * p.per_xcdA, kScreenThreads, p.ldsA, st>>>(a);
+  k_screen_score<S, NT><<<8 * p.per_xcdA, NT, p.ldsA, st>>>(a);
   return hipGetLastError();
+}
+
+template <int S>
+static hipError_t launch_A(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+  if constexpr (S <= kMaxS1024) {
+    if (p.ntA == 1024) return launch_A_nt<S, 1024>(a, p, st);
+  }
+  return launch_A_nt<S, 512>(a, p, st);
 }
 
 template <int HS>

@@ -13,19 +13,19 @@ __host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 1
 
 // LDS layout of the screen kernel (bytes); host and device share it.
 struct ScreenLds {
-  size_t lut, sl, xsel, sc, red, total;
-  __host__ __device__ ScreenLds(int nblk, int n_screen, int S) {
+  size_t lut, sl, rec, sc, red, total;
+  __host__ __device__ ScreenLds(int nblk, int n_screen, int S, int nthreads) {
     size_t o = 0;
     lut = o;  // 256 entries of five fp16 codes
     o += 256 * 16;
     sl = o;
     o += lds_align((size_t)nblk * n_screen);
-    xsel = o;
-    o += lds_align((size_t)nblk * n_screen * 4);
+    rec = o;
+    o += lds_align((size_t)nblk * n_screen * 8);
     sc = o;
     o += lds_align((size_t)nblk * 2 * 5 * S * 4);
     red = o;
-    o += lds_align((size_t)512 * 5 * S * 4);
+    o += lds_align((size_t)nthreads * 5 * S * 4);
     total = o;
   }
 };
@@ -37,25 +37,26 @@ struct SelectLds {
     size_t o = 0;
     xs = o;
     o += lds_align((size_t)H * 4);
+    const size_t npad = (size_t)256 * ((ncand + 255) / 256);  // whole chunks of 256 threads
     keys = o;
-    o += lds_align((size_t)ncand * 4);
+    o += lds_align(npad * 4);
     flags = o;
-    o += lds_align((size_t)ncand);
+    o += lds_align(npad);
     list = o;
     o += lds_align((size_t)(share_max > 0 ? share_max : 1) * 4);
     zred = o;
     o += lds_align((size_t)4 * (rank > 0 ? rank : 1) * 4);
     hist = o;
-    o += 2048 * 4;
+    o += (4096 + 2048) * 4;
     misc = o;
-    o += lds_align(48 * 4);
+    o += lds_align(192 * 4);
     total = o;
   }
 };
 
 // Launch geometry of one decode call.
 struct Plan {
-  int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0;          // screen
+  int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0, ntA = 512;  // screen
   int G = 4, share_max = 0, ZW = 4;                          // select/exact
   int HS = 8, nhs = 0, itemsC = 0, per_xcdC = 0;             // down/recover
   size_t ldsA = 0, ldsB = 0;
