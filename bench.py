@@ -53,7 +53,69 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--main-budget-only", action="store_true",
+                    help="time only the 17.8%% budget (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy, the reference kernel for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="summarise rocprofv3 CSV output under DIR as text and exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(torch):
+    """A plain elementwise copy of known size: reads and writes COPY_BYTES each."""
+    src = torch.randn(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def profile_summary(d):
+    """Text summary of rocprofv3 CSV output (kernel stats and FETCH_SIZE /
+    WRITE_SIZE per dispatch) found under directory d."""
+    import csv
+    import glob
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("cfr::", "")
+        return name.split("(")[0]
+
+    lines = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append(f"kernel stats: {os.path.relpath(f, d)}")
+        lines.append(f"{'kernel':<44} {'calls':>7} {'avg us':>9} {'min us':>9} {'max us':>9} {'% time':>7}")
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                lines.append(f"{short(r['Name'])[:44]:<44} {int(r['Calls']):>7} "
+                             f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['MinNs']) / 1e3:>9.2f} "
+                             f"{float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>7.2f}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        acc = {}
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (short(r["Kernel_Name"]), r["Counter_Name"])
+                a = acc.setdefault(key, [0.0, 0, r["Grid_Size"]])
+                a[0] += float(r["Counter_Value"])
+                a[1] += 1
+        lines.append(f"counters: {os.path.relpath(f, d)} (average per dispatch; FETCH_SIZE and "
+                     "WRITE_SIZE in KiB)")
+        for (k, c), (tot, n, grid) in sorted(acc.items()):
+            lines.append(f"  {k[:44]:<44} {c:<12} dispatches {n:>6}  avg {tot / n:>14.1f}")
+        # the copy reference is the largest elementwise kernel of the run
+        copy = [(k, c, tot / n) for (k, c), (tot, n, _) in acc.items()
+                if "elementwise" in k.lower() and tot / n > 0.25 * (COPY_BYTES >> 10)]
+        for k, c, v in copy:
+            bytes_kib = v
+            ratio = bytes_kib * 1024 / COPY_BYTES
+            lines.append(f"  copy reference {k[:40]} {c}: {bytes_kib:.0f} KiB for {COPY_BYTES >> 10} KiB "
+                         f"moved -> scale {1 / ratio if ratio else float('nan'):.4f}")
+    print("\n".join(lines))
 
 
 def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None):
@@ -140,6 +202,9 @@ def cpu_baseline(wl, layer, X, IDS, W, k, seconds):
 
 def main():
     args = parse()
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs the single-GPU reader only; --gpus {args.gpus} is not supported "
               "(the multi-GPU expert-parallel split is a design note, not a built path).",
@@ -174,7 +239,7 @@ def main():
     W = torch.from_numpy(Wh.reshape(L, 1, s.top)).cuda()
 
     res = {}
-    for k in [k_main] + ([k_low] if k_low else []):
+    for k in [k_main] + ([k_low] if k_low and not args.main_budget_only else []):
         us, nsteps, nwarm = graph_time(torch, readers, X, IDS, W, k, args.steps, args.warmup)
         rb = read_bytes(cfg, k)
         stages = stage_profile(torch, readers, X, IDS, W, k)
@@ -186,6 +251,10 @@ def main():
         dense_us, _, _ = graph_time(torch, readers, X, IDS, W, 0, min(args.steps, 400),
                                     args.warmup, fn="dense")
         log(f"dense BF16 block: {dense_us:.2f} us/token")
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        log(f"copy calibration: {COPY_BYTES >> 20} MiB read and written 4 times")
 
     main_r = res[k_main]
     rb = main_r["bytes"]
