@@ -31,43 +31,51 @@ struct DeviceGuard {
   }
 };
 
-template <typename T>
-T* carve(char*& p, size_t count) {
-  T* out = reinterpret_cast<T*>(p);
-  p += (sizeof(T) * count + 255) / 256 * 256;
-  return out;
-}
+// Workspace, sized for max_batch (see the field comments on cfr_reader).
+struct WorkspaceLayout {
+  size_t acc, wn, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
+  explicit WorkspaceLayout(const cfr_reader& r) {
+    const cfr_config& c = r.cfg;
+    const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
+    const size_t R = c.rank > 0 ? c.rank : 1;
+    auto rnd = [](size_t n) { return (n + 255) / 256 * 256; };
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+      const size_t at = o;
+      o += rnd(bytes);
+      return at;
+    };
+    acc = take(sizeof(unsigned long long) * B * 2 * r.ncp);
+    wn = take(sizeof(float) * B * r.ncp);
+    ypart = take(sizeof(float) * kMaxGatherWgs * H);
+    zpart = take(sizeof(float) * B * kMaxRecoverWgs * R);
+    xrot = take(sizeof(float) * B * H);
+    sel = take(B * r.nblk * c.n_screen);
+    ghat = take(sizeof(float) * B * nc);
+    vhat = take(sizeof(float) * B * nc);
+    score = take(sizeof(float) * B * nc);
+    kept = take(sizeof(int32_t) * B * nc);
+    status = take(sizeof(int32_t));
+    total = o;
+  }
+};
 
-size_t workspace_bytes(const cfr_reader& r) {
-  const cfr_config& c = r.cfg;
-  const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
-  auto rnd = [](size_t n) { return (n + 255) / 256 * 256; };
-  size_t tot = 0;
-  tot += rnd(sizeof(float) * B * H);                          // xrot
-  tot += rnd(B * r.nblk * c.n_screen);                        // sel
-  tot += 4 * rnd(sizeof(float) * B * nc);                     // ghat vhat pact score
-  tot += 2 * rnd(sizeof(int32_t) * B * nc);                   // kept rowidx
-  tot += rnd(sizeof(float) * B * nc);                         // coef
-  tot += rnd(sizeof(float) * r.zrows * (c.rank > 0 ? c.rank : 1));  // zpart
-  tot += 256;                                                 // status
-  return tot;
-}
+size_t workspace_bytes(const cfr_reader& r) { return WorkspaceLayout(r).total; }
 
 void carve_workspace(cfr_reader& r) {
-  const cfr_config& c = r.cfg;
-  const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
+  const WorkspaceLayout l(r);
   char* p = static_cast<char*>(r.ws);
-  r.xrot = carve<float>(p, B * H);
-  r.sel = carve<uint8_t>(p, B * r.nblk * c.n_screen);
-  r.ghat = carve<float>(p, B * nc);
-  r.vhat = carve<float>(p, B * nc);
-  r.pact = carve<float>(p, B * nc);
-  r.score = carve<float>(p, B * nc);
-  r.kept = carve<int32_t>(p, B * nc);
-  r.rowidx = carve<int32_t>(p, B * nc);
-  r.coef = carve<float>(p, B * nc);
-  r.zpart = carve<float>(p, r.zrows * (c.rank > 0 ? c.rank : 1));
-  r.status = carve<int32_t>(p, 1);
+  r.acc = reinterpret_cast<unsigned long long*>(p + l.acc);
+  r.wn = reinterpret_cast<float*>(p + l.wn);
+  r.ypart = reinterpret_cast<float*>(p + l.ypart);
+  r.zpart = reinterpret_cast<float*>(p + l.zpart);
+  r.xrot = reinterpret_cast<float*>(p + l.xrot);
+  r.sel = reinterpret_cast<uint8_t*>(p + l.sel);
+  r.ghat = reinterpret_cast<float*>(p + l.ghat);
+  r.vhat = reinterpret_cast<float*>(p + l.vhat);
+  r.score = reinterpret_cast<float*>(p + l.score);
+  r.kept = reinterpret_cast<int32_t*>(p + l.kept);
+  r.status = reinterpret_cast<int32_t*>(p + l.status);
 }
 
 void free_reader(cfr_reader* r) {
@@ -84,7 +92,10 @@ void init_geometry(cfr_reader& r) {
   r.lp = half_bytes(r.cfg.inter);
   r.unit = unit_bytes(r.cfg.inter);
   r.ncand = r.cfg.top * r.cfg.inter;
-  r.zrows = zpart_rows(r.cfg);
+  {
+    const SelectGeom g = select_geom(r.ncand);
+    r.ncp = g.nt * g.per;
+  }
 }
 
 struct ResidentSizes {
@@ -124,7 +135,9 @@ int alloc_resident(cfr_reader& r, bool with_router) {
   if ((e = hipMalloc(&r.ws, r.ws_bytes)) != hipSuccess)
     return fail(CFR_ENOMEM, std::string("workspace allocation: ") + hipGetErrorString(e));
   carve_workspace(r);
-  // zeroed once: every index a kernel can read from the workspace is then valid
+  // zeroed once: the screen accumulators start at zero (the reduce kernel
+  // clears them after every decode) and every index a kernel can read from
+  // the workspace is then valid
   if ((e = hipMemset(r.ws, 0, r.ws_bytes)) != hipSuccess) return hipf(e, "workspace init");
   return CFR_OK;
 }

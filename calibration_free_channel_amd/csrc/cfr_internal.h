@@ -16,7 +16,7 @@ constexpr int kMaxInter = 4096;
 constexpr int kMaxTop = 16;
 constexpr int kMaxRank = 64;
 constexpr int kMaxBatch = 64;
-constexpr int kMaxHidden = 16384;
+constexpr int kMaxHidden = 4096;
 
 // Error reporting (thread-local message).
 int fail(int code, const std::string& msg);
@@ -50,6 +50,7 @@ double f16_to_f64(uint16_t h);
 struct cfr_reader {
   cfr_config cfg;
   int nblk, lp, unit, ncand;
+  int ncp = 0;  // candidates per token padded for the select kernel (select_geom)
   // resident state
   uint16_t* w3 = nullptr;      // [E][I][3][H] bf16
   uint8_t* codes = nullptr;    // [E][nblk][128][unit]
@@ -60,19 +61,18 @@ struct cfr_reader {
   uint16_t* b = nullptr;       // [E][I][rank] fp16
   float* sigma = nullptr;      // [H] +1 / -1
   uint16_t* router = nullptr;  // [E][H] bf16 or null
-  // workspace (sized for cfg.max_batch)
+  // workspace (sized for cfg.max_batch); one allocation, zeroed once
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  unsigned long long* acc = nullptr;  // [B][2][ncp] fixed-point screen sums (gate, up); zero between calls
+  float* wn = nullptr;         // [B][ncp]  routing weight * ||d_j|| per candidate
+  float* ypart = nullptr;      // [B][kMaxGatherWgs][H]  partial outputs of the gather workgroups
+  float* zpart = nullptr;      // [B][kMaxRecoverWgs][rank]  partial recovery vectors
   float* xrot = nullptr;       // [B][H]   H_128 (sigma x) per block (debug copy only)
   uint8_t* sel = nullptr;      // [B][nblk][n_screen] (debug copy only)
-  float* ghat = nullptr;       // [B][ncand]
-  float* vhat = nullptr;       // [B][ncand]
-  float* pact = nullptr;       // [B][ncand]  p = phi(ghat) vhat
-  float* score = nullptr;      // [B][ncand]
-  int32_t* kept = nullptr;     // [B][ncand]  kept candidates by rank
-  int32_t* rowidx = nullptr;   // [B][ncand]  e*I + j of each kept rank
-  float* coef = nullptr;       // [B][ncand]  w * a of each kept rank
-  float* zpart = nullptr;      // [zrows][rank]  partial recovery vectors
+  float* ghat = nullptr;       // [B][ncand] (debug copy only)
+  float* vhat = nullptr;       // [B][ncand] (debug copy only)
+  float* score = nullptr;      // [B][ncand] (debug copy only)
+  int32_t* kept = nullptr;     // [B][ncand]  kept candidates by rank (debug copy only)
   int32_t* status = nullptr;   // [1]
-  size_t zrows = 0;
 };

@@ -21,7 +21,7 @@ int validate_config(const cfr_config* c) {
   if (!c) return fail(CFR_EINVAL, "config is NULL");
   if (c->hidden <= 0 || c->hidden % kBlock != 0)
     return fail(CFR_EINVAL, "hidden must be a positive multiple of 128");
-  if (c->hidden > kMaxHidden) return fail(CFR_EUNSUPPORTED, "hidden above 16384");
+  if (c->hidden > kMaxHidden) return fail(CFR_EUNSUPPORTED, "hidden above 4096");
   if (c->n_experts <= 0) return fail(CFR_EINVAL, "n_experts must be positive");
   if (c->inter <= 0) return fail(CFR_EINVAL, "inter must be positive");
   if (c->inter > kMaxInter) return fail(CFR_EUNSUPPORTED, "inter above 4096");

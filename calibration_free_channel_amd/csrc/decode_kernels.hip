@@ -3,35 +3,36 @@
 // Per token and layer ([zh §方法步骤详情] decode steps (1)-(4); [zh §核心方法];
 // [ko §어떻게 쓰나]; zh/ko = the Chinese/Korean summary pages of "Channel
 // Selection for Mixture-of-Experts Decoding Needs No Calibration Data"), three
-// kernels separated by the only two global dependencies of the method:
+// kernels; a kernel boundary is the only grid-wide synchronisation:
 //
-//   A  k_screen_score   rotate x (float32 butterfly, H_128 sigma x per block),
-//                       pick the n_screen coordinates of largest |v| per block
-//                       (LDS radix select), read the codes of those coordinates
-//                       for a slice of channels of one routed expert, and emit
-//                       g_hat, v_hat, p = silu(g_hat) v_hat and the output-unit
-//                       score s = w ||d|| |p| of every channel in the slice.
-//   B  k_select_exact   every workgroup finds the exact top-k threshold of its
-//                       token from all scores (radix select, ties to the lower
-//                       candidate index), takes its share of the kept channels,
-//                       computes a_j = silu(g_j.x)(v_j.x) from the native BF16
-//                       rows and w a_j, and a partial recovery vector
-//                       z = sum over its skipped candidates of w p b.
-//   C  k_down_recover   per hidden slice: y = sum over kept of (w a_j) d_j
-//                       (transposed down rows) + U z.
+//   1 k_screen   one workgroup per (token, routed slot, 128-block, half):
+//                rotate the block of x (float32 butterfly of H_128 sigma x),
+//                pick its n_screen coordinates of largest |value| (ties to the
+//                lower index), read the whole half-units of those coordinates
+//                (coalesced: every sketch byte is fetched by exactly one
+//                workgroup), decode the base-3 codes through an LDS table and
+//                add alpha_b * sum_i c_i x_i for every channel of the half into
+//                a 64-bit fixed-point accumulator.  Integer addition is
+//                associative, so the sum over blocks is bit-reproducible
+//                whatever the order the workgroups finish in.
+//   2 k_select   per token, G gather workgroups and Z recovery workgroups.
+//                Each finalises g_hat, v_hat, p = silu(g_hat) v_hat and the
+//                output-unit score s = w ||d|| |p| of every candidate,
+//                finds the exact top-k (radix select on order-preserving
+//                keys, ties to the lower candidate index) and ranks the kept
+//                candidates in index order.  A gather workgroup then loads the
+//                native gate, up and down rows of its share of the kept
+//                channels at once (one memory latency), computes
+//                a_j = silu(g_j.x)(v_j.x) and writes the partial output
+//                sum_j w a_j d_j over its share.  A recovery workgroup reads
+//                b_j of the skipped candidates in its candidate range and
+//                writes the partial recovery vector z = sum w p_j b_j.
+//   3 k_reduce   per hidden slice: y = sum of the partial outputs + U z, and
+//                clears the screen accumulators for the next call.
 //
-// Each workgroup of A owns whole channels (all blocks, all screened
-// coordinates), so no partial sums cross workgroups before the top-k.
-// Cross-workgroup handoff goes through kernel boundaries: on MI355X a kernel
-// boundary costs less than an in-kernel grid barrier, whose agent-scope
-// release has to write back every XCD's L2.
-//
-// Workgroups are mapped XCD-aware: dispatch places workgroup i on XCD i % 8,
-// so work item (i % 8) * per_xcd + i / 8 gives each XCD a contiguous range of
-// items.  In A that puts all slices of one routed expert on one XCD (its L2
-// then fetches each 32-byte sector of a sketch unit once); in C adjacent
-// hidden slices of a row land in the same L2.  The mapping only affects
-// performance, never correctness.
+// In-kernel grid barriers and last-arriver counters were measured slower on
+// MI355X than a kernel boundary (agent-scope atomics on one address
+// serialise), so no kernel waits for another workgroup.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -41,15 +42,38 @@ namespace cfr {
 namespace {
 
 constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
-constexpr int kThreads = 256;
-constexpr int kMaxS1024 = 8;  // widest slice that still fits 128 VGPRs at 1024 threads
-constexpr int kMaxS = 13;  // bytes per half handled by one screen workgroup
+constexpr float kTwo32 = 4294967296.0f;                // 2^32: fixed-point scale of the screen sums
+constexpr int kCB = 8;  // screened coordinates whose code words are in flight together
 
 __device__ __forceinline__ float f16f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
+__device__ __forceinline__ float lo16(uint32_t w) { return f16f((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi16(uint32_t w) { return f16f((uint16_t)(w >> 16)); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) through the hardware exp2 and reciprocal (about
+// one ulp each; the method's tolerances are far wider).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// float -> 64-bit two's complement fixed point with 32 fraction bits, rounded
+// to nearest; exact in float32 arithmetic for |v| < 2^31: v = fl + fr with
+// fl = floor(v) and fr in [0, 1), and fr * 2^32 is an exact float.
+__device__ __forceinline__ unsigned long long to_fix(float v) {
+  const float fl = floorf(v);
+  const float fr = v - fl;
+  const uint32_t hi = (uint32_t)(int)fl;
+  const uint32_t lo = (uint32_t)rintf(fr * kTwo32);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// fixed point -> float (one rounding)
+__device__ __forceinline__ float from_fix(unsigned long long x) {
+  return fmaf((float)(int)(x >> 32), kTwo32, (float)(uint32_t)x) * (1.0f / kTwo32);
+}
 
 __device__ __forceinline__ int clamp_expert(int e, int E, int32_t* status) {
   if (e < 0 || e >= E) {
@@ -57,6 +81,13 @@ __device__ __forceinline__ int clamp_expert(int e, int E, int32_t* status) {
     e = e < 0 ? 0 : E - 1;
   }
   return e;
+}
+
+// Order-preserving map of a float to an unsigned key: a larger float gives a
+// larger key (negative values below positive ones).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Value of lane (lane ^ H) in a wave64, through register-level exchanges:
@@ -109,18 +140,22 @@ __device__ __forceinline__ int wave_scan(int v) {
   return v;
 }
 
-// Inclusive prefix sum over a 256-thread block (4 waves) with one barrier;
-// sh (4 ints) must not be written again before the caller's next barrier.
-__device__ __forceinline__ int block_scan_256(int v, int* sh) {
+// Inclusive prefix sum over the NT threads of a workgroup.  sh: NT/64 ints
+// that nobody else uses between the two barriers inside.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int* sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_scan(v);
   if (lane == 63) sh[w] = v;
   __syncthreads();
   int add = 0;
   for (int q = 0; q < w; ++q) add += sh[q];
+  __syncthreads();
   return v + add;
 }
 
+// Dispatch places workgroup i on XCD i % 8; item (i % 8) * per_xcd + i / 8
+// gives each XCD a contiguous range of items (performance only).
 __device__ __forceinline__ int xcd_item(int id, int per_xcd) {
   return (id & 7) * per_xcd + (id >> 3);
 }
@@ -128,7 +163,7 @@ __device__ __forceinline__ int xcd_item(int id, int per_xcd) {
 }  // namespace
 
 // ===========================================================================
-// A: rotate + select + screen + score
+// 1: rotate + select + screen
 // ===========================================================================
 struct ScreenArgs {
   const float* x;
@@ -138,26 +173,24 @@ struct ScreenArgs {
   const uint8_t* codes;
   const uint16_t* scales;
   const float* norms;
+  unsigned long long* acc;
+  float* wn;
   float* xrot;
   uint8_t* sel;
-  float* ghat;
-  float* vhat;
-  float* pact;
-  float* score;
   int32_t* status;
-  int H, E, I, top, nblk, n_screen, lp, unit, n_slices, items, per_xcd, dbg;
+  int H, E, I, top, ncp, nblk, ns, lp, unit, nd, ng, items, per_xcd, dbg;
 };
 
-// One wave rotates and screens one 128-block held as two values per lane
-// (lane l holds coordinates l and l + 64).  The float32 butterfly runs the
-// stages h = 1 .. 32 across lanes and h = 64 inside the lane, in that order,
-// with the lower element of each pair taking a + b and the upper a - b.
-// The n_screen largest |v| (ties to the lower index) are found by a
-// bit-by-bit search of the n_screen-th largest magnitude over wave ballots,
-// then compacted in ascending coordinate order.
-__device__ __forceinline__ void rotate_select_block(float v0, float v1, int b, int NS,
-                                                    uint8_t* sl, int2* rec, int unit,
-                                                    float* xrot_out) {
+// Wave 0 rotates and ranks one 128-block held as two values per lane (lane l
+// holds coordinates l and l + 64).  The float32 butterfly runs the stages
+// h = 1 .. 32 across lanes and h = 64 inside the lane, in that order, with
+// the lower element of each pair taking a + b and the upper a - b.  The
+// n_screen largest |v| (ties to the lower index) are found by a bit-by-bit
+// search of the n_screen-th largest magnitude over wave ballots, then
+// compacted in ascending coordinate order into sl (coordinate) and rec
+// (byte offset of its unit, value bits).
+__device__ __forceinline__ void rotate_select(float v0, float v1, int NS, uint8_t* sl, int2* rec,
+                                              int unit, float* xrot_out) {
   const int lane = threadIdx.x & 63;
   auto stage = [&](float o0, float o1, int h) {
     if (lane & h) {
@@ -201,84 +234,64 @@ __device__ __forceinline__ void rotate_select_block(float v0, float v1, int b, i
   if (s0) {
     const int pos = __popcll(m0 & lt);
     if (pos < NS) {
-      sl[b * NS + pos] = (uint8_t)lane;
-      rec[b * NS + pos] = make_int2(lane * unit, __float_as_int(v0));
+      sl[pos] = (uint8_t)lane;
+      rec[pos] = make_int2(lane * unit, __float_as_int(v0));
     }
   }
   if (s1) {
     const int pos = __popcll(m0) + __popcll(m1 & lt);
     if (pos < NS) {
-      sl[b * NS + pos] = (uint8_t)(lane + 64);
-      rec[b * NS + pos] = make_int2((lane + 64) * unit, __float_as_int(v1));
+      sl[pos] = (uint8_t)(lane + 64);
+      rec[pos] = make_int2((lane + 64) * unit, __float_as_int(v1));
     }
   }
 }
 
-template <int S, int NT>
-__global__ __launch_bounds__(NT) void k_screen_score(ScreenArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
+template <int NT>
+__global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
+  __shared__ uint4 lut[256];
+  __shared__ int2 rec[128];
+  __shared__ uint8_t sl[128];
+  extern __shared__ __align__(16) float red[];  // [ng][nd * 20]
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
-  const int c = item % a.n_slices;
-  const int ts = item / a.n_slices;
+  const int m = item & 1;          // 0 gate, 1 up
+  const int rb = item >> 1;
+  const int b = rb % a.nblk;       // block
+  const int ts = rb / a.nblk;      // token * top + slot
   const int s = ts % a.top, t = ts / a.top;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NW = NT / 64;
-  const int H = a.H, I = a.I, nblk = a.nblk, NS = a.n_screen;
-  constexpr int NCH = 5 * S;  // channels per half in this slice
-  const ScreenLds L(nblk, NS, S, NT);
-  uint4* lut = reinterpret_cast<uint4*>(smem + L.lut);
-  uint8_t* sl = smem + L.sl;
-  int2* rec = reinterpret_cast<int2*>(smem + L.rec);  // (unit byte offset, x bits) per screened coordinate
-  float* sc = reinterpret_cast<float*>(smem + L.sc);
-  float* red = reinterpret_cast<float*>(smem + L.red);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int H = a.H, I = a.I, NS = a.ns;
+  const int e = clamp_expert(a.ids[ts], a.E, a.status);
 
-  // token and signs of this wave's first blocks: independent of the routing
-  const float* xt = a.x + (size_t)t * H;
-  float xv0[4], xv1[4], sg0[4], sg1[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {  // clamped addresses: every load is issued, none waits
-    const int b = min(wave + u * NW, nblk - 1);
-    xv0[u] = xt[b * 128 + lane];
-    xv1[u] = xt[b * 128 + 64 + lane];
-    sg0[u] = a.sigma[b * 128 + lane];
-    sg1[u] = a.sigma[b * 128 + 64 + lane];
+  // token block and signs (wave 0), scales of the channels this thread
+  // finalises: all issued before any is used
+  float x0 = 0.f, x1 = 0.f, g0 = 0.f, g1 = 0.f;
+  if (tid < 64) {
+    const float* xb = a.x + (size_t)t * H + b * 128;
+    x0 = xb[lane];
+    x1 = xb[lane + 64];
+    g0 = a.sigma[b * 128 + lane];
+    g1 = a.sigma[b * 128 + 64 + lane];
   }
-  const int e = clamp_expert(a.ids[t * a.top + s], a.E, a.status);
-  const float wgt = a.gw[t * a.top + s];
-  const int b0 = c * S;   // first byte of the slice inside each half
-  const int j0 = 5 * b0;  // first channel of the slice
-
-  // scales of the slice for every block and half: the first batch is
-  // loaded now and stored after the rotation, so its latency hides there
-  const int nsc = nblk * 2 * NCH;
-  uint16_t hv[4];
-  auto load_scales = [&](int q0) {
+  constexpr int MAXJ = kMaxInter / NT;
+  uint16_t al[MAXJ];
+  const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = q0 + tid + u * NT;
-      const int jj = q % NCH, bm = q / NCH;  // bm = block * 2 + half
-      const int j = j0 + jj;
-      const bool ok = q < nsc && j < I;
-      const size_t ix = ok ? ((size_t)e * nblk + (bm >> 1)) * 2 * I + (bm & 1) * I + j : 0;
-      hv[u] = a.scales[ix];
-      hv[u] = ok ? hv[u] : (uint16_t)0;
-    }
-  };
-  auto store_scales = [&](int q0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = q0 + tid + u * NT;
-      if (q < nsc) sc[q] = f16f(hv[u]);
-    }
-  };
-  load_scales(0);
-  float nrm = 0.f;
-  if (tid < NCH && j0 + tid < I) nrm = a.norms[(size_t)e * I + j0 + tid];
-
+  for (int q = 0; q < MAXJ; ++q) {
+    const int j = tid + q * NT;
+    al[q] = j < I ? sp[j] : (uint16_t)0;
+  }
+  // routing weight times down-column norm of every channel of this slot,
+  // written once per slot for the score
+  if (b == 0 && m == 1) {
+    const float w = a.gw[ts];
+    float* wo = a.wn + (size_t)t * a.ncp + (size_t)s * I;
+    for (int j = tid; j < I; j += NT) wo[j] = w * a.norms[(size_t)e * I + j];
+  }
   // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
   // 243..255 never occur in a packed unit and decode to zero)
-  if (tid < 256) {  // NT >= 512
+  if (tid < 256) {
     uint32_t h[5] = {0u, 0u, 0u, 0u, 0u};
     if (tid < 243) {
       int q = tid;
@@ -291,118 +304,75 @@ __global__ __launch_bounds__(NT) void k_screen_score(ScreenArgs a) {
     }
     lut[tid] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u);
   }
-
-  // ---- decode step (1): rotation and the partial-screen coordinates ----
-  const bool writer = a.dbg && c == 0 && s == 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int b = wave + u * NW;
-    if (b < nblk)
-      rotate_select_block(xv0[u] * sg0[u], xv1[u] * sg1[u], b, NS, sl, rec, a.unit,
-                          writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
-  }
-  for (int b = wave + 4 * NW; b < nblk; b += NW) {  // hidden above 4096
-    const float v0 = xt[b * 128 + lane] * a.sigma[b * 128 + lane];
-    const float v1 = xt[b * 128 + 64 + lane] * a.sigma[b * 128 + 64 + lane];
-    rotate_select_block(v0, v1, b, NS, sl, rec, a.unit,
-                        writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
-  }
-  __syncthreads();
-  store_scales(0);
-  for (int q0 = NT * 4; q0 < nsc; q0 += NT * 4) {  // large layers only
-    load_scales(q0);
-    store_scales(q0);
-  }
+  // decode step (1): rotation and the partial-screen coordinates
+  const bool writer = a.dbg && s == 0 && m == 0;
+  if (tid < 64)
+    rotate_select(x0 * g0, x1 * g1, NS, sl, rec, a.unit,
+                  writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
   __syncthreads();
   if (writer)
-    for (int q = tid; q < nblk * NS; q += NT) a.sel[(size_t)t * nblk * NS + q] = sl[q];
+    for (int q = tid; q < NS; q += NT) a.sel[((size_t)t * a.nblk + b) * NS + q] = sl[q];
 
-  // ---- screen: codes of the slice at the screened coordinates ----
-  // group g = (block, half) with tpg threads; each thread takes every
-  // tpg-th screened coordinate of its block.
-  const int groups = 2 * nblk;
-  int tpg = 1;
-  while (tpg * 2 * groups <= NT) tpg *= 2;
-  const int g = tid / tpg, lg = tid % tpg;
-  float acc[NCH];
+  // screen: thread (g, d) takes code word d (channels 20d .. 20d+19 of the
+  // half) at every ng-th screened coordinate starting at g
+  const int ND = a.nd, NG = a.ng;
+  const int g = tid / ND, d = tid - g * ND;
+  float acc[20];
 #pragma unroll
-  for (int q = 0; q < NCH; ++q) acc[q] = 0.f;
-  const int nbytes = (I + 4) / 5;
-  const int nb_slice = min(S, nbytes - b0);  // bytes of this slice inside a half
-  if (g < groups) {
-    const int b = g >> 1, m = g & 1;
-    const uint8_t* ubase = a.codes + ((size_t)e * nblk + b) * 128 * a.unit + m * a.lp + (b0 & ~3);
-    const int sh = (b0 & 3) * 8;
-    constexpr int ND = (S + 6) / 4;  // dwords covering S bytes at any 4-byte phase
-    constexpr int CB = 5;            // coordinates whose codes are in flight together
-    for (int q0 = lg; q0 < NS; q0 += tpg * CB) {
-      // all records first, then all code loads: one LDS and one memory latency per batch
-      int2 rc[CB];
+  for (int q = 0; q < 20; ++q) acc[q] = 0.f;
+  if (g < NG) {
+    const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit + m * a.lp + 4 * d;
+    for (int c0 = g; c0 < NS; c0 += NG * kCB) {
+      uint32_t wv[kCB];
+      float xv[kCB];
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const int q = q0 + u * tpg;
-        rc[u] = rec[b * NS + (q < NS ? q : NS - 1)];
-      }
-      uint32_t w[CB][ND];
-      float xv[CB];
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(ubase + rc[u].x);
-#pragma unroll
-        for (int d = 0; d < ND; ++d) w[u][d] = wp[d];
-        xv[u] = q0 + u * tpg < NS ? __int_as_float(rc[u].y) : 0.f;  // past the list: x = 0
+      for (int u = 0; u < kCB; ++u) {
+        const int c = c0 + u * NG;
+        const int2 rc = rec[c < NS ? c : NS - 1];  // clamped; past the list x = 0
+        wv[u] = *reinterpret_cast<const uint32_t*>(ub + rc.x);
+        xv[u] = c < NS ? __int_as_float(rc.y) : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < CB; ++u) {
+      for (int u = 0; u < kCB; ++u) {
 #pragma unroll
-        for (int k = 0; k < S; ++k) {
-          const int bit = sh + 8 * k;
-          const int wi = bit >> 5, bo = bit & 31;
-          const uint32_t byte = wi < ND ? (w[u][wi < ND ? wi : 0] >> bo) & 0xFFu : 121u;
-          if (k < nb_slice) {
-            const uint4 cw = lut[byte];
-            const uint32_t hw[3] = {cw.x, cw.y, cw.z};
-#pragma unroll
-            for (int d = 0; d < 5; ++d) {
-              const uint16_t hb = (uint16_t)(hw[d >> 1] >> ((d & 1) * 16));
-              acc[5 * k + d] = fmaf((float)__builtin_bit_cast(_Float16, hb), xv[u], acc[5 * k + d]);
-            }
-          }
+        for (int kb = 0; kb < 4; ++kb) {
+          const uint4 cw = lut[(wv[u] >> (8 * kb)) & 0xFFu];
+          acc[5 * kb + 0] = fmaf(lo16(cw.x), xv[u], acc[5 * kb + 0]);
+          acc[5 * kb + 1] = fmaf(hi16(cw.x), xv[u], acc[5 * kb + 1]);
+          acc[5 * kb + 2] = fmaf(lo16(cw.y), xv[u], acc[5 * kb + 2]);
+          acc[5 * kb + 3] = fmaf(hi16(cw.y), xv[u], acc[5 * kb + 3]);
+          acc[5 * kb + 4] = fmaf(lo16(cw.z), xv[u], acc[5 * kb + 4]);
         }
       }
     }
-  }
-  if (g < groups) {
+    float* my = red + (size_t)g * ND * 20 + d * 20;
 #pragma unroll
-    for (int q = 0; q < NCH; ++q) red[(size_t)tid * NCH + q] = acc[q];
+    for (int q = 0; q < 20; q += 4) *reinterpret_cast<float4*>(my + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
   }
   __syncthreads();
-  if (g < groups)
-    for (int jj = lg; jj < NCH; jj += tpg) {
-      float v = 0.f;
-      for (int l = 0; l < tpg; ++l) v += red[(size_t)(g * tpg + l) * NCH + jj];
-      sc[g * NCH + jj] *= v;  // alpha_b * sum over screened coordinates
+  // channel j = 20 d + i sits at red[g][j]: sum the coordinate groups, scale
+  // by alpha_b and add to the fixed-point accumulator
+  unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
+#pragma unroll
+  for (int q = 0; q < MAXJ; ++q) {
+    const int j = tid + q * NT;
+    if (j < I) {
+      float S = 0.f;
+      const float* rj = red + j;
+      int gg = 0;
+      for (; gg + 4 <= NG; gg += 4) {  // four LDS reads in flight
+        const float r0 = rj[(size_t)gg * ND * 20], r1 = rj[(size_t)(gg + 1) * ND * 20];
+        const float r2 = rj[(size_t)(gg + 2) * ND * 20], r3 = rj[(size_t)(gg + 3) * ND * 20];
+        S += (r0 + r1) + (r2 + r3);
+      }
+      for (; gg < NG; ++gg) S += rj[(size_t)gg * ND * 20];
+      atomicAdd(ap + j, to_fix(f16f(al[q]) * S));
     }
-  __syncthreads();
-  if (tid < NCH && j0 + tid < I) {
-    float gs = 0.f, vs = 0.f;
-    for (int b = 0; b < nblk; ++b) {
-      gs += sc[(2 * b) * NCH + tid];
-      vs += sc[(2 * b + 1) * NCH + tid];
-    }
-    gs *= kInvSqrt128f;
-    vs *= kInvSqrt128f;
-    const float p = silu(gs) * vs;
-    const size_t o = (size_t)t * a.top * I + (size_t)s * I + j0 + tid;
-    a.ghat[o] = gs;
-    a.vhat[o] = vs;
-    a.pact[o] = p;
-    a.score[o] = fabsf(wgt) * nrm * fabsf(p);  // routing weights are non-negative; |w| keeps the sign bit clear
   }
 }
 
 // ===========================================================================
-// B: exact top-k (redundant per workgroup) + exact kept channels + recovery z
+// 2: finalise scores, exact top-k, gather kept channels / recovery partials
 // ===========================================================================
 struct SelectArgs {
   const float* x;
@@ -410,475 +380,490 @@ struct SelectArgs {
   const float* gw;
   const uint16_t* w3;
   const uint16_t* bmat;
-  const float* score;
-  const float* pact;
-  int32_t* kept;
-  int32_t* rowidx;
-  float* coef;
+  const unsigned long long* acc;
+  const float* wn;
+  float* ypart;
   float* zpart;
+  float* ghat;   // debug outputs (written by workgroup 0 of each token when dbg)
+  float* vhat;
+  float* score;
+  int32_t* kept;
   int32_t* status;
-  int H, E, I, top, ncand, k, rank, G, share_max, ZW;
-  int dense;  // 1: every candidate is kept (the dense baseline); scores unused
+  int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dense, dbg;
 };
 
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void k_select_exact(SelectArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int t = blockIdx.x / a.G, w = blockIdx.x % a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, I = a.I, nc = a.ncand, k = a.k;
-  const SelectLds L(H, nc, a.share_max, a.rank);
-  float* xs = reinterpret_cast<float*>(smem + L.xs);
-  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + L.keys);
-  uint8_t* flags = smem + L.flags;
-  int* list = reinterpret_cast<int*>(smem + L.list);
-  float* zred = reinterpret_cast<float*>(smem + L.zred);
-  int* hist = reinterpret_cast<int*>(smem + L.hist);  // 4096 bins, then 2 x 1024 bins
-  int* hist1 = hist + 4096;
-  int* hist2 = hist1 + 1024;
-  int* misc = reinterpret_cast<int*>(smem + L.misc);
-  // misc: [0..3] [4..7] [12..15] scan scratch, [8] digit [9] need [10] bin count,
-  // [11] gather slot, [16] [17] boundary key and count, [20..35] routed expert
-  // of each slot, [36..51] its weight; bkey/bidx: the boundary bin's elements
-  int* sl_e = misc + 20;
-  float* sl_w = reinterpret_cast<float*>(misc + 36);
-  uint32_t* bkey = reinterpret_cast<uint32_t*>(misc + 64);
-  int* bidx = misc + 128;
+// misc slots
+constexpr int kMiscDigit = 16, kMiscNeed = 17, kMiscCount = 18, kMiscSlot = 19;
+constexpr int kDirectMax = 32;  // boundary sets up to this size are ranked directly
 
-  const bool partial = !a.dense && k > 0 && k < nc;
+template <int NT, int PER, int NCH>
+__global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NW = NT / 64;
+  const int wgs = a.G + a.Z;
+  const int t = blockIdx.x / wgs, w = blockIdx.x - t * wgs;
+  const bool recover = w >= a.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I, nc = a.nc, k = a.k;
+  const GatherLds L(H, a.ncp, NT, a.chan);
+  float* xs = reinterpret_cast<float*>(smem + L.xs);
+  float* pvl = reinterpret_cast<float*>(smem + L.pv);
+  uint8_t* flags = smem + L.flags;
+  float* yred = reinterpret_cast<float*>(smem + L.yred);
+  int* hist = reinterpret_cast<int*>(smem + L.hist);
+  int* list = reinterpret_cast<int*>(smem + L.list);
+  int* misc = reinterpret_cast<int*>(smem + L.misc);
+  uint32_t* bkey = reinterpret_cast<uint32_t*>(smem + L.bkey);
+  int* bidx = reinterpret_cast<int*>(smem + L.bidx);
+  int* sl_e = reinterpret_cast<int*>(smem + L.slot_e);
+  float* sl_w = reinterpret_cast<float*>(smem + L.slot_w);
+  float* zred = reinterpret_cast<float*>(smem + L.zred);
+
   const bool all = a.dense || k == nc;
-  const int per = (nc + kThreads - 1) / kThreads;  // candidates per thread (uniform)
-  // loads first, all issued before any is consumed: routing of the token,
-  // the token itself, its scores
-  const int tsl = min(tid, a.top - 1);
-  const int id_raw = a.ids[t * a.top + tsl];
-  const float gw_raw = a.gw[t * a.top + tsl];
-  const float* xt = a.x + (size_t)t * H;
-  {
-    // four named registers rather than an array: the array form ends up on
-    // the stack once its stores sit below the score loads
-    const int xq0 = min(tid * 4, H - 4), xq1 = min((tid + kThreads) * 4, H - 4);
-    const int xq2 = min((tid + 2 * kThreads) * 4, H - 4), xq3 = min((tid + 3 * kThreads) * 4, H - 4);
-    const float4 xr0 = *reinterpret_cast<const float4*>(xt + xq0);
-    const float4 xr1 = *reinterpret_cast<const float4*>(xt + xq1);
-    const float4 xr2 = *reinterpret_cast<const float4*>(xt + xq2);
-    const float4 xr3 = *reinterpret_cast<const float4*>(xt + xq3);
-    // all KPT score loads are issued unguarded (clamped addresses) and only
-    // consumed after the token's stores, so one memory latency covers them
-    float v[KPT];
-    if (partial) {
-      const float* sct = a.score + (size_t)t * nc;
+  const bool partial = !all && k > 0;
+  const int kk = all ? nc : k;  // kept candidates
+  const int c0 = tid * PER;     // this thread's candidates: [c0, c0 + PER)
+
+  // ---- loads: routing, token, screen sums; all issued before use ----
+  if (tid < a.top) {
+    sl_e[tid] = clamp_expert(a.ids[t * a.top + tid], a.E, a.status);
+    sl_w[tid] = a.gw[t * a.top + tid];
+  }
+  if (!recover)
+    for (int h = tid * 4; h < H; h += NT * 4)
+      *reinterpret_cast<float4*>(xs + h) = *reinterpret_cast<const float4*>(a.x + (size_t)t * H + h);
+  if (partial)
+    for (int q = tid; q < 2048; q += NT) hist[q] = 0;
+  uint32_t key[PER];
+  float pr[PER];
+  if (!a.dense) {
+    ulonglong2 gq[PER / 2], vq[PER / 2];
+    float4 wq[PER / 4];
+    const ulonglong2* ag = reinterpret_cast<const ulonglong2*>(a.acc + (size_t)t * 2 * a.ncp + c0);
+    const ulonglong2* av = reinterpret_cast<const ulonglong2*>(a.acc + ((size_t)t * 2 + 1) * a.ncp + c0);
+    const float4* wp = reinterpret_cast<const float4*>(a.wn + (size_t)t * a.ncp + c0);
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) v[u] = sct[min(tid + u * kThreads, nc - 1)];
+    for (int u = 0; u < PER / 2; ++u) {
+      gq[u] = ag[u];
+      vq[u] = av[u];
     }
-    if (tid < a.top) {
-      sl_e[tid] = clamp_expert(id_raw, a.E, a.status);
-      sl_w[tid] = gw_raw;
-    }
-    // clamped like the loads: duplicate addresses store equal values
-    *reinterpret_cast<float4*>(xs + xq0) = xr0;
-    *reinterpret_cast<float4*>(xs + xq1) = xr1;
-    *reinterpret_cast<float4*>(xs + xq2) = xr2;
-    *reinterpret_cast<float4*>(xs + xq3) = xr3;
-    for (int q = (tid + 4 * kThreads) * 4; q < H; q += kThreads * 4)  // hidden above 4096
-      *reinterpret_cast<float4*>(xs + q) = *reinterpret_cast<const float4*>(xt + q);
-    if (partial) {
-      // keys padded to 256 * per entries; padding keys are 0, the smallest key,
-      // and sit at the highest indices, so the tie rule never keeps them
 #pragma unroll
-      for (int u = 0; u < KPT; ++u)
-        if (u < per) keys[tid + u * kThreads] = tid + u * kThreads < nc ? __float_as_uint(v[u]) : 0u;
+    for (int u = 0; u < PER / 4; ++u) wq[u] = wp[u];
+    const bool dbg = a.dbg && w == 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) hist[tid * 16 + q] = 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) hist1[tid * 8 + q] = 0;  // both 1024-bin histograms
-      if (tid == 0) misc[11] = 0;
+    for (int i = 0; i < PER; ++i) {
+      const float gh = from_fix((i & 1) ? gq[i / 2].y : gq[i / 2].x) * kInvSqrt128f;
+      const float vh = from_fix((i & 1) ? vq[i / 2].y : vq[i / 2].x) * kInvSqrt128f;
+      const float4 w4 = wq[i / 4];
+      const float wn = (i & 3) == 0 ? w4.x : (i & 3) == 1 ? w4.y : (i & 3) == 2 ? w4.z : w4.w;
+      const float p = silu(gh) * vh;
+      const float sc = wn * fabsf(p);
+      const int c = c0 + i;
+      key[i] = c < nc ? order_key(sc) : 0u;  // padding ranks below every real candidate
+      pr[i] = p;
+      if (dbg && c < nc) {
+        a.ghat[(size_t)t * nc + c] = gh;
+        a.vhat[(size_t)t * nc + c] = vh;
+        a.score[(size_t)t * nc + c] = sc;
+      }
     }
   }
+  if (tid == 0) misc[kMiscSlot] = 0;
   __syncthreads();
-  // each thread owns a contiguous chunk of `per` (<= KPT) candidates, in
-  // registers; `per` is uniform, so every guard below is a scalar branch
-  const int lo = tid * per;
-  const int nreal = max(0, min(per, nc - lo));  // real candidates of this chunk
-  uint32_t kr[KPT];
-#pragma unroll
-  for (int q = 0; q < KPT; ++q) kr[q] = (partial && q < per) ? keys[lo + q] : 0u;
+
+  // ---- exact top-k: radix select over 11, 11 and 10 key bits ----
+  // After a pass, candidates whose masked key exceeds `prefix` are kept; the
+  // `need` remaining places go to the boundary set (masked key == prefix):
+  //   mode 0  the whole boundary set (its size equals need)
+  //   mode 1  the members ranked directly (flag 2 = kept, 1 = not)
+  //   mode 2  all boundary keys are equal: the lowest candidate indices
   uint32_t prefix = 0, mask = 0;
-  int need = k;
+  int need = kk, mode = 0;
   if (partial) {
-    // exact k-th largest key.  Scores are non-negative, so bits 30..19
-    // (exponent and 4 mantissa bits) order them; one pass over those 12 bits
-    // finds the boundary bin; a bin of at most 64 keys is then ranked
-    // directly, a larger one (many near-equal scores) is refined by two more
-    // passes over bits 18..9 and 8..0.
-#pragma unroll
-    for (int q = 0; q < KPT; ++q)
-      if (q < per) atomicAdd(&hist[(kr[q] >> 19) & 0xFFFu], 1);
-    __syncthreads();
-    {
-      const int base = 16 * (255 - tid);  // thread tid holds bins [base, base + 16), descending digits
-      int bins[16], own = 0;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint4 hq = *reinterpret_cast<const uint4*>(hist + base + 4 * q4);
-        bins[4 * q4] = (int)hq.x;
-        bins[4 * q4 + 1] = (int)hq.y;
-        bins[4 * q4 + 2] = (int)hq.z;
-        bins[4 * q4 + 3] = (int)hq.w;
-        own += (int)(hq.x + hq.y + hq.z + hq.w);
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nbins = pass == 2 ? 1024 : 2048;
+      const uint32_t dm = (uint32_t)nbins - 1u;
+      if (pass > 0) {
+        for (int q = tid; q < nbins; q += NT) hist[q] = 0;
+        __syncthreads();
       }
-      const int incl = block_scan_256(own, misc);
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (c0 + i < nc && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dm], 1);
+      __syncthreads();
+      // thread tid owns bins [base, base + bpt), highest bins first
+      const int bpt = nbins / NT;
+      const int base = nbins - (tid + 1) * bpt;
+      int own = 0;
+      for (int q = 0; q < bpt; ++q) own += hist[base + q];
+      const int incl = block_scan<NT>(own, misc);
       if (incl >= need && incl - own < need) {
         int cum = incl - own;
-#pragma unroll
-        for (int q = 15; q >= 0; --q) {
-          if (cum < need && cum + bins[q] >= need) {
-            misc[8] = base + q;
-            misc[9] = need - cum;
-            misc[10] = bins[q];
+        for (int q = bpt - 1; q >= 0; --q) {
+          const int hb = hist[base + q];
+          if (cum < need && cum + hb >= need) {
+            misc[kMiscDigit] = base + q;
+            misc[kMiscNeed] = need - cum;
+            misc[kMiscCount] = hb;
           }
-          cum += bins[q];
-        }
-      }
-    }
-    __syncthreads();
-    prefix = (uint32_t)misc[8] << 19;
-    mask = 0x7FF80000u;
-    need = misc[9];
-    const int cb = misc[10];
-    if (cb != need && cb <= 64) {
-      // rank the boundary bin's keys directly (key descending, index ascending)
-#pragma unroll
-      for (int q = 0; q < KPT; ++q)
-        if (q < per && (kr[q] & mask) == prefix) {
-          const int slot = atomicAdd(&misc[11], 1);
-          bkey[slot] = kr[q];
-          bidx[slot] = lo + q;
-        }
-      __syncthreads();
-      if (tid < cb) {
-        const uint32_t ki = bkey[tid];
-        const int ii = bidx[tid];
-        int gt = 0, eqb = 0;
-        for (int jx = 0; jx < cb; ++jx) {
-          const uint32_t kj = bkey[jx];
-          gt += kj > ki;
-          eqb += kj == ki && bidx[jx] < ii;
-        }
-        if (gt + eqb == need - 1) {
-          misc[16] = (int)ki;
-          misc[17] = need - gt;
+          cum += hb;
         }
       }
       __syncthreads();
-      prefix = (uint32_t)misc[16];
-      mask = 0xFFFFFFFFu;
-      need = misc[17];
-    } else if (cb != need) {
-      for (int pass = 1; pass < 3; ++pass) {  // bits 18..9, then 8..0
-        const int shift = pass == 1 ? 9 : 0;
-        const uint32_t dm = pass == 1 ? 0x3FFu : 0x1FFu;
-        int* hcur = pass == 1 ? hist1 : hist2;
+      prefix |= (uint32_t)misc[kMiscDigit] << shift;
+      mask |= dm << shift;
+      need = misc[kMiscNeed];
+      const int cnt = misc[kMiscCount];
+      if (cnt == need) {
+        mode = 0;
+        break;
+      }
+      if (cnt <= kDirectMax) {
+        // rank the boundary set directly (key descending, index ascending)
 #pragma unroll
-        for (int q = 0; q < KPT; ++q)
-          if (q < per && (kr[q] & mask) == prefix) atomicAdd(&hcur[(kr[q] >> shift) & dm], 1);
+        for (int i = 0; i < PER; ++i)
+          if (c0 + i < nc && (key[i] & mask) == prefix) {
+            const int slot = atomicAdd(&misc[kMiscSlot], 1);
+            bkey[slot] = key[i];
+            bidx[slot] = c0 + i;
+            flags[c0 + i] = 1;
+          }
         __syncthreads();
-        const int base = 4 * (255 - tid);
-        const uint4 hq = *reinterpret_cast<const uint4*>(hcur + base);
-        const int bins[4] = {(int)hq.x, (int)hq.y, (int)hq.z, (int)hq.w};
-        const int own = bins[0] + bins[1] + bins[2] + bins[3];
-        const int incl = block_scan_256(own, misc + (pass == 1 ? 4 : 12));
-        if (incl >= need && incl - own < need) {
-          int cum = incl - own;
-#pragma unroll
-          for (int q = 3; q >= 0; --q) {
-            if (cum < need && cum + bins[q] >= need) {
-              misc[8] = base + q;
-              misc[9] = need - cum;
+        if (tid < cnt) {
+          const uint32_t ki = bkey[tid];
+          const int ii = bidx[tid];
+          int rk = 0;
+#pragma unroll 8
+          for (int q = 0; q < kDirectMax; ++q)
+            if (q < cnt) {
+              const uint32_t kq = bkey[q];
+              rk += kq > ki || (kq == ki && bidx[q] < ii);
             }
-            cum += bins[q];
-          }
+          if (rk < need) flags[ii] = 2;
         }
         __syncthreads();
-        prefix |= (uint32_t)misc[8] << shift;
-        mask |= dm << shift;
-        need = misc[9];
-        __syncthreads();
+        mode = 1;
+        break;
       }
-      mask = 0xFFFFFFFFu;  // bit 31 is clear in every key
+      mode = 2;
     }
   }
-  // kept flags and ranks in ascending candidate order
-  int ngt = 0, neq = 0;
-  if (partial)
+
+  // ---- kept flags and ranks in ascending candidate order ----
+  bool on[PER];
+  if (all) {
 #pragma unroll
-    for (int q = 0; q < KPT; ++q)
-      if (q < per) {
-        const uint32_t kv = kr[q] & mask;
-        ngt += kv > prefix;
-        neq += kv == prefix;
-      }
-  __syncthreads();
-  const int eq_incl = block_scan_256(neq, misc);  // scratch [0..3]
-  const int eq_before = eq_incl - neq;
-  int take_eq = 0;
-  if (partial) take_eq = max(0, min(neq, need - eq_before));
-  const int mine = partial ? ngt + take_eq : (all ? nreal : 0);
-  const int pos_incl = block_scan_256(mine, misc + 4);  // scratch [4..7]
-  int rnk = pos_incl - mine;
-  const int share = (k + a.G - 1) / a.G;
-  const int r0 = min(w * share, k), r1 = min(r0 + share, k);
-  if (partial) {
+    for (int i = 0; i < PER; ++i) on[i] = c0 + i < nc;
+  } else if (!partial) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) on[i] = false;
+  } else {
+    int eq_before = 0;
+    if (mode == 2) {
+      int neq = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) neq += c0 + i < nc && (key[i] & mask) == prefix;
+      eq_before = block_scan<NT>(neq, misc) - neq;
+    }
     int eq_seen = 0;
 #pragma unroll
-    for (int q = 0; q < KPT; ++q)
-      if (q < per) {
-        const uint32_t kv = kr[q] & mask;
-        const bool eq = kv == prefix;
-        const bool on = kv > prefix || (eq && eq_seen < take_eq);
-        eq_seen += eq;
-        flags[lo + q] = on;
-        if (on && rnk >= r0 && rnk < r1) list[rnk - r0] = lo + q;
-        rnk += on;
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t km = key[i] & mask;
+      bool o = c0 + i < nc && km > prefix;
+      if (c0 + i < nc && km == prefix) {
+        if (mode == 0) o = true;
+        else if (mode == 1) o = flags[c0 + i] == 2;
+        else o = eq_before + (eq_seen++) < need;
       }
-  } else {
-    for (int q = 0; q < per; ++q) {
-      const bool on = all && q < nreal;
-      flags[lo + q] = on;
-      if (on && rnk >= r0 && rnk < r1) list[rnk - r0] = lo + q;
-      rnk += on;
+      on[i] = o;
+    }
+  }
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += on[i];
+  int rnk = block_scan<NT>(mine, misc) - mine;
+  const int r0 = recover ? 0 : min(w * a.chan, kk);
+  const int r1 = recover ? 0 : min(r0 + a.chan, kk);
+  {
+    const bool dbg = a.dbg && w == 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (on[i]) {
+        if (rnk >= r0 && rnk < r1) list[rnk - r0] = c0 + i;
+        if (dbg) a.kept[(size_t)t * nc + rnk] = c0 + i;
+        ++rnk;
+      }
+  }
+  if (recover) {
+    // p and the kept flags of every candidate, for the recovery ranges
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      *reinterpret_cast<float4*>(pvl + c0 + i) = make_float4(pr[i], pr[i + 1], pr[i + 2], pr[i + 3]);
+      *reinterpret_cast<uint32_t*>(flags + c0 + i) =
+          (uint32_t)on[i] | ((uint32_t)on[i + 1] << 8) | ((uint32_t)on[i + 2] << 16) | ((uint32_t)on[i + 3] << 24);
     }
   }
   __syncthreads();
 
-  // ---- decode step (3): exact kept channels from native BF16 rows ----
-  // one kept channel per wave; all of its gate and up loads in flight together
-  for (int q = wave; q < r1 - r0; q += 4) {
-    const int cnd = list[q];
-    const int sl = cnd / I, j = cnd % I;
-    const size_t row = (size_t)sl_e[sl] * I + j;
-    const uint16_t* gr = a.w3 + row * 3 * H;
-    float gsum = 0.f, vsum = 0.f;
-    for (int hb = 0; hb < H; hb += 512 * 8) {
-      uint4 gq[8], vq[8];
+  if (!recover) {
+    // ---- decode step (3): exact kept channels from native BF16 rows ----
+    // wave v takes list entries [v cpw, (v+1) cpw), two channels at a time
+    // when registers allow, all rows of both in flight together
+    float yv[NCH][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int h = min(hb + u * 512 + lane * 8, H - 8);  // clamped; the tail is skipped below
-        gq[u] = *reinterpret_cast<const uint4*>(gr + h);
-        vq[u] = *reinterpret_cast<const uint4*>(gr + H + h);
+    for (int q = 0; q < NCH; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[q][i] = 0.f;
+    const int nmine = r1 - r0;
+    constexpr bool kPair = NCH <= 4;
+    const int qend = min((wave + 1) * a.cpw, nmine);
+    for (int q0 = wave * a.cpw; q0 < qend; q0 += kPair ? 2 : 1) {
+      const bool two = kPair && q0 + 1 < qend;
+      const int cA = list[q0], cB = two ? list[q0 + 1] : cA;
+      const int sA = cA / I, sB = cB / I;
+      const uint16_t* rowA = a.w3 + ((size_t)sl_e[sA] * I + (cA - sA * I)) * 3 * H;
+      const uint16_t* rowB = a.w3 + ((size_t)sl_e[sB] * I + (cB - sB * I)) * 3 * H;
+      uint4 gq[2][NCH], uq[2][NCH], dq[2][NCH];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
+        gq[0][ch] = *reinterpret_cast<const uint4*>(rowA + h);
+        uq[0][ch] = *reinterpret_cast<const uint4*>(rowA + H + h);
+        dq[0][ch] = *reinterpret_cast<const uint4*>(rowA + 2 * H + h);
       }
+      if (two) {  // wave-uniform
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int h = hb + u * 512 + lane * 8;
+        for (int ch = 0; ch < NCH; ++ch) {
+          const int h = min(ch * 512 + lane * 8, H - 8);
+          gq[1][ch] = *reinterpret_cast<const uint4*>(rowB + h);
+          uq[1][ch] = *reinterpret_cast<const uint4*>(rowB + H + h);
+          dq[1][ch] = *reinterpret_cast<const uint4*>(rowB + 2 * H + h);
+        }
+      } else {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) gq[1][ch] = uq[1][ch] = dq[1][ch] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      float gs[2] = {0.f, 0.f}, vs[2] = {0.f, 0.f};
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int h = ch * 512 + lane * 8;
         if (h < H) {
-          const float4 x0 = *reinterpret_cast<const float4*>(xs + h);
-          const float4 x1 = *reinterpret_cast<const float4*>(xs + h + 4);
-          gsum = fmaf(__uint_as_float(gq[u].x << 16), x0.x, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].x & 0xFFFF0000u), x0.y, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].y << 16), x0.z, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].y & 0xFFFF0000u), x0.w, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].z << 16), x1.x, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].z & 0xFFFF0000u), x1.y, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].w << 16), x1.z, gsum);
-          gsum = fmaf(__uint_as_float(gq[u].w & 0xFFFF0000u), x1.w, gsum);
-          vsum = fmaf(__uint_as_float(vq[u].x << 16), x0.x, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].x & 0xFFFF0000u), x0.y, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].y << 16), x0.z, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].y & 0xFFFF0000u), x0.w, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].z << 16), x1.x, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].z & 0xFFFF0000u), x1.y, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].w << 16), x1.z, vsum);
-          vsum = fmaf(__uint_as_float(vq[u].w & 0xFFFF0000u), x1.w, vsum);
-        }
-      }
-    }
-    gsum = wave_sum(gsum);
-    vsum = wave_sum(vsum);
-    if (lane == 0) {
-      const size_t o = (size_t)t * nc + r0 + q;
-      a.coef[o] = sl_w[sl] * silu(gsum) * vsum;
-      a.rowidx[o] = (int32_t)row;
-      a.kept[o] = cnd;
-    }
-  }
-
-  // ---- decode step (4), first half: z over a range of skipped candidates ----
-  // the first ZW workgroups of the token each take nc/ZW candidates; a
-  // thread handles 8 coefficients (one uint4) of one candidate at a time
-  if (a.rank > 0 && !all && w < a.ZW) {
-    const int R = a.rank, R8 = R / 8;
-    const int zper = (nc + a.ZW - 1) / a.ZW;
-    const int c0 = min(w * zper, nc), c1 = min(c0 + zper, nc);
-    const int cpp = kThreads / R8;  // candidates per pass
-    const int cl = tid / R8, r8 = tid % R8;
-    float zacc[8];
+          const float4 xa = *reinterpret_cast<const float4*>(xs + h);
+          const float4 xb = *reinterpret_cast<const float4*>(xs + h + 4);
+          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-    for (int d = 0; d < 8; ++d) zacc[d] = 0.f;
-    if (cl < cpp)
-      for (int cb = c0 + cl; cb < c1; cb += cpp * 4) {
-        float cf[4];
-        uint4 bq[4];
+          for (int r = 0; r < 2; ++r) {
+            const uint32_t gw4[4] = {gq[r][ch].x, gq[r][ch].y, gq[r][ch].z, gq[r][ch].w};
+            const uint32_t uw4[4] = {uq[r][ch].x, uq[r][ch].y, uq[r][ch].z, uq[r][ch].w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int cnd = cb + u * cpp;
-          const int cc = cnd < c1 ? cnd : c1 - 1;  // clamped: loads always issued
-          const int sl = cc / I, j = cc % I;
-          const float pv = a.pact[(size_t)t * nc + cc];
-          bq[u] = reinterpret_cast<const uint4*>(a.bmat + ((size_t)sl_e[sl] * I + j) * R)[r8];
-          cf[u] = (cnd < c1 && !flags[cc]) ? sl_w[sl] * pv : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t bw[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            zacc[2 * d] = fmaf(cf[u], f16f((uint16_t)(bw[d] & 0xFFFFu)), zacc[2 * d]);
-            zacc[2 * d + 1] = fmaf(cf[u], f16f((uint16_t)(bw[d] >> 16)), zacc[2 * d + 1]);
+            for (int p = 0; p < 4; ++p) {
+              gs[r] = fmaf(bf_lo(gw4[p]), xv[2 * p], gs[r]);
+              gs[r] = fmaf(bf_hi(gw4[p]), xv[2 * p + 1], gs[r]);
+              vs[r] = fmaf(bf_lo(uw4[p]), xv[2 * p], vs[r]);
+              vs[r] = fmaf(bf_hi(uw4[p]), xv[2 * p + 1], vs[r]);
+            }
           }
         }
       }
-    // reduce over candidates: lanes with equal r8 inside a wave, then waves
-    for (int q = 0; q < R * 4; q += kThreads)
-      if (q + tid < R * 4) zred[q + tid] = 0.f;
-    __syncthreads();
-    // lanes 0..R8-1 of each wave end with its sums when R8 is a power of two;
-    // otherwise fall back to shared-memory atomics
-    const bool pow2 = (R8 & (R8 - 1)) == 0;
-    if (pow2) {
+      const float cfA = sl_w[sA] * silu(wave_sum(gs[0])) * wave_sum(vs[0]);
+      const float cfB = two ? sl_w[sB] * silu(wave_sum(gs[1])) * wave_sum(vs[1]) : 0.f;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {  // butterfly over lanes of equal r8
-        float v = zacc[d];
-        if (R8 <= 1) v += xor_lane_f<1>(v);
-        if (R8 <= 2) v += xor_lane_f<2>(v);
-        if (R8 <= 4) v += xor_lane_f<4>(v);
-        if (R8 <= 8) v += xor_lane_f<8>(v);
-        v += xor_lane_f<16>(v);
-        v += xor_lane_f<32>(v);
-        zacc[d] = v;
+      for (int ch = 0; ch < NCH; ++ch) {
+        const uint32_t d0[4] = {dq[0][ch].x, dq[0][ch].y, dq[0][ch].z, dq[0][ch].w};
+        const uint32_t d1[4] = {dq[1][ch].x, dq[1][ch].y, dq[1][ch].z, dq[1][ch].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          yv[ch][2 * p] = fmaf(cfA, bf_lo(d0[p]), yv[ch][2 * p]);
+          yv[ch][2 * p + 1] = fmaf(cfA, bf_hi(d0[p]), yv[ch][2 * p + 1]);
+          yv[ch][2 * p] = fmaf(cfB, bf_lo(d1[p]), yv[ch][2 * p]);
+          yv[ch][2 * p + 1] = fmaf(cfB, bf_hi(d1[p]), yv[ch][2 * p + 1]);
+        }
       }
-      if (lane < R8 && cl < cpp)
+    }
+    // ---- partial output: only waves that took channels contribute ----
+    // waves [0, NW/2) store their rows into NW/2 slots, the others add theirs
+    constexpr int SL = NW / 2;
+    const int used = min(NW, (nmine + a.cpw - 1) / a.cpw);  // waves holding channels
+    const int slot = wave % SL;
+    if (wave < SL) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) zred[wave * R + r8 * 8 + d] = zacc[d];
-    } else if (cl < cpp) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) atomicAdd(&zred[r8 * 8 + d], zacc[d]);
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int h = ch * 512 + lane * 8;
+        if (h < H) {
+          float* o = yred + (size_t)slot * H + h;
+          *reinterpret_cast<float4*>(o) = make_float4(yv[ch][0], yv[ch][1], yv[ch][2], yv[ch][3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(yv[ch][4], yv[ch][5], yv[ch][6], yv[ch][7]);
+        }
+      }
     }
     __syncthreads();
-    if (tid < R)
-      a.zpart[((size_t)t * a.ZW + w) * R + tid] =
-          pow2 ? zred[tid] + zred[R + tid] + zred[2 * R + tid] + zred[3 * R + tid] : zred[tid];
+    if (wave >= SL && wave < used) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int h = ch * 512 + lane * 8;
+        if (h < H) {
+          float* o = yred + (size_t)slot * H + h;
+          float4 p0 = *reinterpret_cast<float4*>(o);
+          float4 p1 = *reinterpret_cast<float4*>(o + 4);
+          p0.x += yv[ch][0];
+          p0.y += yv[ch][1];
+          p0.z += yv[ch][2];
+          p0.w += yv[ch][3];
+          p1.x += yv[ch][4];
+          p1.y += yv[ch][5];
+          p1.z += yv[ch][6];
+          p1.w += yv[ch][7];
+          *reinterpret_cast<float4*>(o) = p0;
+          *reinterpret_cast<float4*>(o + 4) = p1;
+        }
+      }
+    }
+    __syncthreads();
+    const int nsl = min(SL, max(used, 1));  // slots that received rows
+    float* yp = a.ypart + ((size_t)t * a.G + w) * H;
+    for (int h = tid * 4; h < H; h += NT * 4) {
+      float4 v = *reinterpret_cast<const float4*>(yred + h);
+      for (int q = 1; q < nsl; ++q) {
+        const float4 u = *reinterpret_cast<const float4*>(yred + (size_t)q * H + h);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+      *reinterpret_cast<float4*>(yp + h) = v;
+    }
+    return;
+  }
+
+  // ---- decode step (4), first half: z over this workgroup's candidate range ----
+  // R8 threads per candidate, each 8 coefficients (one uint4) of b_j
+  const int zr = w - a.G;
+  const int R = a.rank, R8 = R / 8;
+  const int zper = (nc + a.Z - 1) / a.Z;
+  const int cb0 = min(zr * zper, nc), cb1 = min(cb0 + zper, nc);
+  const int cpp = NT / R8;  // candidates per pass
+  const int cl = tid / R8, r8 = tid - cl * R8;
+  float zacc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) zacc[d] = 0.f;
+  if (cl < cpp) {
+    for (int cb = cb0 + cl; cb < cb1; cb += cpp * 4) {
+      uint4 bq[4];
+      float cf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cnd = cb + u * cpp;
+        const int cc = cnd < cb1 ? cnd : cb1 - 1;  // clamped: loads always issued
+        const int s = cc / I, j = cc - s * I;
+        bq[u] = reinterpret_cast<const uint4*>(a.bmat + ((size_t)sl_e[s] * I + j) * R)[r8];
+        cf[u] = (cnd < cb1 && !flags[cc]) ? sl_w[s] * pvl[cc] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t bw[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          zacc[2 * d] = fmaf(cf[u], lo16(bw[d]), zacc[2 * d]);
+          zacc[2 * d + 1] = fmaf(cf[u], hi16(bw[d]), zacc[2 * d + 1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) zred[(size_t)tid * 8 + d] = cl < cpp ? zacc[d] : 0.f;
+  __syncthreads();
+  if (tid < R) {
+    const int rr8 = tid / 8, d = tid % 8;
+    float z = 0.f;
+    for (int q = rr8; q < cpp * R8; q += R8) z += zred[(size_t)q * 8 + d];
+    a.zpart[((size_t)t * a.Z + zr) * R + tid] = z;
   }
 }
 
 // ===========================================================================
-// C: y = sum over kept of (w a_j) d_j + U z, per hidden slice
+// 3: y = sum of the partial outputs + U z; clear the screen accumulators
 // ===========================================================================
-struct DownArgs {
-  const uint16_t* w3;
-  const uint16_t* U;
-  const int32_t* rowidx;
-  const float* coef;
+struct ReduceArgs {
+  const float* ypart;
   const float* zpart;
+  const uint16_t* U;
   float* y;
-  int H, ncand, k, rank, nz, nhs, items, per_xcd;
+  unsigned long long* acc;
+  int H, G, Z, rank, ncp, nslices, clear;
 };
 
-template <int HS>
-__global__ __launch_bounds__(kThreads) void k_down_recover(DownArgs a) {
-  __shared__ float zl[16 * 64];
+constexpr int kReduceThreads = 256;
+constexpr int kReduceParts = kReduceThreads / kReduceSlice;  // 8
+constexpr int kReducePer = kMaxGatherWgs / kReduceParts;     // partial rows per thread, at most
+
+__global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
+  __shared__ float part[kReduceParts][kReduceSlice];
   __shared__ float zs[64];
-  __shared__ float part[4][HS];
-  const int item = xcd_item(blockIdx.x, a.per_xcd);
-  if (item >= a.items) return;
-  const int t = item / a.nhs, hs = item % a.nhs;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, h0 = hs * HS;
-  // this slice's rows of U, needed last, loaded first (thread tid < HS owns hidden h0 + tid)
+  const int t = blockIdx.x / a.nslices, sl = blockIdx.x - t * a.nslices;
+  const int tid = threadIdx.x;
+  const int H = a.H, h0 = sl * kReduceSlice;
+  const int hl = tid % kReduceSlice, pt = tid / kReduceSlice;
+  // U rows of this slice, the recovery partials and the output partials:
+  // all issued before any is summed
   uint4 uq[8];
-  if (a.nz > 0) {
-    const uint4* up = reinterpret_cast<const uint4*>(a.U + (size_t)(h0 + (tid < HS ? tid : 0)) * a.rank);
+  const bool rec = a.Z > 0;
+  if (rec && tid < kReduceSlice) {
+    const uint4* up = reinterpret_cast<const uint4*>(a.U + (size_t)(h0 + tid) * a.rank);
 #pragma unroll
     for (int r8 = 0; r8 < 8; ++r8) uq[r8] = up[r8 * 8 < a.rank ? r8 : 0];
   }
-  const int nzv = a.nz * a.rank;  // at most 16 * 64 partial values
-  {
-    float zv[4];
+  float zv[kMaxRecoverWgs];
+  if (rec && tid < a.rank) {
+    const float* zp = a.zpart + (size_t)t * a.Z * a.rank + tid;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + u * kThreads;
-      zv[u] = nzv > 0 ? a.zpart[(size_t)t * nzv + (q < nzv ? q : nzv - 1)] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + u * kThreads;
-      if (q < nzv) zl[q] = zv[u];
-    }
+    for (int q = 0; q < kMaxRecoverWgs; ++q) zv[q] = zp[(size_t)(q < a.Z ? q : 0) * a.rank];
   }
-  constexpr int RB = HS >= 64 ? 1 : 64 / HS;  // kept rows in flight per thread
-  float acc[HS];
+  const float* yp = a.ypart + (size_t)t * a.G * H + h0 + hl;
+  float pv[kReducePer];
 #pragma unroll
-  for (int q = 0; q < HS; ++q) acc[q] = 0.f;
-  const int32_t* ri = a.rowidx + (size_t)t * a.ncand;
-  const float* cfp = a.coef + (size_t)t * a.ncand;
-  for (int rb = tid; rb < a.k; rb += kThreads * RB) {
-    int rows[RB];
-    float cf[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {  // clamped: every load is issued; extra ranks get weight 0
-      const int r = rb + u * kThreads;
-      const int rc = r < a.k ? r : a.k - 1;
-      rows[u] = ri[rc];
-      cf[u] = cfp[rc];
-      cf[u] = r < a.k ? cf[u] : 0.f;
-    }
-    uint4 dv[RB][HS / 8];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const uint16_t* d = a.w3 + ((size_t)rows[u] * 3 + 2) * H + h0;
-#pragma unroll
-      for (int q = 0; q < HS / 8; ++q) dv[u][q] = *reinterpret_cast<const uint4*>(d + 8 * q);
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u)
-#pragma unroll
-      for (int q = 0; q < HS / 8; ++q) {
-        const uint32_t dw[4] = {dv[u][q].x, dv[u][q].y, dv[u][q].z, dv[u][q].w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          acc[8 * q + 2 * p] = fmaf(cf[u], __uint_as_float(dw[p] << 16), acc[8 * q + 2 * p]);
-          acc[8 * q + 2 * p + 1] = fmaf(cf[u], __uint_as_float(dw[p] & 0xFFFF0000u), acc[8 * q + 2 * p + 1]);
-        }
-      }
+  for (int u = 0; u < kReducePer; ++u) {
+    const int wq = pt + u * kReduceParts;
+    pv[u] = yp[(size_t)(wq < a.G ? wq : 0) * H];
   }
+  float v = 0.f;
 #pragma unroll
-  for (int q = 0; q < HS; ++q) acc[q] = wave_sum(acc[q]);
-  if (lane == 0)
-#pragma unroll
-    for (int q = 0; q < HS; ++q) part[wave][q] = acc[q];
-  __syncthreads();
+  for (int u = 0; u < kReducePer; ++u) v += pt + u * kReduceParts < a.G ? pv[u] : 0.f;
+  part[pt][hl] = v;
   if (tid < 64) {
     float z = 0.f;
-    if (tid < a.rank)
-      for (int q = 0; q < a.nz; ++q) z += zl[q * a.rank + tid];
+    if (rec && tid < a.rank)
+#pragma unroll
+      for (int q = 0; q < kMaxRecoverWgs; ++q) z += q < a.Z ? zv[q] : 0.f;
     zs[tid] = z;
   }
   __syncthreads();
-  if (tid < HS) {
-    const int h = h0 + tid;
-    float v = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
-    if (a.nz > 0) {
+  if (tid < kReduceSlice) {
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < kReduceParts; ++q) o += part[q][tid];
+    if (rec) {
 #pragma unroll
       for (int r8 = 0; r8 < 8; ++r8)
         if (r8 * 8 < a.rank) {
           const uint32_t uw[4] = {uq[r8].x, uq[r8].y, uq[r8].z, uq[r8].w};
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            v = fmaf(f16f((uint16_t)(uw[d] & 0xFFFFu)), zs[r8 * 8 + 2 * d], v);
-            v = fmaf(f16f((uint16_t)(uw[d] >> 16)), zs[r8 * 8 + 2 * d + 1], v);
+            o = fmaf(lo16(uw[d]), zs[r8 * 8 + 2 * d], o);
+            o = fmaf(hi16(uw[d]), zs[r8 * 8 + 2 * d + 1], o);
           }
         }
     }
-    a.y[(size_t)t * H + h] = v;
+    a.y[(size_t)t * H + h0 + tid] = o;
+  }
+  if (a.clear) {
+    // the screen accumulators of this token (gate then up, ncp each), split
+    // over its slices
+    const int n = 2 * a.ncp;
+    const int per = (n + a.nslices - 1) / a.nslices;
+    const int b0 = sl * per, b1 = min(b0 + per, n);
+    ulonglong2* ap = reinterpret_cast<ulonglong2*>(a.acc + (size_t)t * n);
+    for (int q = b0 / 2 + tid; q < b1 / 2; q += kReduceThreads) ap[q] = make_ulonglong2(0ull, 0ull);
   }
 }
 
@@ -889,144 +874,138 @@ static int hip_fail(hipError_t e, const char* what) {
   return fail(CFR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-Plan make_plan(const cfr_config& c, int batch, int k) {
+Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
   Plan p;
   const int nblk = c.hidden / kBlock, nbytes = (c.inter + 4) / 5, nc = c.top * c.inter;
-  // A: about 32 slices per routed expert, i.e. one workgroup per CU at batch 1
-  p.S = (nbytes + 31) / 32;
-  if (p.S < 1) p.S = 1;
-  if (p.S > kMaxS) p.S = kMaxS;
-  p.n_slices = (nbytes + p.S - 1) / p.S;
-  p.itemsA = batch * c.top * p.n_slices;
-  p.per_xcdA = (p.itemsA + 7) / 8;
-  p.ntA = 1024;
-  p.ldsA = ScreenLds(nblk, c.n_screen, p.S, 1024).total;
-  if (p.S > kMaxS1024 || p.ldsA > kMaxLds) {
-    p.ntA = 512;
-    p.ldsA = ScreenLds(nblk, c.n_screen, p.S, 512).total;
-  }
-  // B: workgroups per token; about one kept channel per wave at batch 1
-  int g = 256 / batch;
-  if (g < 4) g = 4;
-  const int per4 = ((k > 0 ? k : 1) + 3) / 4;
-  if (g > per4) g = per4 < 4 ? 4 : per4;
-  p.G = g;
-  p.share_max = (k + g - 1) / g;
-  p.ZW = g < 16 ? g : 16;
-  p.ldsB = SelectLds(c.hidden, nc, p.share_max, c.rank).total;
-  // C: hidden slices per token (8..64 hidden units each)
-  int hsl = 8;
-  while ((long)batch * (c.hidden / hsl) > 512 && hsl < 64) hsl *= 2;
-  p.HS = hsl;
-  p.nhs = c.hidden / hsl;
-  p.itemsC = batch * p.nhs;
-  p.per_xcdC = (p.itemsC + 7) / 8;
+  // screen
+  p.nd = (nbytes + 3) / 4;
+  p.ng = kScreenThreads / p.nd;
+  if (p.ng < 1) p.ng = 1;
+  p.items1 = batch * c.top * nblk * 2;
+  p.per_xcd1 = (p.items1 + 7) / 8;
+  p.lds1 = (size_t)p.ng * p.nd * 20 * 4;
+  // select/gather: about 240 gather workgroups over the batch plus 16
+  // recovery workgroups, so the whole grid fits one workgroup per CU
+  const SelectGeom g = select_geom(nc);
+  p.nt2 = g.nt;
+  p.per = g.per;
+  p.ncp = g.nt * g.per;
+  const int NW = p.nt2 / 64;
+  const int kk = dense ? nc : k;
+  int gmax = (kMaxGatherWgs - kMaxRecoverWgs) / batch;
+  if (gmax < 1) gmax = 1;
+  p.chan = (kk + gmax - 1) / gmax;
+  if (p.chan < 1) p.chan = 1;
+  p.cpw = (p.chan + NW - 1) / NW;
+  p.G = (kk + p.chan - 1) / p.chan;
+  if (p.G < 1) p.G = 1;
+  int z = kMaxRecoverWgs / batch;
+  if (z < 1) z = 1;
+  p.Z = (!dense && c.rank > 0 && k < nc) ? z : 0;
+  if (p.Z > nc) p.Z = nc;
+  p.nch = 1;
+  while (p.nch * 512 < c.hidden) p.nch *= 2;
+  p.lds2 = GatherLds(c.hidden, p.ncp, p.nt2, p.chan).total;
+  // reduce
+  p.nslices = c.hidden / kReduceSlice;
   return p;
 }
 
 size_t max_lds_needed(const cfr_config& c) {
   size_t m = 0;
-  for (int b = 1; b <= c.max_batch; ++b) {
-    const Plan p = make_plan(c, b, c.top * c.inter);
-    if (p.ldsA > m) m = p.ldsA;
-    if (p.ldsB > m) m = p.ldsB;
-  }
+  const int nc = c.top * c.inter;
+  for (int b = 1; b <= c.max_batch; ++b)
+    for (int kk : {0, 1, nc / 2, nc}) {
+      const Plan p = make_plan(c, b, kk, false);
+      if (p.lds1 + 8192 > m) m = p.lds1 + 8192;  // + the screen kernel's static LDS
+      if (p.lds2 > m) m = p.lds2;
+    }
+  const Plan d = make_plan(c, 1, nc, true);
+  if (d.lds2 > m) m = d.lds2;
   return m;
 }
 
-size_t zpart_rows(const cfr_config& c) { return (size_t)c.max_batch * 16; }
+// Lets a kernel take dynamic LDS up to the workgroup limit minus its static
+// LDS.  A failure here would surface as the launch error, so it is cleared.
+template <typename K>
+static void allow_lds(K kernel) {
+  hipFuncAttributes fa{};
+  size_t stat = 0;
+  if (hipFuncGetAttributes(&fa, (const void*)kernel) == hipSuccess) stat = fa.sharedSizeBytes;
+  (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(kMaxLds - stat));
+  (void)hipGetLastError();
+}
 
-template <int S, int NT>
-static hipError_t launch_A_nt(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+template <int NT, int PER, int NCH>
+static hipError_t launch_select_t(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_screen_score<S, NT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    allow_lds(k_select<NT, PER, NCH>);
     attr = true;
   }
-  k_screen_score<S, NT><<<8 * p.per_xcdA, NT, p.ldsA, st>>>(a);
+  k_select<NT, PER, NCH><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
   return hipGetLastError();
 }
 
-template <int S>
-static hipError_t launch_A(const ScreenArgs& a, const Plan& p, hipStream_t st) {
-  if constexpr (S <= kMaxS1024) {
-    if (p.ntA == 1024) return launch_A_nt<S, 1024>(a, p, st);
-  }
-  return launch_A_nt<S, 512>(a, p, st);
-}
-
-template <int HS>
-static hipError_t launch_C(const DownArgs& a, const Plan& p, hipStream_t st) {
-  k_down_recover<HS><<<8 * p.per_xcdC, kThreads, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-static hipError_t launch_C_any(const DownArgs& a, const Plan& p, hipStream_t st) {
-  switch (p.HS) {
-    case 8: return launch_C<8>(a, p, st);
-    case 16: return launch_C<16>(a, p, st);
-    case 32: return launch_C<32>(a, p, st);
-    default: return launch_C<64>(a, p, st);
+template <int NT, int PER>
+static hipError_t launch_select_n(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+  switch (p.nch) {
+    case 1: return launch_select_t<NT, PER, 1>(a, p, batch, st);
+    case 2: return launch_select_t<NT, PER, 2>(a, p, batch, st);
+    case 4: return launch_select_t<NT, PER, 4>(a, p, batch, st);
+    default: return launch_select_t<NT, PER, 8>(a, p, batch, st);
   }
 }
 
-template <int KPT>
-static hipError_t launch_B_k(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+  switch (p.per) {  // select_geom: 512 threads, 4..32 candidates each
+    case 4: return launch_select_n<512, 4>(a, p, batch, st);
+    case 8: return launch_select_n<512, 8>(a, p, batch, st);
+    case 12: return launch_select_n<512, 12>(a, p, batch, st);
+    case 16: return launch_select_n<512, 16>(a, p, batch, st);
+    case 24: return launch_select_n<512, 24>(a, p, batch, st);
+    default: return launch_select_n<512, 32>(a, p, batch, st);
+  }
+}
+
+static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_select_exact<KPT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    allow_lds(k_screen<kScreenThreads>);
     attr = true;
   }
-  k_select_exact<KPT><<<batch * p.G, kThreads, p.ldsB, st>>>(a);
+  k_screen<kScreenThreads><<<8 * p.per_xcd1, kScreenThreads, p.lds1, st>>>(a);
   return hipGetLastError();
 }
 
-static hipError_t launch_B(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  const int per = a.dense ? 1 : (a.ncand + kThreads - 1) / kThreads;
-  if (per <= 1) return launch_B_k<1>(a, p, batch, st);
-  if (per <= 4) return launch_B_k<4>(a, p, batch, st);
-  if (per <= 16) return launch_B_k<16>(a, p, batch, st);
-  if (per <= 32) return launch_B_k<32>(a, p, batch, st);
-  return launch_B_k<64>(a, p, batch, st);
+static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) {
+  k_reduce<<<batch * a.nslices, kReduceThreads, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev) {
   const cfr_config& c = r->cfg;
-  const Plan p = make_plan(c, batch, k);
+  const Plan p = make_plan(c, batch, k, false);
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], st);
   };
-  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->xrot, r->sel, r->ghat,
-               r->vhat, r->pact, r->score, r->status, c.hidden, c.n_experts, c.inter, c.top,
-               r->nblk, c.n_screen, r->lp, r->unit, p.n_slices, p.itemsA, p.per_xcdA,
-               dbg != nullptr};
-  hipError_t e = hipSuccess;
+  hipError_t e;
   mark(0);
-  switch (p.S) {
-#define CFR_CASE(v) \
-  case v:           \
-    e = launch_A<v>(A, p, st); \
-    break;
-    CFR_CASE(1) CFR_CASE(2) CFR_CASE(3) CFR_CASE(4) CFR_CASE(5) CFR_CASE(6) CFR_CASE(7)
-    CFR_CASE(8) CFR_CASE(9) CFR_CASE(10) CFR_CASE(11) CFR_CASE(12) CFR_CASE(13)
-#undef CFR_CASE
-    default:
-      return fail(CFR_EUNSUPPORTED, "screen slice width");
-  }
-  if (e != hipSuccess) return hip_fail(e, "screen launch");
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->acc, r->wn, r->xrot,
+               r->sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
+               c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr};
+  if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
-  SelectArgs B{x, ids, gw, r->w3, r->b, r->score, r->pact, r->kept, r->rowidx, r->coef,
-               r->zpart, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand, k,
-               c.rank, p.G, p.share_max, p.ZW, 0};
-  if ((e = launch_B(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
+  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, r->ghat, r->vhat,
+               r->score, r->kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
+               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr};
+  if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
-  const int nz = (c.rank > 0 && k < r->ncand) ? p.ZW : 0;
-  DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, r->ncand, k,
-             c.rank, nz, p.nhs, p.itemsC, p.per_xcdC};
-  if ((e = launch_C_any(C, p, st)) != hipSuccess) return hip_fail(e, "down launch");
+  ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
+               p.nslices, 1};
+  if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
   mark(3);
   if (dbg) {
     const int H = c.hidden, nblk = r->nblk, nsc = batch * r->ncand;
@@ -1052,19 +1031,15 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
                  float* y, hipStream_t st) {
   const cfr_config& c = r->cfg;
   const int nc = r->ncand;
-  Plan p = make_plan(c, batch, nc);
-  // the dense block keeps every candidate: one wave per channel
-  p.G = (nc + 3) / 4;
-  p.share_max = 4;
-  p.ldsB = SelectLds(c.hidden, nc, p.share_max, 0).total;
-  SelectArgs B{x, ids, gw, r->w3, r->b, r->score, r->pact, r->kept, r->rowidx, r->coef,
-               r->zpart, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, nc, 0, p.G,
-               p.share_max, 0, 1};
+  const Plan p = make_plan(c, batch, nc, true);
+  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, nullptr, nullptr,
+               nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
+               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0};
   hipError_t e;
-  if ((e = launch_B(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
-  DownArgs C{r->w3, r->u, r->rowidx, r->coef, r->zpart, y, c.hidden, nc, nc, 0, 0,
-             p.nhs, p.itemsC, p.per_xcdC};
-  if ((e = launch_C_any(C, p, st)) != hipSuccess) return hip_fail(e, "dense down launch");
+  if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
+  ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, 0, c.rank, r->ncp,
+               p.nslices, 0};
+  if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "dense reduce launch");
   return CFR_OK;
 }
 

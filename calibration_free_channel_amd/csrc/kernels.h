@@ -8,62 +8,89 @@
 namespace cfr {
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kScreenThreads = 512;     // screen workgroup size
+constexpr int kMaxGatherWgs = 256;      // gather workgroups per call, summed over the batch
+constexpr int kMaxRecoverWgs = 16;      // recovery workgroups per token
+constexpr int kReduceSlice = 32;        // hidden units per reduce workgroup
 
 __host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 16; }
 
-// LDS layout of the screen kernel (bytes); host and device share it.
-struct ScreenLds {
-  size_t lut, sl, rec, sc, red, total;
-  __host__ __device__ ScreenLds(int nblk, int n_screen, int S, int nthreads) {
-    size_t o = 0;
-    lut = o;  // 256 entries of five fp16 codes
-    o += 256 * 16;
-    sl = o;
-    o += lds_align((size_t)nblk * n_screen);
-    rec = o;
-    o += lds_align((size_t)nblk * n_screen * 8);
-    sc = o;
-    o += lds_align((size_t)nblk * 2 * 5 * S * 4);
-    red = o;
-    o += lds_align((size_t)nthreads * 5 * S * 4);
-    total = o;
-  }
+// Thread geometry of the select/gather kernel for nc candidates per token:
+// nt threads, each owning `per` consecutive candidates (a multiple of 4, so
+// its screen sums load as 16-byte vectors).  Per-token candidate arrays are
+// padded to nt * per entries; the padding is never written and stays zero.
+struct SelectGeom {
+  int nt, per;
 };
+__host__ __device__ inline SelectGeom select_geom(int nc) {
+  const int nt = 512;
+  int per = (nc + nt - 1) / nt;
+  per = (per + 3) / 4 * 4;
+  if (per < 4) per = 4;
+  if (per > 16 && per <= 24) per = 24;
+  if (per > 24) per = 32;
+  return {nt, per};
+}
 
-// LDS layout of the select/exact kernel (bytes).
-struct SelectLds {
-  size_t xs, keys, flags, list, zred, hist, misc, total;
-  __host__ __device__ SelectLds(int H, int ncand, int share_max, int rank) {
+// LDS layout of the select/gather kernel (bytes); host and device share it.
+//   xs     fp32 [H]          the token (gather workgroups)
+//   pv     fp32 [ncp]        p of every candidate (recovery workgroups)
+//   flags  u8 [ncp]          kept flag of every candidate (recovery workgroups)
+//   yred   fp32 [NT/128][H]  per-wave partial outputs (gather workgroups)
+//   hist   int [2048]        radix histogram
+//   list   int [chan]        this workgroup's kept candidates, by rank
+//   misc   int [64]          scan scratch and broadcast values
+//   bkey, bidx [64]          the boundary bin, when ranked directly
+//   slot   int [16] + fp32 [16]  routed expert and weight per slot
+//   zred   fp32 [NT][8]      recovery partial sums
+struct GatherLds {
+  size_t xs, pv, flags, yred, hist, list, misc, bkey, bidx, slot_e, slot_w, zred, total;
+  __host__ __device__ GatherLds(int H, int ncp, int nt, int chan) {
     size_t o = 0;
     xs = o;
     o += lds_align((size_t)H * 4);
-    const size_t npad = (size_t)256 * ((ncand + 255) / 256);  // whole chunks of 256 threads
-    keys = o;
-    o += lds_align(npad * 4);
-    flags = o;
-    o += lds_align(npad);
-    list = o;
-    o += lds_align((size_t)(share_max > 0 ? share_max : 1) * 4);
-    zred = o;
-    o += lds_align((size_t)4 * (rank > 0 ? rank : 1) * 4);
+    // pv/flags (recovery workgroups) and yred (gather workgroups) share space
+    const size_t rec = lds_align((size_t)ncp * 4) + lds_align((size_t)ncp);
+    const size_t red = (size_t)(nt / 128) * H * 4;
+    pv = o;
+    flags = o + lds_align((size_t)ncp * 4);
+    yred = o;
+    o += rec > red ? rec : red;
     hist = o;
-    o += (4096 + 2048) * 4;
+    o += 2048 * 4;
+    list = o;
+    o += lds_align((size_t)(chan > 0 ? chan : 1) * 4);
     misc = o;
-    o += lds_align(192 * 4);
+    o += 64 * 4;
+    bkey = o;
+    o += 64 * 4;
+    bidx = o;
+    o += 64 * 4;
+    slot_e = o;
+    o += 16 * 4;
+    slot_w = o;
+    o += 16 * 4;
+    zred = o;
+    o += (size_t)nt * 8 * 4;
     total = o;
   }
 };
 
 // Launch geometry of one decode call.
 struct Plan {
-  int S = 1, n_slices = 1, itemsA = 0, per_xcdA = 0, ntA = 512;  // screen
-  int G = 4, share_max = 0, ZW = 4;                          // select/exact
-  int HS = 8, nhs = 0, itemsC = 0, per_xcdC = 0;             // down/recover
-  size_t ldsA = 0, ldsB = 0;
+  // screen: one workgroup per (token, routed slot, block, half)
+  int items1 = 0, per_xcd1 = 0;
+  int nd = 0;  // 32-bit code words per half-unit that hold codes
+  int ng = 0;  // screened-coordinate groups per workgroup
+  size_t lds1 = 0;
+  // select/gather
+  int nt2 = 512, per = 4, ncp = 0, nch = 1, cpw = 1, chan = 1, G = 1, Z = 0;
+  size_t lds2 = 0;
+  // reduce
+  int nslices = 0;
 };
-Plan make_plan(const cfr_config& c, int batch, int k);
+Plan make_plan(const cfr_config& c, int batch, int k, bool dense);
 size_t max_lds_needed(const cfr_config& c);  // over every batch and k the config allows
-size_t zpart_rows(const cfr_config& c);      // rows of the recovery partial buffer
 
 // Intermediates copied out by the debug entry point (any may be null).
 struct DebugOut {

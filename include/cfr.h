@@ -51,7 +51,7 @@ typedef struct cfr_reader cfr_reader; /* opaque; owned by the library */
 
 /* Layer shape and method constants, fixed at build time. */
 typedef struct cfr_config {
-  int32_t hidden;     /* H: model width, a multiple of 128, at most 16384             */
+  int32_t hidden;     /* H: model width, a multiple of 128, at most 4096              */
   int32_t n_experts;  /* E: experts in the layer                                        */
   int32_t inter;      /* I: channels per expert (expert intermediate size), 1..4096     */
   int32_t top;        /* routed experts per token, 1..16 and <= E                       */
