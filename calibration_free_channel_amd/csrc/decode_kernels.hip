@@ -37,6 +37,14 @@
 
 #include "kernels.h"
 
+// Optional device-side phase trace: a build that defines CFR_TRACE_PHASE(k, i)
+// records a timestamp at each numbered phase of each kernel.  Empty otherwise.
+#ifndef CFR_TRACE_PHASE
+#define CFR_TRACE_PHASE(kernel, phase) \
+  do {                                  \
+  } while (0)
+#endif
+
 namespace cfr {
 
 namespace {
@@ -140,17 +148,33 @@ __device__ __forceinline__ int wave_scan(int v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load of the wave; these kernels exchange data
+// through LDS alone, so loads issued early stay in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum over the NT threads of a workgroup.  sh: NT/64 ints
 // that nobody else uses between the two barriers inside.
 template <int NT>
 __device__ __forceinline__ int block_scan(int v, int* sh) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "whole groups of four waves");
+  constexpr int NQ = NT / 256;  // int4 groups of wave totals
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_scan(v);
   if (lane == 63) sh[w] = v;
-  __syncthreads();
+  lds_barrier();
   int add = 0;
-  for (int q = 0; q < w; ++q) add += sh[q];
-  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int4 p = reinterpret_cast<const int4*>(sh)[q];
+    add += (4 * q < w ? p.x : 0) + (4 * q + 1 < w ? p.y : 0) + (4 * q + 2 < w ? p.z : 0) +
+           (4 * q + 3 < w ? p.w : 0);
+  }
+  lds_barrier();
   return v + add;
 }
 
@@ -181,16 +205,16 @@ struct ScreenArgs {
   int H, E, I, top, ncp, nblk, ns, lp, unit, nd, ng, items, per_xcd, dbg;
 };
 
-// Wave 0 rotates and ranks one 128-block held as two values per lane (lane l
-// holds coordinates l and l + 64).  The float32 butterfly runs the stages
-// h = 1 .. 32 across lanes and h = 64 inside the lane, in that order, with
-// the lower element of each pair taking a + b and the upper a - b.  The
-// n_screen largest |v| (ties to the lower index) are found by a bit-by-bit
-// search of the n_screen-th largest magnitude over wave ballots, then
-// compacted in ascending coordinate order into sl (coordinate) and rec
-// (byte offset of its unit, value bits).
-__device__ __forceinline__ void rotate_select(float v0, float v1, int NS, uint8_t* sl, int2* rec,
-                                              int unit, float* xrot_out) {
+// Wave 0 rotates one 128-block held as two values per lane (lane l holds
+// coordinates l and l + 64) and picks the n_screen coordinates of largest
+// magnitude, ties to the lower index.  The float32 butterfly runs the stages
+// h = 1 .. 32 across lanes and h = 64 inside the lane, in that order, with the
+// lower element of each pair taking a + b and the upper a - b.  The n_screen-th
+// largest magnitude T is found bit by bit from wave ballots (all in
+// registers); the kept coordinates are then compacted in ascending order into
+// rec (byte offset of the coordinate's unit, value bits) and, when asked, sel.
+__device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int unit, int2* rec,
+                                              uint8_t* sel_out, float* xrot_out) {
   const int lane = threadIdx.x & 63;
   auto stage = [&](float o0, float o1, int h) {
     if (lane & h) {
@@ -231,19 +255,14 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, uint8_
   const bool s0 = k0 > T || (k0 == T && __popcll(eq0 & lt) < need);
   const bool s1 = k1 > T || (k1 == T && __popcll(eq0) + __popcll(eq1 & lt) < need);
   const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+  const int p0 = __popcll(m0 & lt), p1 = __popcll(m0) + __popcll(m1 & lt);
   if (s0) {
-    const int pos = __popcll(m0 & lt);
-    if (pos < NS) {
-      sl[pos] = (uint8_t)lane;
-      rec[pos] = make_int2(lane * unit, __float_as_int(v0));
-    }
+    rec[p0] = make_int2(lane * unit, __float_as_int(v0));
+    if (sel_out) sel_out[p0] = (uint8_t)lane;
   }
   if (s1) {
-    const int pos = __popcll(m0) + __popcll(m1 & lt);
-    if (pos < NS) {
-      sl[pos] = (uint8_t)(lane + 64);
-      rec[pos] = make_int2((lane + 64) * unit, __float_as_int(v1));
-    }
+    rec[p1] = make_int2((lane + 64) * unit, __float_as_int(v1));
+    if (sel_out) sel_out[p1] = (uint8_t)(lane + 64);
   }
 }
 
@@ -251,8 +270,8 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   __shared__ uint4 lut[256];
   __shared__ int2 rec[128];
-  __shared__ uint8_t sl[128];
   extern __shared__ __align__(16) float red[];  // [ng][nd * 20]
+  CFR_TRACE_PHASE(0, 0);
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
   const int m = item & 1;          // 0 gate, 1 up
@@ -262,10 +281,8 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   const int s = ts % a.top, t = ts / a.top;
   const int tid = threadIdx.x, lane = tid & 63;
   const int H = a.H, I = a.I, NS = a.ns;
-  const int e = clamp_expert(a.ids[ts], a.E, a.status);
-
-  // token block and signs (wave 0), scales of the channels this thread
-  // finalises: all issued before any is used
+  // token block and signs (wave 0) first: the rotation waits on them; then
+  // the routed expert and everything that depends on it
   float x0 = 0.f, x1 = 0.f, g0 = 0.f, g1 = 0.f;
   if (tid < 64) {
     const float* xb = a.x + (size_t)t * H + b * 128;
@@ -274,20 +291,29 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     g0 = a.sigma[b * 128 + lane];
     g1 = a.sigma[b * 128 + 64 + lane];
   }
+  const int e = clamp_expert(a.ids[ts], a.E, a.status);
+  CFR_TRACE_PHASE(0, 5);
+  // scales of the channels this thread finalises (used at the end)
   constexpr int MAXJ = kMaxInter / NT;
   uint16_t al[MAXJ];
   const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
 #pragma unroll
   for (int q = 0; q < MAXJ; ++q) {
     const int j = tid + q * NT;
-    al[q] = j < I ? sp[j] : (uint16_t)0;
+    al[q] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
   }
-  // routing weight times down-column norm of every channel of this slot,
-  // written once per slot for the score
-  if (b == 0 && m == 1) {
-    const float w = a.gw[ts];
-    float* wo = a.wn + (size_t)t * a.ncp + (size_t)s * I;
-    for (int j = tid; j < I; j += NT) wo[j] = w * a.norms[(size_t)e * I + j];
+  // routing weight times down-column norm of every channel of this slot, for
+  // the score: loaded now by one workgroup per slot, stored at the end
+  const bool wn_writer = b == 0 && m == 1;
+  float nw[MAXJ];
+  float wslot = 0.f;
+  if (wn_writer) {
+    wslot = a.gw[ts];
+#pragma unroll
+    for (int q = 0; q < MAXJ; ++q) {
+      const int j = tid + q * NT;
+      nw[q] = a.norms[(size_t)e * I + (j < I ? j : I - 1)];
+    }
   }
   // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
   // 243..255 never occur in a packed unit and decode to zero)
@@ -307,11 +333,12 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   // decode step (1): rotation and the partial-screen coordinates
   const bool writer = a.dbg && s == 0 && m == 0;
   if (tid < 64)
-    rotate_select(x0 * g0, x1 * g1, NS, sl, rec, a.unit,
+    rotate_select(x0 * g0, x1 * g1, NS, a.unit, rec,
+                  writer ? a.sel + ((size_t)t * a.nblk + b) * NS : nullptr,
                   writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
-  __syncthreads();
-  if (writer)
-    for (int q = tid; q < NS; q += NT) a.sel[((size_t)t * a.nblk + b) * NS + q] = sl[q];
+  CFR_TRACE_PHASE(0, 6);
+  lds_barrier();
+  CFR_TRACE_PHASE(0, 1);
 
   // screen: thread (g, d) takes code word d (channels 20d .. 20d+19 of the
   // half) at every ng-th screened coordinate starting at g
@@ -321,7 +348,9 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
 #pragma unroll
   for (int q = 0; q < 20; ++q) acc[q] = 0.f;
   if (g < NG) {
-    const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit + m * a.lp + 4 * d;
+    // uniform base of this (expert, block) and 32-bit per-coordinate offsets
+    const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit;
+    const uint32_t col = (uint32_t)(m * a.lp + 4 * d);
     for (int c0 = g; c0 < NS; c0 += NG * kCB) {
       uint32_t wv[kCB];
       float xv[kCB];
@@ -329,7 +358,7 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
       for (int u = 0; u < kCB; ++u) {
         const int c = c0 + u * NG;
         const int2 rc = rec[c < NS ? c : NS - 1];  // clamped; past the list x = 0
-        wv[u] = *reinterpret_cast<const uint32_t*>(ub + rc.x);
+        wv[u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
         xv[u] = c < NS ? __int_as_float(rc.y) : 0.f;
       }
 #pragma unroll
@@ -345,11 +374,13 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
         }
       }
     }
+    CFR_TRACE_PHASE(0, 2);
     float* my = red + (size_t)g * ND * 20 + d * 20;
 #pragma unroll
     for (int q = 0; q < 20; q += 4) *reinterpret_cast<float4*>(my + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
   }
-  __syncthreads();
+  lds_barrier();
+  CFR_TRACE_PHASE(0, 3);
   // channel j = 20 d + i sits at red[g][j]: sum the coordinate groups, scale
   // by alpha_b and add to the fixed-point accumulator
   unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
@@ -369,6 +400,15 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
       atomicAdd(ap + j, to_fix(f16f(al[q]) * S));
     }
   }
+  if (wn_writer) {
+    float* wo = a.wn + (size_t)t * a.ncp + (size_t)s * I;
+#pragma unroll
+    for (int q = 0; q < MAXJ; ++q) {
+      const int j = tid + q * NT;
+      if (j < I) wo[j] = wslot * nw[q];
+    }
+  }
+  CFR_TRACE_PHASE(0, 4);
 }
 
 // ===========================================================================
@@ -400,6 +440,7 @@ template <int NT, int PER, int NCH>
 __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NW = NT / 64;
+  CFR_TRACE_PHASE(1, 0);
   const int wgs = a.G + a.Z;
   const int t = blockIdx.x / wgs, w = blockIdx.x - t * wgs;
   const bool recover = w >= a.G;
@@ -424,21 +465,13 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   const int kk = all ? nc : k;  // kept candidates
   const int c0 = tid * PER;     // this thread's candidates: [c0, c0 + PER)
 
-  // ---- loads: routing, token, screen sums; all issued before use ----
-  if (tid < a.top) {
-    sl_e[tid] = clamp_expert(a.ids[t * a.top + tid], a.E, a.status);
-    sl_w[tid] = a.gw[t * a.top + tid];
-  }
-  if (!recover)
-    for (int h = tid * 4; h < H; h += NT * 4)
-      *reinterpret_cast<float4*>(xs + h) = *reinterpret_cast<const float4*>(a.x + (size_t)t * H + h);
-  if (partial)
-    for (int q = tid; q < 2048; q += NT) hist[q] = 0;
-  uint32_t key[PER];
-  float pr[PER];
+  // ---- loads, all issued up front in straight-line code at clamped
+  // addresses (a guarded load compiles to a branch that waits on it):
+  // screen sums, w ||d||, routing and the token ----
+  static_assert(kMaxHidden <= 2 * NT * 4, "the token is two float4 per thread at most");
+  ulonglong2 gq[PER / 2], vq[PER / 2];
+  float4 wq[PER / 4];
   if (!a.dense) {
-    ulonglong2 gq[PER / 2], vq[PER / 2];
-    float4 wq[PER / 4];
     const ulonglong2* ag = reinterpret_cast<const ulonglong2*>(a.acc + (size_t)t * 2 * a.ncp + c0);
     const ulonglong2* av = reinterpret_cast<const ulonglong2*>(a.acc + ((size_t)t * 2 + 1) * a.ncp + c0);
     const float4* wp = reinterpret_cast<const float4*>(a.wn + (size_t)t * a.ncp + c0);
@@ -449,6 +482,20 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < PER / 4; ++u) wq[u] = wp[u];
+  }
+  const int rslot = tid < a.top ? tid : a.top - 1;
+  const int id_raw = a.ids[t * a.top + rslot];
+  const float gw_raw = a.gw[t * a.top + rslot];
+  // the token, for the gather (written to LDS after the selection)
+  const float* xt = a.x + (size_t)t * H;
+  const int hx0 = tid * 4, hx1 = (tid + NT) * 4;
+  const float4 xr0 = *reinterpret_cast<const float4*>(xt + (hx0 < H ? hx0 : H - 4));
+  const float4 xr1 = *reinterpret_cast<const float4*>(xt + (hx1 < H ? hx1 : H - 4));
+  if (partial)
+    for (int q = tid; q < 2048; q += NT) hist[q] = 0;
+  uint32_t key[PER];
+  float pr[PER];
+  if (!a.dense) {
     const bool dbg = a.dbg && w == 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -468,8 +515,13 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       }
     }
   }
+  if (tid < a.top) {
+    sl_e[tid] = clamp_expert(id_raw, a.E, a.status);
+    sl_w[tid] = gw_raw;
+  }
   if (tid == 0) misc[kMiscSlot] = 0;
-  __syncthreads();
+  lds_barrier();
+  CFR_TRACE_PHASE(1, 1);
 
   // ---- exact top-k: radix select over 11, 11 and 10 key bits ----
   // After a pass, candidates whose masked key exceeds `prefix` are kept; the
@@ -486,12 +538,12 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       const uint32_t dm = (uint32_t)nbins - 1u;
       if (pass > 0) {
         for (int q = tid; q < nbins; q += NT) hist[q] = 0;
-        __syncthreads();
+        lds_barrier();
       }
 #pragma unroll
       for (int i = 0; i < PER; ++i)
         if (c0 + i < nc && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dm], 1);
-      __syncthreads();
+      lds_barrier();
       // thread tid owns bins [base, base + bpt), highest bins first
       const int bpt = nbins / NT;
       const int base = nbins - (tid + 1) * bpt;
@@ -510,7 +562,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
           cum += hb;
         }
       }
-      __syncthreads();
+      lds_barrier();
       prefix |= (uint32_t)misc[kMiscDigit] << shift;
       mask |= dm << shift;
       need = misc[kMiscNeed];
@@ -529,7 +581,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
             bidx[slot] = c0 + i;
             flags[c0 + i] = 1;
           }
-        __syncthreads();
+        lds_barrier();
         if (tid < cnt) {
           const uint32_t ki = bkey[tid];
           const int ii = bidx[tid];
@@ -542,7 +594,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
             }
           if (rk < need) flags[ii] = 2;
         }
-        __syncthreads();
+        lds_barrier();
         mode = 1;
         break;
       }
@@ -550,6 +602,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
     }
   }
 
+  CFR_TRACE_PHASE(1, 2);
   // ---- kept flags and ranks in ascending candidate order ----
   bool on[PER];
   if (all) {
@@ -604,9 +657,13 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
           (uint32_t)on[i] | ((uint32_t)on[i + 1] << 8) | ((uint32_t)on[i + 2] << 16) | ((uint32_t)on[i + 3] << 24);
     }
   }
-  __syncthreads();
+  lds_barrier();
+  CFR_TRACE_PHASE(1, 3);
 
   if (!recover) {
+    if (hx0 < H) *reinterpret_cast<float4*>(xs + hx0) = xr0;
+    if (hx1 < H) *reinterpret_cast<float4*>(xs + hx1) = xr1;
+    lds_barrier();
     // ---- decode step (3): exact kept channels from native BF16 rows ----
     // wave v takes list entries [v cpw, (v+1) cpw), two channels at a time
     // when registers allow, all rows of both in flight together
@@ -681,6 +738,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         }
       }
     }
+    CFR_TRACE_PHASE(1, 4);
     // ---- partial output: only waves that took channels contribute ----
     // waves [0, NW/2) store their rows into NW/2 slots, the others add theirs
     constexpr int SL = NW / 2;
@@ -697,7 +755,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave >= SL && wave < used) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
@@ -719,7 +777,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int nsl = min(SL, max(used, 1));  // slots that received rows
     float* yp = a.ypart + ((size_t)t * a.G + w) * H;
     for (int h = tid * 4; h < H; h += NT * 4) {
@@ -733,6 +791,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       }
       *reinterpret_cast<float4*>(yp + h) = v;
     }
+    CFR_TRACE_PHASE(1, 5);
     return;
   }
 
@@ -772,13 +831,35 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   }
 #pragma unroll
   for (int d = 0; d < 8; ++d) zred[(size_t)tid * 8 + d] = cl < cpp ? zacc[d] : 0.f;
-  __syncthreads();
-  if (tid < R) {
-    const int rr8 = tid / 8, d = tid % 8;
-    float z = 0.f;
-    for (int q = rr8; q < cpp * R8; q += R8) z += zred[(size_t)q * 8 + d];
-    a.zpart[((size_t)t * a.Z + zr) * R + tid] = z;
+  lds_barrier();
+  // component r = 8 r8 + d sums zred[(cl R8 + r8) 8 + d] over cl < cpp: tpo
+  // consecutive threads per component (a power of two, at most 64) each sum a
+  // strided share, then a lane butterfly combines them
+  int tpo = 1;
+  while (tpo * 2 * R <= NT && tpo < 64) tpo *= 2;
+  const int r = tid / tpo, jq = tid - r * tpo;
+  float z = 0.f;
+  if (r < R) {
+    const int rr8 = r >> 3, d = r & 7;
+    for (int q0 = jq; q0 < cpp; q0 += tpo * 4) {
+      float zz[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * tpo;
+        zz[u] = zred[(size_t)((q < cpp ? q : 0) * R8 + rr8) * 8 + d];
+        zz[u] = q < cpp ? zz[u] : 0.f;
+      }
+      z += (zz[0] + zz[1]) + (zz[2] + zz[3]);
+    }
   }
+  if (tpo > 1) z += xor_lane_f<1>(z);
+  if (tpo > 2) z += xor_lane_f<2>(z);
+  if (tpo > 4) z += xor_lane_f<4>(z);
+  if (tpo > 8) z += xor_lane_f<8>(z);
+  if (tpo > 16) z += xor_lane_f<16>(z);
+  if (tpo > 32) z += xor_lane_f<32>(z);
+  if (r < R && jq == 0) a.zpart[((size_t)t * a.Z + zr) * R + r] = z;
+  CFR_TRACE_PHASE(1, 6);
 }
 
 // ===========================================================================
@@ -800,6 +881,7 @@ constexpr int kReducePer = kMaxGatherWgs / kReduceParts;     // partial rows per
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
   __shared__ float part[kReduceParts][kReduceSlice];
   __shared__ float zs[64];
+  CFR_TRACE_PHASE(2, 0);
   const int t = blockIdx.x / a.nslices, sl = blockIdx.x - t * a.nslices;
   const int tid = threadIdx.x;
   const int H = a.H, h0 = sl * kReduceSlice;
@@ -829,6 +911,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
   float v = 0.f;
 #pragma unroll
   for (int u = 0; u < kReducePer; ++u) v += pt + u * kReduceParts < a.G ? pv[u] : 0.f;
+  CFR_TRACE_PHASE(2, 1);
   part[pt][hl] = v;
   if (tid < 64) {
     float z = 0.f;
@@ -837,7 +920,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
       for (int q = 0; q < kMaxRecoverWgs; ++q) z += q < a.Z ? zv[q] : 0.f;
     zs[tid] = z;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < kReduceSlice) {
     float o = 0.f;
 #pragma unroll
@@ -856,6 +939,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
     }
     a.y[(size_t)t * H + h0 + tid] = o;
   }
+  CFR_TRACE_PHASE(2, 2);
   if (a.clear) {
     // the screen accumulators of this token (gate then up, ncp each), split
     // over its slices
@@ -865,6 +949,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
     ulonglong2* ap = reinterpret_cast<ulonglong2*>(a.acc + (size_t)t * n);
     for (int q = b0 / 2 + tid; q < b1 / 2; q += kReduceThreads) ap[q] = make_ulonglong2(0ull, 0ull);
   }
+  CFR_TRACE_PHASE(2, 3);
 }
 
 // ===========================================================================
