@@ -260,9 +260,9 @@ def main():
     rb = main_r["bytes"]
     # algorithmic bytes of each kernel per launch (one token)
     stage_bytes = {
-        "screen_score": rb["codes"] + rb["scales"] + rb["norms"],
-        "select_exact": k_main * 2 * s.hidden * 2 + rb["b"],
-        "down_recover": k_main * s.hidden * 2 + rb["u"],
+        "screen": rb["codes"] + rb["scales"] + rb["norms"],
+        "select": rb["exact"] + rb["b"],
+        "reduce": rb["u"],
     }
     dom = max(stage_bytes, key=lambda n: main_r["stages"].get(n, 0.0))
     dom_us = main_r["stages"][dom]

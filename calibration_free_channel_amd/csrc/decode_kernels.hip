@@ -35,6 +35,8 @@
 // serialise), so no kernel waits for another workgroup.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 // Optional device-side phase trace: a build that defines CFR_TRACE_PHASE(k, i)
@@ -155,6 +157,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  // compiler-only barrier: global loads issued before stay before (nothing
+  // waits for them here), so they remain in flight across the barrier
+  asm volatile("" ::: "memory");
 }
 
 // Inclusive prefix sum over the NT threads of a workgroup.  sh: NT/64 ints
@@ -430,91 +435,219 @@ struct SelectArgs {
   int32_t* kept;
   int32_t* status;
   int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dense, dbg;
+  float invI;  // 1 / I rounded to float (exact slot division below 2^17)
 };
 
 // misc slots
-constexpr int kMiscDigit = 16, kMiscNeed = 17, kMiscCount = 18, kMiscSlot = 19;
-constexpr int kDirectMax = 32;  // boundary sets up to this size are ranked directly
+constexpr int kMiscDigit = 16, kMiscNeed = 17, kMiscCount = 18, kMiscSlot = 19, kMiscDT = 20,
+              kMiscCT = 21, kMiscMax = 32;
+constexpr int kDirectMax = 64;  // boundary sets up to this size are ranked directly
+// First selection pass: candidates are binned by how far their key lies below
+// the largest key, 2^kBinShift key units per bin (1/128 of an octave of the
+// score for positive scores); the last bin collects everything further down.
+constexpr int kBinShift = 16;
+constexpr int kBins = 2048;
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)xor_lane<1>((int)v));
+  v = max(v, (uint32_t)xor_lane<2>((int)v));
+  v = max(v, (uint32_t)xor_lane<4>((int)v));
+  v = max(v, (uint32_t)xor_lane<8>((int)v));
+  v = max(v, (uint32_t)xor_lane<16>((int)v));
+  v = max(v, (uint32_t)xor_lane<32>((int)v));
+  return v;
+}
+
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Output-unit score of one candidate from its fixed-point screen sums and
+// w ||d||: sets g_hat, v_hat, p = silu(g_hat) v_hat and s = w ||d|| |p|, and
+// returns the order-preserving key of s.
+__device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned long long v, float wn,
+                                              float& gh, float& vh, float& p, float& sc) {
+  gh = from_fix(g) * kInvSqrt128f;
+  vh = from_fix(v) * kInvSqrt128f;
+  p = silu(gh) * vh;
+  sc = wn * fabsf(p);
+  return order_key(sc);
+}
+
+// Buffer resource over `bytes` bytes at p (gfx9 layout): a raw buffer load at
+// an offset past the end returns zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kNoLoad = 0x80000000u;  // offset past the end of any buffer here
+
+// One wave finds the bin where the running count over bins 0, 1, ... first
+// reaches need (need >= 1 and at most the total count), and writes the bin,
+// the places left in it and its size to misc.  Lane l first sums the NB/64
+// consecutive bins it owns; then the lanes take one bin each of the lane
+// range where the count crosses.
+template <int NB>
+__device__ __forceinline__ void find_crossing_wave(const int* hist, int need, int* misc) {
+  constexpr int BPL = NB / 64;
+  static_assert(BPL % 4 == 0 && BPL <= 64, "whole int4 groups per lane");
+  const int lane = threadIdx.x & 63;
+  const int4* hp = reinterpret_cast<const int4*>(hist + lane * BPL);
+  int own = 0;
+#pragma unroll
+  for (int q = 0; q < BPL / 4; ++q) {
+    const int4 v = hp[q];
+    own += (v.x + v.y) + (v.z + v.w);
+  }
+  const int incl = wave_scan(own);
+  const int L = max(__builtin_ffsll((long long)__ballot(incl >= need)) - 1, 0);  // first lane reaching need
+  const int before = __builtin_amdgcn_readlane(incl - own, L);
+  const int hb = lane < BPL ? hist[L * BPL + lane] : 0;
+  const int run = wave_scan(hb) + before;  // count through this bin
+  const int b = __builtin_ffsll((long long)__ballot(lane < BPL && run >= need)) - 1;
+  if (lane == b) {
+    misc[kMiscDigit] = L * BPL + b;
+    misc[kMiscNeed] = need - (run - hb);
+    misc[kMiscCount] = hb;
+  }
+}
+
+// Ranks of flagged candidates in ascending candidate order, the order
+// (pair slot i, wave, lane, j) for pair P = i NT + tid holding candidates 2P
+// and 2P + 1: out[i] = flagged candidates before candidate 2P.  wc: P2 * NW
+// ints not reused before the next barrier.  One barrier inside; every wave
+// scans the per-(slot, wave) counts itself (lane l holds entries 2l, 2l + 1).
+template <int NT, int PER>
+__device__ __forceinline__ void ordered_counts(const bool (&f)[PER], int* wc, int (&out)[PER / 2]) {
+  constexpr int NW = NT / 64, P2 = PER / 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  unsigned long long b0[P2], b1[P2];
+#pragma unroll
+  for (int i = 0; i < P2; ++i) {
+    b0[i] = __ballot(f[2 * i]);
+    b1[i] = __ballot(f[2 * i + 1]);
+    if (lane == 0) wc[i * NW + wave] = __popcll(b0[i]) + __popcll(b1[i]);
+  }
+  lds_barrier();
+  const int q0 = 2 * lane < P2 * NW ? wc[2 * lane] : 0;
+  const int q1 = 2 * lane + 1 < P2 * NW ? wc[2 * lane + 1] : 0;
+  const int incl = wave_scan(q0 + q1);
+  const int excl = incl - q0 - q1;
+#pragma unroll
+  for (int i = 0; i < P2; ++i) {
+    const int qq = i * NW + wave;
+    const int base = __builtin_amdgcn_readlane(excl, qq >> 1) + ((qq & 1) ? __builtin_amdgcn_readlane(q0, qq >> 1) : 0);
+    out[i] = base + lanes_below(b0[i]) + lanes_below(b1[i]);
+  }
+}
+
+// Writes the flagged candidates to kept_out in ascending order (at most kk).
+template <int NT, int PER>
+__device__ __forceinline__ void write_kept_debug(const bool (&f)[PER], int* wc, int32_t* kept_out, int kk) {
+  int rk[PER / 2];
+  ordered_counts<NT, PER>(f, wc, rk);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PER / 2; ++i) {
+    const int rA = rk[i], rB = rA + (int)f[2 * i];
+    const int c = 2 * (i * NT + tid);
+    if (f[2 * i] && rA < kk) kept_out[rA] = c;
+    if (f[2 * i + 1] && rB < kk) kept_out[rB] = c + 1;
+  }
+}
 
 template <int NT, int PER, int NCH>
 __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NW = NT / 64;
+  constexpr int NW = NT / 64, P2 = PER / 2;
+  static_assert(PER % 2 == 0, "candidates are taken in pairs");
+  static_assert(P2 * NW <= 128, "two wave counts per lane");
   CFR_TRACE_PHASE(1, 0);
   const int wgs = a.G + a.Z;
   const int t = blockIdx.x / wgs, w = blockIdx.x - t * wgs;
   const bool recover = w >= a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, I = a.I, nc = a.nc, k = a.k;
   const GatherLds L(H, a.ncp, NT, a.chan);
   float* xs = reinterpret_cast<float*>(smem + L.xs);
   float* pvl = reinterpret_cast<float*>(smem + L.pv);
   uint8_t* flags = smem + L.flags;
+  uint32_t* dl = reinterpret_cast<uint32_t*>(smem + L.dl);
   float* yred = reinterpret_cast<float*>(smem + L.yred);
   int* hist = reinterpret_cast<int*>(smem + L.hist);
   int* list = reinterpret_cast<int*>(smem + L.list);
   int* misc = reinterpret_cast<int*>(smem + L.misc);
-  uint32_t* bkey = reinterpret_cast<uint32_t*>(smem + L.bkey);
-  int* bidx = reinterpret_cast<int*>(smem + L.bidx);
+  int2* bmem = reinterpret_cast<int2*>(smem + L.bmem);
+  int* wcnt = reinterpret_cast<int*>(smem + L.wcnt);
   int* sl_e = reinterpret_cast<int*>(smem + L.slot_e);
   float* sl_w = reinterpret_cast<float*>(smem + L.slot_w);
-  float* zred = reinterpret_cast<float*>(smem + L.zred);
+  float* zw = reinterpret_cast<float*>(smem + L.zred);
 
   const bool all = a.dense || k == nc;
   const bool partial = !all && k > 0;
   const int kk = all ? nc : k;  // kept candidates
-  const int c0 = tid * PER;     // this thread's candidates: [c0, c0 + PER)
+  const int r0 = recover ? 0 : min(w * a.chan, kk);
+  const int r1 = recover ? 0 : min(r0 + a.chan, kk);
+  const bool dbgw = a.dbg && w == 0;
+  // slot of candidate c (c < 2^17): exact through the float reciprocal of I
+  auto slot_of = [&](int c) { return (int)(((float)c + 0.5f) * a.invI); };
 
   // ---- loads, all issued up front in straight-line code at clamped
   // addresses (a guarded load compiles to a branch that waits on it):
-  // screen sums, w ||d||, routing and the token ----
+  // screen sums and w ||d|| of this thread's candidate pairs, routing, the
+  // token.  Pair P = i NT + tid holds candidates 2P and 2P + 1. ----
   static_assert(kMaxHidden <= 2 * NT * 4, "the token is two float4 per thread at most");
-  ulonglong2 gq[PER / 2], vq[PER / 2];
-  float4 wq[PER / 4];
+  ulonglong2 gq[P2], vq[P2];
+  float2 wq[P2];
   if (!a.dense) {
-    const ulonglong2* ag = reinterpret_cast<const ulonglong2*>(a.acc + (size_t)t * 2 * a.ncp + c0);
-    const ulonglong2* av = reinterpret_cast<const ulonglong2*>(a.acc + ((size_t)t * 2 + 1) * a.ncp + c0);
-    const float4* wp = reinterpret_cast<const float4*>(a.wn + (size_t)t * a.ncp + c0);
+    const ulonglong2* ag = reinterpret_cast<const ulonglong2*>(a.acc + (size_t)t * 2 * a.ncp);
+    const ulonglong2* av = reinterpret_cast<const ulonglong2*>(a.acc + ((size_t)t * 2 + 1) * a.ncp);
+    const float2* wp = reinterpret_cast<const float2*>(a.wn + (size_t)t * a.ncp);
 #pragma unroll
-    for (int u = 0; u < PER / 2; ++u) {
-      gq[u] = ag[u];
-      vq[u] = av[u];
+    for (int i = 0; i < P2; ++i) {
+      gq[i] = ag[i * NT + tid];
+      vq[i] = av[i * NT + tid];
+      wq[i] = wp[i * NT + tid];
     }
-#pragma unroll
-    for (int u = 0; u < PER / 4; ++u) wq[u] = wp[u];
   }
   const int rslot = tid < a.top ? tid : a.top - 1;
   const int id_raw = a.ids[t * a.top + rslot];
   const float gw_raw = a.gw[t * a.top + rslot];
-  // the token, for the gather (written to LDS after the selection)
   const float* xt = a.x + (size_t)t * H;
   const int hx0 = tid * 4, hx1 = (tid + NT) * 4;
   const float4 xr0 = *reinterpret_cast<const float4*>(xt + (hx0 < H ? hx0 : H - 4));
   const float4 xr1 = *reinterpret_cast<const float4*>(xt + (hx1 < H ? hx1 : H - 4));
   if (partial)
-    for (int q = tid; q < 2048; q += NT) hist[q] = 0;
+    for (int q = tid; q < kBins; q += NT) hist[q] = 0;
+
+  // ---- scores: s = w ||d|| |silu(g_hat) v_hat| as order-preserving keys;
+  // padding candidates (index >= nc) get key 0, below every real one ----
   uint32_t key[PER];
   float pr[PER];
+  uint32_t kmax = 0u;
   if (!a.dense) {
-    const bool dbg = a.dbg && w == 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const float gh = from_fix((i & 1) ? gq[i / 2].y : gq[i / 2].x) * kInvSqrt128f;
-      const float vh = from_fix((i & 1) ? vq[i / 2].y : vq[i / 2].x) * kInvSqrt128f;
-      const float4 w4 = wq[i / 4];
-      const float wn = (i & 3) == 0 ? w4.x : (i & 3) == 1 ? w4.y : (i & 3) == 2 ? w4.z : w4.w;
-      const float p = silu(gh) * vh;
-      const float sc = wn * fabsf(p);
-      const int c = c0 + i;
-      key[i] = c < nc ? order_key(sc) : 0u;  // padding ranks below every real candidate
-      pr[i] = p;
-      if (dbg && c < nc) {
-        a.ghat[(size_t)t * nc + c] = gh;
-        a.vhat[(size_t)t * nc + c] = vh;
-        a.score[(size_t)t * nc + c] = sc;
+    for (int i = 0; i < P2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float gh, vh, p, sc;
+        const uint32_t k0 = score_key(j ? gq[i].y : gq[i].x, j ? vq[i].y : vq[i].x, j ? wq[i].y : wq[i].x,
+                                      gh, vh, p, sc);
+        const int c = 2 * (i * NT + tid) + j;
+        const uint32_t kv = c < nc ? k0 : 0u;
+        key[2 * i + j] = kv;
+        pr[2 * i + j] = p;
+        kmax = max(kmax, kv);
+        if (dbgw && c < nc) {
+          a.ghat[(size_t)t * nc + c] = gh;
+          a.vhat[(size_t)t * nc + c] = vh;
+          a.score[(size_t)t * nc + c] = sc;
+        }
       }
-    }
+    kmax = wave_max_u32(kmax);
   }
+  if (lane == 0) misc[kMiscMax + wave] = (int)kmax;
   if (tid < a.top) {
     sl_e[tid] = clamp_expert(id_raw, a.E, a.status);
     sl_w[tid] = gw_raw;
@@ -523,150 +656,305 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   lds_barrier();
   CFR_TRACE_PHASE(1, 1);
 
-  // ---- exact top-k: radix select over 11, 11 and 10 key bits ----
-  // After a pass, candidates whose masked key exceeds `prefix` are kept; the
-  // `need` remaining places go to the boundary set (masked key == prefix):
-  //   mode 0  the whole boundary set (its size equals need)
-  //   mode 1  the members ranked directly (flag 2 = kept, 1 = not)
-  //   mode 2  all boundary keys are equal: the lowest candidate indices
-  uint32_t prefix = 0, mask = 0;
-  int need = kk, mode = 0;
+  // ---- exact top-k ----
+  // Distance below the largest key M, d = M - key: a smaller d is a larger
+  // score; among equal d the lower candidate index wins.  Pass 1 counts the
+  // bins min(d >> kBinShift, last) and finds the bin b* where the running
+  // count reaches k: bins before it are kept (S1), bins after it are not.
+  uint32_t M = 0u;
+#pragma unroll
+  for (int q = 0; q < NW; q += 4) {
+    const int4 m4 = *reinterpret_cast<const int4*>(misc + kMiscMax + q);
+    M = max(M, max(max((uint32_t)m4.x, (uint32_t)m4.y), max((uint32_t)m4.z, (uint32_t)m4.w)));
+  }
+  uint32_t bin[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    key[q] = M - key[q];  // key now holds d
+    bin[q] = min(key[q] >> kBinShift, (uint32_t)(kBins - 1));
+  }
+  if (recover && partial) {
+    // d and p of every candidate, for the recovery threads' early b requests
+#pragma unroll
+    for (int i = 0; i < P2; ++i) {
+      const int P = i * NT + tid;
+      *reinterpret_cast<uint2*>(dl + 2 * P) = make_uint2(key[2 * i], key[2 * i + 1]);
+      *reinterpret_cast<float2*>(pvl + 2 * P) = make_float2(pr[2 * i], pr[2 * i + 1]);
+    }
+  }
+  int bstar = 0, need = kk, cnt = 0;
   if (partial) {
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int nbins = pass == 2 ? 1024 : 2048;
-      const uint32_t dm = (uint32_t)nbins - 1u;
-      if (pass > 0) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) atomicAdd(&hist[bin[q]], 1);
+    lds_barrier();
+    if (wave == 0) find_crossing_wave<kBins>(hist, kk, misc);
+    lds_barrier();
+    bstar = misc[kMiscDigit];
+    need = misc[kMiscNeed];
+    cnt = misc[kMiscCount];
+  }
+  CFR_TRACE_PHASE(1, 2);
+
+  // recovery geometry: Rp = rank / 8 rounded up to a power of two threads
+  // per candidate, each 8 coefficients (one uint4) of b_j; thread (zcl, zr8)
+  // takes candidates zcb0 + zcl + u zcpp of this workgroup's range
+  int rp_log = 0;
+  while ((8 << rp_log) < a.rank) ++rp_log;
+  const int R8 = a.rank >> 3;
+  const int zcpp = NT >> rp_log;
+  const int zcl = tid >> rp_log, zr8 = tid & ((1 << rp_log) - 1);
+  int zcb0 = 0, zcb1 = 0;
+  if (recover) {
+    const int zper = (nc + a.Z - 1) / a.Z;
+    zcb0 = min((w - a.G) * zper, nc);
+    zcb1 = min(zcb0 + zper, nc);
+  }
+  const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(a.bmat, (uint32_t)((size_t)a.E * I * a.rank * 2));
+  // byte offset of this thread's uint4 of b_j for candidate cc
+  auto brow = [&](int cc) -> uint32_t {
+    const int sl = slot_of(cc);
+    return (uint32_t)((((size_t)sl_e[sl] * I + (cc - sl * I)) * a.rank + zr8 * 8) * 2);
+  };
+  uint4 zb[4];
+
+  const bool fast = partial && cnt <= kDirectMax;
+  if (fast) {
+    // ---- the usual case: a boundary bin small enough to rank directly ----
+    // S1 (n1 candidates) takes ranks [0, n1) in candidate order; b*'s members
+    // are ranked by (d, index) and the first `need` take ranks [n1, k).
+    const int n1 = kk - need;
+    bool s1[PER], mem[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      s1[q] = bin[q] < (uint32_t)bstar;
+      mem[q] = bin[q] == (uint32_t)bstar;
+    }
+    if (recover) {
+      // b rows of the first pass, except candidates surely kept
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cnd = zcb0 + zcl + u * zcpp;
+        const int cc = min(cnd, max(zcb1 - 1, 0));
+        const bool ld = cnd < zcb1 && zr8 < R8 && (dl[cc] >> kBinShift) >= (uint32_t)bstar;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, ld ? brow(cc) : kNoLoad, 0, 0);
+        zb[u] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      asm volatile("" ::: "memory");  // keeps the requests here, ahead of the barriers below
+    }
+    // S1 counts per (pair slot, wave) for the ranks (gather workgroups)
+    unsigned long long ba[PER];
+    if (!recover) {
+#pragma unroll
+      for (int i = 0; i < P2; ++i) {
+        ba[2 * i] = __ballot(s1[2 * i]);
+        ba[2 * i + 1] = __ballot(s1[2 * i + 1]);
+        if (lane == 0) wcnt[i * NW + wave] = __popcll(ba[2 * i]) + __popcll(ba[2 * i + 1]);
+      }
+    }
+    // b*'s members into bmem (a few per workgroup: one LDS atomic each)
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (mem[q]) {
+        const int slot = atomicAdd(&misc[kMiscSlot], 1);
+        if (slot < kDirectMax) bmem[slot] = make_int2((int)key[q], 2 * ((q >> 1) * NT + tid) + (q & 1));
+      }
+    const bool wantflags = recover || dbgw;
+    if (wantflags) {
+#pragma unroll
+      for (int i = 0; i < P2; ++i)
+        *reinterpret_cast<uint16_t*>(flags + 2 * (i * NT + tid)) =
+            (uint16_t)((uint32_t)s1[2 * i] | ((uint32_t)s1[2 * i + 1] << 8));
+    }
+    if (!recover) {
+      if (hx0 < H) *reinterpret_cast<float4*>(xs + hx0) = xr0;
+      if (hx1 < H) *reinterpret_cast<float4*>(xs + hx1) = xr1;
+    }
+    CFR_TRACE_PHASE(1, 7);
+    lds_barrier();
+    if (!recover && r0 < n1) {
+      // every wave scans the counts itself (lane l holds entries 2l, 2l + 1)
+      // and writes its S1 candidates whose rank falls in [r0, min(r1, n1))
+      const int hi = min(r1, n1);
+      const int q0 = 2 * lane < P2 * NW ? wcnt[2 * lane] : 0;
+      const int q1 = 2 * lane + 1 < P2 * NW ? wcnt[2 * lane + 1] : 0;
+      const int incl = wave_scan(q0 + q1);
+      const int excl = incl - q0 - q1;
+#pragma unroll
+      for (int i = 0; i < P2; ++i) {
+        const int qq = i * NW + wave;
+        const int base = __builtin_amdgcn_readlane(excl, qq >> 1) + ((qq & 1) ? __builtin_amdgcn_readlane(q0, qq >> 1) : 0);
+        const int n = __popcll(ba[2 * i]) + __popcll(ba[2 * i + 1]);
+        if (base < hi && base + n > r0) {  // wave-uniform
+          const int rA = base + lanes_below(ba[2 * i]) + lanes_below(ba[2 * i + 1]);
+          const int rB = rA + (int)s1[2 * i];
+          const int c = 2 * (i * NT + tid);
+          if (s1[2 * i] && rA >= r0 && rA < hi) list[rA - r0] = c;
+          if (s1[2 * i + 1] && rB >= r0 && rB < hi) list[rB - r0] = c + 1;
+        }
+      }
+    }
+    if (wave == 0 && (r1 > n1 || wantflags)) {
+      // one member per lane; each compares itself with every other member
+      // through lane broadcasts
+      const int2 me = bmem[lane < cnt ? lane : 0];
+      const uint32_t md = lane < cnt ? (uint32_t)me.x : 0xFFFFFFFFu;
+      const int mi = lane < cnt ? me.y : 0x7FFFFFFF;
+      const int n = __builtin_amdgcn_readfirstlane(cnt);
+      int rk = 0;
+      for (int q = 0; q < n; ++q) {
+        const uint32_t od = (uint32_t)__builtin_amdgcn_readlane((int)md, q);
+        const int oi = __builtin_amdgcn_readlane(mi, q);
+        rk += (int)((od < md) | ((od == md) & (oi < mi)));
+      }
+      if (lane < cnt && rk < need) {
+        const int r = n1 + rk;
+        if (r >= r0 && r < r1) list[r - r0] = mi;
+        if (wantflags) flags[mi] = 1;
+      }
+    }
+    lds_barrier();
+    if (dbgw) {
+      // the debug copy of the kept list, in candidate order
+      bool on[PER];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) on[q] = flags[2 * ((q >> 1) * NT + tid) + (q & 1)] != 0;
+      write_kept_debug<NT, PER>(on, wcnt + 128, a.kept + (size_t)t * nc, kk);
+    }
+  } else {
+    // ---- general case: keep all, keep none, or a large boundary bin ----
+    uint32_t dT = 0u;
+    int cT = -1;
+    if (partial) {
+      // boundary set: d in bin b* with (d & mask) == prefix
+      uint32_t prefix = 0u, mask = 0u;
+      auto member = [&](int q) { return bin[q] == (uint32_t)bstar && (key[q] & mask) == prefix; };
+      // 0: the whole boundary set is kept; 1: rank it directly; 2: equal keys
+      int mode = cnt == need ? 0 : -1;
+      for (int pass = 0; pass < 3 && mode < 0; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nbins = pass == 2 ? 1024 : 2048;
+        const uint32_t dm = (uint32_t)nbins - 1u;
         for (int q = tid; q < nbins; q += NT) hist[q] = 0;
         lds_barrier();
-      }
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (c0 + i < nc && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dm], 1);
-      lds_barrier();
-      // thread tid owns bins [base, base + bpt), highest bins first
-      const int bpt = nbins / NT;
-      const int base = nbins - (tid + 1) * bpt;
-      int own = 0;
-      for (int q = 0; q < bpt; ++q) own += hist[base + q];
-      const int incl = block_scan<NT>(own, misc);
-      if (incl >= need && incl - own < need) {
-        int cum = incl - own;
-        for (int q = bpt - 1; q >= 0; --q) {
-          const int hb = hist[base + q];
-          if (cum < need && cum + hb >= need) {
-            misc[kMiscDigit] = base + q;
-            misc[kMiscNeed] = need - cum;
-            misc[kMiscCount] = hb;
-          }
-          cum += hb;
+        for (int q = 0; q < PER; ++q)
+          if (member(q)) atomicAdd(&hist[(key[q] >> shift) & dm], 1);
+        lds_barrier();
+        if (wave == 0) {
+          if (pass == 2) find_crossing_wave<1024>(hist, need, misc);
+          else find_crossing_wave<2048>(hist, need, misc);
         }
+        lds_barrier();
+        prefix |= (uint32_t)misc[kMiscDigit] << shift;
+        mask |= dm << shift;
+        need = misc[kMiscNeed];
+        cnt = misc[kMiscCount];
+        mode = cnt == need ? 0 : (cnt <= kDirectMax ? 1 : (pass == 2 ? 2 : -1));
       }
-      lds_barrier();
-      prefix |= (uint32_t)misc[kMiscDigit] << shift;
-      mask |= dm << shift;
-      need = misc[kMiscNeed];
-      const int cnt = misc[kMiscCount];
-      if (cnt == need) {
-        mode = 0;
-        break;
-      }
-      if (cnt <= kDirectMax) {
-        // rank the boundary set directly (key descending, index ascending)
+      if (mode == 0) {
+        // every d of the boundary set is kept: the boundary is its largest d
+        dT = mask == 0u ? (bstar == kBins - 1 ? 0xFFFFFFFFu : (((uint32_t)bstar + 1u) << kBinShift) - 1u)
+                        : (prefix | ~mask);
+        cT = 0x7FFFFFFF;
+      } else if (mode == 1) {
+        // rank the members (d ascending, index ascending); the need-th is the boundary
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (c0 + i < nc && (key[i] & mask) == prefix) {
+        for (int q = 0; q < PER; ++q)
+          if (member(q)) {
             const int slot = atomicAdd(&misc[kMiscSlot], 1);
-            bkey[slot] = key[i];
-            bidx[slot] = c0 + i;
-            flags[c0 + i] = 1;
+            if (slot < kDirectMax) bmem[slot] = make_int2((int)key[q], 2 * ((q >> 1) * NT + tid) + (q & 1));
           }
         lds_barrier();
-        if (tid < cnt) {
-          const uint32_t ki = bkey[tid];
-          const int ii = bidx[tid];
+        if (wave == 0) {
+          const int2 me = bmem[lane < cnt ? lane : 0];
+          const uint32_t md = lane < cnt ? (uint32_t)me.x : 0xFFFFFFFFu;
+          const int mi = lane < cnt ? me.y : 0x7FFFFFFF;
+          const int n = __builtin_amdgcn_readfirstlane(cnt);
           int rk = 0;
-#pragma unroll 8
-          for (int q = 0; q < kDirectMax; ++q)
-            if (q < cnt) {
-              const uint32_t kq = bkey[q];
-              rk += kq > ki || (kq == ki && bidx[q] < ii);
-            }
-          if (rk < need) flags[ii] = 2;
+          for (int q = 0; q < n; ++q) {
+            const uint32_t od = (uint32_t)__builtin_amdgcn_readlane((int)md, q);
+            const int oi = __builtin_amdgcn_readlane(mi, q);
+            rk += (int)((od < md) | ((od == md) & (oi < mi)));
+          }
+          if (lane < cnt && rk == need - 1) {
+            misc[kMiscDT] = (int)md;
+            misc[kMiscCT] = mi;
+          }
         }
         lds_barrier();
-        mode = 1;
-        break;
+        dT = (uint32_t)misc[kMiscDT];
+        cT = misc[kMiscCT];
+      } else {
+        // all members share one d: the need lowest indices among them
+        dT = prefix;
+        bool mb[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) mb[q] = member(q);
+        int ob[P2];
+        ordered_counts<NT, PER>(mb, wcnt + 128, ob);
+#pragma unroll
+        for (int i = 0; i < P2; ++i) {
+          const int o1 = ob[i] + (int)mb[2 * i];
+          if (mb[2 * i] && ob[i] == need - 1) misc[kMiscCT] = 2 * (i * NT + tid);
+          if (mb[2 * i + 1] && o1 == need - 1) misc[kMiscCT] = 2 * (i * NT + tid) + 1;
+        }
+        lds_barrier();
+        cT = misc[kMiscCT];
       }
-      mode = 2;
     }
-  }
-
-  CFR_TRACE_PHASE(1, 2);
-  // ---- kept flags and ranks in ascending candidate order ----
-  bool on[PER];
-  if (all) {
+    // kept flags and ranks in ascending candidate order
+    bool on[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) on[i] = c0 + i < nc;
-  } else if (!partial) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) on[i] = false;
-  } else {
-    int eq_before = 0;
-    if (mode == 2) {
-      int neq = 0;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) neq += c0 + i < nc && (key[i] & mask) == prefix;
-      eq_before = block_scan<NT>(neq, misc) - neq;
+    for (int q = 0; q < PER; ++q) {
+      const int c = 2 * ((q >> 1) * NT + tid) + (q & 1);
+      on[q] = all ? c < nc : (partial && ((key[q] < dT) | ((key[q] == dT) & (c <= cT))));
     }
-    int eq_seen = 0;
+    if (recover) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t km = key[i] & mask;
-      bool o = c0 + i < nc && km > prefix;
-      if (c0 + i < nc && km == prefix) {
-        if (mode == 0) o = true;
-        else if (mode == 1) o = flags[c0 + i] == 2;
-        else o = eq_before + (eq_seen++) < need;
+      for (int i = 0; i < P2; ++i) {
+        const int P = i * NT + tid;
+        *reinterpret_cast<uint16_t*>(flags + 2 * P) = (uint16_t)((uint32_t)on[2 * i] | ((uint32_t)on[2 * i + 1] << 8));
+        *reinterpret_cast<float2*>(pvl + 2 * P) = make_float2(pr[2 * i], pr[2 * i + 1]);
       }
-      on[i] = o;
     }
-  }
-  int mine = 0;
+    if (!recover) {
+      if (hx0 < H) *reinterpret_cast<float4*>(xs + hx0) = xr0;
+      if (hx1 < H) *reinterpret_cast<float4*>(xs + hx1) = xr1;
+    }
+    int rk[P2];
+    ordered_counts<NT, PER>(on, wcnt, rk);  // one barrier inside
 #pragma unroll
-  for (int i = 0; i < PER; ++i) mine += on[i];
-  int rnk = block_scan<NT>(mine, misc) - mine;
-  const int r0 = recover ? 0 : min(w * a.chan, kk);
-  const int r1 = recover ? 0 : min(r0 + a.chan, kk);
-  {
-    const bool dbg = a.dbg && w == 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (on[i]) {
-        if (rnk >= r0 && rnk < r1) list[rnk - r0] = c0 + i;
-        if (dbg) a.kept[(size_t)t * nc + rnk] = c0 + i;
-        ++rnk;
+    for (int i = 0; i < P2; ++i) {
+      const int rA = rk[i], rB = rA + (int)on[2 * i];
+      const int c = 2 * (i * NT + tid);
+      if (on[2 * i]) {
+        if (rA >= r0 && rA < r1) list[rA - r0] = c;
+        if (dbgw && rA < kk) a.kept[(size_t)t * nc + rA] = c;
       }
-  }
-  if (recover) {
-    // p and the kept flags of every candidate, for the recovery ranges
+      if (on[2 * i + 1]) {
+        if (rB >= r0 && rB < r1) list[rB - r0] = c + 1;
+        if (dbgw && rB < kk) a.kept[(size_t)t * nc + rB] = c + 1;
+      }
+    }
+    lds_barrier();
+    if (recover) {
+      // b rows of the first pass, kept candidates skipped
 #pragma unroll
-    for (int i = 0; i < PER; i += 4) {
-      *reinterpret_cast<float4*>(pvl + c0 + i) = make_float4(pr[i], pr[i + 1], pr[i + 2], pr[i + 3]);
-      *reinterpret_cast<uint32_t*>(flags + c0 + i) =
-          (uint32_t)on[i] | ((uint32_t)on[i + 1] << 8) | ((uint32_t)on[i + 2] << 16) | ((uint32_t)on[i + 3] << 24);
+      for (int u = 0; u < 4; ++u) {
+        const int cnd = zcb0 + zcl + u * zcpp;
+        const int cc = min(cnd, max(zcb1 - 1, 0));
+        const bool ld = cnd < zcb1 && zr8 < R8 && !flags[cc];
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, ld ? brow(cc) : kNoLoad, 0, 0);
+        zb[u] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
     }
   }
-  lds_barrier();
   CFR_TRACE_PHASE(1, 3);
 
   if (!recover) {
-    if (hx0 < H) *reinterpret_cast<float4*>(xs + hx0) = xr0;
-    if (hx1 < H) *reinterpret_cast<float4*>(xs + hx1) = xr1;
-    lds_barrier();
     // ---- decode step (3): exact kept channels from native BF16 rows ----
     // wave v takes list entries [v cpw, (v+1) cpw), two channels at a time
-    // when registers allow, all rows of both in flight together
+    // when registers allow, all rows in flight together
     float yv[NCH][8];
 #pragma unroll
     for (int q = 0; q < NCH; ++q)
@@ -674,34 +962,35 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       for (int i = 0; i < 8; ++i) yv[q][i] = 0.f;
     const int nmine = r1 - r0;
     constexpr bool kPair = NCH <= 4;
+    constexpr int NR = kPair ? 2 : 1;
     const int qend = min((wave + 1) * a.cpw, nmine);
-    for (int q0 = wave * a.cpw; q0 < qend; q0 += kPair ? 2 : 1) {
+    for (int q0 = wave * a.cpw; q0 < qend; q0 += NR) {
       const bool two = kPair && q0 + 1 < qend;
-      const int cA = list[q0], cB = two ? list[q0 + 1] : cA;
-      const int sA = cA / I, sB = cB / I;
-      const uint16_t* rowA = a.w3 + ((size_t)sl_e[sA] * I + (cA - sA * I)) * 3 * H;
-      const uint16_t* rowB = a.w3 + ((size_t)sl_e[sB] * I + (cB - sB * I)) * 3 * H;
-      uint4 gq[2][NCH], uq[2][NCH], dq[2][NCH];
+      int cc[NR];
+      cc[0] = list[q0];
+      if constexpr (kPair) cc[NR - 1] = two ? list[q0 + 1] : cc[0];
+      uint4 gq2[NR][NCH], uq2[NR][NCH], dq2[NR][NCH];
+      int sr[NR];
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
-        gq[0][ch] = *reinterpret_cast<const uint4*>(rowA + h);
-        uq[0][ch] = *reinterpret_cast<const uint4*>(rowA + H + h);
-        dq[0][ch] = *reinterpret_cast<const uint4*>(rowA + 2 * H + h);
-      }
-      if (two) {  // wave-uniform
+      for (int r = 0; r < NR; ++r) {
+        sr[r] = slot_of(cc[r]);
+        const uint16_t* row = a.w3 + ((size_t)sl_e[sr[r]] * I + (cc[r] - sr[r] * I)) * 3 * H;
+        if (r == 0 || two) {  // wave-uniform
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          const int h = min(ch * 512 + lane * 8, H - 8);
-          gq[1][ch] = *reinterpret_cast<const uint4*>(rowB + h);
-          uq[1][ch] = *reinterpret_cast<const uint4*>(rowB + H + h);
-          dq[1][ch] = *reinterpret_cast<const uint4*>(rowB + 2 * H + h);
+          for (int ch = 0; ch < NCH; ++ch) {
+            const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
+            gq2[r][ch] = *reinterpret_cast<const uint4*>(row + h);
+            uq2[r][ch] = *reinterpret_cast<const uint4*>(row + H + h);
+            dq2[r][ch] = *reinterpret_cast<const uint4*>(row + 2 * H + h);
+          }
+        } else {
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) gq2[r][ch] = uq2[r][ch] = dq2[r][ch] = make_uint4(0u, 0u, 0u, 0u);
         }
-      } else {
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) gq[1][ch] = uq[1][ch] = dq[1][ch] = make_uint4(0u, 0u, 0u, 0u);
       }
-      float gs[2] = {0.f, 0.f}, vs[2] = {0.f, 0.f};
+      float gs[NR], vs[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) gs[r] = vs[r] = 0.f;
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int h = ch * 512 + lane * 8;
@@ -710,9 +999,9 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
           const float4 xb = *reinterpret_cast<const float4*>(xs + h + 4);
           const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const uint32_t gw4[4] = {gq[r][ch].x, gq[r][ch].y, gq[r][ch].z, gq[r][ch].w};
-            const uint32_t uw4[4] = {uq[r][ch].x, uq[r][ch].y, uq[r][ch].z, uq[r][ch].w};
+          for (int r = 0; r < NR; ++r) {
+            const uint32_t gw4[4] = {gq2[r][ch].x, gq2[r][ch].y, gq2[r][ch].z, gq2[r][ch].w};
+            const uint32_t uw4[4] = {uq2[r][ch].x, uq2[r][ch].y, uq2[r][ch].z, uq2[r][ch].w};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               gs[r] = fmaf(bf_lo(gw4[p]), xv[2 * p], gs[r]);
@@ -723,28 +1012,30 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
           }
         }
       }
-      const float cfA = sl_w[sA] * silu(wave_sum(gs[0])) * wave_sum(vs[0]);
-      const float cfB = two ? sl_w[sB] * silu(wave_sum(gs[1])) * wave_sum(vs[1]) : 0.f;
+      float cf[NR];
+      cf[0] = sl_w[sr[0]] * silu(wave_sum(gs[0])) * wave_sum(vs[0]);
+      if constexpr (kPair) cf[NR - 1] = two ? sl_w[sr[NR - 1]] * silu(wave_sum(gs[NR - 1])) * wave_sum(vs[NR - 1]) : 0.f;
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const uint32_t d0[4] = {dq[0][ch].x, dq[0][ch].y, dq[0][ch].z, dq[0][ch].w};
-        const uint32_t d1[4] = {dq[1][ch].x, dq[1][ch].y, dq[1][ch].z, dq[1][ch].w};
+      for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          yv[ch][2 * p] = fmaf(cfA, bf_lo(d0[p]), yv[ch][2 * p]);
-          yv[ch][2 * p + 1] = fmaf(cfA, bf_hi(d0[p]), yv[ch][2 * p + 1]);
-          yv[ch][2 * p] = fmaf(cfB, bf_lo(d1[p]), yv[ch][2 * p]);
-          yv[ch][2 * p + 1] = fmaf(cfB, bf_hi(d1[p]), yv[ch][2 * p + 1]);
+        for (int r = 0; r < NR; ++r) {
+          const uint32_t dw[4] = {dq2[r][ch].x, dq2[r][ch].y, dq2[r][ch].z, dq2[r][ch].w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            yv[ch][2 * p] = fmaf(cf[r], bf_lo(dw[p]), yv[ch][2 * p]);
+            yv[ch][2 * p + 1] = fmaf(cf[r], bf_hi(dw[p]), yv[ch][2 * p + 1]);
+          }
         }
-      }
     }
     CFR_TRACE_PHASE(1, 4);
     // ---- partial output: only waves that took channels contribute ----
-    // waves [0, NW/2) store their rows into NW/2 slots, the others add theirs
-    constexpr int SL = NW / 2;
+    // With one LDS slot per wave (rows up to 2048 wide) each such wave stores
+    // its rows in its slot; otherwise waves [0, NW/2) store and the others
+    // add theirs.  The slots are then summed in a fixed order.
+    constexpr int SL = NCH <= 4 ? NW : NW / 2;
     const int used = min(NW, (nmine + a.cpw - 1) / a.cpw);  // waves holding channels
     const int slot = wave % SL;
-    if (wave < SL) {
+    if (wave < SL && (SL == NW ? wave < used : true)) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int h = ch * 512 + lane * 8;
@@ -755,34 +1046,36 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         }
       }
     }
-    lds_barrier();
-    if (wave >= SL && wave < used) {
+    if constexpr (SL < NW) {
+      lds_barrier();
+      if (wave >= SL && wave < used) {
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const int h = ch * 512 + lane * 8;
-        if (h < H) {
-          float* o = yred + (size_t)slot * H + h;
-          float4 p0 = *reinterpret_cast<float4*>(o);
-          float4 p1 = *reinterpret_cast<float4*>(o + 4);
-          p0.x += yv[ch][0];
-          p0.y += yv[ch][1];
-          p0.z += yv[ch][2];
-          p0.w += yv[ch][3];
-          p1.x += yv[ch][4];
-          p1.y += yv[ch][5];
-          p1.z += yv[ch][6];
-          p1.w += yv[ch][7];
-          *reinterpret_cast<float4*>(o) = p0;
-          *reinterpret_cast<float4*>(o + 4) = p1;
+        for (int ch = 0; ch < NCH; ++ch) {
+          const int h = ch * 512 + lane * 8;
+          if (h < H) {
+            float* o = yred + (size_t)slot * H + h;
+            float4 p0 = *reinterpret_cast<float4*>(o);
+            float4 p1 = *reinterpret_cast<float4*>(o + 4);
+            p0.x += yv[ch][0];
+            p0.y += yv[ch][1];
+            p0.z += yv[ch][2];
+            p0.w += yv[ch][3];
+            p1.x += yv[ch][4];
+            p1.y += yv[ch][5];
+            p1.z += yv[ch][6];
+            p1.w += yv[ch][7];
+            *reinterpret_cast<float4*>(o) = p0;
+            *reinterpret_cast<float4*>(o + 4) = p1;
+          }
         }
       }
     }
     lds_barrier();
-    const int nsl = min(SL, max(used, 1));  // slots that received rows
+    const int nsl = min(SL, used);  // slots that received rows
     float* yp = a.ypart + ((size_t)t * a.G + w) * H;
     for (int h = tid * 4; h < H; h += NT * 4) {
-      float4 v = *reinterpret_cast<const float4*>(yred + h);
-      for (int q = 1; q < nsl; ++q) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int q = 0; q < nsl; ++q) {
         const float4 u = *reinterpret_cast<const float4*>(yred + (size_t)q * H + h);
         v.x += u.x;
         v.y += u.y;
@@ -796,69 +1089,65 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   }
 
   // ---- decode step (4), first half: z over this workgroup's candidate range ----
-  // R8 threads per candidate, each 8 coefficients (one uint4) of b_j
-  const int zr = w - a.G;
-  const int R = a.rank, R8 = R / 8;
-  const int zper = (nc + a.Z - 1) / a.Z;
-  const int cb0 = min(zr * zper, nc), cb1 = min(cb0 + zper, nc);
-  const int cpp = NT / R8;  // candidates per pass
-  const int cl = tid / R8, r8 = tid - cl * R8;
+  // z = sum over skipped candidates of w p_j b_j; the first pass was
+  // requested during the selection, later passes skip kept candidates' rows
   float zacc[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) zacc[d] = 0.f;
-  if (cl < cpp) {
-    for (int cb = cb0 + cl; cb < cb1; cb += cpp * 4) {
-      uint4 bq[4];
-      float cf[4];
+  auto zadd = [&](const uint4& bq, float cf) {
+    const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int cnd = cb + u * cpp;
-        const int cc = cnd < cb1 ? cnd : cb1 - 1;  // clamped: loads always issued
-        const int s = cc / I, j = cc - s * I;
-        bq[u] = reinterpret_cast<const uint4*>(a.bmat + ((size_t)sl_e[s] * I + j) * R)[r8];
-        cf[u] = (cnd < cb1 && !flags[cc]) ? sl_w[s] * pvl[cc] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t bw[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          zacc[2 * d] = fmaf(cf[u], lo16(bw[d]), zacc[2 * d]);
-          zacc[2 * d + 1] = fmaf(cf[u], hi16(bw[d]), zacc[2 * d + 1]);
-        }
-      }
+    for (int d = 0; d < 4; ++d) {
+      zacc[2 * d] = fmaf(cf, lo16(bw[d]), zacc[2 * d]);
+      zacc[2 * d + 1] = fmaf(cf, hi16(bw[d]), zacc[2 * d + 1]);
     }
-  }
+  };
 #pragma unroll
-  for (int d = 0; d < 8; ++d) zred[(size_t)tid * 8 + d] = cl < cpp ? zacc[d] : 0.f;
+  for (int u = 0; u < 4; ++u) {
+    const int cnd = zcb0 + zcl + u * zcpp;
+    const int cc = min(cnd, max(zcb1 - 1, 0));
+    zadd(zb[u], (cnd < zcb1 && !flags[cc]) ? sl_w[slot_of(cc)] * pvl[cc] : 0.f);
+  }
+  CFR_TRACE_PHASE(1, 4);
+  for (int cb = zcb0 + zcl + 4 * zcpp; cb < zcb1; cb += 4 * zcpp) {
+    uint4 bq[4];
+    float cf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cnd = cb + u * zcpp;
+      const int cc = cnd < zcb1 ? cnd : zcb1 - 1;
+      const bool skip = cnd < zcb1 && !flags[cc];
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, (skip && zr8 < R8) ? brow(cc) : kNoLoad, 0, 0);
+      bq[u] = make_uint4(v[0], v[1], v[2], v[3]);
+      cf[u] = skip ? sl_w[slot_of(cc)] * pvl[cc] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zadd(bq[u], cf[u]);
+  }
+  // sum over the candidates of the wave (lanes with equal zr8), then over waves
+  auto zfold = [&](auto hc) {
+    constexpr int HH = decltype(hc)::value;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) zacc[d] += xor_lane_f<HH>(zacc[d]);
+  };
+  if (rp_log == 0) zfold(std::integral_constant<int, 1>{});
+  if (rp_log <= 1) zfold(std::integral_constant<int, 2>{});
+  if (rp_log <= 2) zfold(std::integral_constant<int, 4>{});
+  if (rp_log <= 3) zfold(std::integral_constant<int, 8>{});
+  zfold(std::integral_constant<int, 16>{});
+  zfold(std::integral_constant<int, 32>{});
+  if (lane < (1 << rp_log) && lane < R8) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) zw[wave * 64 + lane * 8 + d] = zacc[d];
+  }
   lds_barrier();
-  // component r = 8 r8 + d sums zred[(cl R8 + r8) 8 + d] over cl < cpp: tpo
-  // consecutive threads per component (a power of two, at most 64) each sum a
-  // strided share, then a lane butterfly combines them
-  int tpo = 1;
-  while (tpo * 2 * R <= NT && tpo < 64) tpo *= 2;
-  const int r = tid / tpo, jq = tid - r * tpo;
-  float z = 0.f;
-  if (r < R) {
-    const int rr8 = r >> 3, d = r & 7;
-    for (int q0 = jq; q0 < cpp; q0 += tpo * 4) {
-      float zz[4];
+  CFR_TRACE_PHASE(1, 5);
+  if (tid < a.rank) {
+    float z = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = q0 + u * tpo;
-        zz[u] = zred[(size_t)((q < cpp ? q : 0) * R8 + rr8) * 8 + d];
-        zz[u] = q < cpp ? zz[u] : 0.f;
-      }
-      z += (zz[0] + zz[1]) + (zz[2] + zz[3]);
-    }
+    for (int v = 0; v < NW; ++v) z += zw[v * 64 + tid];
+    a.zpart[((size_t)t * a.Z + (w - a.G)) * a.rank + tid] = z;
   }
-  if (tpo > 1) z += xor_lane_f<1>(z);
-  if (tpo > 2) z += xor_lane_f<2>(z);
-  if (tpo > 4) z += xor_lane_f<4>(z);
-  if (tpo > 8) z += xor_lane_f<8>(z);
-  if (tpo > 16) z += xor_lane_f<16>(z);
-  if (tpo > 32) z += xor_lane_f<32>(z);
-  if (r < R && jq == 0) a.zpart[((size_t)t * a.Z + zr) * R + r] = z;
   CFR_TRACE_PHASE(1, 6);
 }
 
@@ -1033,24 +1322,26 @@ static hipError_t launch_select_t(const SelectArgs& a, const Plan& p, int batch,
   return hipGetLastError();
 }
 
-template <int NT, int PER>
+template <int PER>
 static hipError_t launch_select_n(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   switch (p.nch) {
-    case 1: return launch_select_t<NT, PER, 1>(a, p, batch, st);
-    case 2: return launch_select_t<NT, PER, 2>(a, p, batch, st);
-    case 4: return launch_select_t<NT, PER, 4>(a, p, batch, st);
-    default: return launch_select_t<NT, PER, 8>(a, p, batch, st);
+    case 1: return launch_select_t<512, PER, 1>(a, p, batch, st);
+    case 2: return launch_select_t<512, PER, 2>(a, p, batch, st);
+    case 4: return launch_select_t<512, PER, 4>(a, p, batch, st);
+    default: return launch_select_t<512, PER, 8>(a, p, batch, st);
   }
 }
 
 static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  switch (p.per) {  // select_geom: 512 threads, 4..32 candidates each
-    case 4: return launch_select_n<512, 4>(a, p, batch, st);
-    case 8: return launch_select_n<512, 8>(a, p, batch, st);
-    case 12: return launch_select_n<512, 12>(a, p, batch, st);
-    case 16: return launch_select_n<512, 16>(a, p, batch, st);
-    case 24: return launch_select_n<512, 24>(a, p, batch, st);
-    default: return launch_select_n<512, 32>(a, p, batch, st);
+  switch (p.per) {  // select_geom: 512 threads, 2..32 candidates each
+    case 2: return launch_select_n<2>(a, p, batch, st);
+    case 4: return launch_select_n<4>(a, p, batch, st);
+    case 6: return launch_select_n<6>(a, p, batch, st);
+    case 8: return launch_select_n<8>(a, p, batch, st);
+    case 12: return launch_select_n<12>(a, p, batch, st);
+    case 16: return launch_select_n<16>(a, p, batch, st);
+    case 24: return launch_select_n<24>(a, p, batch, st);
+    default: return launch_select_n<32>(a, p, batch, st);
   }
 }
 
@@ -1085,7 +1376,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   mark(1);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, r->ghat, r->vhat,
                r->score, r->kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
-               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr};
+               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter};
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
@@ -1119,7 +1410,7 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   const Plan p = make_plan(c, batch, nc, true);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, nullptr, nullptr,
                nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
-               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0};
+               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter};
   hipError_t e;
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, 0, c.rank, r->ncp,

@@ -16,17 +16,20 @@ constexpr int kReduceSlice = 32;        // hidden units per reduce workgroup
 __host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 16; }
 
 // Thread geometry of the select/gather kernel for nc candidates per token:
-// nt threads, each owning `per` consecutive candidates (a multiple of 4, so
-// its screen sums load as 16-byte vectors).  Per-token candidate arrays are
-// padded to nt * per entries; the padding is never written and stays zero.
+// nt threads, each owning `per` candidates taken in pairs (pair P = i nt + tid
+// holds candidates 2P and 2P + 1, so a wave's loads of the screen sums are
+// contiguous).  Per-token candidate arrays are padded to nt * per entries;
+// the padding is never written and stays zero.
 struct SelectGeom {
   int nt, per;
 };
 __host__ __device__ inline SelectGeom select_geom(int nc) {
   const int nt = 512;
   int per = (nc + nt - 1) / nt;
-  per = (per + 3) / 4 * 4;
-  if (per < 4) per = 4;
+  per = (per + 1) / 2 * 2;
+  if (per < 2) per = 2;
+  if (per > 8 && per <= 12) per = 12;
+  if (per > 12 && per <= 16) per = 16;
   if (per > 16 && per <= 24) per = 24;
   if (per > 24) per = 32;
   return {nt, per};
@@ -35,25 +38,29 @@ __host__ __device__ inline SelectGeom select_geom(int nc) {
 // LDS layout of the select/gather kernel (bytes); host and device share it.
 //   xs     fp32 [H]          the token (gather workgroups)
 //   pv     fp32 [ncp]        p of every candidate (recovery workgroups)
-//   flags  u8 [ncp]          kept flag of every candidate (recovery workgroups)
-//   yred   fp32 [NT/128][H]  per-wave partial outputs (gather workgroups)
-//   hist   int [2048]        radix histogram
+//   dl     u32 [ncp]         key distance d of every candidate (recovery)
+//   flags  u8 [ncp]          kept flag of every candidate (recovery, debug)
+//   yred   fp32 [S][H]       partial outputs, S = NT/64 slots for H <= 2048
+//                            else NT/128 (gather workgroups; shares the
+//                            space of pv, dl and flags)
+//   hist   int [2048]        selection histogram
 //   list   int [chan]        this workgroup's kept candidates, by rank
 //   misc   int [64]          scan scratch and broadcast values
-//   bkey, bidx [64]          the boundary bin, when ranked directly
+//   bmem   int2 [64]         the boundary set, when ranked directly
+//   wcnt   int [256]         per-wave counts of the ordered prefix sums
 //   slot   int [16] + fp32 [16]  routed expert and weight per slot
-//   zred   fp32 [NT][8]      recovery partial sums
+//   zred   fp32 [NT/64][64]  per-wave recovery sums
 struct GatherLds {
-  size_t xs, pv, flags, yred, hist, list, misc, bkey, bidx, slot_e, slot_w, zred, total;
+  size_t xs, pv, dl, flags, yred, hist, list, misc, bmem, wcnt, slot_e, slot_w, zred, total;
   __host__ __device__ GatherLds(int H, int ncp, int nt, int chan) {
     size_t o = 0;
     xs = o;
     o += lds_align((size_t)H * 4);
-    // pv/flags (recovery workgroups) and yred (gather workgroups) share space
-    const size_t rec = lds_align((size_t)ncp * 4) + lds_align((size_t)ncp);
-    const size_t red = (size_t)(nt / 128) * H * 4;
+    const size_t rec = 2 * lds_align((size_t)ncp * 4) + lds_align((size_t)ncp);
+    const size_t red = (size_t)(H <= 2048 ? nt / 64 : nt / 128) * H * 4;
     pv = o;
-    flags = o + lds_align((size_t)ncp * 4);
+    dl = o + lds_align((size_t)ncp * 4);
+    flags = o + 2 * lds_align((size_t)ncp * 4);
     yred = o;
     o += rec > red ? rec : red;
     hist = o;
@@ -62,16 +69,16 @@ struct GatherLds {
     o += lds_align((size_t)(chan > 0 ? chan : 1) * 4);
     misc = o;
     o += 64 * 4;
-    bkey = o;
-    o += 64 * 4;
-    bidx = o;
-    o += 64 * 4;
+    bmem = o;
+    o += 64 * 8;
+    wcnt = o;
+    o += 256 * 4;
     slot_e = o;
     o += 16 * 4;
     slot_w = o;
     o += 16 * 4;
     zred = o;
-    o += (size_t)nt * 8 * 4;
+    o += (size_t)nt * 4;
     total = o;
   }
 };

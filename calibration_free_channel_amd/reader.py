@@ -179,7 +179,7 @@ class Reader:
         o["kept"] = o["kept"][:, :int(k)]
         return o
 
-    STAGES = ("screen_score", "select_exact", "down_recover")
+    STAGES = ("screen", "select", "reduce")
 
     def decode_profile(self, x, expert_ids, gate_w, k: int, out=None, stream=None) -> dict:
         """Decode with an event after every stage; returns {stage: microseconds}.

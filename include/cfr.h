@@ -161,8 +161,10 @@ int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
 /* Stages of the decode path, in launch order; cfr_reader_decode_profile
  * reports one duration per stage. */
 #define CFR_NUM_STAGES 3
-/* 0 rotate + select + screen + score, 1 top-k + exact gate/up + recovery z,
- * 2 down projection of kept channels + U z */
+/* 0 screen: rotate, partial screen, sketch screen sums (k_screen);
+ * 1 select: scores, exact top-k, exact gather of the kept channels and the
+ *   recovery projection of the skipped ones (k_select);
+ * 2 reduce: sum of the partial outputs plus U z (k_reduce) */
 
 /*
  * Measurement entry: the same computation as cfr_reader_decode with a HIP
