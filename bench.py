@@ -15,8 +15,12 @@ Method:
     replays, after warm-up replays;
   * inputs (x, expert ids, routing weights) are synthetic and already resident
     in device memory when the timed region starts;
-  * per-stage durations come from events the library records on its launch
-    stream (cfr_reader_decode_profile) over a pass of the same steps;
+  * the per-kernel durations come from each kernel launched alone
+    (cfr_reader_decode_stage), back to back over the layer copies in a HIP
+    graph timed with events on its replay stream; `roofline` divides the
+    dominant kernel's algorithmic bytes by its duration, and `traffic` is the
+    HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    summary (null when the kernel source changed since it was taken);
   * the dense-BF16 routed-expert block on the same weights and the CPU oracle
     (float64, host cores, bounded sample) are reported beside the reader.
 
@@ -87,6 +91,7 @@ def profile_summary(d):
         return name.split("(")[0]
 
     lines = []
+    traffic = {}
     for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
         lines.append(f"kernel stats: {os.path.relpath(f, d)}")
         lines.append(f"{'kernel':<44} {'calls':>7} {'avg us':>9} {'min us':>9} {'max us':>9} {'% time':>7}")
@@ -113,9 +118,21 @@ def profile_summary(d):
         for k, c, v in copy:
             bytes_kib = v
             ratio = bytes_kib * 1024 / COPY_BYTES
+            scale = 1 / ratio if ratio else float("nan")
             lines.append(f"  copy reference {k[:40]} {c}: {bytes_kib:.0f} KiB for {COPY_BYTES >> 10} KiB "
-                         f"moved -> scale {1 / ratio if ratio else float('nan'):.4f}")
+                         f"moved -> scale {scale:.4f}")
+            traffic[c + "_scale"] = round(scale, 4)
+        for (k, c), (tot, n, _) in acc.items():
+            name = {"k_screen": "screen", "k_select": "select", "k_reduce": "reduce"}.get(k.split("<")[0].split()[-1])
+            if name:
+                traffic.setdefault("kernels", {}).setdefault(name, {})[
+                    "fetch_kib" if c == "FETCH_SIZE" else "write_kib"] = round(tot / n, 1)
     print("\n".join(lines))
+    traffic = {"source_sha256": source_digest(),
+               "fetch_scale": traffic.get("FETCH_SIZE_scale"), "write_scale": traffic.get("WRITE_SIZE_scale"),
+               "kernels": traffic.get("kernels", {})}
+    with open(os.path.join(d, "traffic.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1)
 
 
 def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None):
@@ -159,18 +176,74 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None)
     return 1000.0 * total_ms / (reps * L), reps * L, wreps * L
 
 
-def stage_profile(torch, readers, X, IDS, W, k, passes=2):
-    acc = None
-    n = 0
-    for _ in range(passes):
+def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
+    """Average duration of each decode kernel: the kernel launched alone, back
+    to back over all layer copies in one HIP graph, timed with HIP events on
+    the replay stream; returns {stage: microseconds per launch}.  Stage order
+    keeps every launch meaningful: the screen is timed first (its sums pile
+    up), a reduce pass clears them, a real screen pass fills them, then the
+    select (which only reads them) and the reduce (which clears them)."""
+    L = len(readers)
+    s = torch.cuda.Stream()
+    Y = torch.empty((L, 1, X.shape[-1]), dtype=torch.float32, device=X.device)
+
+    def one_pass(stage):
         for i, r in enumerate(readers):
-            d = r.decode_profile(X[i], IDS[i], W[i], k)
-            if acc is None:
-                acc = dict.fromkeys(d, 0.0)
-            for key, v in d.items():
-                acc[key] += v
-            n += 1
-    return {key: v / n for key, v in acc.items()}
+            r.decode_stage(stage, X[i], IDS[i], W[i], k, out=Y[i])
+
+    def timed(stage):
+        g = torch.cuda.CUDAGraph()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=s):
+            one_pass(stage)
+        torch.cuda.synchronize()
+        reps = max(1, -(-steps // L))
+        with torch.cuda.stream(s):
+            for _ in range(max(1, -(-warmup // L))):
+                g.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        del g
+        return 1000.0 * e0.elapsed_time(e1) / (reps * L)
+
+    out = {"screen": timed(0)}
+    with torch.cuda.stream(s):
+        one_pass(2)
+        one_pass(0)
+    torch.cuda.synchronize()
+    out["select"] = timed(1)
+    out["reduce"] = timed(2)
+    return out
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3-30b-a3b_k756.json")
+KERNEL_SOURCE = os.path.join(ROOT, "calibration_free_channel_amd", "csrc", "decode_kernels.hip")
+
+
+def source_digest():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def traffic_bytes(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    counter summary, each counter scaled by what it reads for a plain copy of
+    known size; None when there is none, or when the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest() or kernel not in t.get("kernels", {}):
+        return None
+    c = t["kernels"][kernel]
+    return int(round(1024.0 * (c["fetch_kib"] * t["fetch_scale"] + c["write_kib"] * t["write_scale"])))
 
 
 def cpu_baseline(wl, layer, X, IDS, W, k, seconds):
@@ -242,7 +315,7 @@ def main():
     for k in [k_main] + ([k_low] if k_low and not args.main_budget_only else []):
         us, nsteps, nwarm = graph_time(torch, readers, X, IDS, W, k, args.steps, args.warmup)
         rb = read_bytes(cfg, k)
-        stages = stage_profile(torch, readers, X, IDS, W, k)
+        stages = stage_times(torch, readers, X, IDS, W, k, min(args.steps, 400), args.warmup)
         res[k] = {"us": us, "steps": nsteps, "warmup": nwarm, "bytes": rb, "stages": stages}
         log(f"k={k}: {us:.2f} us/token, {rb['total'] / us / 1e3:.1f} GB/s counted; stages "
             + ", ".join(f"{n}={v:.1f}" for n, v in stages.items()))
@@ -267,6 +340,7 @@ def main():
     dom = max(stage_bytes, key=lambda n: main_r["stages"].get(n, 0.0))
     dom_us = main_r["stages"][dom]
     achieved = stage_bytes[dom] / dom_us / 1e3  # GB/s
+    traffic = traffic_bytes(dom)
     path_gbps = rb["total"] / main_r["us"] / 1e3
 
     cpu = None
@@ -306,9 +380,10 @@ def main():
         "dense_achieved_GBps": None if dense_us is None else round(rb["dense"] / dense_us / 1e3, 1),
         "speedup_vs_dense": None if dense_us is None else round(dense_us / main_r["us"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": dom, "bytes_per_launch": stage_bytes[dom],
-                     "us_per_launch": round(dom_us, 3)},
+                     "us_per_launch": round(dom_us, 3),
+                     "timing": "kernel alone, back to back over the layer copies in a HIP graph"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -265,6 +265,16 @@ int cfr_reader_decode_profile(cfr_reader* r, const float* x, const int32_t* ids,
   return CFR_OK;
 }
 
+int cfr_reader_decode_stage(cfr_reader* r, int32_t stage, const float* x, const int32_t* ids,
+                            const float* gw, int32_t batch, int32_t k, float* y, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, k, y);
+  if (rc) return rc;
+  if (stage < 0 || stage >= CFR_NUM_STAGES) return fail(CFR_EINVAL, "stage out of range");
+  DeviceGuard guard(r->cfg.device);
+  return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr,
+                       nullptr, stage);
+}
+
 int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
                      int32_t batch, float* y, void* stream) {
   int rc = check_decode_args(r, x, ids, gw, batch, 0, y);

@@ -1361,7 +1361,7 @@ static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) 
 }
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
-                  int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev) {
+                  int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev, int only) {
   const cfr_config& c = r->cfg;
   const Plan p = make_plan(c, batch, k, false);
   auto mark = [&](int i) {
@@ -1372,16 +1372,19 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->acc, r->wn, r->xrot,
                r->sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
                c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr};
-  if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
+  if (only < 0 || only == 0)
+    if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, r->ghat, r->vhat,
                r->score, r->kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
                r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter};
-  if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
+  if (only < 0 || only == 1)
+    if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
                p.nslices, 1};
-  if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
+  if (only < 0 || only == 2)
+    if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
   mark(3);
   if (dbg) {
     const int H = c.hidden, nblk = r->nblk, nsc = batch * r->ncand;

@@ -109,9 +109,10 @@ struct DebugOut {
   int32_t* kept = nullptr;
 };
 
+// only: -1 launches every stage; 0, 1 or 2 launches that stage's kernel alone
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t stream, const DebugOut* dbg,
-                  hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */);
+                  hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t stream);
 

@@ -195,6 +195,19 @@ class Reader:
                                                self._stream(stream)))
         return dict(zip(self.STAGES, list(us)))
 
+    def decode_stage(self, stage: int, x, expert_ids, gate_w, k: int, out=None, stream=None):
+        """Launch one decode stage's kernel alone (0 screen, 1 select, 2 reduce);
+        for timing a kernel in isolation.  y is the decode's only when the three
+        stages run in order for the same inputs."""
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        if out is None:
+            out = torch.empty((B, self.cfg.hidden), dtype=torch.float32, device=x.device)
+        py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
+        check(load().cfr_reader_decode_stage(self._h, int(stage), px, pi, pw, B, int(k), py,
+                                             self._stream(stream)))
+        return out
+
     def dense(self, x, expert_ids, gate_w, out=None, stream=None):
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)

@@ -177,6 +177,19 @@ int cfr_reader_decode_profile(cfr_reader* r, const float* x, const int32_t* expe
                               const float* gate_w, int32_t batch, int32_t k, float* y,
                               float* stage_us, void* stream);
 
+/*
+ * Measurement entry: launches the kernel of one decode stage alone on
+ * `stream` (stage 0, 1 or 2, as listed above), with the arguments
+ * cfr_reader_decode would give it; no host synchronisation.  A stage reads
+ * what the previous stage left in the reader's workspace, so y is the
+ * decode's result only when stages 0, 1, 2 run in that order for the same
+ * inputs; any other order reads stale but in-range workspace contents.  For
+ * timing one kernel in isolation (for example many launches in a HIP graph).
+ * Errors as cfr_reader_decode, plus CFR_EINVAL for a stage out of range.
+ */
+int cfr_reader_decode_stage(cfr_reader* r, int32_t stage, const float* x, const int32_t* expert_ids,
+                            const float* gate_w, int32_t batch, int32_t k, float* y, void* stream);
+
 /* Copy the built state to host buffers (any may be NULL); sizes from
  * cfr_sizes_of.  codes uint8, scales/rho/U/b fp16 bits, norms fp32,
  * sigma fp32 (+1/-1).  Synchronises the reader's device. */
