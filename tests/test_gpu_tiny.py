@@ -164,3 +164,20 @@ def test_argument_errors(reader):
     with pytest.raises(CfrError):
         reader.decode(big, torch.zeros((9, S.top), dtype=torch.int32, device="cuda"),
                       torch.zeros((9, S.top), device="cuda"), 3)
+
+
+def test_stages_in_order_equal_decode(reader, layer):
+    """The measurement entry (one kernel per call) run as screen, select,
+    reduce reproduces cfr_reader_decode bit for bit; a bad stage is refused."""
+    from calibration_free_channel_amd._lib import CfrError
+    X = make_tokens(WL, 4, seed_offset=11)
+    ids, w = _routed(layer, X)
+    x, i, ww = _dev(X), _dev(ids), _dev(w)
+    y_ref = reader.decode(x, i, ww, 23)
+    y = torch.empty_like(y_ref)
+    for stage in range(3):
+        reader.decode_stage(stage, x, i, ww, 23, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    with pytest.raises(CfrError):
+        reader.decode_stage(3, x, i, ww, 23, out=y)
