@@ -1,0 +1,76 @@
+"""The 48-layer stack workload (Qwen3-30B-A3B-shaped layers with independent
+weights, residual x <- x + y carried from layer to layer, k = 756): its first
+three layers.  Each layer's decode is checked against the oracle on the
+oracle chain's input, and the library's own chain is compared with the
+oracle chain at the end.  Routing comes from each layer's router applied to
+the oracle chain's x (the library does not route), so both chains use the
+same experts."""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+from tests._parity import check_token, rel_l2
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+torch = pytest.importorskip("torch")
+
+from calibration_free_channel_amd import Config, Reader  # noqa: E402
+from oracle import OracleReader, route  # noqa: E402
+from synth import make_layer, make_tokens, workload  # noqa: E402
+
+WL = workload("qwen3-30b-a3b-48l")
+S = WL.shape
+K = 756
+NL = 3
+
+
+def _log(msg):
+    print(f"[stack] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def stack():
+    layers, oracles, readers = [], [], []
+    for l in range(NL):
+        t = time.time()
+        L = make_layer(WL, layer=l)
+        o = OracleReader(S.hidden, S.n_experts, S.inter, S.top, L["gate"], L["up"], L["down"],
+                         L["router"], rot_seed=WL.rot_seed)
+        r = Reader.build(Config(hidden=S.hidden, n_experts=S.n_experts, inter=S.inter, top=S.top,
+                                rot_seed=WL.rot_seed, max_batch=1), L["gate"], L["up"], L["down"])
+        layers.append(L)
+        oracles.append(o)
+        readers.append(r)
+        _log(f"layer {l} ready in {time.time() - t:.1f}s")
+    yield layers, oracles, readers
+    for r in readers:
+        r.close()
+
+
+def test_stack_layers_and_chain(stack):
+    layers, oracles, readers = stack
+    X = make_tokens(WL, 2)
+    for step in range(2):
+        xo = X[step].astype(np.float64)
+        xg = torch.from_numpy(X[step:step + 1].copy()).cuda()
+        for l in range(NL):
+            ids, w, _ = route(layers[l]["router"], xo.astype(np.float32), S.top)
+            ids = ids.astype(np.int32)[None]
+            w = w.astype(np.float32)[None]
+            xin = xo.astype(np.float32)
+            lib = {k: v.cpu().numpy() for k, v in readers[l].decode_debug(
+                torch.from_numpy(xin[None].copy()).cuda(), torch.from_numpy(ids).cuda(),
+                torch.from_numpy(w).cuda(), K).items()}
+            ref = oracles[l].decode(xin, ids[0], w[0], K)
+            err, ndiff = check_token(lib, ref, oracles[l], xin, ids[0], w[0], K)
+            _log(f"step {step} layer {l}: y rel L2 {err:.2e}, swaps {ndiff}")
+            yg = readers[l].decode(xg, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), K)
+            xg = xg + yg
+            xo = xo + ref["y"]
+        d = rel_l2(xg[0].cpu().numpy(), xo)
+        _log(f"step {step}: chain rel L2 after {NL} layers {d:.2e}")
+        assert d < 2e-3
