@@ -140,7 +140,7 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None)
     L = len(readers)
     s = torch.cuda.Stream()
     if Y is None:
-        Y = torch.empty((L, 1, X.shape[-1]), dtype=torch.float32, device=X.device)
+        Y = torch.empty((L, X.shape[1], X.shape[-1]), dtype=torch.float32, device=X.device)
 
     def one_pass():
         for i, r in enumerate(readers):
@@ -297,7 +297,7 @@ def main():
     layer = make_layer(wl)
     log(f"weights generated in {time.time() - t:.1f}s")
     cfg = Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
-                 rank=s.rank, n_screen=s.n_screen, max_batch=1, rot_seed=wl.rot_seed)
+                 rank=s.rank, n_screen=s.n_screen, max_batch=4, rot_seed=wl.rot_seed)
     t = time.time()
     base = Reader.build(cfg, layer["gate"], layer["up"], layer["down"])
     log(f"reader built in {time.time() - t:.1f}s")
@@ -324,6 +324,23 @@ def main():
         dense_us, _, _ = graph_time(torch, readers, X, IDS, W, 0, min(args.steps, 400),
                                     args.warmup, fn="dense")
         log(f"dense BF16 block: {dense_us:.2f} us/token")
+
+    # batch 4 (per-token routing and top-k), the configuration's batched case:
+    # µs per token = µs per call / 4
+    batch4 = {}
+    if not args.main_budget_only:
+        X4 = torch.from_numpy(make_tokens(wl, 4 * L, seed_offset=7).reshape(L, 4, s.hidden)).cuda()
+        I4h, W4h = make_routing_inputs(wl, 4 * L, seed_offset=7)
+        I4 = torch.from_numpy(I4h.reshape(L, 4, s.top)).cuda()
+        W4 = torch.from_numpy(W4h.reshape(L, 4, s.top)).cuda()
+        for k in [k_main] + ([k_low] if k_low else []):
+            us4, _, _ = graph_time(torch, readers, X4, I4, W4, k, min(args.steps, 400), args.warmup)
+            batch4[f"k={k}"] = round(us4 / 4, 3)
+        if not args.no_dense:
+            us4, _, _ = graph_time(torch, readers, X4, I4, W4, 0, min(args.steps, 400), args.warmup,
+                                   fn="dense")
+            batch4["dense"] = round(us4 / 4, 3)
+        log("batch 4, us/token: " + ", ".join(f"{n}={v}" for n, v in batch4.items()))
 
     if args.copy_calibration:
         copy_calibration(torch)
@@ -384,6 +401,7 @@ def main():
                      "kernel": dom, "bytes_per_launch": stage_bytes[dom],
                      "us_per_launch": round(dom_us, 3),
                      "timing": "kernel alone, back to back over the layer copies in a HIP graph"},
+        "batch4_us_per_token": batch4 or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

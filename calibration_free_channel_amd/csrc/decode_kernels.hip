@@ -53,7 +53,6 @@ namespace {
 
 constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
 constexpr float kTwo32 = 4294967296.0f;                // 2^32: fixed-point scale of the screen sums
-constexpr int kCB = 8;  // screened coordinates whose code words are in flight together
 
 __device__ __forceinline__ float f16f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -271,11 +270,13 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int un
   }
 }
 
-template <int NT>
+// NG: threads per code word (a power of two, at most 16), CPB: screened
+// coordinates per thread whose code words are in flight together.
+template <int NT, int NG, int CPB>
 __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
+  static_assert(NG >= 1 && NG <= 16 && (NG & (NG - 1)) == 0, "word groups within a row of lanes");
   __shared__ uint4 lut[256];
   __shared__ int2 rec[128];
-  extern __shared__ __align__(16) float red[];  // [ng][nd * 20]
   CFR_TRACE_PHASE(0, 0);
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
@@ -298,14 +299,18 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   }
   const int e = clamp_expert(a.ids[ts], a.E, a.status);
   CFR_TRACE_PHASE(0, 5);
-  // scales of the channels this thread finalises (used at the end)
+  // thread (d, g) = tid: code word d (channels 20d .. 20d+19 of the half),
+  // lane g of the NG consecutive lanes that share it; after the decode, lane g
+  // finalises channels 20d + g + NG r (r < RPL): their scales, loaded now
   constexpr int MAXJ = kMaxInter / NT;
-  uint16_t al[MAXJ];
+  constexpr int RPL = (20 + NG - 1) / NG;
+  const int d = tid / NG, g = tid & (NG - 1);
   const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
+  uint16_t al[RPL];
 #pragma unroll
-  for (int q = 0; q < MAXJ; ++q) {
-    const int j = tid + q * NT;
-    al[q] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
+  for (int r = 0; r < RPL; ++r) {
+    const int j = 20 * d + g + NG * r;
+    al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
   }
   // routing weight times down-column norm of every channel of this slot, for
   // the score: loaded now by one workgroup per slot, stored at the end
@@ -345,29 +350,29 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   lds_barrier();
   CFR_TRACE_PHASE(0, 1);
 
-  // screen: thread (g, d) takes code word d (channels 20d .. 20d+19 of the
-  // half) at every ng-th screened coordinate starting at g
-  const int ND = a.nd, NG = a.ng;
-  const int g = tid / ND, d = tid - g * ND;
+  // screen: thread (d, g) decodes code word d at screened coordinates
+  // g, g + NG, g + 2 NG, ..., all its words in flight together (CPB at a time)
+  const int ND = a.nd;
+  const bool active = d < ND;
   float acc[20];
 #pragma unroll
   for (int q = 0; q < 20; ++q) acc[q] = 0.f;
-  if (g < NG) {
+  if (active) {
     // uniform base of this (expert, block) and 32-bit per-coordinate offsets
     const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit;
     const uint32_t col = (uint32_t)(m * a.lp + 4 * d);
-    for (int c0 = g; c0 < NS; c0 += NG * kCB) {
-      uint32_t wv[kCB];
-      float xv[kCB];
+    for (int c0 = g; c0 < NS; c0 += NG * CPB) {
+      uint32_t wv[CPB];
+      float xv[CPB];
 #pragma unroll
-      for (int u = 0; u < kCB; ++u) {
+      for (int u = 0; u < CPB; ++u) {
         const int c = c0 + u * NG;
         const int2 rc = rec[c < NS ? c : NS - 1];  // clamped; past the list x = 0
         wv[u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
         xv[u] = c < NS ? __int_as_float(rc.y) : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < kCB; ++u) {
+      for (int u = 0; u < CPB; ++u) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const uint4 cw = lut[(wv[u] >> (8 * kb)) & 0xFFu];
@@ -379,30 +384,46 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
         }
       }
     }
-    CFR_TRACE_PHASE(0, 2);
-    float* my = red + (size_t)g * ND * 20 + d * 20;
-#pragma unroll
-    for (int q = 0; q < 20; q += 4) *reinterpret_cast<float4*>(my + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
   }
-  lds_barrier();
-  CFR_TRACE_PHASE(0, 3);
-  // channel j = 20 d + i sits at red[g][j]: sum the coordinate groups, scale
-  // by alpha_b and add to the fixed-point accumulator
-  unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
+  CFR_TRACE_PHASE(0, 2);
+  // sum over the NG lanes of each word (register butterfly, every lane ends
+  // with the totals), then lane g scales channel 20d + g + NG r by alpha_b
+  // and adds it to the fixed-point accumulator
 #pragma unroll
-  for (int q = 0; q < MAXJ; ++q) {
-    const int j = tid + q * NT;
-    if (j < I) {
-      float S = 0.f;
-      const float* rj = red + j;
-      int gg = 0;
-      for (; gg + 4 <= NG; gg += 4) {  // four LDS reads in flight
-        const float r0 = rj[(size_t)gg * ND * 20], r1 = rj[(size_t)(gg + 1) * ND * 20];
-        const float r2 = rj[(size_t)(gg + 2) * ND * 20], r3 = rj[(size_t)(gg + 3) * ND * 20];
-        S += (r0 + r1) + (r2 + r3);
-      }
-      for (; gg < NG; ++gg) S += rj[(size_t)gg * ND * 20];
-      atomicAdd(ap + j, to_fix(f16f(al[q]) * S));
+  for (int q = 0; q < 20; ++q) {
+    if constexpr (NG > 1) acc[q] += xor_lane_f<1>(acc[q]);
+    if constexpr (NG > 2) acc[q] += xor_lane_f<2>(acc[q]);
+    if constexpr (NG > 4) acc[q] += xor_lane_f<4>(acc[q]);
+    if constexpr (NG > 8) acc[q] += xor_lane_f<8>(acc[q]);
+  }
+  CFR_TRACE_PHASE(0, 3);
+  // Every loaded value is consumed before the first atomic or store: on this
+  // target the in-order memory counter also counts stores and atomics, so a
+  // wait for a load placed after them would wait for them as well.
+  float alf[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    alf[r] = f16f(al[r]);
+    asm volatile("" ::"v"(alf[r]));
+  }
+  float wv[MAXJ];
+  if (wn_writer) {
+#pragma unroll
+    for (int q = 0; q < MAXJ; ++q) {
+      wv[q] = wslot * nw[q];
+      asm volatile("" ::"v"(wv[q]));
+    }
+  }
+  unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      float v = acc[(NG * r < 20) ? NG * r : 19];
+#pragma unroll
+      for (int q = 1; q < NG; ++q)
+        if (NG * r + q < 20) v = g == q ? acc[NG * r + q] : v;
+      const int i = g + NG * r, j = 20 * d + i;
+      if (i < 20 && j < I) atomicAdd(ap + j, to_fix(alf[r] * v));
     }
   }
   if (wn_writer) {
@@ -410,7 +431,7 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
 #pragma unroll
     for (int q = 0; q < MAXJ; ++q) {
       const int j = tid + q * NT;
-      if (j < I) wo[j] = wslot * nw[q];
+      if (j < I) wo[j] = wv[q];
     }
   }
   CFR_TRACE_PHASE(0, 4);
@@ -1253,11 +1274,11 @@ Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
   const int nblk = c.hidden / kBlock, nbytes = (c.inter + 4) / 5, nc = c.top * c.inter;
   // screen
   p.nd = (nbytes + 3) / 4;
-  p.ng = kScreenThreads / p.nd;
-  if (p.ng < 1) p.ng = 1;
+  p.ng = 16;  // threads per code word: a power of two with ng * nd <= threads
+  while (p.ng > 1 && p.ng * p.nd > kScreenThreads) p.ng /= 2;
   p.items1 = batch * c.top * nblk * 2;
   p.per_xcd1 = (p.items1 + 7) / 8;
-  p.lds1 = (size_t)p.ng * p.nd * 20 * 4;
+  p.lds1 = 0;
   // select/gather: about 240 gather workgroups over the batch plus 16
   // recovery workgroups, so the whole grid fits one workgroup per CU
   const SelectGeom g = select_geom(nc);
@@ -1345,14 +1366,21 @@ static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, h
   }
 }
 
-static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    allow_lds(k_screen<kScreenThreads>);
-    attr = true;
-  }
-  k_screen<kScreenThreads><<<8 * p.per_xcd1, kScreenThreads, p.lds1, st>>>(a);
+// coordinates per thread batch: the n_screen = 80 share of one thread
+template <int NG, int CPB>
+static hipError_t launch_screen_t(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+  k_screen<kScreenThreads, NG, CPB><<<8 * p.per_xcd1, kScreenThreads, 0, st>>>(a);
   return hipGetLastError();
+}
+
+static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+  switch (p.ng) {
+    case 16: return launch_screen_t<16, 5>(a, p, st);
+    case 8: return launch_screen_t<8, 10>(a, p, st);
+    case 4: return launch_screen_t<4, 20>(a, p, st);
+    case 2: return launch_screen_t<2, 20>(a, p, st);
+    default: return launch_screen_t<1, 20>(a, p, st);
+  }
 }
 
 static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) {
