@@ -65,7 +65,6 @@ struct cfr_reader {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   unsigned long long* acc = nullptr;  // [B][2][ncp] fixed-point screen sums (gate, up); zero between calls
-  float* wn = nullptr;         // [B][ncp]  routing weight * ||d_j|| per candidate
   float* ypart = nullptr;      // [B][kMaxGatherWgs][H]  partial outputs of the gather workgroups
   float* zpart = nullptr;      // [B][kMaxRecoverWgs][rank]  partial recovery vectors
   float* xrot = nullptr;       // [B][H]   H_128 (sigma x) per block (debug copy only)

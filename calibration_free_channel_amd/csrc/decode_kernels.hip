@@ -202,7 +202,6 @@ struct ScreenArgs {
   const uint16_t* scales;
   const float* norms;
   unsigned long long* acc;
-  float* wn;
   float* xrot;
   uint8_t* sel;
   int32_t* status;
@@ -302,7 +301,6 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   // thread (d, g) = tid: code word d (channels 20d .. 20d+19 of the half),
   // lane g of the NG consecutive lanes that share it; after the decode, lane g
   // finalises channels 20d + g + NG r (r < RPL): their scales, loaded now
-  constexpr int MAXJ = kMaxInter / NT;
   constexpr int RPL = (20 + NG - 1) / NG;
   const int d = tid / NG, g = tid & (NG - 1);
   const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
@@ -312,17 +310,16 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     const int j = 20 * d + g + NG * r;
     al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
   }
-  // routing weight times down-column norm of every channel of this slot, for
-  // the score: loaded now by one workgroup per slot, stored at the end
-  const bool wn_writer = b == 0 && m == 1;
-  float nw[MAXJ];
-  float wslot = 0.f;
-  if (wn_writer) {
-    wslot = a.gw[ts];
+  // the up half carries ||d_j|| into its sums (v_hat' = ||d_j|| v_hat), so the
+  // score needs no per-candidate norm read later: those norms, loaded now
+  float nrm[RPL];
 #pragma unroll
-    for (int q = 0; q < MAXJ; ++q) {
-      const int j = tid + q * NT;
-      nw[q] = a.norms[(size_t)e * I + (j < I ? j : I - 1)];
+  for (int r = 0; r < RPL; ++r) nrm[r] = 1.f;
+  if (m == 1) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int j = 20 * d + g + NG * r;
+      nrm[r] = a.norms[(size_t)e * I + (j < I ? j : I - 1)];
     }
   }
   // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
@@ -403,16 +400,8 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   float alf[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    alf[r] = f16f(al[r]);
+    alf[r] = f16f(al[r]) * nrm[r];
     asm volatile("" ::"v"(alf[r]));
-  }
-  float wv[MAXJ];
-  if (wn_writer) {
-#pragma unroll
-    for (int q = 0; q < MAXJ; ++q) {
-      wv[q] = wslot * nw[q];
-      asm volatile("" ::"v"(wv[q]));
-    }
   }
   unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
   if (active) {
@@ -424,14 +413,6 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
         if (NG * r + q < 20) v = g == q ? acc[NG * r + q] : v;
       const int i = g + NG * r, j = 20 * d + i;
       if (i < 20 && j < I) atomicAdd(ap + j, to_fix(alf[r] * v));
-    }
-  }
-  if (wn_writer) {
-    float* wo = a.wn + (size_t)t * a.ncp + (size_t)s * I;
-#pragma unroll
-    for (int q = 0; q < MAXJ; ++q) {
-      const int j = tid + q * NT;
-      if (j < I) wo[j] = wv[q];
     }
   }
   CFR_TRACE_PHASE(0, 4);
@@ -447,7 +428,7 @@ struct SelectArgs {
   const uint16_t* w3;
   const uint16_t* bmat;
   const unsigned long long* acc;
-  const float* wn;
+  const float* norms;  // ||d_j|| [E][I]
   float* ypart;
   float* zpart;
   float* ghat;   // debug outputs (written by workgroup 0 of each token when dbg)
@@ -456,7 +437,8 @@ struct SelectArgs {
   int32_t* kept;
   int32_t* status;
   int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dense, dbg;
-  float invI;  // 1 / I rounded to float (exact slot division below 2^17)
+  float invI;   // 1 / I rounded to float (exact slot division below 2^17)
+  int cps_mul;  // I % 128 == 0: ceil(2^16 / (I / 128)), else 0
 };
 
 // misc slots
@@ -483,15 +465,16 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Output-unit score of one candidate from its fixed-point screen sums and
-// w ||d||: sets g_hat, v_hat, p = silu(g_hat) v_hat and s = w ||d|| |p|, and
-// returns the order-preserving key of s.
-__device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned long long v, float wn,
+// Output-unit score of one candidate from its fixed-point screen sums (the
+// up sum carries ||d_j||) and routing weight w: sets g_hat, v_hat' = ||d_j||
+// v_hat, p' = silu(g_hat) v_hat' = ||d_j|| p and s = w |p'| = w ||d_j|| |p|,
+// and returns the order-preserving key of s.
+__device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned long long v, float w,
                                               float& gh, float& vh, float& p, float& sc) {
   gh = from_fix(g) * kInvSqrt128f;
   vh = from_fix(v) * kInvSqrt128f;
   p = silu(gh) * vh;
-  sc = wn * fabsf(p);
+  sc = w * fabsf(p);
   return order_key(sc);
 }
 
@@ -619,17 +602,25 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   // screen sums and w ||d|| of this thread's candidate pairs, routing, the
   // token.  Pair P = i NT + tid holds candidates 2P and 2P + 1. ----
   static_assert(kMaxHidden <= 2 * NT * 4, "the token is two float4 per thread at most");
+  // the token's routing weights first, lane s holding slot s's (for the
+  // scores): loads complete in issue order, so waiting for these must not
+  // wait for the screen sums issued after them
+  const float gwl = a.gw[t * a.top + min(lane, a.top - 1)];
+  // (issued on every path, as buffer loads that the dense mode points past
+  // the end: a load on one path only would make every later wait on the
+  // other path conservative)
   ulonglong2 gq[P2], vq[P2];
   float2 wq[P2];
-  if (!a.dense) {
-    const ulonglong2* ag = reinterpret_cast<const ulonglong2*>(a.acc + (size_t)t * 2 * a.ncp);
-    const ulonglong2* av = reinterpret_cast<const ulonglong2*>(a.acc + ((size_t)t * 2 + 1) * a.ncp);
-    const float2* wp = reinterpret_cast<const float2*>(a.wn + (size_t)t * a.ncp);
+  {
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a.acc + (size_t)t * 2 * a.ncp, (uint32_t)(a.ncp * 16));
+    const uint32_t vofs = (uint32_t)a.ncp * 8u;
 #pragma unroll
     for (int i = 0; i < P2; ++i) {
-      gq[i] = ag[i * NT + tid];
-      vq[i] = av[i * NT + tid];
-      wq[i] = wp[i * NT + tid];
+      const uint32_t o = a.dense ? kNoLoad : (uint32_t)(i * NT + tid) * 16u;
+      const auto g4 = __builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0);
+      const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + vofs, 0, 0);
+      gq[i] = make_ulonglong2(((unsigned long long)g4[1] << 32) | g4[0], ((unsigned long long)g4[3] << 32) | g4[2]);
+      vq[i] = make_ulonglong2(((unsigned long long)v4[1] << 32) | v4[0], ((unsigned long long)v4[3] << 32) | v4[2]);
     }
   }
   const int rslot = tid < a.top ? tid : a.top - 1;
@@ -649,7 +640,19 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   uint32_t kmax = 0u;
   if (!a.dense) {
 #pragma unroll
-    for (int i = 0; i < P2; ++i)
+    for (int i = 0; i < P2; ++i) {
+      if (a.cps_mul) {
+        // I a multiple of 128: the wave's 128 candidates of pair slot i (chunk
+        // q = i NW + wave) lie in routed slot q / (I / 128), scalar arithmetic
+        const int q = i * NW + wave;
+        const int sl = min((q * a.cps_mul) >> 16, a.top - 1);
+        const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwl), sl));
+        wq[i] = make_float2(wv, wv);
+      } else {
+        const int c2 = 2 * (i * NT + tid);
+        wq[i] = make_float2(__shfl(gwl, min(slot_of(c2), a.top - 1)),
+                            __shfl(gwl, min(slot_of(c2 + 1), a.top - 1)));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float gh, vh, p, sc;
@@ -660,12 +663,8 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         key[2 * i + j] = kv;
         pr[2 * i + j] = p;
         kmax = max(kmax, kv);
-        if (dbgw && c < nc) {
-          a.ghat[(size_t)t * nc + c] = gh;
-          a.vhat[(size_t)t * nc + c] = vh;
-          a.score[(size_t)t * nc + c] = sc;
-        }
       }
+    }
     kmax = wave_max_u32(kmax);
   }
   if (lane == 0) misc[kMiscMax + wave] = (int)kmax;
@@ -676,6 +675,20 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   if (tid == 0) misc[kMiscSlot] = 0;
   lds_barrier();
   CFR_TRACE_PHASE(1, 1);
+  if (dbgw && !a.dense) {
+    // debug copies of g_hat, v_hat and the scores: a separate pass that reads
+    // the sums again (kept out of the loop above, whose loads it would stall)
+    for (int c = tid; c < nc; c += NT) {
+      const int sl = slot_of(c);
+      float gh, vh, p, sc;
+      score_key(a.acc[(size_t)t * 2 * a.ncp + c], a.acc[((size_t)t * 2 + 1) * a.ncp + c], sl_w[sl], gh, vh,
+                p, sc);
+      const float nd = a.norms[(size_t)sl_e[sl] * I + (c - sl * I)];
+      a.ghat[(size_t)t * nc + c] = gh;
+      a.vhat[(size_t)t * nc + c] = nd > 0.f ? vh / nd : 0.f;
+      a.score[(size_t)t * nc + c] = sc;
+    }
+  }
 
   // ---- exact top-k ----
   // Distance below the largest key M, d = M - key: a smaller d is a larger
@@ -737,6 +750,11 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
     return (uint32_t)((((size_t)sl_e[sl] * I + (cc - sl * I)) * a.rank + zr8 * 8) * 2);
   };
   uint4 zb[4];
+  float zn[4];  // ||d_j|| of the first-pass candidates (p = p' / ||d_j||)
+  auto norm_of = [&](int cc) {
+    const int sl = slot_of(cc);
+    return a.norms[(size_t)sl_e[sl] * I + (cc - sl * I)];
+  };
 
   const bool fast = partial && cnt <= kDirectMax;
   if (fast) {
@@ -759,6 +777,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         const bool ld = cnd < zcb1 && zr8 < R8 && (dl[cc] >> kBinShift) >= (uint32_t)bstar;
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, ld ? brow(cc) : kNoLoad, 0, 0);
         zb[u] = make_uint4(v[0], v[1], v[2], v[3]);
+        zn[u] = norm_of(cc);
       }
       asm volatile("" ::: "memory");  // keeps the requests here, ahead of the barriers below
     }
@@ -967,6 +986,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
         const bool ld = cnd < zcb1 && zr8 < R8 && !flags[cc];
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, ld ? brow(cc) : kNoLoad, 0, 0);
         zb[u] = make_uint4(v[0], v[1], v[2], v[3]);
+        zn[u] = norm_of(cc);
       }
     }
   }
@@ -1123,11 +1143,15 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       zacc[2 * d + 1] = fmaf(cf, hi16(bw[d]), zacc[2 * d + 1]);
     }
   };
+  // w p_j b_j with p_j = p'_j / ||d_j|| (a zero norm means b_j = U^T d_j = 0)
+  auto coef = [&](bool skip, int cc, float nd) {
+    return (skip && nd > 0.f) ? sl_w[slot_of(cc)] * (pvl[cc] / nd) : 0.f;
+  };
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int cnd = zcb0 + zcl + u * zcpp;
     const int cc = min(cnd, max(zcb1 - 1, 0));
-    zadd(zb[u], (cnd < zcb1 && !flags[cc]) ? sl_w[slot_of(cc)] * pvl[cc] : 0.f);
+    zadd(zb[u], coef(cnd < zcb1 && !flags[cc], cc, zn[u]));
   }
   CFR_TRACE_PHASE(1, 4);
   for (int cb = zcb0 + zcl + 4 * zcpp; cb < zcb1; cb += 4 * zcpp) {
@@ -1140,7 +1164,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       const bool skip = cnd < zcb1 && !flags[cc];
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(brs, (skip && zr8 < R8) ? brow(cc) : kNoLoad, 0, 0);
       bq[u] = make_uint4(v[0], v[1], v[2], v[3]);
-      cf[u] = skip ? sl_w[slot_of(cc)] * pvl[cc] : 0.f;
+      cf[u] = coef(skip, cc, norm_of(cc));
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) zadd(bq[u], cf[u]);
@@ -1265,6 +1289,14 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
 // ===========================================================================
 // host side
 // ===========================================================================
+// Multiplier m with floor(q / (I / 128)) == (q m) >> 16 for the chunk
+// indices q < 2048 used here (I / 128 <= 32); 0 when I is not a multiple of 128.
+static int cps_mul(int inter) {
+  if (inter % 128) return 0;
+  const int cps = inter / 128;
+  return (65536 + cps - 1) / cps;
+}
+
 static int hip_fail(hipError_t e, const char* what) {
   return fail(CFR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -1397,15 +1429,16 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   };
   hipError_t e;
   mark(0);
-  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->acc, r->wn, r->xrot,
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->acc, r->xrot,
                r->sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
                c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr};
   if (only < 0 || only == 0)
     if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
-  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, r->ghat, r->vhat,
+  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->ypart, r->zpart, r->ghat, r->vhat,
                r->score, r->kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
-               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter};
+               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter,
+               cps_mul(c.inter)};
   if (only < 0 || only == 1)
     if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
@@ -1439,9 +1472,9 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   const cfr_config& c = r->cfg;
   const int nc = r->ncand;
   const Plan p = make_plan(c, batch, nc, true);
-  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->wn, r->ypart, r->zpart, nullptr, nullptr,
+  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->ypart, r->zpart, nullptr, nullptr,
                nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
-               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter};
+               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter)};
   hipError_t e;
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, 0, c.rank, r->ncp,
