@@ -182,6 +182,13 @@ __device__ __forceinline__ int block_scan(int v, int* sh) {
   return v + add;
 }
 
+// Buffer resource over `bytes` bytes at p (gfx9 layout): a raw buffer load at
+// an offset past the end returns zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kNoLoad = 0x80000000u;  // offset past the end of any buffer here
+
 // Dispatch places workgroup i on XCD i % 8; item (i % 8) * per_xcd + i / 8
 // gives each XCD a contiguous range of items (performance only).
 __device__ __forceinline__ int xcd_item(int id, int per_xcd) {
@@ -245,11 +252,16 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int un
   }
   const uint32_t k0 = __float_as_uint(v0) & 0x7FFFFFFFu;
   const uint32_t k1 = __float_as_uint(v1) & 0x7FFFFFFFu;
+  // Once exactly NS magnitudes are >= a prefix, those NS are the kept set
+  // (every later T lies between that prefix and their minimum), so the search
+  // stops there.
   uint32_t T = 0;
+#pragma unroll
   for (int bit = 30; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
     if (cnt >= NS) T = cand;
+    if (cnt == NS) break;
   }
   const unsigned long long lt = (1ull << lane) - 1ull;
   const unsigned long long gt0 = __ballot(k0 > T), gt1 = __ballot(k1 > T);
@@ -478,12 +490,6 @@ __device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned lon
   return order_key(sc);
 }
 
-// Buffer resource over `bytes` bytes at p (gfx9 layout): a raw buffer load at
-// an offset past the end returns zeros without a memory access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-constexpr uint32_t kNoLoad = 0x80000000u;  // offset past the end of any buffer here
 
 // One wave finds the bin where the running count over bins 0, 1, ... first
 // reaches need (need >= 1 and at most the total count), and writes the bin,
