@@ -30,6 +30,8 @@ from .dense import dense_moe
 from .route import route
 from .topk import topk_desc
 from .accounting import read_bytes, resident_bytes
+from .expected_error import (silu_grad, block_norms2, sketch_variance, activation_variance,
+                             expected_error_score)
 from .reader import OracleReader
 
 __all__ = [
@@ -37,5 +39,6 @@ __all__ = [
     "sign_vector", "sylvester_hadamard", "rotate_rows", "rotate_x_f64",
     "rotate_x_f32_unscaled", "rotation_matrix", "SQRT128", "ternarize_blocks",
     "unit_geometry", "pack_units", "unpack_units", "recovery_basis", "dense_moe",
-    "route", "topk_desc", "read_bytes", "resident_bytes", "OracleReader",
+    "route", "topk_desc", "read_bytes", "resident_bytes", "OracleReader", "silu_grad",
+    "block_norms2", "sketch_variance", "activation_variance", "expected_error_score",
 ]

@@ -12,6 +12,8 @@ Per token and layer the reader touches, in whole 32-B sectors:
   codes   top * nblk * n_screen units (one unit per screened coordinate)
   scales  top * nblk pieces of 2*I fp16 (gate and up scales of one block)
   norms   top pieces of I fp32
+  rho     top * nblk pieces of 2*I fp16, only for the expected-error ranking
+          of budgets from 28.7% on ([zh §方法步骤详情] decode step (2))
   exact   k channels * 3 rows of H bf16 (gate row, up row, transposed down row)
   b       (top*I - k) skipped channels * rank fp16
   U       H * rank fp16
@@ -27,18 +29,19 @@ def _sect(nbytes: int) -> int:
     return -(-nbytes // 32) * 32
 
 
-def read_bytes(hidden, inter, top, k, rank=32, n_screen=80, block=128):
+def read_bytes(hidden, inter, top, k, rank=32, n_screen=80, block=128, rho=False):
     nblk = hidden // block
     _, unit = unit_geometry(inter)
     r = {
         "codes": top * nblk * n_screen * _sect(unit),
         "scales": top * nblk * _sect(2 * inter * 2),
+        "rho": top * nblk * _sect(2 * inter * 2) if rho else 0,
         "norms": top * _sect(inter * 4),
         "exact": k * _sect(3 * hidden * 2),
         "b": (top * inter - k) * _sect(rank * 2),
         "U": _sect(hidden * rank * 2),
     }
-    r["sketch"] = r["codes"] + r["scales"] + r["norms"]
+    r["sketch"] = r["codes"] + r["scales"] + r["rho"] + r["norms"]
     r["recovery"] = r["b"] + r["U"]
     r["total"] = r["sketch"] + r["exact"] + r["recovery"]
     r["dense"] = top * 3 * inter * hidden * 2

@@ -15,7 +15,9 @@ Decode, per token and layer ([zh §方法步骤详情] decode steps (1)-(4);
       g_hat_j ~= g_j^T x and v_hat_j ~= v_j^T x from codes and scales;
   (2) score every candidate channel of the routed experts in output units,
       s_j = w_j ||d_j|| |phi(g_hat_j) v_hat_j|, and keep exactly the top k
-      across all routed experts;
+      across all routed experts; from the 28.7% budget on, read the whole
+      sketch and rank by the expected squared output error of skipping, with
+      rho_b (``ranking="expected_error"``, module expected_error);
   (3) for kept channels read the native BF16 rows: a_j = phi(g_j^T x)(v_j^T x),
       output part one = sum_K w_j a_j d_j;
   (4) output part two = U sum_S w_j b_j p_j over the skipped channels S, with
@@ -52,6 +54,7 @@ from .lowrank import recovery_basis
 from .dense import silu
 from .topk import topk_desc
 from .route import route as _route
+from .expected_error import block_norms2, sketch_variance, expected_error_score
 
 DEFAULT_ROT_SEED = 0x5EED_0000_CAFE_F00D
 
@@ -84,6 +87,7 @@ class OracleReader:
                 if self.rot_rows is not None:
                     self.rot_rows[e, m] = (u / np.sqrt(128.0)).transpose(1, 2, 0)
         self.alpha = f16_bits_to_f64(self.alpha_bits)
+        self.rho = f16_bits_to_f64(self.rho_bits)
         self.units = pack_units(self.codes[:, 0], self.codes[:, 1])  # [E][nb][128][unit]
 
         # load step (2): down-column norms, summed over h in index order
@@ -132,8 +136,12 @@ class OracleReader:
                 est[m, s] = acc
         return est[0], est[1]
 
-    def decode(self, x, ids, w, k, kept=None):
-        """One token.  Returns a dict of every intermediate and y (float64 [H])."""
+    def decode(self, x, ids, w, k, kept=None, ranking="score"):
+        """One token.  Returns a dict of every intermediate and y (float64 [H]).
+
+        ranking="score": the output-unit score s_j (budgets below 28.7%);
+        ranking="expected_error": e_j from the whole sketch and rho
+        (n_screen must be 128); "score" then holds e_j."""
         H, I = self.H, self.I
         ids = np.asarray(ids, dtype=np.int64)
         w = np.asarray(w, dtype=np.float32).astype(np.float64)
@@ -141,7 +149,17 @@ class OracleReader:
         v32, sel = self.select(x)
         ghat, vhat = self.screen(x, ids, sel)
         p = silu(ghat) * vhat
-        score = w[:, None] * self.norms[ids].astype(np.float64) * np.abs(p)
+        dn = self.norms[ids].astype(np.float64)
+        if ranking == "score":
+            score = w[:, None] * dn * np.abs(p)
+        elif ranking == "expected_error":
+            assert self.n_screen == self.block, "expected-error ranking reads the whole sketch"
+            xb2 = block_norms2(x, self.block)
+            var_g = sketch_variance(self.rho[ids, :, 0, :].transpose(0, 2, 1), xb2)
+            var_v = sketch_variance(self.rho[ids, :, 1, :].transpose(0, 2, 1), xb2)
+            score = expected_error_score(ghat, vhat, var_g, var_v, w[:, None], dn)
+        else:
+            raise ValueError(f"unknown ranking {ranking!r}")
         flat = score.reshape(-1)
         kk = topk_desc(flat, k) if kept is None else np.sort(np.asarray(kept, dtype=np.int64))
         mask = np.zeros(flat.shape[0], dtype=bool)
@@ -164,8 +182,8 @@ class OracleReader:
                 "score": score, "kept": kk, "a": a, "y_exact": y_exact, "z": z,
                 "y_rec": y_rec, "y": y_exact + y_rec}
 
-    def decode_batch(self, X, IDS, W, k, kept=None):
-        outs = [self.decode(X[t], IDS[t], W[t], k, None if kept is None else kept[t])
+    def decode_batch(self, X, IDS, W, k, kept=None, ranking="score"):
+        outs = [self.decode(X[t], IDS[t], W[t], k, None if kept is None else kept[t], ranking)
                 for t in range(X.shape[0])]
         return outs
 
