@@ -14,7 +14,7 @@ CFR_OK, CFR_EINVAL, CFR_ENOMEM, CFR_EHIP, CFR_EUNSUPPORTED, CFR_ESOLVER = 0, -1,
 class CfrConfig(ctypes.Structure):
     _fields_ = [("hidden", c_int32), ("n_experts", c_int32), ("inter", c_int32), ("top", c_int32),
                 ("rank", c_int32), ("n_screen", c_int32), ("max_batch", c_int32),
-                ("device", c_int32), ("rot_seed", c_uint64)]
+                ("device", c_int32), ("rot_seed", c_uint64), ("ranking", c_int32)]
 
 
 class CfrSizes(ctypes.Structure):
@@ -25,8 +25,9 @@ class CfrSizes(ctypes.Structure):
 
 
 class CfrReadStats(ctypes.Structure):
-    _fields_ = [("codes", c_int64), ("scales", c_int64), ("norms", c_int64), ("exact", c_int64),
-                ("b", c_int64), ("u", c_int64), ("total", c_int64), ("dense", c_int64)]
+    _fields_ = [("codes", c_int64), ("scales", c_int64), ("norms", c_int64), ("rho", c_int64),
+                ("exact", c_int64), ("b", c_int64), ("u", c_int64), ("total", c_int64),
+                ("dense", c_int64)]
 
 
 _P = c_void_p

@@ -45,7 +45,7 @@ struct WorkspaceLayout {
       o += rnd(bytes);
       return at;
     };
-    acc = take(sizeof(unsigned long long) * B * 2 * r.ncp);
+    acc = take(sizeof(unsigned long long) * B * (c.ranking == CFR_RANK_EXPECTED_ERROR ? 4 : 2) * r.ncp);
     ypart = take(sizeof(float) * kMaxGatherWgs * H);
     zpart = take(sizeof(float) * B * kMaxRecoverWgs * R);
     xrot = take(sizeof(float) * B * H);

@@ -36,6 +36,10 @@ int validate_config(const cfr_config* c) {
   if (c->max_batch < 1) return fail(CFR_EINVAL, "max_batch must be at least 1");
   if (c->max_batch > kMaxBatch) return fail(CFR_EUNSUPPORTED, "max_batch above 64");
   if (c->device < 0) return fail(CFR_EINVAL, "device must be non-negative");
+  if (c->ranking != CFR_RANK_SCORE && c->ranking != CFR_RANK_EXPECTED_ERROR)
+    return fail(CFR_EINVAL, "ranking must be CFR_RANK_SCORE or CFR_RANK_EXPECTED_ERROR");
+  if (c->ranking == CFR_RANK_EXPECTED_ERROR && c->n_screen != kBlock)
+    return fail(CFR_EINVAL, "the expected-error ranking reads the whole sketch: n_screen must be 128");
   return CFR_OK;
 }
 
@@ -76,10 +80,11 @@ int cfr_read_bytes(const cfr_config* c, int32_t k, cfr_read_stats* out) {
   out->codes = top * nblk * c->n_screen * sect(unit_bytes(c->inter));
   out->scales = top * nblk * sect(2 * I * 2);
   out->norms = top * sect(I * 4);
+  out->rho = c->ranking == CFR_RANK_EXPECTED_ERROR ? top * nblk * sect(2 * I * 2) : 0;
   out->exact = (int64_t)k * sect(3 * H * 2);
   out->b = (top * I - k) * sect((int64_t)c->rank * 2);
   out->u = sect(H * (int64_t)c->rank * 2);
-  out->total = out->codes + out->scales + out->norms + out->exact + out->b + out->u;
+  out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
   out->dense = top * 3 * I * H * 2;
   return CFR_OK;
 }

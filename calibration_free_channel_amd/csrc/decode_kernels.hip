@@ -208,11 +208,13 @@ struct ScreenArgs {
   const uint8_t* codes;
   const uint16_t* scales;
   const float* norms;
+  const uint16_t* rho;  // [E][nblk][2][I] fp16 (expected-error ranking only)
   unsigned long long* acc;
   float* xrot;
   uint8_t* sel;
   int32_t* status;
   int H, E, I, top, ncp, nblk, ns, lp, unit, nd, ng, items, per_xcd, dbg;
+  int nacc;  // accumulator rows per token: 2 (gate, up sums) or 4 (then their sketch variances)
 };
 
 // Wave 0 rotates one 128-block held as two values per lane (lane l holds
@@ -282,12 +284,16 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int un
 }
 
 // NG: threads per code word (a power of two, at most 16), CPB: screened
-// coordinates per thread whose code words are in flight together.
-template <int NT, int NG, int CPB>
+// coordinates per thread whose code words are in flight together.  VAR (the
+// expected-error ranking, whole sketch): also add rho_b ||x_b||^2 per channel
+// (times ||d_j||^2 for the up half) into the variance rows of the
+// accumulator, the sketch-error variance of g_hat and of v_hat'.
+template <int NT, int NG, int CPB, bool VAR>
 __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   static_assert(NG >= 1 && NG <= 16 && (NG & (NG - 1)) == 0, "word groups within a row of lanes");
   __shared__ uint4 lut[256];
   __shared__ int2 rec[128];
+  __shared__ float xn2;  // ||x_b||^2 (VAR)
   CFR_TRACE_PHASE(0, 0);
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
@@ -322,6 +328,15 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     const int j = 20 * d + g + NG * r;
     al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
   }
+  uint16_t rh[RPL];
+  if constexpr (VAR) {
+    const uint16_t* rp = a.rho + (((size_t)e * a.nblk + b) * 2 + m) * I;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int j = 20 * d + g + NG * r;
+      rh[r] = rp[j < I ? j : I - 1];
+    }
+  }
   // the up half carries ||d_j|| into its sums (v_hat' = ||d_j|| v_hat), so the
   // score needs no per-candidate norm read later: those norms, loaded now
   float nrm[RPL];
@@ -351,10 +366,15 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   }
   // decode step (1): rotation and the partial-screen coordinates
   const bool writer = a.dbg && s == 0 && m == 0;
-  if (tid < 64)
+  if (tid < 64) {
     rotate_select(x0 * g0, x1 * g1, NS, a.unit, rec,
                   writer ? a.sel + ((size_t)t * a.nblk + b) * NS : nullptr,
                   writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
+    if constexpr (VAR) {
+      const float q = wave_sum(x0 * x0 + x1 * x1);
+      if (lane == 0) xn2 = q;
+    }
+  }
   CFR_TRACE_PHASE(0, 6);
   lds_barrier();
   CFR_TRACE_PHASE(0, 1);
@@ -409,13 +429,18 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   // Every loaded value is consumed before the first atomic or store: on this
   // target the in-order memory counter also counts stores and atomics, so a
   // wait for a load placed after them would wait for them as well.
-  float alf[RPL];
+  float alf[RPL], vt[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     alf[r] = f16f(al[r]) * nrm[r];
     asm volatile("" ::"v"(alf[r]));
+    if constexpr (VAR) {
+      vt[r] = f16f(rh[r]) * xn2 * (m == 1 ? nrm[r] * nrm[r] : 1.f);
+      asm volatile("" ::"v"(vt[r]));
+    }
   }
-  unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
+  unsigned long long* ap = a.acc + ((size_t)t * a.nacc + m) * a.ncp + (size_t)s * I;
+  unsigned long long* vp = ap + 2 * (size_t)a.ncp;  // the variance rows (VAR)
   if (active) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
@@ -424,7 +449,10 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
       for (int q = 1; q < NG; ++q)
         if (NG * r + q < 20) v = g == q ? acc[NG * r + q] : v;
       const int i = g + NG * r, j = 20 * d + i;
-      if (i < 20 && j < I) atomicAdd(ap + j, to_fix(alf[r] * v));
+      if (i < 20 && j < I) {
+        atomicAdd(ap + j, to_fix(alf[r] * v));
+        if constexpr (VAR) atomicAdd(vp + j, to_fix(vt[r]));
+      }
     }
   }
   CFR_TRACE_PHASE(0, 4);
@@ -451,6 +479,7 @@ struct SelectArgs {
   int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dense, dbg;
   float invI;   // 1 / I rounded to float (exact slot division below 2^17)
   int cps_mul;  // I % 128 == 0: ceil(2^16 / (I / 128)), else 0
+  int nacc;     // accumulator rows per token (2, or 4 with the sketch variances)
 };
 
 // misc slots
@@ -487,6 +516,25 @@ __device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned lon
   vh = from_fix(v) * kInvSqrt128f;
   p = silu(gh) * vh;
   sc = w * fabsf(p);
+  return order_key(sc);
+}
+
+// The expected-error ranking ([zh §方法步骤详情] decode step (2), budgets from
+// 28.7%): with the sketch-error variances of g_hat and of v_hat' (the
+// latter carrying ||d_j||^2), the first-order variance of the activation
+// Var[a'] = (phi'(g_hat) v_hat')^2 var_g + phi(g_hat)^2 var_v' and
+// e = w sqrt(p'^2 + Var[a']) = w ||d_j|| sqrt(p^2 + Var[a]); returns its key.
+__device__ __forceinline__ uint32_t error_key(unsigned long long g, unsigned long long v,
+                                              unsigned long long vg, unsigned long long vv, float w,
+                                              float& gh, float& vh, float& p, float& sc) {
+  gh = from_fix(g) * kInvSqrt128f;
+  vh = from_fix(v) * kInvSqrt128f;
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gh));  // sigma(g_hat)
+  const float phi = gh * sg;
+  const float dphi = sg * (1.0f + gh * (1.0f - sg));
+  p = phi * vh;
+  const float t = dphi * vh;
+  sc = w * sqrtf(p * p + t * t * from_fix(vg) + phi * phi * from_fix(vv));
   return order_key(sc);
 }
 
@@ -566,7 +614,9 @@ __device__ __forceinline__ void write_kept_debug(const bool (&f)[PER], int* wc, 
   }
 }
 
-template <int NT, int PER, int NCH>
+// VAR: rank by the expected squared error of skipping (error_key) instead of
+// the output-unit score.
+template <int NT, int PER, int NCH, bool VAR>
 __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NW = NT / 64, P2 = PER / 2;
@@ -615,18 +665,24 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   // (issued on every path, as buffer loads that the dense mode points past
   // the end: a load on one path only would make every later wait on the
   // other path conservative)
-  ulonglong2 gq[P2], vq[P2];
+  ulonglong2 gq[P2], vq[P2], gvq[VAR ? P2 : 1], vvq[VAR ? P2 : 1];
   float2 wq[P2];
   {
-    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a.acc + (size_t)t * 2 * a.ncp, (uint32_t)(a.ncp * 16));
+    const __amdgpu_buffer_rsrc_t ars =
+        buffer_rsrc(a.acc + (size_t)t * a.nacc * a.ncp, (uint32_t)(a.nacc * a.ncp * 8));
     const uint32_t vofs = (uint32_t)a.ncp * 8u;
+    auto u64x2 = [](const decltype(__builtin_amdgcn_raw_buffer_load_b128(ars, 0u, 0, 0))& q) {
+      return make_ulonglong2(((unsigned long long)q[1] << 32) | q[0], ((unsigned long long)q[3] << 32) | q[2]);
+    };
 #pragma unroll
     for (int i = 0; i < P2; ++i) {
       const uint32_t o = a.dense ? kNoLoad : (uint32_t)(i * NT + tid) * 16u;
-      const auto g4 = __builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0);
-      const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + vofs, 0, 0);
-      gq[i] = make_ulonglong2(((unsigned long long)g4[1] << 32) | g4[0], ((unsigned long long)g4[3] << 32) | g4[2]);
-      vq[i] = make_ulonglong2(((unsigned long long)v4[1] << 32) | v4[0], ((unsigned long long)v4[3] << 32) | v4[2]);
+      gq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0));
+      vq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + vofs, 0, 0));
+      if constexpr (VAR) {
+        gvq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + 2 * vofs, 0, 0));
+        vvq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + 3 * vofs, 0, 0));
+      }
     }
   }
   const int rslot = tid < a.top ? tid : a.top - 1;
@@ -662,8 +718,13 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         float gh, vh, p, sc;
-        const uint32_t k0 = score_key(j ? gq[i].y : gq[i].x, j ? vq[i].y : vq[i].x, j ? wq[i].y : wq[i].x,
-                                      gh, vh, p, sc);
+        uint32_t k0;
+        if constexpr (VAR)
+          k0 = error_key(j ? gq[i].y : gq[i].x, j ? vq[i].y : vq[i].x, j ? gvq[i].y : gvq[i].x,
+                         j ? vvq[i].y : vvq[i].x, j ? wq[i].y : wq[i].x, gh, vh, p, sc);
+        else
+          k0 = score_key(j ? gq[i].y : gq[i].x, j ? vq[i].y : vq[i].x, j ? wq[i].y : wq[i].x, gh, vh, p,
+                         sc);
         const int c = 2 * (i * NT + tid) + j;
         const uint32_t kv = c < nc ? k0 : 0u;
         key[2 * i + j] = kv;
@@ -687,8 +748,11 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
     for (int c = tid; c < nc; c += NT) {
       const int sl = slot_of(c);
       float gh, vh, p, sc;
-      score_key(a.acc[(size_t)t * 2 * a.ncp + c], a.acc[((size_t)t * 2 + 1) * a.ncp + c], sl_w[sl], gh, vh,
-                p, sc);
+      const unsigned long long* at = a.acc + (size_t)t * a.nacc * a.ncp + c;
+      if constexpr (VAR)
+        error_key(at[0], at[a.ncp], at[2 * (size_t)a.ncp], at[3 * (size_t)a.ncp], sl_w[sl], gh, vh, p, sc);
+      else
+        score_key(at[0], at[a.ncp], sl_w[sl], gh, vh, p, sc);
       const float nd = a.norms[(size_t)sl_e[sl] * I + (c - sl * I)];
       a.ghat[(size_t)t * nc + c] = gh;
       a.vhat[(size_t)t * nc + c] = nd > 0.f ? vh / nd : 0.f;
@@ -1212,6 +1276,7 @@ struct ReduceArgs {
   float* y;
   unsigned long long* acc;
   int H, G, Z, rank, ncp, nslices, clear;
+  int nacc;  // accumulator rows per token to clear
 };
 
 constexpr int kReduceThreads = 256;
@@ -1281,9 +1346,10 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
   }
   CFR_TRACE_PHASE(2, 2);
   if (a.clear) {
-    // the screen accumulators of this token (gate then up, ncp each), split
+    // the screen accumulators of this token (gate then up sums, then the
+    // variances when ranked by expected error; ncp each), split
     // over its slices
-    const int n = 2 * a.ncp;
+    const int n = a.nacc * a.ncp;
     const int per = (n + a.nslices - 1) / a.nslices;
     const int b0 = sl * per, b1 = min(b0 + per, n);
     ulonglong2* ap = reinterpret_cast<ulonglong2*>(a.acc + (size_t)t * n);
@@ -1370,55 +1436,67 @@ static void allow_lds(K kernel) {
   (void)hipGetLastError();
 }
 
-template <int NT, int PER, int NCH>
+template <int NT, int PER, int NCH, bool VAR>
 static hipError_t launch_select_t(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    allow_lds(k_select<NT, PER, NCH>);
+    allow_lds(k_select<NT, PER, NCH, VAR>);
     attr = true;
   }
-  k_select<NT, PER, NCH><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
+  k_select<NT, PER, NCH, VAR><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
   return hipGetLastError();
 }
 
-template <int PER>
+template <int PER, bool VAR>
 static hipError_t launch_select_n(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   switch (p.nch) {
-    case 1: return launch_select_t<512, PER, 1>(a, p, batch, st);
-    case 2: return launch_select_t<512, PER, 2>(a, p, batch, st);
-    case 4: return launch_select_t<512, PER, 4>(a, p, batch, st);
-    default: return launch_select_t<512, PER, 8>(a, p, batch, st);
+    case 1: return launch_select_t<512, PER, 1, VAR>(a, p, batch, st);
+    case 2: return launch_select_t<512, PER, 2, VAR>(a, p, batch, st);
+    case 4: return launch_select_t<512, PER, 4, VAR>(a, p, batch, st);
+    default: return launch_select_t<512, PER, 8, VAR>(a, p, batch, st);
+  }
+}
+
+template <bool VAR>
+static hipError_t launch_select_v(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
+  switch (p.per) {  // select_geom: 512 threads, 2..32 candidates each
+    case 2: return launch_select_n<2, VAR>(a, p, batch, st);
+    case 4: return launch_select_n<4, VAR>(a, p, batch, st);
+    case 6: return launch_select_n<6, VAR>(a, p, batch, st);
+    case 8: return launch_select_n<8, VAR>(a, p, batch, st);
+    case 12: return launch_select_n<12, VAR>(a, p, batch, st);
+    case 16: return launch_select_n<16, VAR>(a, p, batch, st);
+    case 24: return launch_select_n<24, VAR>(a, p, batch, st);
+    default: return launch_select_n<32, VAR>(a, p, batch, st);
   }
 }
 
 static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  switch (p.per) {  // select_geom: 512 threads, 2..32 candidates each
-    case 2: return launch_select_n<2>(a, p, batch, st);
-    case 4: return launch_select_n<4>(a, p, batch, st);
-    case 6: return launch_select_n<6>(a, p, batch, st);
-    case 8: return launch_select_n<8>(a, p, batch, st);
-    case 12: return launch_select_n<12>(a, p, batch, st);
-    case 16: return launch_select_n<16>(a, p, batch, st);
-    case 24: return launch_select_n<24>(a, p, batch, st);
-    default: return launch_select_n<32>(a, p, batch, st);
-  }
+  return a.nacc == 4 && !a.dense ? launch_select_v<true>(a, p, batch, st)
+                                 : launch_select_v<false>(a, p, batch, st);
 }
 
-// coordinates per thread batch: the n_screen = 80 share of one thread
-template <int NG, int CPB>
+// coordinates per thread batch: the n_screen = 80 share of one thread (the
+// whole sketch takes two batches)
+template <int NG, int CPB, bool VAR>
 static hipError_t launch_screen_t(const ScreenArgs& a, const Plan& p, hipStream_t st) {
-  k_screen<kScreenThreads, NG, CPB><<<8 * p.per_xcd1, kScreenThreads, 0, st>>>(a);
+  k_screen<kScreenThreads, NG, CPB, VAR><<<8 * p.per_xcd1, kScreenThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+template <bool VAR>
+static hipError_t launch_screen_v(const ScreenArgs& a, const Plan& p, hipStream_t st) {
   switch (p.ng) {
-    case 16: return launch_screen_t<16, 5>(a, p, st);
-    case 8: return launch_screen_t<8, 10>(a, p, st);
-    case 4: return launch_screen_t<4, 20>(a, p, st);
-    case 2: return launch_screen_t<2, 20>(a, p, st);
-    default: return launch_screen_t<1, 20>(a, p, st);
+    case 16: return launch_screen_t<16, 5, VAR>(a, p, st);
+    case 8: return launch_screen_t<8, 10, VAR>(a, p, st);
+    case 4: return launch_screen_t<4, 20, VAR>(a, p, st);
+    case 2: return launch_screen_t<2, 20, VAR>(a, p, st);
+    default: return launch_screen_t<1, 20, VAR>(a, p, st);
   }
+}
+
+static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+  return a.nacc == 4 ? launch_screen_v<true>(a, p, st) : launch_screen_v<false>(a, p, st);
 }
 
 static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) {
@@ -1435,21 +1513,24 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   };
   hipError_t e;
   mark(0);
-  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->acc, r->xrot,
+  // accumulator rows per token: gate and up sums, and with the
+  // expected-error ranking their sketch variances
+  const int nacc = c.ranking == CFR_RANK_EXPECTED_ERROR ? 4 : 2;
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->rho, r->acc, r->xrot,
                r->sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
-               c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr};
+               c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr, nacc};
   if (only < 0 || only == 0)
     if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->ypart, r->zpart, r->ghat, r->vhat,
                r->score, r->kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
                r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter,
-               cps_mul(c.inter)};
+               cps_mul(c.inter), nacc};
   if (only < 0 || only == 1)
     if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
-               p.nslices, 1};
+               p.nslices, 1, nacc};
   if (only < 0 || only == 2)
     if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
   mark(3);
@@ -1480,11 +1561,11 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   const Plan p = make_plan(c, batch, nc, true);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->ypart, r->zpart, nullptr, nullptr,
                nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
-               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter)};
+               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter), 2};
   hipError_t e;
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, 0, c.rank, r->ncp,
-               p.nslices, 0};
+               p.nslices, 0, 2};
   if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "dense reduce launch");
   return CFR_OK;
 }

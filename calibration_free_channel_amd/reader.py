@@ -16,6 +16,8 @@ from . import _lib
 from ._lib import CfrConfig, CfrReadStats, CfrSizes, check, load
 
 DEFAULT_ROT_SEED = 0x5EED_0000_CAFE_F00D
+RANK_SCORE = 0            # output-unit score, partial screen (low budgets)
+RANK_EXPECTED_ERROR = 1   # whole sketch, expected squared error with rho (from 28.7%)
 
 
 @dataclass(frozen=True)
@@ -29,10 +31,12 @@ class Config:
     max_batch: int = 1
     device: int = 0
     rot_seed: int = DEFAULT_ROT_SEED
+    ranking: int = RANK_SCORE
 
     def c(self) -> CfrConfig:
         return CfrConfig(self.hidden, self.n_experts, self.inter, self.top, self.rank,
-                         self.n_screen, self.max_batch, self.device, self.rot_seed & (2 ** 64 - 1))
+                         self.n_screen, self.max_batch, self.device, self.rot_seed & (2 ** 64 - 1),
+                         self.ranking)
 
 
 def sizes(cfg: Config) -> dict:

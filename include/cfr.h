@@ -60,7 +60,20 @@ typedef struct cfr_config {
   int32_t max_batch;  /* largest batch a decode call may pass, 1..64                    */
   int32_t device;     /* HIP device ordinal the reader lives on                         */
   uint64_t rot_seed;  /* SplitMix64 seed of the rotation's sign vector                 */
+  int32_t ranking;    /* how candidates are ranked ([zh §方法步骤详情] decode step (2)):
+                       *   CFR_RANK_SCORE: output-unit score s_j = w_j ||d_j||
+                       *     |phi(g_hat_j) v_hat_j| (the low budgets, 12.8% and
+                       *     17.8%, with the partial screen);
+                       *   CFR_RANK_EXPECTED_ERROR: the whole sketch is read
+                       *     (n_screen must be 128) and candidates are ranked by
+                       *     e_j = w_j ||d_j|| sqrt(p_j^2 + Var[a_j]), the root
+                       *     of the expected squared output error of skipping j,
+                       *     with Var[a_j] from the stored rho_b and the block
+                       *     norms of x (budgets from 28.7% on).                  */
 } cfr_config;
+
+#define CFR_RANK_SCORE 0
+#define CFR_RANK_EXPECTED_ERROR 1
 
 /* Buffer sizes and layout constants implied by a config (see cfr_sizes_of()). */
 typedef struct cfr_sizes {
@@ -82,6 +95,7 @@ typedef struct cfr_read_stats {
   int64_t codes;   /* sketch codes of the screened coordinates                    */
   int64_t scales;  /* fp16 scales of the routed experts                            */
   int64_t norms;   /* ||d_j|| of the routed experts                                */
+  int64_t rho;     /* fp16 rho_b of the routed experts (CFR_RANK_EXPECTED_ERROR)   */
   int64_t exact;   /* native gate row, up row and transposed down row, k channels */
   int64_t b;       /* recovery coefficients of the skipped channels                */
   int64_t u;       /* the recovery basis U                                         */

@@ -55,10 +55,22 @@ def test_read_bytes_match_oracle_accounting(k):
     assert got["u"] == ref["U"]
 
 
+@pytest.mark.parametrize("k", [0, 1234, 6144])
+def test_read_bytes_with_rho_match_oracle_accounting(k):
+    # the expected-error ranking reads the whole sketch and rho_b as well
+    cfg = Config(hidden=2048, n_experts=128, inter=768, top=8, n_screen=128, ranking=1)
+    got = read_bytes(cfg, k)
+    ref = oracle_read_bytes(2048, 768, 8, k, n_screen=128, rho=True)
+    for key in ("codes", "scales", "rho", "norms", "exact", "b", "total", "dense"):
+        assert got[key] == ref[key], key
+    assert read_bytes(Config(hidden=2048, n_experts=128, inter=768, top=8), k)["rho"] == 0
+
+
 @pytest.mark.parametrize("bad", [dict(hidden=200), dict(hidden=0), dict(top=0), dict(top=17),
                                  dict(n_screen=0), dict(n_screen=129), dict(rank=65), dict(rank=12),
                                  dict(max_batch=0), dict(inter=0), dict(inter=5000),
-                                 dict(n_experts=1, top=2)])
+                                 dict(n_experts=1, top=2), dict(ranking=2), dict(ranking=-1),
+                                 dict(ranking=1, n_screen=80)])
 def test_invalid_configs_rejected(bad):
     with pytest.raises(CfrError) as ei:
         sizes(_cfg(**bad))
