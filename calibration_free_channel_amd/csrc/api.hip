@@ -33,7 +33,7 @@ struct DeviceGuard {
 
 // Workspace, sized for max_batch (see the field comments on cfr_reader).
 struct WorkspaceLayout {
-  size_t acc, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
+  size_t acc, var, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
   explicit WorkspaceLayout(const cfr_reader& r) {
     const cfr_config& c = r.cfg;
     const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
@@ -45,7 +45,8 @@ struct WorkspaceLayout {
       o += rnd(bytes);
       return at;
     };
-    acc = take(sizeof(unsigned long long) * B * (c.ranking == CFR_RANK_EXPECTED_ERROR ? 4 : 2) * r.ncp);
+    acc = take(sizeof(unsigned long long) * B * 2 * r.ncp);
+    var = take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0);
     ypart = take(sizeof(float) * kMaxGatherWgs * H);
     zpart = take(sizeof(float) * B * kMaxRecoverWgs * R);
     xrot = take(sizeof(float) * B * H);
@@ -65,6 +66,7 @@ void carve_workspace(cfr_reader& r) {
   const WorkspaceLayout l(r);
   char* p = static_cast<char*>(r.ws);
   r.acc = reinterpret_cast<unsigned long long*>(p + l.acc);
+  r.var = reinterpret_cast<float*>(p + l.var);
   r.ypart = reinterpret_cast<float*>(p + l.ypart);
   r.zpart = reinterpret_cast<float*>(p + l.zpart);
   r.xrot = reinterpret_cast<float*>(p + l.xrot);

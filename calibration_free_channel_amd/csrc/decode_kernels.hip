@@ -210,11 +210,11 @@ struct ScreenArgs {
   const float* norms;
   const uint16_t* rho;  // [E][nblk][2][I] fp16 (expected-error ranking only)
   unsigned long long* acc;
+  float* var;  // [B][2][ncp] sketch-error variances of g_hat and v_hat' (expected-error ranking)
   float* xrot;
   uint8_t* sel;
   int32_t* status;
   int H, E, I, top, ncp, nblk, ns, lp, unit, nd, ng, items, per_xcd, dbg;
-  int nacc;  // accumulator rows per token: 2 (gate, up sums) or 4 (then their sketch variances)
 };
 
 // Wave 0 rotates one 128-block held as two values per lane (lane l holds
@@ -256,10 +256,10 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int un
   const uint32_t k1 = __float_as_uint(v1) & 0x7FFFFFFFu;
   // Once exactly NS magnitudes are >= a prefix, those NS are the kept set
   // (every later T lies between that prefix and their minimum), so the search
-  // stops there.
+  // stops there.  The whole block (NS = 128) needs no search: T = 0 keeps all.
   uint32_t T = 0;
 #pragma unroll
-  for (int bit = 30; bit >= 0; --bit) {
+  for (int bit = 30; bit >= 0 && NS < 128; --bit) {
     const uint32_t cand = T | (1u << bit);
     const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
     if (cnt >= NS) T = cand;
@@ -285,15 +285,17 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int un
 
 // NG: threads per code word (a power of two, at most 16), CPB: screened
 // coordinates per thread whose code words are in flight together.  VAR (the
-// expected-error ranking, whole sketch): also add rho_b ||x_b||^2 per channel
-// (times ||d_j||^2 for the up half) into the variance rows of the
-// accumulator, the sketch-error variance of g_hat and of v_hat'.
+// expected-error ranking, whole sketch): the workgroup also writes, for its
+// 1/nblk share of the half's channels, the sketch-error variance
+// sum_b rho_b ||x_b||^2 (times ||d_j||^2 for the up half: the variance of
+// v_hat'), every term from stored values, so no accumulation across
+// workgroups is needed.
 template <int NT, int NG, int CPB, bool VAR>
 __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   static_assert(NG >= 1 && NG <= 16 && (NG & (NG - 1)) == 0, "word groups within a row of lanes");
   __shared__ uint4 lut[256];
   __shared__ int2 rec[128];
-  __shared__ float xn2;  // ||x_b||^2 (VAR)
+  __shared__ float qn2[VAR ? kMaxHidden / 128 : 1];  // ||x_b||^2 of every block (VAR)
   CFR_TRACE_PHASE(0, 0);
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
@@ -314,6 +316,15 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     g0 = a.sigma[b * 128 + lane];
     g1 = a.sigma[b * 128 + 64 + lane];
   }
+  // VAR: the token, four coordinates per thread and chunk, for the block
+  // norms (before the loads that wait on the routed expert)
+  float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;
+  if constexpr (VAR) {
+    const float* xt = a.x + (size_t)t * H;
+    const int h0 = 4 * tid, h1 = 4 * (tid + NT);
+    q0 = *reinterpret_cast<const float4*>(xt + (h0 < H ? h0 : H - 4));
+    q1 = *reinterpret_cast<const float4*>(xt + (h1 < H ? h1 : H - 4));
+  }
   const int e = clamp_expert(a.ids[ts], a.E, a.status);
   CFR_TRACE_PHASE(0, 5);
   // thread (d, g) = tid: code word d (channels 20d .. 20d+19 of the half),
@@ -328,14 +339,26 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     const int j = 20 * d + g + NG * r;
     al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
   }
-  uint16_t rh[RPL];
+  // VAR: this workgroup owns channels [b vper, (b + 1) vper) of the half;
+  // thread tid < vper loads channel b vper + tid's rho in every block and
+  // ||d_j|| now, as buffer loads that the other threads point past the end
+  // (issued by every thread: no wait depends on which path a thread took);
+  // channels past NT of the share, if any, are done at the end
+  constexpr int VB = VAR ? kMaxHidden / 128 : 1;
+  const int vper = (I + a.nblk - 1) / a.nblk;
+  const bool vown = VAR && tid < vper && b * vper + tid < I;
+  uint16_t vrho[VB];
+  float vdn = 1.f;
   if constexpr (VAR) {
-    const uint16_t* rp = a.rho + (((size_t)e * a.nblk + b) * 2 + m) * I;
+    const __amdgpu_buffer_rsrc_t rrs = buffer_rsrc(a.rho + (size_t)e * a.nblk * 2 * I, (uint32_t)(a.nblk * 2 * I * 2));
+    const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(a.norms + (size_t)e * I, (uint32_t)I * 4u);
+    const uint32_t jb = (uint32_t)(m * I + b * vper + tid) * 2u;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int j = 20 * d + g + NG * r;
-      rh[r] = rp[j < I ? j : I - 1];
-    }
+    for (int q = 0; q < VB; ++q)
+      vrho[q] = __builtin_amdgcn_raw_buffer_load_b16(rrs, vown && q < a.nblk ? jb + (uint32_t)q * 4u * I : kNoLoad,
+                                                     0, 0);
+    vdn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        drs, vown ? (uint32_t)(b * vper + tid) * 4u : kNoLoad, 0, 0));
   }
   // the up half carries ||d_j|| into its sums (v_hat' = ||d_j|| v_hat), so the
   // score needs no per-candidate norm read later: those norms, loaded now
@@ -370,9 +393,26 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     rotate_select(x0 * g0, x1 * g1, NS, a.unit, rec,
                   writer ? a.sel + ((size_t)t * a.nblk + b) * NS : nullptr,
                   writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
-    if constexpr (VAR) {
-      const float q = wave_sum(x0 * x0 + x1 * x1);
-      if (lane == 0) xn2 = q;
+  }
+  if constexpr (VAR) {
+    // ||x_b||^2 of every block: 32 lanes hold one block's 128 coordinates
+    static_assert(kMaxHidden <= 8 * NT, "the token is two float4 per thread at most");
+    const int h0 = 4 * tid, h1 = 4 * (tid + NT);
+    float s0 = h0 < H ? q0.x * q0.x + q0.y * q0.y + q0.z * q0.z + q0.w * q0.w : 0.f;
+    float s1 = h1 < H ? q1.x * q1.x + q1.y * q1.y + q1.z * q1.z + q1.w * q1.w : 0.f;
+    s0 += xor_lane_f<1>(s0);
+    s1 += xor_lane_f<1>(s1);
+    s0 += xor_lane_f<2>(s0);
+    s1 += xor_lane_f<2>(s1);
+    s0 += xor_lane_f<4>(s0);
+    s1 += xor_lane_f<4>(s1);
+    s0 += xor_lane_f<8>(s0);
+    s1 += xor_lane_f<8>(s1);
+    s0 += xor_lane_f<16>(s0);
+    s1 += xor_lane_f<16>(s1);
+    if ((lane & 31) == 0) {
+      if (h0 < H) qn2[h0 >> 7] = s0;
+      if (h1 < H) qn2[h1 >> 7] = s1;
     }
   }
   CFR_TRACE_PHASE(0, 6);
@@ -429,18 +469,21 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   // Every loaded value is consumed before the first atomic or store: on this
   // target the in-order memory counter also counts stores and atomics, so a
   // wait for a load placed after them would wait for them as well.
-  float alf[RPL], vt[RPL];
+  float alf[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
     alf[r] = f16f(al[r]) * nrm[r];
     asm volatile("" ::"v"(alf[r]));
-    if constexpr (VAR) {
-      vt[r] = f16f(rh[r]) * xn2 * (m == 1 ? nrm[r] * nrm[r] : 1.f);
-      asm volatile("" ::"v"(vt[r]));
-    }
   }
-  unsigned long long* ap = a.acc + ((size_t)t * a.nacc + m) * a.ncp + (size_t)s * I;
-  unsigned long long* vp = ap + 2 * (size_t)a.ncp;  // the variance rows (VAR)
+  float vsum = 0.f;
+  if constexpr (VAR) {
+    // block order, the same in whichever workgroup owns the channel
+#pragma unroll
+    for (int q = 0; q < VB; ++q) vsum += q < a.nblk ? f16f(vrho[q]) * qn2[q] : 0.f;
+    if (m == 1) vsum *= vdn * vdn;
+    asm volatile("" ::"v"(vsum));
+  }
+  unsigned long long* ap = a.acc + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
   if (active) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
@@ -449,10 +492,24 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
       for (int q = 1; q < NG; ++q)
         if (NG * r + q < 20) v = g == q ? acc[NG * r + q] : v;
       const int i = g + NG * r, j = 20 * d + i;
-      if (i < 20 && j < I) {
-        atomicAdd(ap + j, to_fix(alf[r] * v));
-        if constexpr (VAR) atomicAdd(vp + j, to_fix(vt[r]));
+      if (i < 20 && j < I) atomicAdd(ap + j, to_fix(alf[r] * v));
+    }
+  }
+  if constexpr (VAR) {
+    float* vo = a.var + ((size_t)t * 2 + m) * a.ncp + (size_t)s * I;
+    if (vown) vo[b * vper + tid] = vsum;
+    // the rest of a share wider than the workgroup (not at the configured
+    // shapes): the same sum with plain loads
+    for (int c = NT + tid; c < vper && b * vper + c < I; c += NT) {
+      const int j = b * vper + c;
+      const uint16_t* rp = a.rho + ((size_t)e * a.nblk * 2 + m) * I + j;
+      float v = 0.f;
+      for (int q = 0; q < a.nblk; ++q) v += f16f(rp[(size_t)q * 2 * I]) * qn2[q];
+      if (m == 1) {
+        const float dn = a.norms[(size_t)e * I + j];
+        v *= dn * dn;
       }
+      vo[j] = v;
     }
   }
   CFR_TRACE_PHASE(0, 4);
@@ -479,7 +536,7 @@ struct SelectArgs {
   int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dense, dbg;
   float invI;   // 1 / I rounded to float (exact slot division below 2^17)
   int cps_mul;  // I % 128 == 0: ceil(2^16 / (I / 128)), else 0
-  int nacc;     // accumulator rows per token (2, or 4 with the sketch variances)
+  const float* var;  // [B][2][ncp] sketch-error variances (expected-error ranking)
 };
 
 // misc slots
@@ -524,9 +581,9 @@ __device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned lon
 // latter carrying ||d_j||^2), the first-order variance of the activation
 // Var[a'] = (phi'(g_hat) v_hat')^2 var_g + phi(g_hat)^2 var_v' and
 // e = w sqrt(p'^2 + Var[a']) = w ||d_j|| sqrt(p^2 + Var[a]); returns its key.
-__device__ __forceinline__ uint32_t error_key(unsigned long long g, unsigned long long v,
-                                              unsigned long long vg, unsigned long long vv, float w,
-                                              float& gh, float& vh, float& p, float& sc) {
+__device__ __forceinline__ uint32_t error_key(unsigned long long g, unsigned long long v, float vg,
+                                              float vv, float w, float& gh, float& vh, float& p,
+                                              float& sc) {
   gh = from_fix(g) * kInvSqrt128f;
   vh = from_fix(v) * kInvSqrt128f;
   const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gh));  // sigma(g_hat)
@@ -534,7 +591,7 @@ __device__ __forceinline__ uint32_t error_key(unsigned long long g, unsigned lon
   const float dphi = sg * (1.0f + gh * (1.0f - sg));
   p = phi * vh;
   const float t = dphi * vh;
-  sc = w * sqrtf(p * p + t * t * from_fix(vg) + phi * phi * from_fix(vv));
+  sc = w * sqrtf(p * p + t * t * vg + phi * phi * vv);
   return order_key(sc);
 }
 
@@ -665,23 +722,30 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   // (issued on every path, as buffer loads that the dense mode points past
   // the end: a load on one path only would make every later wait on the
   // other path conservative)
-  ulonglong2 gq[P2], vq[P2], gvq[VAR ? P2 : 1], vvq[VAR ? P2 : 1];
+  ulonglong2 gq[P2], vq[P2];
+  float2 gvq[VAR ? P2 : 1], vvq[VAR ? P2 : 1];
   float2 wq[P2];
   {
-    const __amdgpu_buffer_rsrc_t ars =
-        buffer_rsrc(a.acc + (size_t)t * a.nacc * a.ncp, (uint32_t)(a.nacc * a.ncp * 8));
+    const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(a.acc + (size_t)t * 2 * a.ncp, (uint32_t)(a.ncp * 16));
     const uint32_t vofs = (uint32_t)a.ncp * 8u;
-    auto u64x2 = [](const decltype(__builtin_amdgcn_raw_buffer_load_b128(ars, 0u, 0, 0))& q) {
-      return make_ulonglong2(((unsigned long long)q[1] << 32) | q[0], ((unsigned long long)q[3] << 32) | q[2]);
-    };
 #pragma unroll
     for (int i = 0; i < P2; ++i) {
       const uint32_t o = a.dense ? kNoLoad : (uint32_t)(i * NT + tid) * 16u;
-      gq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0));
-      vq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + vofs, 0, 0));
-      if constexpr (VAR) {
-        gvq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + 2 * vofs, 0, 0));
-        vvq[i] = u64x2(__builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + 3 * vofs, 0, 0));
+      const auto g4 = __builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0);
+      const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + vofs, 0, 0);
+      gq[i] = make_ulonglong2(((unsigned long long)g4[1] << 32) | g4[0], ((unsigned long long)g4[3] << 32) | g4[2]);
+      vq[i] = make_ulonglong2(((unsigned long long)v4[1] << 32) | v4[0], ((unsigned long long)v4[3] << 32) | v4[2]);
+    }
+    if constexpr (VAR) {
+      const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(a.var + (size_t)t * 2 * a.ncp, (uint32_t)(a.ncp * 8));
+      const uint32_t wofs = (uint32_t)a.ncp * 4u;
+#pragma unroll
+      for (int i = 0; i < P2; ++i) {
+        const uint32_t o = (uint32_t)(i * NT + tid) * 8u;
+        const auto g2 = __builtin_amdgcn_raw_buffer_load_b64(vrs, o, 0, 0);
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(vrs, o + wofs, 0, 0);
+        gvq[i] = make_float2(__uint_as_float(g2[0]), __uint_as_float(g2[1]));
+        vvq[i] = make_float2(__uint_as_float(v2[0]), __uint_as_float(v2[1]));
       }
     }
   }
@@ -748,11 +812,13 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
     for (int c = tid; c < nc; c += NT) {
       const int sl = slot_of(c);
       float gh, vh, p, sc;
-      const unsigned long long* at = a.acc + (size_t)t * a.nacc * a.ncp + c;
-      if constexpr (VAR)
-        error_key(at[0], at[a.ncp], at[2 * (size_t)a.ncp], at[3 * (size_t)a.ncp], sl_w[sl], gh, vh, p, sc);
-      else
+      const unsigned long long* at = a.acc + (size_t)t * 2 * a.ncp + c;
+      if constexpr (VAR) {
+        const float* vt = a.var + (size_t)t * 2 * a.ncp + c;
+        error_key(at[0], at[a.ncp], vt[0], vt[a.ncp], sl_w[sl], gh, vh, p, sc);
+      } else {
         score_key(at[0], at[a.ncp], sl_w[sl], gh, vh, p, sc);
+      }
       const float nd = a.norms[(size_t)sl_e[sl] * I + (c - sl * I)];
       a.ghat[(size_t)t * nc + c] = gh;
       a.vhat[(size_t)t * nc + c] = nd > 0.f ? vh / nd : 0.f;
@@ -1276,7 +1342,6 @@ struct ReduceArgs {
   float* y;
   unsigned long long* acc;
   int H, G, Z, rank, ncp, nslices, clear;
-  int nacc;  // accumulator rows per token to clear
 };
 
 constexpr int kReduceThreads = 256;
@@ -1346,10 +1411,9 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
   }
   CFR_TRACE_PHASE(2, 2);
   if (a.clear) {
-    // the screen accumulators of this token (gate then up sums, then the
-    // variances when ranked by expected error; ncp each), split
+    // the screen accumulators of this token (gate then up, ncp each), split
     // over its slices
-    const int n = a.nacc * a.ncp;
+    const int n = 2 * a.ncp;
     const int per = (n + a.nslices - 1) / a.nslices;
     const int b0 = sl * per, b1 = min(b0 + per, n);
     ulonglong2* ap = reinterpret_cast<ulonglong2*>(a.acc + (size_t)t * n);
@@ -1472,8 +1536,7 @@ static hipError_t launch_select_v(const SelectArgs& a, const Plan& p, int batch,
 }
 
 static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  return a.nacc == 4 && !a.dense ? launch_select_v<true>(a, p, batch, st)
-                                 : launch_select_v<false>(a, p, batch, st);
+  return a.var && !a.dense ? launch_select_v<true>(a, p, batch, st) : launch_select_v<false>(a, p, batch, st);
 }
 
 // coordinates per thread batch: the n_screen = 80 share of one thread (the
@@ -1496,7 +1559,7 @@ static hipError_t launch_screen_v(const ScreenArgs& a, const Plan& p, hipStream_
 }
 
 static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t st) {
-  return a.nacc == 4 ? launch_screen_v<true>(a, p, st) : launch_screen_v<false>(a, p, st);
+  return a.var ? launch_screen_v<true>(a, p, st) : launch_screen_v<false>(a, p, st);
 }
 
 static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) {
@@ -1513,24 +1576,23 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   };
   hipError_t e;
   mark(0);
-  // accumulator rows per token: gate and up sums, and with the
-  // expected-error ranking their sketch variances
-  const int nacc = c.ranking == CFR_RANK_EXPECTED_ERROR ? 4 : 2;
-  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->rho, r->acc, r->xrot,
+  // the sketch-error variances, with the expected-error ranking only
+  float* var = c.ranking == CFR_RANK_EXPECTED_ERROR ? r->var : nullptr;
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->rho, r->acc, var, r->xrot,
                r->sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
-               c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr, nacc};
+               c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr};
   if (only < 0 || only == 0)
     if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->ypart, r->zpart, r->ghat, r->vhat,
                r->score, r->kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
                r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter,
-               cps_mul(c.inter), nacc};
+               cps_mul(c.inter), var};
   if (only < 0 || only == 1)
     if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
-               p.nslices, 1, nacc};
+               p.nslices, 1};
   if (only < 0 || only == 2)
     if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
   mark(3);
@@ -1561,11 +1623,11 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   const Plan p = make_plan(c, batch, nc, true);
   SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->ypart, r->zpart, nullptr, nullptr,
                nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
-               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter), 2};
+               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter), nullptr};
   hipError_t e;
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, 0, c.rank, r->ncp,
-               p.nslices, 0, 2};
+               p.nslices, 0};
   if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "dense reduce launch");
   return CFR_OK;
 }
