@@ -69,6 +69,9 @@ def parse():
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="summarise rocprofv3 CSV output under DIR as text and exit")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the 48-layer batch-1 decode step instead (route, decode, residual "
+                         "per layer, captured as one HIP graph); prints its own JSON line")
     return ap.parse_args()
 
 
@@ -302,10 +305,111 @@ def cpu_baseline(wl, layer, X, IDS, W, k, seconds):
             "single_core": one, "cpu_model": _cpu_model()}
 
 
+def stack_step(args):
+    """The 48-layer stack of Qwen3-30B-A3B-shaped layers (independent weights
+    per layer) as one batch-1 decode step: per layer h = RMSNorm(x) (unit
+    weights, fused into the library's routing), the library routes h and
+    decodes it at k = 756, and the
+    residual x += y is carried on; the whole step is captured as one HIP graph
+    and replayed, each replay from the same x0.  The dense BF16 block in the
+    same chain is timed the same way, and so are the 48 routings alone."""
+    import torch
+
+    from calibration_free_channel_amd import Config, Reader, read_bytes
+    from synth import make_layer, make_tokens, workload
+
+    wl = workload("qwen3-30b-a3b-48l")
+    s = wl.shape
+    k = wl.ks[0]
+    cfg = Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top, rank=s.rank,
+                 n_screen=s.n_screen, max_batch=1, rot_seed=wl.rot_seed)
+    readers = []
+    t = time.time()
+    for l in range(wl.n_layers):
+        L = make_layer(wl, layer=l)
+        readers.append(Reader.build(cfg, L["gate"], L["up"], L["down"], L["router"]))
+        del L
+        if l % 8 == 7:
+            log(f"{l + 1} layers built ({time.time() - t:.0f}s)")
+    torch.cuda.synchronize()
+    x0 = torch.from_numpy(make_tokens(wl, 1)).cuda()
+    x, y, h = torch.empty_like(x0), torch.empty_like(x0), torch.empty_like(x0)
+    ids = torch.empty((1, s.top), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, s.top), dtype=torch.float32, device="cuda")
+    st = torch.cuda.Stream()
+
+    def one_step(mode):
+        x.copy_(x0)
+        for r in readers:
+            r.route(x, ids, w, norm_out=h, norm_eps=1e-6)
+            if mode == "route":
+                continue
+            if mode == "dense":
+                r.dense(h, ids, w, out=y)
+            else:
+                r.decode(h, ids, w, k, out=y)
+            x.add_(y)
+
+    def timed(mode, steps, warmup):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            one_step(mode)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            one_step(mode)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            for _ in range(warmup):
+                g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(steps):
+                g.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        del g
+        return 1000.0 * ms / steps
+
+    steps = min(args.steps, 200)
+    warm = max(2, min(args.warmup, 20))
+    us = timed("reader", steps, warm)
+    xr = x.clone()
+    dense_us = timed("dense", steps, warm)
+    route_us = timed("route", steps, warm)
+    rb = read_bytes(cfg, k)
+    per_layer = rb["total"] + s.n_experts * s.hidden * 2  # reader reads + router weights
+    out = {
+        "metric": "48-layer batch-1 decode step us (route, reader at 17.8% reads, residual)",
+        "value": round(us, 2), "unit": "us/step", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "higher_is_better": False, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "48-layer stack of qwen3-30b-a3b-shaped layers, batch 1, k=756, "
+                               "pre-norm (RMSNorm, unit weights) and residual",
+                   "layers": wl.n_layers, "timing": "one hip graph per step, replayed"},
+        "us_per_layer": round(us / wl.n_layers, 3),
+        "bytes_per_step": per_layer * wl.n_layers,
+        "achieved_GBps": round(per_layer * wl.n_layers / us / 1e3, 1),
+        "dense_bf16_us_per_step": round(dense_us, 2),
+        "norm_and_route_us_per_step": round(route_us, 2),
+        "speedup_vs_dense": round(dense_us / us, 3),
+        "final_x_finite": bool(torch.isfinite(xr).all().item()),
+    }
+    print(json.dumps(out), flush=True)
+    for r in readers:
+        r.close()
+
+
 def main():
     args = parse()
     if args.profile_summary:
         profile_summary(args.profile_summary)
+        return
+    if args.stack:
+        if args.gpus != 1:
+            print("bench.py --stack runs on one GPU only.", file=sys.stderr)
+            sys.exit(2)
+        stack_step(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs the single-GPU reader only; --gpus {args.gpus} is not supported "

@@ -41,6 +41,7 @@ SIGNATURES = {
                                           _P, _P, _P]),
     "cfr_reader_decode_profile": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),
     "cfr_reader_decode_stage": (c_int32, [_P, c_int32, _P, _P, _P, c_int32, c_int32, _P, _P]),
+    "cfr_reader_route": (c_int32, [_P, _P, c_int32, ctypes.c_float, _P, _P, _P, _P]),
     "cfr_dense_decode": (c_int32, [_P, _P, _P, _P, c_int32, _P, _P]),
     "cfr_reader_export": (c_int32, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "cfr_pack_host": (c_int32, [POINTER(CfrConfig), _P, _P, _P, _P, _P, _P, _P]),

@@ -33,7 +33,7 @@ struct DeviceGuard {
 
 // Workspace, sized for max_batch (see the field comments on cfr_reader).
 struct WorkspaceLayout {
-  size_t acc, var, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
+  size_t acc, var, rlog, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
   explicit WorkspaceLayout(const cfr_reader& r) {
     const cfr_config& c = r.cfg;
     const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
@@ -47,6 +47,7 @@ struct WorkspaceLayout {
     };
     acc = take(sizeof(unsigned long long) * B * 2 * r.ncp);
     var = take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0);
+    rlog = take(sizeof(float) * B * c.n_experts);
     ypart = take(sizeof(float) * kMaxGatherWgs * H);
     zpart = take(sizeof(float) * B * kMaxRecoverWgs * R);
     xrot = take(sizeof(float) * B * H);
@@ -67,6 +68,7 @@ void carve_workspace(cfr_reader& r) {
   char* p = static_cast<char*>(r.ws);
   r.acc = reinterpret_cast<unsigned long long*>(p + l.acc);
   r.var = reinterpret_cast<float*>(p + l.var);
+  r.rlog = reinterpret_cast<float*>(p + l.rlog);
   r.ypart = reinterpret_cast<float*>(p + l.ypart);
   r.zpart = reinterpret_cast<float*>(p + l.zpart);
   r.xrot = reinterpret_cast<float*>(p + l.xrot);
@@ -281,6 +283,23 @@ int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* ids, const fl
   if (rc) return rc;
   DeviceGuard guard(r->cfg.device);
   return launch_dense(r, x, ids, gw, batch, y, static_cast<hipStream_t>(stream));
+}
+
+int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_eps, float* x_norm,
+                     int32_t* expert_ids, float* gate_w, void* stream) {
+  clear_error();
+  if (!r) return fail(CFR_EINVAL, "reader is NULL");
+  if (!x || !expert_ids || !gate_w) return fail(CFR_EINVAL, "x, expert_ids and gate_w must be non-NULL");
+  if (batch < 1 || batch > r->cfg.max_batch) return fail(CFR_EINVAL, "batch must be in 1..max_batch");
+  if (!r->router) return fail(CFR_EINVAL, "the reader was built without router weights");
+  if (x_norm && !(norm_eps >= 0.f)) return fail(CFR_EINVAL, "norm_eps must be >= 0");
+  if (x_norm == x) return fail(CFR_EINVAL, "x_norm must not alias x");
+  if (route_lds_bytes(r->cfg) + 2 * kMaxTop * 4 > kMaxLds)
+    return fail(CFR_EUNSUPPORTED, "n_experts too large for the router's top-k");
+  DeviceGuard guard(r->cfg.device);
+  const hipError_t e = launch_route(x, r->router, r->cfg, batch, x_norm ? norm_eps : -1.f, x_norm, r->rlog,
+                                    expert_ids, gate_w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CFR_OK : hipf(e, "route launch");
 }
 
 int cfr_reader_export(const cfr_reader* r, uint8_t* codes, uint16_t* scales, uint16_t* rho,

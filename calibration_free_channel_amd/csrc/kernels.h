@@ -113,6 +113,12 @@ struct DebugOut {
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t stream, const DebugOut* dbg,
                   hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1);
+// Softmax top-k routing (route_kernel.hip): LDS bytes of the top-k kernel and
+// the launch of both kernels (logits into logits[batch][E], then the pick).
+size_t route_lds_bytes(const cfr_config& c);
+// eps < 0: route on x; else on h = RMSNorm(x) (unit weights), written to h.
+hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
+                        float* h, float* logits, int32_t* ids, float* gw, hipStream_t st);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t stream);
 

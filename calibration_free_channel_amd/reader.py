@@ -212,6 +212,28 @@ class Reader:
                                              self._stream(stream)))
         return out
 
+    def route(self, x, ids_out=None, w_out=None, stream=None, norm_out=None, norm_eps=1e-6):
+        """Softmax top-k routing of x [batch, hidden] with the router weights
+        given at build time: (expert_ids int32 [batch, top], gate_w float32
+        [batch, top]), by weight descending.  With norm_out (a [batch, hidden]
+        float32 tensor) the router reads RMSNorm(x) (unit weights, norm_eps)
+        and writes it to norm_out."""
+        torch = _torch()
+        if x.dim() != 2:
+            raise ValueError("x must be [batch, hidden]")
+        B, c = x.shape[0], self.cfg
+        px = _dev_tensor(x, torch.float32, (B, c.hidden), "x", c.device)
+        if ids_out is None:
+            ids_out = torch.empty((B, c.top), dtype=torch.int32, device=x.device)
+        if w_out is None:
+            w_out = torch.empty((B, c.top), dtype=torch.float32, device=x.device)
+        pi = _dev_tensor(ids_out, torch.int32, (B, c.top), "ids_out", c.device)
+        pw = _dev_tensor(w_out, torch.float32, (B, c.top), "w_out", c.device)
+        pn = None if norm_out is None else _dev_tensor(norm_out, torch.float32, (B, c.hidden), "norm_out",
+                                                          c.device)
+        check(load().cfr_reader_route(self._h, px, B, float(norm_eps), pn, pi, pw, self._stream(stream)))
+        return ids_out, w_out
+
     def dense(self, x, expert_ids, gate_w, out=None, stream=None):
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)

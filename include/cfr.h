@@ -164,6 +164,29 @@ int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* expert
                             float* score, int32_t* kept, void* stream);
 
 /*
+ * The experts a token activates and their weights, from the router weights
+ * given at build time ([zh §前置知识 / Mixture-of-Experts (MoE)]; a channel's
+ * routing weight is its expert's, [zh §核心方法]): logits = W_router u,
+ * softmax over all n_experts, the `top` largest kept (ties to the lower
+ * expert index) and their probabilities renormalised to sum to one.
+ *   x          fp32  [batch][hidden]    device, read only
+ *   x_norm     fp32  [batch][hidden]    device, written, or NULL
+ *   expert_ids int32 [batch][top]       device, written: by weight, descending
+ *   gate_w     fp32  [batch][top]       device, written
+ * With x_norm NULL, u = x.  Otherwise u = x / sqrt(mean(x^2) + norm_eps), the
+ * pre-norm of a transformer block with unit weights, written to x_norm for
+ * the decode (the block reads u; the residual adds its output to x).
+ * Outputs feed cfr_reader_decode directly.  Runs on `stream`; no host sync,
+ * no allocation.  Float32 logits: experts whose logits differ by a few
+ * float32 ulps from the top-th may be ordered differently from a float64
+ * computation.  CFR_EINVAL if the reader was built without router weights,
+ * batch is outside 1..max_batch, norm_eps < 0 with x_norm given, or x_norm
+ * aliases x.
+ */
+int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_eps, float* x_norm,
+                     int32_t* expert_ids, float* gate_w, void* stream);
+
+/*
  * The dense routed-expert gated MLP on the same resident BF16 weights
  * ([zh §前置知识 / 门控MLP与通道]): y = sum_s w_s D_e (phi(G_e x) * V_e x).
  * The baseline the reader is measured against.  Same argument rules as

@@ -1,0 +1,88 @@
+"""GPU parity of the softmax top-k router (cfr_reader_route) against the
+oracle's route: logits = W_router x, softmax over all experts, the top
+largest kept (ties to the lower index), renormalised.  The choice is an
+argmax on floating point, so the kept experts are compared exactly only
+where the oracle's logits around the top-th place are separated by more than
+a relative band; the weights of agreeing picks within 1e-5."""
+import numpy as np
+import pytest
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+torch = pytest.importorskip("torch")
+
+from calibration_free_channel_amd import Config, Reader  # noqa: E402
+from calibration_free_channel_amd._lib import CfrError  # noqa: E402
+from oracle import route  # noqa: E402
+from synth import make_layer, make_tokens, workload  # noqa: E402
+
+BAND = 1e-5
+
+
+def _check(ids, w, router_bits, X, top):
+    for t in range(X.shape[0]):
+        rid, rw, logits = route(router_bits, X[t], top)
+        srt = np.sort(logits)[::-1]
+        gap = (srt[top - 1] - srt[top]) / max(abs(srt[top - 1]), 1e-30) if top < logits.shape[0] else 1.0
+        if gap > BAND:
+            assert set(ids[t].tolist()) == set(rid.tolist()), (t, ids[t], rid)
+            # order by weight, descending; equal-weight neighbours may swap
+            for a, b in zip(ids[t].tolist(), rid.tolist()):
+                if a != b:
+                    assert abs(logits[a] - logits[b]) <= BAND * abs(logits[b]), (t, a, b)
+            np.testing.assert_allclose(np.sort(w[t])[::-1], np.sort(rw)[::-1], rtol=0, atol=1e-5)
+        assert abs(float(w[t].sum()) - 1.0) < 1e-5
+        assert np.all(np.diff(w[t]) <= 1e-7), "weights not descending"
+
+
+@pytest.mark.parametrize("name,batch", [("tiny", 8), ("qwen3-30b-a3b", 4)])
+def test_route_matches_oracle(name, batch):
+    wl = workload(name)
+    s = wl.shape
+    layer = make_layer(wl)
+    r = Reader.build(Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
+                            rot_seed=wl.rot_seed, max_batch=batch),
+                     layer["gate"], layer["up"], layer["down"], layer["router"])
+    try:
+        X = make_tokens(wl, 4 * batch, seed_offset=3)
+        for b0 in range(0, X.shape[0], batch):
+            xs = torch.from_numpy(X[b0:b0 + batch]).cuda()
+            ids, w = r.route(xs)
+            _check(ids.cpu().numpy(), w.cpu().numpy(), layer["router"], X[b0:b0 + batch], s.top)
+    finally:
+        r.close()
+
+
+def test_route_with_prenorm_matches_oracle():
+    # the router reading RMSNorm(x) (unit weights): the normalised token
+    # against float64, the choice against the oracle's route of it
+    wl = workload("qwen3-30b-a3b")
+    s = wl.shape
+    layer = make_layer(wl)
+    r = Reader.build(Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
+                            rot_seed=wl.rot_seed, max_batch=4),
+                     layer["gate"], layer["up"], layer["down"], layer["router"])
+    try:
+        X = make_tokens(wl, 4, seed_offset=4) * np.float32(3.0)
+        xs = torch.from_numpy(X).cuda()
+        h = torch.empty_like(xs)
+        ids, w = r.route(xs, norm_out=h, norm_eps=1e-6)
+        H = X.astype(np.float64)
+        H = H / np.sqrt(np.mean(H * H, axis=1, keepdims=True) + 1e-6)
+        np.testing.assert_allclose(h.cpu().numpy(), H, rtol=1e-5, atol=1e-6)
+        _check(ids.cpu().numpy(), w.cpu().numpy(), layer["router"], H.astype(np.float32), s.top)
+    finally:
+        r.close()
+
+
+def test_route_needs_router_weights():
+    wl = workload("tiny")
+    s = wl.shape
+    layer = make_layer(wl)
+    r = Reader.build(Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
+                            rot_seed=wl.rot_seed), layer["gate"], layer["up"], layer["down"])
+    try:
+        with pytest.raises(CfrError):
+            r.route(torch.from_numpy(make_tokens(wl, 1)).cuda())
+    finally:
+        r.close()

@@ -1,6 +1,7 @@
 """The 48-layer stack workload (Qwen3-30B-A3B-shaped layers with independent
-weights, residual x <- x + y carried from layer to layer, k = 756): its first
-three layers.  Each layer's decode is checked against the oracle on the
+weights, k = 756; each layer's MoE block reads RMSNorm(x), unit weights,
+eps 1e-6, and the residual x <- x + y is carried on; without the norm the
+chain overflows float32 within a dozen layers): its first three layers.  Each layer's decode is checked against the oracle on the
 oracle chain's input, and the library's own chain is compared with the
 oracle chain at the end.  Routing comes from each layer's router applied to
 the oracle chain's x (the library does not route), so both chains use the
@@ -41,7 +42,8 @@ def stack():
         o = OracleReader(S.hidden, S.n_experts, S.inter, S.top, L["gate"], L["up"], L["down"],
                          L["router"], rot_seed=WL.rot_seed)
         r = Reader.build(Config(hidden=S.hidden, n_experts=S.n_experts, inter=S.inter, top=S.top,
-                                rot_seed=WL.rot_seed, max_batch=1), L["gate"], L["up"], L["down"])
+                                rot_seed=WL.rot_seed, max_batch=1), L["gate"], L["up"], L["down"],
+                         L["router"])
         layers.append(L)
         oracles.append(o)
         readers.append(r)
@@ -51,6 +53,13 @@ def stack():
         r.close()
 
 
+EPS = 1e-6
+
+
+def _rmsnorm64(x):
+    return x / np.sqrt(np.mean(x * x) + EPS)
+
+
 def test_stack_layers_and_chain(stack):
     layers, oracles, readers = stack
     X = make_tokens(WL, 2)
@@ -58,17 +67,21 @@ def test_stack_layers_and_chain(stack):
         xo = X[step].astype(np.float64)
         xg = torch.from_numpy(X[step:step + 1].copy()).cuda()
         for l in range(NL):
-            ids, w, _ = route(layers[l]["router"], xo.astype(np.float32), S.top)
+            xin = _rmsnorm64(xo).astype(np.float32)
+            ids, w, _ = route(layers[l]["router"], xin, S.top)
             ids = ids.astype(np.int32)[None]
             w = w.astype(np.float32)[None]
-            xin = xo.astype(np.float32)
             lib = {k: v.cpu().numpy() for k, v in readers[l].decode_debug(
                 torch.from_numpy(xin[None].copy()).cuda(), torch.from_numpy(ids).cuda(),
                 torch.from_numpy(w).cuda(), K).items()}
             ref = oracles[l].decode(xin, ids[0], w[0], K)
             err, ndiff = check_token(lib, ref, oracles[l], xin, ids[0], w[0], K)
             _log(f"step {step} layer {l}: y rel L2 {err:.2e}, swaps {ndiff}")
-            yg = readers[l].decode(xg, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), K)
+            # the library's fused pre-norm (its routing is checked elsewhere;
+            # both chains use the oracle's experts here)
+            hg = torch.empty_like(xg)
+            readers[l].route(xg, norm_out=hg, norm_eps=EPS)
+            yg = readers[l].decode(hg, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), K)
             xg = xg + yg
             xo = xo + ref["y"]
         d = rel_l2(xg[0].cpu().numpy(), xo)
