@@ -18,9 +18,10 @@
 //   2 k_select   per token, G gather workgroups and Z recovery workgroups.
 //                Each finalises g_hat, v_hat, p = silu(g_hat) v_hat and the
 //                output-unit score s = w ||d|| |p| of every candidate,
-//                finds the exact top-k (radix select on order-preserving
-//                keys, ties to the lower candidate index) and ranks the kept
-//                candidates in index order.  A gather workgroup then loads the
+//                finds the exact top-k (one histogram pass over the keys'
+//                distance below the largest, the boundary bin ranked
+//                directly, or radix passes when it is large; ties to the
+//                lower candidate index) and ranks the kept candidates.  A gather workgroup then loads the
 //                native gate, up and down rows of its share of the kept
 //                channels at once (one memory latency), computes
 //                a_j = silu(g_j.x)(v_j.x) and writes the partial output
@@ -711,9 +712,9 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   auto slot_of = [&](int c) { return (int)(((float)c + 0.5f) * a.invI); };
 
   // ---- loads, all issued up front in straight-line code at clamped
-  // addresses (a guarded load compiles to a branch that waits on it):
-  // screen sums and w ||d|| of this thread's candidate pairs, routing, the
-  // token.  Pair P = i NT + tid holds candidates 2P and 2P + 1. ----
+  // addresses (a guarded load compiles to a branch that waits on it): the
+  // screen sums of this thread's candidate pairs (the up sums carry ||d||),
+  // routing, the token.  Pair P = i NT + tid holds candidates 2P and 2P + 1. ----
   static_assert(kMaxHidden <= 2 * NT * 4, "the token is two float4 per thread at most");
   // the token's routing weights first, lane s holding slot s's (for the
   // scores): loads complete in issue order, so waiting for these must not
