@@ -25,7 +25,9 @@ Method:
     (float64, host cores, bounded sample) are reported beside the reader;
   * the 28.7% budget is timed the same way on a second set of layer copies
     built for the ranking the method uses from that budget on (whole sketch,
-    expected squared error with rho), k chosen by the read accounting.
+    expected squared error with rho), k chosen by the read accounting;
+  * the Qwen3-235B-A22B-shaped layer (hidden 4096, 128 experts, intermediate
+    1536) at batch 8 and k = 1511, on 8 copies, beside its dense block.
 
 Prints ONE JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
@@ -64,6 +66,8 @@ def parse():
                     help="time only the 17.8%% budget (profiling runs)")
     ap.add_argument("--no-high-budget", action="store_true",
                     help="skip the 28.7%% budget (expected-error ranking, whole sketch)")
+    ap.add_argument("--no-c5", action="store_true",
+                    help="skip the Qwen3-235B-A22B-shaped layer at batch 8")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -501,6 +505,45 @@ def main():
         for r in readers_h:
             r.close()
 
+    # the Qwen3-235B-A22B-shaped layer at batch 8 (per-token routing and top-k)
+    c5 = None
+    if not args.main_budget_only and not args.no_c5:
+        for r in readers[1:]:
+            r.close()
+        readers = readers[:1]
+        torch.cuda.empty_cache()
+        w5 = workload("qwen3-235b-a22b")
+        s5 = w5.shape
+        t = time.time()
+        l5 = make_layer(w5)
+        cfg5 = Config(hidden=s5.hidden, n_experts=s5.n_experts, inter=s5.inter, top=s5.top, rank=s5.rank,
+                      n_screen=s5.n_screen, max_batch=8, rot_seed=w5.rot_seed)
+        b5 = Reader.build(cfg5, l5["gate"], l5["up"], l5["down"])
+        del l5
+        L5 = 8
+        r5 = [b5] + [b5.clone() for _ in range(L5 - 1)]
+        torch.cuda.synchronize()
+        log(f"qwen3-235b-a22b layer built and copied in {time.time() - t:.1f}s")
+        X5 = torch.from_numpy(make_tokens(w5, 8 * L5).reshape(L5, 8, s5.hidden)).cuda()
+        i5, g5 = make_routing_inputs(w5, 8 * L5)
+        I5 = torch.from_numpy(i5.reshape(L5, 8, s5.top).astype(np.int32)).cuda()
+        W5 = torch.from_numpy(g5.reshape(L5, 8, s5.top).astype(np.float32)).cuda()
+        k5 = w5.ks[0]
+        us5, _, _ = graph_time(torch, r5, X5, I5, W5, k5, min(args.steps, 200), args.warmup)
+        ud5 = None
+        if not args.no_dense:
+            ud5, _, _ = graph_time(torch, r5, X5, I5, W5, 0, min(args.steps, 200), args.warmup, fn="dense")
+        rb5 = read_bytes(cfg5, k5)
+        c5 = {"k": k5, "batch": 8, "us_per_token": round(us5 / 8, 3),
+              "read_pct_of_dense": round(100.0 * rb5["total"] / rb5["dense"], 2),
+              "achieved_GBps": round(8 * rb5["total"] / us5 / 1e3, 1),
+              "dense_us_per_token": None if ud5 is None else round(ud5 / 8, 3),
+              "speedup_vs_dense": None if ud5 is None else round(ud5 / us5, 3)}
+        log(f"qwen3-235b-a22b batch 8, k={k5}: {us5 / 8:.2f} us/token"
+            + ("" if ud5 is None else f", dense {ud5 / 8:.2f} us/token"))
+        for r in r5:
+            r.close()
+
     if args.copy_calibration:
         copy_calibration(torch)
         log(f"copy calibration: {COPY_BYTES >> 20} MiB read and written 4 times")
@@ -569,6 +612,7 @@ def main():
                      "us_per_launch": round(dom_us, 3),
                      "timing": "kernel alone, back to back over the layer copies in a HIP graph"},
         "batch4_us_per_token": batch4 or None,
+        "qwen3_235b_a22b_batch8": c5,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
