@@ -147,8 +147,10 @@ def profile_summary(d):
         json.dump(traffic, fh, indent=1)
 
 
-def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None):
-    """Capture one pass over all copies in a graph; return microseconds per step."""
+def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None, spread=None):
+    """Capture one pass over all copies in a graph; return microseconds per step.
+    With spread (a dict), also the median and 90th percentile of the per-pass
+    averages (an event after every replay)."""
     L = len(readers)
     s = torch.cuda.Stream()
     if Y is None:
@@ -176,14 +178,18 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None)
         for _ in range(wreps):
             g.replay()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(s)
+        for i in range(reps):
             g.replay()
-        e1.record(s)
+            ev[i + 1].record(s)
     torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
+    total_ms = ev[0].elapsed_time(ev[-1])
+    if spread is not None:
+        per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) / L for i in range(reps))
+        spread["median"] = round(per[len(per) // 2], 3)
+        spread["p90"] = round(per[min(len(per) - 1, int(0.9 * len(per)))], 3)
+        spread["passes"] = reps
     del g
     return 1000.0 * total_ms / (reps * L), reps * L, wreps * L
 
@@ -450,10 +456,11 @@ def main():
 
     res = {}
     for k in [k_main] + ([k_low] if k_low and not args.main_budget_only else []):
-        us, nsteps, nwarm = graph_time(torch, readers, X, IDS, W, k, args.steps, args.warmup)
+        spread = {}
+        us, nsteps, nwarm = graph_time(torch, readers, X, IDS, W, k, args.steps, args.warmup, spread=spread)
         rb = read_bytes(cfg, k)
         stages = stage_times(torch, readers, X, IDS, W, k, min(args.steps, 400), args.warmup)
-        res[k] = {"us": us, "steps": nsteps, "warmup": nwarm, "bytes": rb, "stages": stages}
+        res[k] = {"us": us, "steps": nsteps, "warmup": nwarm, "bytes": rb, "stages": stages, "spread": spread}
         log(f"k={k}: {us:.2f} us/token, {rb['total'] / us / 1e3:.1f} GB/s counted; stages "
             + ", ".join(f"{n}={v:.1f}" for n, v in stages.items()))
     dense_us = None
@@ -593,6 +600,7 @@ def main():
         "budgets": {
             f"{100.0 * r['bytes']['total'] / r['bytes']['dense']:.1f}%": {
                 "k": kk, "us_per_token": round(r["us"], 3),
+                "per_pass_median_us": r["spread"].get("median"), "per_pass_p90_us": r["spread"].get("p90"),
                 "achieved_GBps": round(r["bytes"]["total"] / r["us"] / 1e3, 1),
                 "stages_us": {n: round(v, 2) for n, v in r["stages"].items()}}
             for kk, r in res.items()},
