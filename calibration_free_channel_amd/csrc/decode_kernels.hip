@@ -1503,11 +1503,8 @@ static void allow_lds(K kernel) {
 
 template <int NT, int PER, int NCH, bool VAR>
 static hipError_t launch_select_t(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    allow_lds(k_select<NT, PER, NCH, VAR>);
-    attr = true;
-  }
+  static OncePerDevice attr;
+  attr([] { allow_lds(k_select<NT, PER, NCH, VAR>); });
   k_select<NT, PER, NCH, VAR><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
   return hipGetLastError();
 }

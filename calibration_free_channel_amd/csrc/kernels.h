@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "cfr_internal.h"
 
 namespace cfr {
@@ -113,6 +115,22 @@ struct DebugOut {
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t stream, const DebugOut* dbg,
                   hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1);
+// Kernel attributes (hipFuncSetAttribute) apply to the current device: a
+// launcher sets them once per device, the first time it runs there.  Setting
+// them twice (two threads at once) is harmless.
+constexpr int kMaxDevices = 64;
+struct OncePerDevice {
+  std::atomic<bool> done[kMaxDevices] = {};
+  template <typename F>
+  void operator()(F&& set) {
+    int d = 0;
+    const bool known = hipGetDevice(&d) == hipSuccess && d >= 0 && d < kMaxDevices;
+    if (known && done[d].load(std::memory_order_acquire)) return;
+    set();
+    if (known) done[d].store(true, std::memory_order_release);
+  }
+};
+
 // Softmax top-k routing (route_kernel.hip): LDS bytes of the top-k kernel and
 // the launch of both kernels (logits into logits[batch][E], then the pick).
 size_t route_lds_bytes(const cfr_config& c);

@@ -143,13 +143,12 @@ size_t route_lds_bytes(const cfr_config& c) { return (size_t)(c.n_experts + 3) /
 
 hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
                         float* h, float* logits, int32_t* ids, float* gw, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
+  static OncePerDevice attr;
+  attr([] {
     (void)hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)(kMaxLds - kMaxTop * 4));
     (void)hipGetLastError();
-    attr = true;
-  }
+  });
   const int per = kRouteThreads / 64;
   k_route_logits<<<dim3((c.n_experts + per - 1) / per, batch), kRouteThreads, 0, st>>>(x, router, c.hidden,
                                                                                       c.n_experts, eps, h, logits);
