@@ -193,11 +193,24 @@ void pack_expert(const PackJob& J, int e, std::vector<int8_t>& trits) {
   }
 }
 
+// True when any of n BF16 bit patterns is an infinity or a NaN (exponent
+// field all ones).
+static bool any_nonfinite_bf16(const uint16_t* a, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if ((a[i] & 0x7F80u) == 0x7F80u) return true;
+  return false;
+}
+
 }  // namespace
 
 int pack_host(const cfr_config& c, const uint16_t* gate, const uint16_t* up,
               const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
               float* norms, uint16_t* w3, float* sigma_out) {
+  // the sketch, the norms and the recovery basis are only defined for finite
+  // weights: a NaN or an infinity is rejected before any work
+  const size_t nw = (size_t)c.n_experts * c.inter * c.hidden;
+  if (any_nonfinite_bf16(gate, nw) || any_nonfinite_bf16(up, nw) || any_nonfinite_bf16(down, nw))
+    return fail(CFR_EINVAL, "weights contain NaN or infinity");
   PackJob J;
   J.c = &c;
   J.gate = gate;

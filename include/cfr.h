@@ -125,8 +125,9 @@ int cfr_read_bytes(const cfr_config* cfg, int32_t k, cfr_read_stats* out);
  *   gate, up: [E][I][H]   down: [E][H][I]   router: [E][H] or NULL.
  * On success *out owns device memory for the native weights, the sketch,
  * norms, U, b, the router and a decode workspace sized for max_batch.
- * Errors: CFR_EINVAL (config/pointers), CFR_EUNSUPPORTED, CFR_ENOMEM,
- * CFR_EHIP, CFR_ESOLVER.  *out is left NULL on failure.
+ * Errors: CFR_EINVAL (config/pointers, or a NaN or infinite weight),
+ * CFR_EUNSUPPORTED, CFR_ENOMEM, CFR_EHIP, CFR_ESOLVER.  *out is left NULL on
+ * failure.
  */
 int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t* up,
                      const uint16_t* down, const uint16_t* router, cfr_reader** out);

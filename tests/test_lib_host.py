@@ -109,6 +109,21 @@ def _compare_pack(wl, n_experts=None, seed_layer=0):
     assert np.array_equal(got["norms"], ref.norms)
 
 
+def test_host_pack_rejects_nonfinite_weights():
+    # a NaN or an infinity in any weight is rejected before any work
+    from synth import make_layer, workload
+    wl = workload("tiny")
+    s = wl.shape
+    L = make_layer(wl)
+    cfg = Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top)
+    for name, bits in (("gate", 0x7FC0), ("up", 0x7F80), ("down", 0xFF80)):
+        bad = {k: v.copy() for k, v in L.items()}
+        bad[name].reshape(-1)[17] = bits
+        with pytest.raises(CfrError) as ei:
+            pack_host(cfg, bad["gate"], bad["up"], bad["down"])
+        assert ei.value.code == -1
+
+
 def test_host_pack_bit_exact_tiny():
     _compare_pack(workload("tiny"))
 
