@@ -112,7 +112,18 @@ __global__ __launch_bounds__(64) void k_route_topk(const float* logits, int E, i
   float* lg = reinterpret_cast<float*>(lg4);
   const int t = blockIdx.x, lane = threadIdx.x;
   const int E4 = (E + 3) / 4;
-  for (int e = lane; e < 4 * E4; e += 64) lg[e] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+  const float* lt = logits + (size_t)t * E;
+  for (int base = 0; base < 4 * E4; base += 256) {
+    // four loads per lane in flight (clamped addresses), then the stores
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = lt[min(base + lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = base + lane + 64 * i;
+      if (e < 4 * E4) lg[e] = e < E ? v[i] : -INFINITY;
+    }
+  }
   __syncthreads();
   for (int e = lane; e < E; e += 64) {
     const float v = lg[e];
