@@ -1545,11 +1545,12 @@ static hipError_t launch_screen_t(const ScreenArgs& a, const Plan& p, hipStream_
   return hipGetLastError();
 }
 
+// (the whole sketch, VAR: 128 coordinates, all of a lane's words in one batch)
 template <bool VAR>
 static hipError_t launch_screen_v(const ScreenArgs& a, const Plan& p, hipStream_t st) {
   switch (p.ng) {
-    case 16: return launch_screen_t<16, 5, VAR>(a, p, st);
-    case 8: return launch_screen_t<8, 10, VAR>(a, p, st);
+    case 16: return launch_screen_t<16, VAR ? 8 : 5, VAR>(a, p, st);
+    case 8: return launch_screen_t<8, VAR ? 16 : 10, VAR>(a, p, st);
     case 4: return launch_screen_t<4, 20, VAR>(a, p, st);
     case 2: return launch_screen_t<2, 20, VAR>(a, p, st);
     default: return launch_screen_t<1, 20, VAR>(a, p, st);
