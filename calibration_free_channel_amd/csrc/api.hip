@@ -33,7 +33,7 @@ struct DeviceGuard {
 
 // Workspace, sized for max_batch (see the field comments on cfr_reader).
 struct WorkspaceLayout {
-  size_t acc, var, rlog, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
+  size_t acc, var, rlog, rarr, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
   explicit WorkspaceLayout(const cfr_reader& r) {
     const cfr_config& c = r.cfg;
     const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
@@ -48,6 +48,7 @@ struct WorkspaceLayout {
     acc = take(sizeof(unsigned long long) * B * 2 * r.ncp);
     var = take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0);
     rlog = take(sizeof(float) * B * c.n_experts);
+    rarr = take(sizeof(int32_t) * B);
     ypart = take(sizeof(float) * kMaxGatherWgs * H);
     zpart = take(sizeof(float) * B * kMaxRecoverWgs * R);
     xrot = take(sizeof(float) * B * H);
@@ -69,6 +70,7 @@ void carve_workspace(cfr_reader& r) {
   r.acc = reinterpret_cast<unsigned long long*>(p + l.acc);
   r.var = reinterpret_cast<float*>(p + l.var);
   r.rlog = reinterpret_cast<float*>(p + l.rlog);
+  r.rarr = reinterpret_cast<int32_t*>(p + l.rarr);
   r.ypart = reinterpret_cast<float*>(p + l.ypart);
   r.zpart = reinterpret_cast<float*>(p + l.zpart);
   r.xrot = reinterpret_cast<float*>(p + l.xrot);
@@ -294,11 +296,11 @@ int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_ep
   if (!r->router) return fail(CFR_EINVAL, "the reader was built without router weights");
   if (x_norm && !(norm_eps >= 0.f)) return fail(CFR_EINVAL, "norm_eps must be >= 0");
   if (x_norm == x) return fail(CFR_EINVAL, "x_norm must not alias x");
-  if (route_lds_bytes(r->cfg) + 2 * kMaxTop * 4 > kMaxLds)
+  if (route_lds_bytes(r->cfg) + 128 > kMaxLds)
     return fail(CFR_EUNSUPPORTED, "n_experts too large for the router's top-k");
   DeviceGuard guard(r->cfg.device);
   const hipError_t e = launch_route(x, r->router, r->cfg, batch, x_norm ? norm_eps : -1.f, x_norm, r->rlog,
-                                    expert_ids, gate_w, static_cast<hipStream_t>(stream));
+                                    r->rarr, expert_ids, gate_w, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CFR_OK : hipf(e, "route launch");
 }
 

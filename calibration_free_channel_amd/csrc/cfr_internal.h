@@ -67,6 +67,7 @@ struct cfr_reader {
   unsigned long long* acc = nullptr;  // [B][2][ncp] fixed-point screen sums (gate, up); zero between calls
   float* var = nullptr;        // [B][2][ncp] sketch-error variances of g_hat, v_hat' (expected-error ranking)
   float* rlog = nullptr;       // [B][E] router logits (cfr_reader_route)
+  int32_t* rarr = nullptr;     // [B] workgroups of the route that have finished; zero between calls
   float* ypart = nullptr;      // [B][kMaxGatherWgs][H]  partial outputs of the gather workgroups
   float* zpart = nullptr;      // [B][kMaxRecoverWgs][rank]  partial recovery vectors
   float* xrot = nullptr;       // [B][H]   H_128 (sigma x) per block (debug copy only)

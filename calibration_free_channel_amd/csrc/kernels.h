@@ -131,12 +131,13 @@ struct OncePerDevice {
   }
 };
 
-// Softmax top-k routing (route_kernel.hip): LDS bytes of the top-k kernel and
-// the launch of both kernels (logits into logits[batch][E], then the pick).
+// Softmax top-k routing (route_kernel.hip): dynamic LDS bytes of the pick and the
+// launch (logits into logits[batch][E]; arrived[batch] must be zero before
+// the first call and is zero again after each).
 size_t route_lds_bytes(const cfr_config& c);
 // eps < 0: route on x; else on h = RMSNorm(x) (unit weights), written to h.
 hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
-                        float* h, float* logits, int32_t* ids, float* gw, hipStream_t st);
+                        float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t stream);
 

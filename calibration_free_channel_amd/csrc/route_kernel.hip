@@ -8,6 +8,10 @@
 // lower expert index), renormalise the kept probabilities to sum to one.
 // The full softmax denominator cancels in the renormalisation, so the weights
 // are a softmax over the kept logits alone.
+//
+// One launch: the workgroups of a token compute its logits, and the last of
+// them to finish (a per-token arrival counter, which that workgroup sets back
+// to zero for the next call) picks the top experts and their weights.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -26,21 +30,26 @@ __device__ __forceinline__ float route_wave_sum(float v) {
   return v;
 }
 
-// Logits: grid (ceil(E / 8), batch); wave w of workgroup g computes expert
-// 8 g + w for token blockIdx.y, lane l the 8-element chunks l, l + 64, ...
-// of the token and of its row: the token's chunks first, then the row's, all
-// in flight together.  With eps >= 0 the router reads h = x / sqrt(mean(x^2)
-// + eps) (RMSNorm, unit weights): every wave forms sum x^2 over the same
-// chunks in the same order, so each gets the same scale; workgroup 0's first
-// wave writes h.
-__global__ __launch_bounds__(kRouteThreads) void k_route_logits(const float* x, const uint16_t* router,
-                                                                int H, int E, float eps, float* h,
-                                                                float* logits) {
+// Grid (ceil(E / 8), batch); wave w of workgroup g computes expert 8 g + w for
+// token blockIdx.y, lane l the 8-element chunks l, l + 64, ... (CH of them,
+// clamped to the last) of the token and of its row: the token's chunks first,
+// then the row's, all in flight together.  With eps >= 0 the router reads
+// h = x / sqrt(mean(x^2) + eps) (RMSNorm, unit weights): every wave forms
+// sum x^2 over the same chunks in the same order, so each gets the same
+// scale; workgroup 0's first wave writes h.
+template <int CH>
+__global__ __launch_bounds__(kRouteThreads) void k_route(const float* x, const uint16_t* router, int H, int E,
+                                                         int top, float eps, float* h, float* logits,
+                                                         int* arrived, int32_t* ids, float* gw) {
+  // the last workgroup: the logits padded to a multiple of 4 with -inf, then
+  // each expert's rank
+  extern __shared__ float4 lg4[];
+  __shared__ int last;
+  __shared__ float selv[kMaxTop];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
   const float* xt = x + (size_t)t * H;
-  constexpr int CH = kMaxHidden / 512;  // chunks per lane, at most
   const int nch = H / 8;
   float4 xa[CH], xb[CH];
 #pragma unroll
@@ -82,7 +91,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_logits(const float* x, 
       }
     }
   }
-  if (e >= E) return;
   float acc = 0.f;
 #pragma unroll
   for (int q = 0; q < CH; ++q) {
@@ -97,76 +105,90 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_logits(const float* x, 
     }
   }
   acc = route_wave_sum(acc);
-  if (lane == 0) logits[(size_t)t * E + e] = acc;
-}
+  float* lt = logits + (size_t)t * E;
+  if (e < E && lane == 0) lt[e] = acc;
 
-// Top experts by logit (ties to the lower index) and their weights, a
-// softmax over the kept logits: one wave per token.  Each expert's rank is
-// the number of experts ahead of it (a larger logit, or an equal one with a
-// lower index), counted against the logits staged in LDS; the top ranks
-// write themselves.
-__global__ __launch_bounds__(64) void k_route_topk(const float* logits, int E, int top, int32_t* ids,
-                                                   float* gw) {
-  extern __shared__ float4 lg4[];  // the logits, padded to a multiple of 4 with -inf
-  __shared__ float selv[kMaxTop];
-  float* lg = reinterpret_cast<float*>(lg4);
-  const int t = blockIdx.x, lane = threadIdx.x;
+  // arrival: this workgroup's logits are visible device-wide before it counts
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(arrived + t, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // every workgroup of the token has counted: their logits are visible
   const int E4 = (E + 3) / 4;
-  const float* lt = logits + (size_t)t * E;
-  for (int base = 0; base < 4 * E4; base += 256) {
-    // four loads per lane in flight (clamped addresses), then the stores
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = lt[min(base + lane + 64 * i, E - 1)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = base + lane + 64 * i;
-      if (e < 4 * E4) lg[e] = e < E ? v[i] : -INFINITY;
+  float* lg = reinterpret_cast<float*>(lg4);
+  int* rank = reinterpret_cast<int*>(lg4 + E4);
+  for (int i = threadIdx.x; i < 4 * E4; i += kRouteThreads) {
+    lg[i] = i < E ? __hip_atomic_load(lt + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
+    if (i < E) rank[i] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) arrived[t] = 0;  // no workgroup of this launch counts again
+  // rank of expert e = the experts ahead of it (a larger logit, or an equal
+  // one with a lower index); P threads count it, each over its share of the
+  // logits (read four at a time), and add their counts in LDS
+  const int P = max(1, min(16, kRouteThreads / E));
+  const int L = (E4 + P - 1) / P;
+  for (int idx = threadIdx.x; idx < E * P; idx += kRouteThreads) {
+    const int j = idx / P, part = idx - j * P;
+    const float v = lg[j];
+    const int q1 = min(E4, (part + 1) * L);
+    int cnt = 0;
+    for (int q = part * L; q < q1; ++q) {
+      const float4 o = lg4[q];
+      const int i = 4 * q;
+      cnt += (o.x > v) | ((o.x == v) & (i < j));
+      cnt += (o.y > v) | ((o.y == v) & (i + 1 < j));
+      cnt += (o.z > v) | ((o.z == v) & (i + 2 < j));
+      cnt += (o.w > v) | ((o.w == v) & (i + 3 < j));
+    }
+    if (cnt) atomicAdd(rank + j, cnt);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < E; j += kRouteThreads) {
+    const int k = rank[j];
+    if (k < top) {
+      ids[(size_t)t * top + k] = j;
+      selv[k] = lg[j];
     }
   }
   __syncthreads();
-  for (int e = lane; e < E; e += 64) {
-    const float v = lg[e];
-    int rank = 0;
-#pragma unroll 4
-    for (int q = 0; q < E4; ++q) {
-      const float4 o = lg4[q];  // the same address in every lane: a broadcast read
-      const int b = 4 * q;
-      rank += (o.x > v) | ((o.x == v) & (b < e));
-      rank += (o.y > v) | ((o.y == v) & (b + 1 < e));
-      rank += (o.z > v) | ((o.z == v) & (b + 2 < e));
-      rank += (o.w > v) | ((o.w == v) & (b + 3 < e));
-    }
-    if (rank < top) {
-      ids[(size_t)t * top + rank] = e;
-      selv[rank] = v;
-    }
-  }
-  __syncthreads();
+  if (threadIdx.x >= 64) return;
   const float ev = lane < top ? __expf(selv[lane] - selv[0]) : 0.f;
   const float sum = route_wave_sum(ev);
   if (lane < top) gw[(size_t)t * top + lane] = ev / sum;
 }
 
-}  // namespace
-
-size_t route_lds_bytes(const cfr_config& c) { return (size_t)(c.n_experts + 3) / 4 * 16; }
-
-hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
-                        float* h, float* logits, int32_t* ids, float* gw, hipStream_t st) {
+template <int CH>
+hipError_t launch_route_t(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
+                          float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st) {
   static OncePerDevice attr;
   attr([] {
-    (void)hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(kMaxLds - kMaxTop * 4));
+    (void)hipFuncSetAttribute((const void*)k_route<CH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(kMaxLds - 128));
     (void)hipGetLastError();
   });
   const int per = kRouteThreads / 64;
-  k_route_logits<<<dim3((c.n_experts + per - 1) / per, batch), kRouteThreads, 0, st>>>(x, router, c.hidden,
-                                                                                      c.n_experts, eps, h, logits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_route_topk<<<batch, 64, route_lds_bytes(c), st>>>(logits, c.n_experts, c.top, ids, gw);
+  k_route<CH><<<dim3((c.n_experts + per - 1) / per, batch), kRouteThreads, route_lds_bytes(c), st>>>(
+      x, router, c.hidden, c.n_experts, c.top, eps, h, logits, arrived, ids, gw);
   return hipGetLastError();
+}
+
+}  // namespace
+
+size_t route_lds_bytes(const cfr_config& c) {
+  return (size_t)(c.n_experts + 3) / 4 * 16 + (size_t)c.n_experts * 4;
+}
+
+hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
+                        float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st) {
+  // chunks of 8 per lane: the fewest of 1, 2, 4, 8 that cover hidden / 8
+  static_assert(kMaxHidden / 8 <= 64 * 8, "eight chunks per lane cover the largest token");
+  const int need = (c.hidden / 8 + 63) / 64;
+  if (need <= 1) return launch_route_t<1>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
+  if (need <= 2) return launch_route_t<2>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
+  if (need <= 4) return launch_route_t<4>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
+  return launch_route_t<8>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
 }
 
 }  // namespace cfr

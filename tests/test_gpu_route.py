@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 from calibration_free_channel_amd import Config, Reader  # noqa: E402
 from calibration_free_channel_amd._lib import CfrError  # noqa: E402
 from oracle import route  # noqa: E402
-from synth import make_layer, make_tokens, workload  # noqa: E402
+from synth import LayerShape, make_layer, make_tokens, workload  # noqa: E402
 
 BAND = 1e-5
 
@@ -49,6 +49,54 @@ def test_route_matches_oracle(name, batch):
             xs = torch.from_numpy(X[b0:b0 + batch]).cuda()
             ids, w = r.route(xs)
             _check(ids.cpu().numpy(), w.cpu().numpy(), layer["router"], X[b0:b0 + batch], s.top)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("hidden,n_experts,top", [(640, 13, 13), (384, 200, 16), (4096, 128, 8), (128, 5, 1)])
+def test_route_odd_shapes(hidden, n_experts, top):
+    # experts not a multiple of a workgroup's eight, top = all experts, more
+    # experts than a wave has lanes, the largest token (eight chunks per
+    # lane), one chunk per lane with lanes idle; then batch sizes that shrink
+    # and grow on the same reader (each token's arrival counter is reused)
+    shape = LayerShape(hidden=hidden, n_experts=n_experts, inter=64, top=top)
+    wl = workload("tiny", shape=shape)
+    layer = make_layer(wl)
+    r = Reader.build(Config(hidden=hidden, n_experts=n_experts, inter=64, top=top, rot_seed=wl.rot_seed,
+                            max_batch=6),
+                     layer["gate"], layer["up"], layer["down"], layer["router"])
+    try:
+        X = make_tokens(wl, 16, seed_offset=5)
+        b0 = 0
+        for batch in (6, 1, 3, 6):
+            xs = torch.from_numpy(X[b0:b0 + batch]).cuda()
+            ids, w = r.route(xs)
+            _check(ids.cpu().numpy(), w.cpu().numpy(), layer["router"], X[b0:b0 + batch], top)
+            b0 += batch
+    finally:
+        r.close()
+
+
+def test_route_ties_to_lower_index():
+    # router rows repeated in pairs: every logit ties with its twin's, and the
+    # lower expert index of each tied pair is ranked first
+    wl = workload("tiny")
+    s = wl.shape
+    layer = make_layer(wl)
+    router = layer["router"].copy()
+    router[1::2] = router[0::2]
+    r = Reader.build(Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=4,
+                            rot_seed=wl.rot_seed, max_batch=4),
+                     layer["gate"], layer["up"], layer["down"], router)
+    try:
+        X = make_tokens(wl, 4, seed_offset=6)
+        ids, w = r.route(torch.from_numpy(X).cuda())
+        ids, w = ids.cpu().numpy(), w.cpu().numpy()
+        for t in range(4):
+            rid, rw, _ = route(router, X[t], 4)
+            assert ids[t].tolist() == rid.tolist(), (t, ids[t], rid)
+            assert ids[t][0] % 2 == 0 and ids[t][1] == ids[t][0] + 1
+            np.testing.assert_allclose(w[t], rw, rtol=0, atol=1e-5)
     finally:
         r.close()
 
