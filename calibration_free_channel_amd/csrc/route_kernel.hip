@@ -105,25 +105,29 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* x, const u
     }
   }
   acc = route_wave_sum(acc);
+  // Hand-over between the workgroups of a token, through device-scope atomic
+  // read-modify-writes only (performed where every workgroup sees them, so no
+  // cache write-back is needed, which a release fence would force on every
+  // dirty line of the L2): each wave swaps its logit in and waits for the
+  // swap to complete before the barrier; then the workgroup counts itself in;
+  // the last to count reads the logits back with atomics and zeroes the
+  // counter.
   float* lt = logits + (size_t)t * E;
-  if (e < E && lane == 0) lt[e] = acc;
-
-  // arrival: this workgroup's logits are visible device-wide before it counts
-  __threadfence();
+  if (e < E && lane == 0) atomicExch(lt + e, acc);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) last = atomicAdd(arrived + t, 1) == (int)gridDim.x - 1;
   __syncthreads();
   if (!last) return;
-  __threadfence();  // every workgroup of the token has counted: their logits are visible
   const int E4 = (E + 3) / 4;
   float* lg = reinterpret_cast<float*>(lg4);
   int* rank = reinterpret_cast<int*>(lg4 + E4);
   for (int i = threadIdx.x; i < 4 * E4; i += kRouteThreads) {
-    lg[i] = i < E ? __hip_atomic_load(lt + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
+    lg[i] = i < E ? __uint_as_float(atomicOr(reinterpret_cast<unsigned*>(lt) + i, 0u)) : -INFINITY;
     if (i < E) rank[i] = 0;
   }
+  if (threadIdx.x == 0) atomicExch(arrived + t, 0);  // no workgroup of this launch counts again
   __syncthreads();
-  if (threadIdx.x == 0) arrived[t] = 0;  // no workgroup of this launch counts again
   // rank of expert e = the experts ahead of it (a larger logit, or an equal
   // one with a lower index); P threads count it, each over its share of the
   // logits (read four at a time), and add their counts in LDS

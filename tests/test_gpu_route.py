@@ -77,6 +77,34 @@ def test_route_odd_shapes(hidden, n_experts, top):
         r.close()
 
 
+def test_route_back_to_back_calls():
+    # 64 routes of different tokens queued with no host synchronisation in
+    # between, each into its own output rows: a pick made from a logit left
+    # by the previous call (the workgroups of a call hand their logits to the
+    # last of them through device-scope atomics) would show up here
+    wl = workload("qwen3-30b-a3b")
+    s = wl.shape
+    layer = make_layer(wl)
+    r = Reader.build(Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
+                            rot_seed=wl.rot_seed, max_batch=2),
+                     layer["gate"], layer["up"], layer["down"], layer["router"])
+    try:
+        n = 64
+        X = make_tokens(wl, 2 * n, seed_offset=7)
+        xs = torch.from_numpy(X).cuda()
+        ids = torch.empty((2 * n, s.top), dtype=torch.int32, device="cuda")
+        w = torch.empty((2 * n, s.top), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(n):
+            b = 1 + (i % 2)
+            r.route(xs[2 * i:2 * i + b], ids[2 * i:2 * i + b], w[2 * i:2 * i + b])
+        torch.cuda.synchronize()
+        rows = [2 * i + j for i in range(n) for j in range(1 + (i % 2))]
+        _check(ids.cpu().numpy()[rows], w.cpu().numpy()[rows], layer["router"], X[rows], s.top)
+    finally:
+        r.close()
+
+
 def test_route_ties_to_lower_index():
     # router rows repeated in pairs: every logit ties with its twin's, and the
     # lower expert index of each tied pair is ranked first
