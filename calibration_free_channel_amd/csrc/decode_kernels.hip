@@ -1537,15 +1537,15 @@ static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, h
   return a.var && !a.dense ? launch_select_v<true>(a, p, batch, st) : launch_select_v<false>(a, p, batch, st);
 }
 
-// coordinates per thread batch: the n_screen = 80 share of one thread (the
-// whole sketch takes two batches)
+// CPB: coordinates per thread batch, the n_screen = 80 share of one thread in
+// one batch
 template <int NG, int CPB, bool VAR>
 static hipError_t launch_screen_t(const ScreenArgs& a, const Plan& p, hipStream_t st) {
   k_screen<kScreenThreads, NG, CPB, VAR><<<8 * p.per_xcd1, kScreenThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-// (the whole sketch, VAR: 128 coordinates, all of a lane's words in one batch)
+// (the whole sketch, VAR: a thread's share of all 128 coordinates in one batch)
 template <bool VAR>
 static hipError_t launch_screen_v(const ScreenArgs& a, const Plan& p, hipStream_t st) {
   switch (p.ng) {
