@@ -178,13 +178,14 @@ int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* expert
  * pre-norm of a transformer block with unit weights, written to x_norm for
  * the decode (the block reads u; the residual adds its output to x).
  * Outputs feed cfr_reader_decode directly.  Runs on `stream`; no host sync,
- * no allocation.  Calls on one reader must not overlap in time (they share
- * its logit buffer and per-token arrival counters): serialise them on one
- * stream or clone the reader.  Float32 logits: experts whose logits differ by a few
- * float32 ulps from the top-th may be ordered differently from a float64
- * computation.  CFR_EINVAL if the reader was built without router weights,
- * batch is outside 1..max_batch, norm_eps < 0 with x_norm given, or x_norm
- * aliases x.
+ * no allocation.  Route calls on one reader must not overlap in time (they
+ * share its logit buffer and per-token arrival counters): serialise them on
+ * one stream or clone the reader.  Float32 logits: experts whose logits
+ * differ by a few float32 ulps from the top-th may be ordered differently
+ * from a float64 computation.  CFR_EINVAL if the reader was built without
+ * router weights, batch is outside 1..max_batch, norm_eps < 0 with x_norm
+ * given, or x_norm aliases x; CFR_EUNSUPPORTED if the pick's 8 bytes of LDS
+ * per expert do not fit one workgroup (n_experts above about 20 000).
  */
 int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_eps, float* x_norm,
                      int32_t* expert_ids, float* gate_w, void* stream);
