@@ -37,12 +37,14 @@ SIGNATURES = {
     "cfr_read_bytes": (c_int32, [POINTER(CfrConfig), c_int32, POINTER(CfrReadStats)]),
     "cfr_build_reader": (c_int32, [POINTER(CfrConfig), _P, _P, _P, _P, POINTER(c_void_p)]),
     "cfr_reader_decode": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P]),
+    "cfr_reader_decode_residual": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),
     "cfr_reader_decode_debug": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P, _P, _P,
                                           _P, _P, _P]),
     "cfr_reader_decode_profile": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),
     "cfr_reader_decode_stage": (c_int32, [_P, c_int32, _P, _P, _P, c_int32, c_int32, _P, _P]),
     "cfr_reader_route": (c_int32, [_P, _P, c_int32, ctypes.c_float, _P, _P, _P, _P]),
     "cfr_dense_decode": (c_int32, [_P, _P, _P, _P, c_int32, _P, _P]),
+    "cfr_dense_decode_residual": (c_int32, [_P, _P, _P, _P, c_int32, _P, _P, _P]),
     "cfr_reader_export": (c_int32, [_P, _P, _P, _P, _P, _P, _P, _P]),
     "cfr_pack_host": (c_int32, [POINTER(CfrConfig), _P, _P, _P, _P, _P, _P, _P]),
     "cfr_reader_clone": (c_int32, [_P, POINTER(c_void_p)]),

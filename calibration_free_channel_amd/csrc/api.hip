@@ -227,6 +227,17 @@ int cfr_reader_decode(cfr_reader* r, const float* x, const int32_t* ids, const f
   return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr);
 }
 
+int cfr_reader_decode_residual(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                               int32_t batch, int32_t k, const float* resid, float* y, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, k, y);
+  if (rc) return rc;
+  if (!resid) return fail(CFR_EINVAL, "resid is NULL");
+  if (resid == x) return fail(CFR_EINVAL, "resid must not alias x");
+  DeviceGuard guard(r->cfg.device);
+  return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr, nullptr, -1,
+                       resid);
+}
+
 int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
                             int32_t batch, int32_t k, float* y, float* xrot, uint8_t* sel,
                             float* ghat, float* vhat, float* score, int32_t* kept, void* stream) {
@@ -285,6 +296,16 @@ int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* ids, const fl
   if (rc) return rc;
   DeviceGuard guard(r->cfg.device);
   return launch_dense(r, x, ids, gw, batch, y, static_cast<hipStream_t>(stream));
+}
+
+int cfr_dense_decode_residual(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                              int32_t batch, const float* resid, float* y, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, 0, y);
+  if (rc) return rc;
+  if (!resid) return fail(CFR_EINVAL, "resid is NULL");
+  if (resid == x) return fail(CFR_EINVAL, "resid must not alias x");
+  DeviceGuard guard(r->cfg.device);
+  return launch_dense(r, x, ids, gw, batch, y, static_cast<hipStream_t>(stream), resid);
 }
 
 int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_eps, float* x_norm,

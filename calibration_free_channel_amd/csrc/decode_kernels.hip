@@ -1343,6 +1343,7 @@ struct ReduceArgs {
   float* y;
   unsigned long long* acc;
   int H, G, Z, rank, ncp, nslices, clear;
+  const float* resid = nullptr;  // non-null: y = resid + output (resid may be y)
 };
 
 constexpr int kReduceThreads = 256;
@@ -1379,6 +1380,9 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
     const int wq = pt + u * kReduceParts;
     pv[u] = yp[(size_t)(wq < a.G ? wq : 0) * H];
   }
+  // the residual last: the waits above do not wait for it
+  float rv = 0.f;
+  if (a.resid && tid < kReduceSlice) rv = a.resid[(size_t)t * H + h0 + tid];
   float v = 0.f;
 #pragma unroll
   for (int u = 0; u < kReducePer; ++u) v += pt + u * kReduceParts < a.G ? pv[u] : 0.f;
@@ -1408,7 +1412,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
           }
         }
     }
-    a.y[(size_t)t * H + h0 + tid] = o;
+    // the residual is added to the finished output, as a separate add would
+    a.y[(size_t)t * H + h0 + tid] = a.resid ? rv + o : o;
   }
   CFR_TRACE_PHASE(2, 2);
   if (a.clear) {
@@ -1567,7 +1572,8 @@ static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) 
 }
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
-                  int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev, int only) {
+                  int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev, int only,
+                  const float* resid) {
   const cfr_config& c = r->cfg;
   const Plan p = make_plan(c, batch, k, false);
   auto mark = [&](int i) {
@@ -1591,7 +1597,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
     if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
-               p.nslices, 1};
+               p.nslices, 1, resid};
   if (only < 0 || only == 2)
     if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
   mark(3);
@@ -1616,7 +1622,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
 }
 
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
-                 float* y, hipStream_t st) {
+                 float* y, hipStream_t st, const float* resid) {
   const cfr_config& c = r->cfg;
   const int nc = r->ncand;
   const Plan p = make_plan(c, batch, nc, true);
@@ -1626,7 +1632,7 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   hipError_t e;
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
   ReduceArgs C{r->ypart, r->zpart, r->u, y, r->acc, c.hidden, p.G, 0, c.rank, r->ncp,
-               p.nslices, 0};
+               p.nslices, 0, resid};
   if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "dense reduce launch");
   return CFR_OK;
 }

@@ -114,7 +114,8 @@ struct DebugOut {
 // only: -1 launches every stage; 0, 1 or 2 launches that stage's kernel alone
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t stream, const DebugOut* dbg,
-                  hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1);
+                  hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1,
+                  const float* resid = nullptr /* non-null: y = resid + output */);
 // Kernel attributes (hipFuncSetAttribute) apply to the current device: a
 // launcher sets them once per device, the first time it runs there.  Setting
 // them twice (two threads at once) is harmless.
@@ -139,7 +140,7 @@ size_t route_lds_bytes(const cfr_config& c);
 hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
                         float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
-                 float* y, hipStream_t stream);
+                 float* y, hipStream_t stream, const float* resid = nullptr);
 
 // Load step (3) on the device: U (fp16 [H][rank]) and b (fp16 [E][I][rank])
 // from the resident down rows.  Synchronous.

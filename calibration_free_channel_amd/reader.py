@@ -153,13 +153,21 @@ class Reader:
                 _dev_tensor(ids, torch.int32, (B, c.top), "expert_ids", c.device),
                 _dev_tensor(w, torch.float32, (B, c.top), "gate_w", c.device))
 
-    def decode(self, x, expert_ids, gate_w, k: int, out=None, stream=None):
+    def decode(self, x, expert_ids, gate_w, k: int, out=None, stream=None, residual=None):
+        """The reader's output for x [batch, hidden]; with `residual` (a
+        [batch, hidden] float32 tensor, which may be `out` but not x) the
+        output plus residual, added in the last kernel."""
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)
         if out is None:
             out = torch.empty((B, self.cfg.hidden), dtype=torch.float32, device=x.device)
         py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
-        check(load().cfr_reader_decode(self._h, px, pi, pw, B, int(k), py, self._stream(stream)))
+        if residual is None:
+            check(load().cfr_reader_decode(self._h, px, pi, pw, B, int(k), py, self._stream(stream)))
+        else:
+            pr = _dev_tensor(residual, torch.float32, (B, self.cfg.hidden), "residual", self.cfg.device)
+            check(load().cfr_reader_decode_residual(self._h, px, pi, pw, B, int(k), pr, py,
+                                                    self._stream(stream)))
         return out
 
     def decode_debug(self, x, expert_ids, gate_w, k: int, stream=None) -> dict:
@@ -234,13 +242,17 @@ class Reader:
         check(load().cfr_reader_route(self._h, px, B, float(norm_eps), pn, pi, pw, self._stream(stream)))
         return ids_out, w_out
 
-    def dense(self, x, expert_ids, gate_w, out=None, stream=None):
+    def dense(self, x, expert_ids, gate_w, out=None, stream=None, residual=None):
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)
         if out is None:
             out = torch.empty((B, self.cfg.hidden), dtype=torch.float32, device=x.device)
         py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
-        check(load().cfr_dense_decode(self._h, px, pi, pw, B, py, self._stream(stream)))
+        if residual is None:
+            check(load().cfr_dense_decode(self._h, px, pi, pw, B, py, self._stream(stream)))
+        else:
+            pr = _dev_tensor(residual, torch.float32, (B, self.cfg.hidden), "residual", self.cfg.device)
+            check(load().cfr_dense_decode_residual(self._h, px, pi, pw, B, pr, py, self._stream(stream)))
         return out
 
     # -- state ----------------------------------------------------------------

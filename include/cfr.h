@@ -151,6 +151,20 @@ int cfr_reader_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
                       const float* gate_w, int32_t batch, int32_t k, float* y, void* stream);
 
 /*
+ * cfr_reader_decode with the block's residual added in its last kernel:
+ * y = resid + (the decode's output), in float32, the residual added to the
+ * finished output (bit for bit what a separate add after cfr_reader_decode
+ * gives).  resid fp32 [batch][H], device; it may be y itself (an in-place
+ * residual stream x += block(RMSNorm(x))) but must not be x.  The pages'
+ * reader replaces one MoE block of a transformer layer, whose output joins
+ * the residual stream ([zh §前置知识 / Mixture-of-Experts (MoE)]).
+ * Errors: those of cfr_reader_decode, and CFR_EINVAL if resid is NULL or x.
+ */
+int cfr_reader_decode_residual(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                               const float* gate_w, int32_t batch, int32_t k, const float* resid,
+                               float* y, void* stream);
+
+/*
  * Same computation as cfr_reader_decode, also copying the intermediates to
  * the caller's device buffers (any may be NULL):
  *   xrot  fp32  [batch][H]              H_128 (sigma * x) per block, before the 1/sqrt(128)
@@ -198,6 +212,12 @@ int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_ep
  */
 int cfr_dense_decode(cfr_reader* r, const float* x, const int32_t* expert_ids,
                      const float* gate_w, int32_t batch, float* y, void* stream);
+
+/* cfr_dense_decode with the residual added in its last kernel; the rules of
+ * cfr_reader_decode_residual. */
+int cfr_dense_decode_residual(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                              const float* gate_w, int32_t batch, const float* resid, float* y,
+                              void* stream);
 
 /* Stages of the decode path, in launch order; cfr_reader_decode_profile
  * reports one duration per stage. */
