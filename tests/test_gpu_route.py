@@ -53,12 +53,15 @@ def test_route_matches_oracle(name, batch):
         r.close()
 
 
-@pytest.mark.parametrize("hidden,n_experts,top", [(640, 13, 13), (384, 200, 16), (4096, 128, 8), (128, 5, 1)])
+@pytest.mark.parametrize("hidden,n_experts,top", [(640, 13, 13), (384, 200, 16), (4096, 128, 8), (128, 5, 1),
+                                                   (128, 600, 16)])
 def test_route_odd_shapes(hidden, n_experts, top):
     # experts not a multiple of a workgroup's eight, top = all experts, more
     # experts than a wave has lanes, the largest token (eight chunks per
-    # lane), one chunk per lane with lanes idle; then batch sizes that shrink
-    # and grow on the same reader (each token's arrival counter is reused)
+    # lane), one chunk per lane with lanes idle, more experts than the picking
+    # workgroup has threads (each thread ranks several); then batch sizes that
+    # shrink and grow on the same reader (each token's arrival counter is
+    # reused)
     shape = LayerShape(hidden=hidden, n_experts=n_experts, inter=64, top=top)
     wl = workload("tiny", shape=shape)
     layer = make_layer(wl)
