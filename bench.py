@@ -23,6 +23,11 @@ Method:
     summary (null when the kernel source changed since it was taken);
   * the dense-BF16 routed-expert block on the same weights and the CPU oracle
     (float64, host cores, bounded sample) are reported beside the reader;
+  * a batch-1 layer step per copy (`layer_step_batch1`): the library's
+    routing of RMSNorm(x) with the fused pre-norm, then the decode of the
+    normed token with its output added to the residual stream x in the
+    decode's last kernel; the same with the dense block, and the routing
+    alone (the 48-layer stack is `--stack`);
   * the 28.7% budget is timed the same way on a second set of layer copies
     built for the ranking the method uses from that budget on (whole sketch,
     expected squared error with rho), k chosen by the read accounting;
@@ -150,18 +155,31 @@ def profile_summary(d):
 def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None, spread=None):
     """Capture one pass over all copies in a graph; return microseconds per step.
     With spread (a dict), also the median and 90th percentile of the per-pass
-    averages (an event after every replay)."""
+    averages (an event after every replay).  fn: "decode", "dense", or a
+    layer step on copies built with router weights, on the residual stream
+    x = Y[i]: "route" (routing of RMSNorm(x) alone), "layer" (that routing,
+    then the decode of the normed token, its output added to x in the
+    decode's last kernel), "layer_dense" (the same with the dense block); IDS
+    and W are then the routing's outputs."""
     L = len(readers)
     s = torch.cuda.Stream()
     if Y is None:
         Y = torch.empty((L, X.shape[1], X.shape[-1]), dtype=torch.float32, device=X.device)
+    Hn = torch.empty_like(Y) if fn in ("route", "layer", "layer_dense") else None
 
     def one_pass():
         for i, r in enumerate(readers):
             if fn == "decode":
                 r.decode(X[i], IDS[i], W[i], k, out=Y[i])
-            else:
+            elif fn == "dense":
                 r.dense(X[i], IDS[i], W[i], out=Y[i])
+            else:
+                # x <- x + block(RMSNorm(x)) on the residual stream Y[i]
+                r.route(Y[i], IDS[i], W[i], norm_out=Hn[i], norm_eps=1e-6)
+                if fn == "layer":
+                    r.decode(Hn[i], IDS[i], W[i], k, out=Y[i], residual=Y[i])
+                elif fn == "layer_dense":
+                    r.dense(Hn[i], IDS[i], W[i], out=Y[i], residual=Y[i])
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -471,7 +489,8 @@ def main():
     cfg = Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
                  rank=s.rank, n_screen=s.n_screen, max_batch=4, rot_seed=wl.rot_seed)
     t = time.time()
-    base = Reader.build(cfg, layer["gate"], layer["up"], layer["down"])
+    # with the router's weights (for the layer-step leg; the decode never reads them)
+    base = Reader.build(cfg, layer["gate"], layer["up"], layer["down"], layer["router"])
     log(f"reader built in {time.time() - t:.1f}s")
     readers = [base] + [base.clone() for _ in range(L - 1)]
     torch.cuda.synchronize()
@@ -497,6 +516,22 @@ def main():
         dense_us, _, _ = graph_time(torch, readers, X, IDS, W, 0, min(args.steps, 400),
                                     args.warmup, fn="dense")
         log(f"dense BF16 block: {dense_us:.2f} us/token")
+
+    # one batch-1 layer step per copy: route RMSNorm(x) (the library's fused
+    # pre-norm), decode the normed token with the residual added in the
+    # decode's last kernel; the dense block the same way; the routing alone
+    layer_step = {}
+    if not args.main_budget_only:
+        IDr = torch.empty_like(IDS)
+        Wr = torch.empty_like(W)
+        Xr = X.clone()  # the residual stream, carried on over the replays
+        for name, fn in (("reader", "layer"), ("dense", "layer_dense"), ("route", "route")):
+            us_l, _, _ = graph_time(torch, readers, X, IDr, Wr, k_main, min(args.steps, 400), args.warmup,
+                                    fn=fn, Y=Xr)
+            layer_step[f"{name}_us"] = round(us_l, 3)
+        layer_step["speedup_vs_dense"] = round(layer_step["dense_us"] / layer_step["reader_us"], 3)
+        layer_step["residual_finite"] = bool(torch.isfinite(Xr).all())
+        log("layer step, us: " + ", ".join(f"{n}={v}" for n, v in layer_step.items()))
 
     # batch 4 (per-token routing and top-k), the configuration's batched case:
     # µs per token = µs per call / 4
@@ -658,6 +693,10 @@ def main():
                      "us_per_launch": round(dom_us, 3),
                      "timing": "kernel alone, back to back over the layer copies in a HIP graph"},
         "batch4_us_per_token": batch4 or None,
+        "layer_step_batch1": (dict(layer_step, what="per layer copy: route RMSNorm(x), decode it at k="
+                                   f"{k_main}, output added to x in the decode's last kernel; dense: the same "
+                                   "with the dense block; route: the routing alone")
+                              if layer_step else None),
         "qwen3_235b_a22b_batch8": c5,
         "cpu_baseline": cpu,
     }
