@@ -212,35 +212,6 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None,
     return 1000.0 * total_ms / (reps * L), reps * L, wreps * L
 
 
-def union_bytes(cfg, ids, sel, kept, k):
-    """Distinct 32-byte sectors one batched call touches: every sketch unit,
-    scale block, norm row, exact channel and skipped b row counted once
-    however many tokens read it, plus U once.  ids [B][top], sel
-    [B][nblk][n_screen] (screened coordinates), kept [B][k] (candidates,
-    slot * I + j)."""
-    sect = lambda n: -(-n // 32) * 32  # noqa: E731
-    cdiv = lambda a, b: -(-a // b)  # noqa: E731
-    H, I, top, R = cfg.hidden, cfg.inter, cfg.top, cfg.rank
-    nblk = H // 128
-    lp = cdiv(cdiv(I, 5), 16) * 16  # bytes of one half of a sketch unit
-    unit = cdiv(2 * lp, 32) * 32
-    units, blocks, experts, exact, skipped = set(), set(), set(), set(), set()
-    for t in range(ids.shape[0]):
-        kt = set(kept[t, :k].tolist())
-        for sl in range(top):
-            e = int(ids[t, sl])
-            experts.add(e)
-            for b in range(nblk):
-                blocks.add((e, b))
-                for i in sel[t, b].tolist():
-                    units.add((e, b, int(i)))
-            for j in range(I):
-                (exact if sl * I + j in kt else skipped).add((e, j))
-    total = (len(units) * sect(unit) + len(blocks) * sect(2 * I * 2) + len(experts) * sect(I * 4)
-             + len(exact) * sect(3 * H * 2) + len(skipped) * sect(R * 2) + sect(H * R * 2))
-    return total
-
-
 def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
     """Average duration of each decode kernel: the kernel launched alone, back
     to back over all layer copies in one HIP graph, timed with HIP events on
@@ -475,7 +446,7 @@ def main():
         sys.exit(2)
     import torch
 
-    from calibration_free_channel_amd import RANK_EXPECTED_ERROR, Config, Reader, read_bytes
+    from calibration_free_channel_amd import RANK_EXPECTED_ERROR, Config, Reader, read_bytes, read_bytes_batch
     from synth import make_layer, make_routing_inputs, make_tokens, workload
 
     wl = workload(args.workload)
@@ -545,7 +516,7 @@ def main():
             us4, _, _ = graph_time(torch, readers, X4, I4, W4, k, min(args.steps, 400), args.warmup)
             batch4[f"k={k}"] = round(us4 / 4, 3)
             dbg = {n: v.cpu().numpy() for n, v in readers[0].decode_debug(X4[0], I4[0], W4[0], k).items()}
-            ub4 = union_bytes(cfg, I4[0].cpu().numpy(), dbg["sel"], dbg["kept"], k)
+            ub4 = read_bytes_batch(cfg, I4[0].cpu().numpy(), dbg["sel"], dbg["kept"], k)["total"]
             batch4[f"k={k}_union_GBps"] = round(ub4 / us4 / 1e3, 1)
         if not args.no_dense:
             us4, _, _ = graph_time(torch, readers, X4, I4, W4, 0, min(args.steps, 400), args.warmup,
@@ -609,7 +580,7 @@ def main():
             ud5, _, _ = graph_time(torch, r5, X5, I5, W5, 0, min(args.steps, 200), args.warmup, fn="dense")
         rb5 = read_bytes(cfg5, k5)
         dbg = {n: v.cpu().numpy() for n, v in r5[0].decode_debug(X5[0], I5[0], W5[0], k5).items()}
-        ub5 = union_bytes(cfg5, I5[0].cpu().numpy(), dbg["sel"], dbg["kept"], k5)
+        ub5 = read_bytes_batch(cfg5, I5[0].cpu().numpy(), dbg["sel"], dbg["kept"], k5)["total"]
         c5 = {"k": k5, "batch": 8, "us_per_token": round(us5 / 8, 3),
               "union_bytes_per_call": ub5, "union_GBps": round(ub5 / us5 / 1e3, 1),
               "read_pct_of_dense": round(100.0 * rb5["total"] / rb5["dense"], 2),

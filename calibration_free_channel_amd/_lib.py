@@ -35,6 +35,8 @@ _P = c_void_p
 SIGNATURES = {
     "cfr_sizes_of": (c_int32, [POINTER(CfrConfig), POINTER(CfrSizes)]),
     "cfr_read_bytes": (c_int32, [POINTER(CfrConfig), c_int32, POINTER(CfrReadStats)]),
+    "cfr_read_bytes_batch": (c_int32, [POINTER(CfrConfig), c_int32, c_int32, _P, _P, _P,
+                                       POINTER(CfrReadStats)]),
     "cfr_build_reader": (c_int32, [POINTER(CfrConfig), _P, _P, _P, _P, POINTER(c_void_p)]),
     "cfr_reader_decode": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P]),
     "cfr_reader_decode_residual": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),

@@ -321,7 +321,7 @@ int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_ep
     return fail(CFR_EUNSUPPORTED, "n_experts too large for the router's top-k");
   DeviceGuard guard(r->cfg.device);
   const hipError_t e = launch_route(x, r->router, r->cfg, batch, x_norm ? norm_eps : -1.f, x_norm, r->rlog,
-                                    r->rarr, expert_ids, gate_w, static_cast<hipStream_t>(stream));
+                                    r->rarr, expert_ids, gate_w, r->status, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? CFR_OK : hipf(e, "route launch");
 }
 

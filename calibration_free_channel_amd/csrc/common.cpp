@@ -2,7 +2,9 @@
 // accounting and the host pack entry point.  No HIP calls in this file.
 #include <string.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "cfr_internal.h"
 
@@ -86,6 +88,62 @@ int cfr_read_bytes(const cfr_config* c, int32_t k, cfr_read_stats* out) {
   out->u = sect(H * (int64_t)c->rank * 2);
   out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
   out->dense = top * 3 * I * H * 2;
+  return CFR_OK;
+}
+
+int cfr_read_bytes_batch(const cfr_config* c, int32_t batch, int32_t k, const int32_t* ids,
+                         const uint8_t* sel, const int32_t* kept, cfr_read_stats* out) {
+  int rc = validate_config(c);
+  if (rc) return rc;
+  if (!out || !ids || !sel || (k > 0 && !kept)) return fail(CFR_EINVAL, "null argument");
+  const int64_t E = c->n_experts, I = c->inter, H = c->hidden, top = c->top, nblk = H / kBlock;
+  const int64_t ns = c->n_screen, nc = top * I;
+  if (batch < 1) return fail(CFR_EINVAL, "batch must be at least 1");
+  if (k < 0 || k > nc) return fail(CFR_EINVAL, "k must be in 0..top*inter");
+  // one flag per sketch unit (expert, block, coordinate), per scale block
+  // (expert, block), per expert, and per channel read exactly / skipped
+  std::vector<uint8_t> unit_seen(E * nblk * kBlock, 0), block_seen(E * nblk, 0), expert_seen(E, 0);
+  std::vector<uint8_t> exact_seen(E * I, 0), skip_seen(E * I, 0), kept_here(nc, 0);
+  int64_t n_unit = 0, n_block = 0, n_expert = 0, n_exact = 0, n_skip = 0;
+  for (int64_t t = 0; t < batch; ++t) {
+    std::fill(kept_here.begin(), kept_here.end(), 0);
+    for (int64_t q = 0; q < k; ++q) {
+      const int32_t cand = kept[t * k + q];
+      if (cand < 0 || cand >= nc) return fail(CFR_EINVAL, "kept candidate out of range");
+      kept_here[cand] = 1;
+    }
+    for (int64_t s = 0; s < top; ++s) {
+      const int32_t e = ids[t * top + s];
+      if (e < 0 || e >= E) return fail(CFR_EINVAL, "expert id out of range");
+      if (!expert_seen[e]) expert_seen[e] = 1, ++n_expert;
+      for (int64_t b = 0; b < nblk; ++b) {
+        if (!block_seen[e * nblk + b]) block_seen[e * nblk + b] = 1, ++n_block;
+        const uint8_t* sb = sel + (t * nblk + b) * ns;
+        for (int64_t q = 0; q < ns; ++q) {
+          if (sb[q] >= kBlock) return fail(CFR_EINVAL, "screened coordinate out of range");
+          uint8_t& u = unit_seen[(e * nblk + b) * kBlock + sb[q]];
+          if (!u) u = 1, ++n_unit;
+        }
+      }
+      for (int64_t j = 0; j < I; ++j) {
+        const bool keep = kept_here[s * I + j] != 0;
+        uint8_t& f = keep ? exact_seen[e * I + j] : skip_seen[e * I + j];
+        if (!f) {
+          f = 1;
+          ++(keep ? n_exact : n_skip);
+        }
+      }
+    }
+  }
+  out->codes = n_unit * sect(unit_bytes(c->inter));
+  out->scales = n_block * sect(2 * I * 2);
+  out->norms = n_expert * sect(I * 4);
+  out->rho = c->ranking == CFR_RANK_EXPECTED_ERROR ? n_block * sect(2 * I * 2) : 0;
+  out->exact = n_exact * sect(3 * H * 2);
+  out->b = n_skip * sect((int64_t)c->rank * 2);
+  out->u = sect(H * (int64_t)c->rank * 2);
+  out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
+  out->dense = n_expert * 3 * I * H * 2;
   return CFR_OK;
 }
 

@@ -138,7 +138,8 @@ struct OncePerDevice {
 size_t route_lds_bytes(const cfr_config& c);
 // eps < 0: route on x; else on h = RMSNorm(x) (unit weights), written to h.
 hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
-                        float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st);
+                        float* h, float* logits, int* arrived, int32_t* ids, float* gw, int32_t* status,
+                        hipStream_t st);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t stream, const float* resid = nullptr);
 

@@ -24,6 +24,19 @@ namespace {
 
 constexpr int kRouteThreads = 512;  // eight experts per workgroup, one per wave
 
+// Total order on logits: a larger float gives a larger key; NaN takes key 0,
+// below every other value (including -inf), so the ranks below always form a
+// permutation of the experts.
+__device__ __forceinline__ uint32_t route_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// the float a key came from (NaN for key 0)
+__device__ __forceinline__ float route_unkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ float route_wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -40,10 +53,11 @@ __device__ __forceinline__ float route_wave_sum(float v) {
 template <int CH>
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* x, const uint16_t* router, int H, int E,
                                                          int top, float eps, float* h, float* logits,
-                                                         int* arrived, int32_t* ids, float* gw) {
-  // the last workgroup: the logits padded to a multiple of 4 with -inf, then
-  // each expert's rank
-  extern __shared__ float4 lg4[];
+                                                         int* arrived, int32_t* ids, float* gw,
+                                                         int32_t* status) {
+  // the last workgroup: the logits' order keys padded to a multiple of 4 with
+  // key 0, then each expert's rank
+  extern __shared__ uint4 lg4[];
   __shared__ int last;
   __shared__ float selv[kMaxTop];
   const int t = blockIdx.y;
@@ -120,26 +134,33 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* x, const u
   __syncthreads();
   if (!last) return;
   const int E4 = (E + 3) / 4;
-  float* lg = reinterpret_cast<float*>(lg4);
+  uint32_t* lg = reinterpret_cast<uint32_t*>(lg4);
   int* rank = reinterpret_cast<int*>(lg4 + E4);
+  bool bad = false;
   for (int i = threadIdx.x; i < 4 * E4; i += kRouteThreads) {
-    lg[i] = i < E ? __uint_as_float(atomicOr(reinterpret_cast<unsigned*>(lt) + i, 0u)) : -INFINITY;
+    const float v = i < E ? __uint_as_float(atomicOr(reinterpret_cast<unsigned*>(lt) + i, 0u)) : 0.f;
+    bad |= !isfinite(v);
+    lg[i] = i < E ? route_key(v) : 0u;
     if (i < E) rank[i] = 0;
   }
+  // a non-finite logit (from a non-finite token, or inf * 0 in the norm):
+  // bit 1 of the reader's status word
+  if (bad) atomicOr(status, 2);
   if (threadIdx.x == 0) atomicExch(arrived + t, 0);  // no workgroup of this launch counts again
   __syncthreads();
-  // rank of expert e = the experts ahead of it (a larger logit, or an equal
-  // one with a lower index); P threads count it, each over its share of the
-  // logits (read four at a time), and add their counts in LDS
+  // rank of expert e = the experts ahead of it (a larger key, or an equal one
+  // with a lower index); P threads count it, each over its share of the keys
+  // (read four at a time), and add their counts in LDS.  Padding (index >= E,
+  // key 0) is never ahead of an expert.
   const int P = max(1, min(16, kRouteThreads / E));
   const int L = (E4 + P - 1) / P;
   for (int idx = threadIdx.x; idx < E * P; idx += kRouteThreads) {
     const int j = idx / P, part = idx - j * P;
-    const float v = lg[j];
+    const uint32_t v = lg[j];
     const int q1 = min(E4, (part + 1) * L);
     int cnt = 0;
     for (int q = part * L; q < q1; ++q) {
-      const float4 o = lg4[q];
+      const uint4 o = lg4[q];
       const int i = 4 * q;
       cnt += (o.x > v) | ((o.x == v) & (i < j));
       cnt += (o.y > v) | ((o.y == v) & (i + 1 < j));
@@ -153,7 +174,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* x, const u
     const int k = rank[j];
     if (k < top) {
       ids[(size_t)t * top + k] = j;
-      selv[k] = lg[j];
+      selv[k] = route_unkey(lg[j]);
     }
   }
   __syncthreads();
@@ -165,7 +186,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* x, const u
 
 template <int CH>
 hipError_t launch_route_t(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
-                          float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st) {
+                          float* h, float* logits, int* arrived, int32_t* ids, float* gw, int32_t* status,
+                          hipStream_t st) {
   static OncePerDevice attr;
   attr([] {
     (void)hipFuncSetAttribute((const void*)k_route<CH>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -174,7 +196,7 @@ hipError_t launch_route_t(const float* x, const uint16_t* router, const cfr_conf
   });
   const int per = kRouteThreads / 64;
   k_route<CH><<<dim3((c.n_experts + per - 1) / per, batch), kRouteThreads, route_lds_bytes(c), st>>>(
-      x, router, c.hidden, c.n_experts, c.top, eps, h, logits, arrived, ids, gw);
+      x, router, c.hidden, c.n_experts, c.top, eps, h, logits, arrived, ids, gw, status);
   return hipGetLastError();
 }
 
@@ -185,14 +207,15 @@ size_t route_lds_bytes(const cfr_config& c) {
 }
 
 hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config& c, int batch, float eps,
-                        float* h, float* logits, int* arrived, int32_t* ids, float* gw, hipStream_t st) {
+                        float* h, float* logits, int* arrived, int32_t* ids, float* gw, int32_t* status,
+                        hipStream_t st) {
   // chunks of 8 per lane: the fewest of 1, 2, 4, 8 that cover hidden / 8
   static_assert(kMaxHidden / 8 <= 64 * 8, "eight chunks per lane cover the largest token");
   const int need = (c.hidden / 8 + 63) / 64;
-  if (need <= 1) return launch_route_t<1>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
-  if (need <= 2) return launch_route_t<2>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
-  if (need <= 4) return launch_route_t<4>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
-  return launch_route_t<8>(x, router, c, batch, eps, h, logits, arrived, ids, gw, st);
+  if (need <= 1) return launch_route_t<1>(x, router, c, batch, eps, h, logits, arrived, ids, gw, status, st);
+  if (need <= 2) return launch_route_t<2>(x, router, c, batch, eps, h, logits, arrived, ids, gw, status, st);
+  if (need <= 4) return launch_route_t<4>(x, router, c, batch, eps, h, logits, arrived, ids, gw, status, st);
+  return launch_route_t<8>(x, router, c, batch, eps, h, logits, arrived, ids, gw, status, st);
 }
 
 }  // namespace cfr

@@ -51,6 +51,23 @@ def read_bytes(cfg: Config, k: int) -> dict:
     return {f: getattr(s, f) for f, _ in CfrReadStats._fields_}
 
 
+def read_bytes_batch(cfg: Config, expert_ids, sel, kept, k: int) -> dict:
+    """Distinct 32-byte sectors one batched decode call reads (the library's
+    union count), from the call's expert ids [B][top], screened coordinates
+    [B][nblk][n_screen] and kept candidates [B][k] (host arrays, as
+    decode_debug returns them)."""
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    sel = np.ascontiguousarray(sel, dtype=np.uint8)
+    kept = np.ascontiguousarray(np.asarray(kept)[:, :k], dtype=np.int32)
+    B = ids.shape[0]
+    if ids.shape != (B, cfg.top) or sel.shape != (B, cfg.hidden // 128, cfg.n_screen) or kept.shape != (B, k):
+        raise ValueError("expert_ids [B][top], sel [B][nblk][n_screen] and kept [B][k] expected")
+    s = CfrReadStats()
+    check(load().cfr_read_bytes_batch(ctypes.byref(cfg.c()), B, int(k), _ptr(ids), _ptr(sel),
+                                      _ptr(kept) if k > 0 else None, ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in CfrReadStats._fields_}
+
+
 def _u16(a, shape, name):
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16 or a.shape != tuple(shape):

@@ -111,6 +111,26 @@ int cfr_sizes_of(const cfr_config* cfg, cfr_sizes* out);
 int cfr_read_bytes(const cfr_config* cfg, int32_t k, cfr_read_stats* out);
 
 /*
+ * Distinct reads of one batched decode call, in whole 32-byte sectors
+ * ([zh §前置知识 / 显存带宽受限的解码]: every touched sector is charged, once):
+ * the union over the batch's tokens of the sketch units of the screened
+ * coordinates, the scale (and, for CFR_RANK_EXPECTED_ERROR, rho) blocks and
+ * the norm rows of the routed experts, the exact rows of every channel some
+ * token keeps, the b rows of every channel some token skips, and U once.
+ * A sector several tokens read counts once.  `dense` is the BF16 bytes of
+ * the distinct routed experts.  Inputs, host memory, as cfr_reader_decode_debug
+ * returns them for the call:
+ *   expert_ids int32 [batch][top]   sel uint8 [batch][H/128][n_screen]
+ *   kept       int32 [batch][k]     (candidates slot * I + j; NULL if k = 0)
+ * With batch = 1 and distinct ids and coordinates the result equals
+ * cfr_read_bytes(cfg, k).  Host only.  CFR_EINVAL for a null pointer,
+ * batch < 1, k outside 0..top*I, or an id, coordinate or candidate out of
+ * range.
+ */
+int cfr_read_bytes_batch(const cfr_config* cfg, int32_t batch, int32_t k, const int32_t* expert_ids,
+                         const uint8_t* sel, const int32_t* kept, cfr_read_stats* out);
+
+/*
  * Load-time work for one layer ([zh §方法步骤详情] load steps (1)-(4);
  * [ko §어떻게 쓰나]):
  *   (1) rotate every gate/up row per 128-block and store TWN ternary codes,
@@ -196,10 +216,14 @@ int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* expert
  * share its logit buffer and per-token arrival counters): serialise them on
  * one stream or clone the reader.  Float32 logits: experts whose logits
  * differ by a few float32 ulps from the top-th may be ordered differently
- * from a float64 computation.  CFR_EINVAL if the reader was built without
- * router weights, batch is outside 1..max_batch, norm_eps < 0 with x_norm
- * given, or x_norm aliases x; CFR_EUNSUPPORTED if the pick's 8 bytes of LDS
- * per expert do not fit one workgroup (n_experts above about 20 000).
+ * from a float64 computation.  A NaN logit ranks below every other value
+ * (ties to the lower index), so every slot of expert_ids is written with
+ * distinct experts; any non-finite logit sets bit 1 of the reader's status
+ * word (cfr_reader_status) and leaves that token's weights unspecified.
+ * CFR_EINVAL if the reader was built without router weights, batch is
+ * outside 1..max_batch, norm_eps < 0 with x_norm given, or x_norm aliases x;
+ * CFR_EUNSUPPORTED if the pick's 8 bytes of LDS per expert do not fit one
+ * workgroup (n_experts above about 20 000).
  */
 int cfr_reader_route(cfr_reader* r, const float* x, int32_t batch, float norm_eps, float* x_norm,
                      int32_t* expert_ids, float* gate_w, void* stream);
@@ -276,7 +300,8 @@ int cfr_reader_clone(const cfr_reader* src, cfr_reader** out);
 int cfr_reader_config(const cfr_reader* r, cfr_config* out);
 
 /* Read (and clear) the reader's device status word: bit 0 = an expert id
- * was out of range and clamped.  Synchronises the reader's device. */
+ * was out of range and clamped; bit 1 = a router logit was not finite
+ * (cfr_reader_route).  Synchronises the reader's device. */
 int cfr_reader_status(cfr_reader* r, int32_t* flags);
 
 /* Release the reader and all its device memory.  NULL-safe. */

@@ -22,7 +22,7 @@ Parity status per function (what pins it) is listed in each module header.
 """
 from .numerics import bf16_to_f64, f64_to_f16_bits, f16_bits_to_f64
 from .rotation import (splitmix64_stream, sign_vector, sylvester_hadamard,
-                       rotate_rows, rotate_x_f64, rotate_x_f32_unscaled,
+                       rotate_rows, rotate_x_f64,
                        rotation_matrix, SQRT128)
 from .sketch import ternarize_blocks, unit_geometry, pack_units, unpack_units
 from .lowrank import recovery_basis
@@ -37,7 +37,7 @@ from .reader import OracleReader
 __all__ = [
     "bf16_to_f64", "f64_to_f16_bits", "f16_bits_to_f64", "splitmix64_stream",
     "sign_vector", "sylvester_hadamard", "rotate_rows", "rotate_x_f64",
-    "rotate_x_f32_unscaled", "rotation_matrix", "SQRT128", "ternarize_blocks",
+    "rotation_matrix", "SQRT128", "ternarize_blocks",
     "unit_geometry", "pack_units", "unpack_units", "recovery_basis", "dense_moe",
     "route", "topk_desc", "read_bytes", "resident_bytes", "OracleReader", "silu_grad",
     "block_norms2", "sketch_variance", "activation_variance", "expected_error_score",

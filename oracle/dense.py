@@ -6,8 +6,10 @@ sum_j a_j d_j ([zh §前置知识 / 门控MLP与通道]).  The MoE block output 
 routing-weighted sum over the token's routed experts.  phi is SiLU,
 phi(z) = z / (1 + exp(-z)) (reading: the Qwen3 family the pages evaluate).
 
-Pins (tests/test_oracle_reader.py): a hand-worked one-channel case and the
-per-channel sum form  sum_j w a_j d_j  on random data.
+Pins (tests/test_oracle_reader.py): hand-worked cases with exact BF16 values
+(one expert and one channel at H = 2; two weighted experts), which fix the
+orientation of D, the activation and the routing weight; the reader's
+per-channel decode at k = all channels equals this function on random data.
 """
 import numpy as np
 

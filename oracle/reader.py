@@ -27,10 +27,9 @@ Readings of open points (each also listed in the design notes):
   * score bars: s_j = w_j ||d_j|| * |phi(g_hat_j) * v_hat_j|, the absolute value
     of the whole product ([ko §어떻게 쓰나] derives it from the output
     contribution w_j ||d_j|| |a_j|);
-  * no rescaling of the partial screen; ties in the coordinate ranking go to
-    the lower index; the same coordinates serve gate, up and every expert;
-  * the ranking is taken on the float32 butterfly values (see rotation);
-    all arithmetic after it uses float64 R x;
+  * no rescaling of the partial screen; the coordinates are ranked by the
+    float64 |R x|, ties to the lower index; the same coordinates serve gate,
+    up and every expert;
   * stored formats: scales, rho, U and b in fp16 (round to nearest even),
     norms in fp32; the oracle computes with those stored values;
   * the exact part multiplies native (unrotated) BF16 rows with the token x.
@@ -48,7 +47,7 @@ printed worked example: beyond those identities they are parity unpinned.
 import numpy as np
 
 from .numerics import bf16_to_f64, f64_to_f16_bits, f16_bits_to_f64
-from .rotation import sign_vector, rotate_rows, rotate_x_f64, rotate_x_f32_unscaled
+from .rotation import sign_vector, rotate_rows, rotate_x_f64
 from .sketch import ternarize_blocks, pack_units
 from .lowrank import recovery_basis
 from .dense import silu
@@ -111,14 +110,15 @@ class OracleReader:
 
     # -- decode -------------------------------------------------------------
     def select(self, x):
-        """Per block, the n_screen coordinates of largest |R x| (ascending index)."""
-        v = rotate_x_f32_unscaled(x, self.sigma, self.block)  # [nb][128] float32
+        """R x (float64, [nblk][128]) and, per block, the n_screen coordinates of
+        largest |R x|, ties to the lower index, in ascending order."""
+        xr = rotate_x_f64(np.asarray(x, dtype=np.float32).astype(np.float64), self.sigma, self.block)
         sel = np.empty((self.nblk, self.n_screen), dtype=np.int64)
         idx = np.arange(self.block)
         for b in range(self.nblk):
-            order = np.lexsort((idx, -np.abs(v[b])))
+            order = np.lexsort((idx, -np.abs(xr[b])))
             sel[b] = np.sort(order[:self.n_screen])
-        return v, sel
+        return xr, sel
 
     def screen(self, x, ids, sel):
         xr = rotate_x_f64(np.asarray(x, dtype=np.float32).astype(np.float64), self.sigma, self.block)
@@ -136,17 +136,20 @@ class OracleReader:
                 est[m, s] = acc
         return est[0], est[1]
 
-    def decode(self, x, ids, w, k, kept=None, ranking="score"):
+    def decode(self, x, ids, w, k, kept=None, ranking="score", sel=None):
         """One token.  Returns a dict of every intermediate and y (float64 [H]).
 
         ranking="score": the output-unit score s_j (budgets below 28.7%);
         ranking="expected_error": e_j from the whole sketch and rho
-        (n_screen must be 128); "score" then holds e_j."""
+        (n_screen must be 128); "score" then holds e_j.
+        kept / sel, when given, replace the kept set / the screened coordinates
+        (for comparisons where neighbouring values tie within rounding)."""
         H, I = self.H, self.I
         ids = np.asarray(ids, dtype=np.int64)
         w = np.asarray(w, dtype=np.float32).astype(np.float64)
         x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
-        v32, sel = self.select(x)
+        xr, own_sel = self.select(x)
+        sel = own_sel if sel is None else np.sort(np.asarray(sel, dtype=np.int64), axis=-1)
         ghat, vhat = self.screen(x, ids, sel)
         p = silu(ghat) * vhat
         dn = self.norms[ids].astype(np.float64)
@@ -178,7 +181,7 @@ class OracleReader:
         coef = w[s_slot] * p.reshape(-1)[sk]
         z = coef @ self.b[ids[s_slot], s_j] if sk.size else np.zeros(self.rank)
         y_rec = self.U @ z
-        return {"v32": v32, "sel": sel, "ghat": ghat, "vhat": vhat, "p": p,
+        return {"xr": xr, "sel": sel, "ranking": ranking, "ghat": ghat, "vhat": vhat, "p": p,
                 "score": score, "kept": kk, "a": a, "y_exact": y_exact, "z": z,
                 "y_rec": y_rec, "y": y_exact + y_rec}
 

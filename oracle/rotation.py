@@ -17,20 +17,14 @@ Reading of what the pages leave open (the library implements the same):
     advances by 0x9E3779B97F4A7C15 and each output is the state passed
     through the finalizer  z ^= z>>30; z *= 0xBF58476D1CE4E5B9;
     z ^= z>>27; z *= 0x94D049BB133111EB; z ^= z>>31  (all mod 2^64).
-  * The partial screen ranks coordinates by |(R x)_i|.  That decision is an
-    integer outcome of floating point, so the oracle takes it on the same
-    float32 values the kernel computes: the un-normalised transform
-    v = H_128 (sigma * x) evaluated by the in-place butterfly
-    for h = 1, 2, 4, ..., 64: (v_i, v_{i+h}) <- (v_i + v_{i+h}, v_i - v_{i+h})
-    for every i with i & h == 0, in float32 (no fused multiply-add; the
-    1/sqrt(128) factor is left out because a positive scale cannot change
-    the ranking, and leaving it out avoids ties that the extra rounding
-    could create).
+  * The partial screen ranks coordinates by |(R x)_i|, evaluated here in
+    float64 (the module reader takes the ranking on these values; ties go to
+    the lower index).
 
 Pins (tests/test_oracle_rotation.py): H_128 equals scipy.linalg.hadamard(128)
-and the explicit recursion; R^T R = I; g^T x = (Rg)^T (Rx); the float32
-butterfly equals the exact transform on integer inputs; SplitMix64's first
-outputs for seed 0 equal the generator's published reference values.
+and the explicit recursion; R^T R = I; g^T x = (Rg)^T (Rx); R x of a one-hot
+block is +-1/sqrt(128) everywhere; SplitMix64's first outputs for seed 0 equal
+the generator's published reference values.
 """
 import numpy as np
 
@@ -93,20 +87,3 @@ def rotate_rows(w: np.ndarray, sigma: np.ndarray, block: int = 128) -> np.ndarra
 def rotate_x_f64(x: np.ndarray, sigma: np.ndarray, block: int = 128) -> np.ndarray:
     """R x in float64, shape [..., H/128, 128]."""
     return rotate_rows(x, sigma, block) / SQRT128
-
-
-def rotate_x_f32_unscaled(x: np.ndarray, sigma: np.ndarray, block: int = 128) -> np.ndarray:
-    """H_128 (sigma * x) per block by the float32 butterfly; shape [..., H/128, 128]."""
-    x = np.asarray(x, dtype=np.float32)
-    hid = x.shape[-1]
-    nb = hid // block
-    v = (x * sigma.astype(np.float32)).reshape(x.shape[:-1] + (nb, block)).astype(np.float32)
-    h = 1
-    while h < block:
-        shp = v.shape[:-1] + (block // (2 * h), 2, h)
-        vv = v.reshape(shp)
-        a = vv[..., 0, :]
-        b = vv[..., 1, :]
-        v = np.stack([a + b, a - b], axis=-2).reshape(v.shape)
-        h *= 2
-    return v

@@ -165,3 +165,36 @@ def test_route_needs_router_weights():
             r.route(torch.from_numpy(make_tokens(wl, 1)).cuda())
     finally:
         r.close()
+
+
+def test_route_non_finite_token_is_flagged_and_ranks_stay_a_permutation():
+    # a NaN in one token makes every logit of that token NaN; an infinite
+    # coordinate makes them +-inf or NaN.  The ranks must still place each
+    # expert once (distinct ids in range, every slot written), the other
+    # tokens of the batch are routed as usual, and bit 1 of the status word
+    # records the non-finite logits.
+    wl = workload("tiny")
+    s = wl.shape
+    layer = make_layer(wl)
+    r = Reader.build(Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top,
+                            rot_seed=wl.rot_seed, max_batch=4),
+                     layer["gate"], layer["up"], layer["down"], layer["router"])
+    try:
+        assert r.status() == 0
+        X = make_tokens(wl, 4, seed_offset=9)
+        X[1, 5] = np.nan
+        X[3, 17] = np.inf
+        ids_out = torch.full((4, s.top), -7, dtype=torch.int32, device="cuda")
+        ids, w = r.route(torch.from_numpy(X).cuda(), ids_out=ids_out)
+        ids, w = ids.cpu().numpy(), w.cpu().numpy()
+        for t in range(4):
+            assert len(set(ids[t].tolist())) == s.top and ids[t].min() >= 0 and ids[t].max() < s.n_experts
+        _check(ids[[0, 2]], w[[0, 2]], layer["router"], X[[0, 2]], s.top)
+        # an all-NaN token: every key ties, so the lowest indices win
+        assert ids[1].tolist() == list(range(s.top))
+        assert r.status() & 2
+        # the flag is cleared by reading it, and finite tokens do not set it
+        r.route(torch.from_numpy(X[[0, 2]]).cuda())
+        assert r.status() == 0
+    finally:
+        r.close()

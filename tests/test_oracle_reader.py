@@ -177,8 +177,46 @@ def test_ternary_screen_on_exactly_ternary_rows():
             assert np.allclose(est[s], ref, rtol=1e-12, atol=1e-14)
 
 
+def _bits(a):
+    return f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def test_dense_hand_worked_one_channel():
+    # H = 2, one expert, one channel: g = (2, 0), v = (3, 0), d = (1, -1),
+    # x = (1, 0): g.x = 2, v.x = 3, so y = 3 phi(2) (1, -1) with
+    # phi(2) = 2 / (1 + e^-2).  A transposed D, a wrong activation or a
+    # dropped weight gives another vector.
+    gate = _bits([[[2.0, 0.0]]])          # [E][I][H]
+    up = _bits([[[3.0, 0.0]]])
+    down = _bits([[[1.0], [-1.0]]])       # [E][H][I]: column j is d_j
+    y = dense_moe(gate, up, down, np.array([1.0, 0.0]), [0], [1.0])
+    phi2 = 2.0 / (1.0 + np.exp(-2.0))
+    assert np.allclose(y, [3.0 * phi2, -3.0 * phi2], rtol=1e-15, atol=0)
+
+
+def test_dense_hand_worked_two_experts_weighted():
+    # expert 0 as above; expert 1: g = (0, 1), v = (1, 1), d = (2, 0).
+    # x = (1, -2): expert 0 has g.x = 2, v.x = 3, a = 3 phi(2); expert 1 has
+    # g.x = -2, v.x = -1, a = -phi(-2) = 2 / (1 + e^2).  Weights 0.75, 0.25:
+    # y = 0.75 * 3 phi(2) (1, -1) + 0.25 * 2/(1 + e^2) (2, 0).
+    gate = _bits([[[2.0, 0.0]], [[0.0, 1.0]]])
+    up = _bits([[[3.0, 0.0]], [[1.0, 1.0]]])
+    down = _bits([[[1.0], [-1.0]], [[2.0], [0.0]]])
+    x = np.array([1.0, -2.0])
+    phi2 = 2.0 / (1.0 + np.exp(-2.0))
+    a1 = 2.0 / (1.0 + np.exp(2.0))
+    want = 0.75 * 3.0 * phi2 * np.array([1.0, -1.0]) + 0.25 * a1 * np.array([2.0, 0.0])
+    y = dense_moe(gate, up, down, x, [0, 1], [0.75, 0.25])
+    assert np.allclose(y, want, rtol=1e-15, atol=1e-16)
+    # the routed order does not matter; an expert not routed does not count
+    assert np.allclose(dense_moe(gate, up, down, x, [1, 0], [0.25, 0.75]), want, rtol=1e-15, atol=1e-16)
+    assert np.allclose(dense_moe(gate, up, down, x, [0], [0.75]),
+                       0.75 * 3.0 * phi2 * np.array([1.0, -1.0]), rtol=1e-15, atol=0)
+
+
 def test_score_is_norm_of_channel_contribution(tiny_layer):
-    # exact sketch + full screen: g_hat = g^T x, so s_j = ||w a_j d_j||_2
+    # exact sketch + full screen: g_hat = g^T x, so s_j = ||w a_j d_j||_2, the
+    # norm of the dense block's output with every other down column zeroed
     r = _reader(tiny_layer, sketch="exact", n_screen=128)
     x = _tokens(1)[0]
     ids, w, _ = route(tiny_layer["router"], x, S.top)
@@ -186,12 +224,12 @@ def test_score_is_norm_of_channel_contribution(tiny_layer):
     out = r.decode(x, ids, w32, 10)
     assert (out["ghat"] < 0).any()
     for s, e in enumerate(ids):
-        g = bf16_to_f64(tiny_layer["gate"][e]) @ x.astype(np.float64)
-        v = bf16_to_f64(tiny_layer["up"][e]) @ x.astype(np.float64)
-        a = silu(g) * v
-        d = bf16_to_f64(tiny_layer["down"][e])  # [H][I]
-        contrib = np.linalg.norm(np.float64(w32[s]) * a[None, :] * d, axis=0)
-        assert np.allclose(out["score"][s], contrib, rtol=1e-6, atol=1e-12)
+        for j in range(S.inter):
+            down = np.zeros_like(tiny_layer["down"])
+            down[e, :, j] = tiny_layer["down"][e, :, j]
+            contrib = dense_moe(tiny_layer["gate"], tiny_layer["up"], down, x.astype(np.float64),
+                                [e], [np.float64(w32[s])])
+            assert np.isclose(out["score"][s, j], np.linalg.norm(contrib), rtol=1e-6, atol=1e-12)
 
 
 def test_scores_nonnegative_and_norms(tiny_reader, tiny_layer):

@@ -2,8 +2,8 @@
 import numpy as np
 import scipy.linalg
 
-from oracle.rotation import (SQRT128, rotate_rows, rotate_x_f64, rotate_x_f32_unscaled,
-                             rotation_matrix, sign_vector, splitmix64_stream, sylvester_hadamard)
+from oracle.rotation import (SQRT128, rotate_rows, rotate_x_f64, rotation_matrix,
+                             sign_vector, splitmix64_stream, sylvester_hadamard)
 
 
 def test_sylvester_equals_scipy_and_recursion():
@@ -43,15 +43,16 @@ def test_splitmix64_reference_outputs():
                                              0x883EBCE5A3F27C77]
 
 
-def test_f32_butterfly_exact_on_integers_and_close_otherwise():
-    rng = np.random.default_rng(1)
+def test_one_hot_block_rotates_to_signed_constant():
+    # R e_i = sigma_i h_i / sqrt(128): every coordinate of the block has
+    # magnitude 1/sqrt(128), with the signs of column i of H_128 times sigma_i
     sig = sign_vector(99, 256)
-    xi = rng.integers(-1000, 1000, 256).astype(np.float32)
-    v = rotate_x_f32_unscaled(xi, sig)
-    exact = (sylvester_hadamard(128) @ (xi.astype(np.float64) * sig).reshape(2, 128).T).T
-    assert np.array_equal(v.astype(np.float64), exact)
-    x = rng.standard_normal(256).astype(np.float32)
-    v = rotate_x_f32_unscaled(x, sig).astype(np.float64)
-    ref = rotate_rows(x.astype(np.float64), sig)
-    assert np.abs(v - ref).max() < 1e-5 * np.abs(ref).max()
-    assert rotate_x_f32_unscaled(x, sig).dtype == np.float32
+    h = sylvester_hadamard(128)
+    for i in (0, 1, 77, 128, 200, 255):
+        x = np.zeros(256)
+        x[i] = 1.0
+        rx = rotate_x_f64(x, sig)
+        b, c = divmod(i, 128)
+        assert np.array_equal(np.abs(rx[b]), np.full(128, 1.0 / SQRT128))
+        assert np.array_equal(np.sign(rx[b]), sig[i] * h[:, c])
+        assert not rx[1 - b].any()
