@@ -33,7 +33,8 @@ struct DeviceGuard {
 
 // Workspace, sized for max_batch (see the field comments on cfr_reader).
 struct WorkspaceLayout {
-  size_t acc, var, rlog, rarr, ypart, zpart, xrot, sel, ghat, vhat, score, kept, status, total;
+  size_t acc, var, rlog, rarr, rowid, coef, zpk, ltag, ctag, ztag, xrot, sel, ghat, vhat, score, kept, status,
+      total;
   explicit WorkspaceLayout(const cfr_reader& r) {
     const cfr_config& c = r.cfg;
     const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
@@ -49,8 +50,12 @@ struct WorkspaceLayout {
     var = take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0);
     rlog = take(sizeof(float) * B * c.n_experts);
     rarr = take(sizeof(int32_t) * B);
-    ypart = take(sizeof(float) * kMaxGatherWgs * H);
-    zpart = take(sizeof(float) * B * kMaxRecoverWgs * R);
+    rowid = take(sizeof(unsigned long long) * B * nc);
+    coef = take(sizeof(unsigned long long) * B * nc);
+    zpk = take(sizeof(unsigned long long) * B * kMaxRecoverWgs * R);
+    ltag = take(sizeof(uint32_t) * B * kMaxGatherWgs);
+    ctag = take(sizeof(uint32_t) * B * kMaxGatherWgs);
+    ztag = take(sizeof(uint32_t) * B * kMaxRecoverWgs);
     xrot = take(sizeof(float) * B * H);
     sel = take(B * r.nblk * c.n_screen);
     ghat = take(sizeof(float) * B * nc);
@@ -71,8 +76,12 @@ void carve_workspace(cfr_reader& r) {
   r.var = reinterpret_cast<float*>(p + l.var);
   r.rlog = reinterpret_cast<float*>(p + l.rlog);
   r.rarr = reinterpret_cast<int32_t*>(p + l.rarr);
-  r.ypart = reinterpret_cast<float*>(p + l.ypart);
-  r.zpart = reinterpret_cast<float*>(p + l.zpart);
+  r.rowid = reinterpret_cast<unsigned long long*>(p + l.rowid);
+  r.coef = reinterpret_cast<unsigned long long*>(p + l.coef);
+  r.zpk = reinterpret_cast<unsigned long long*>(p + l.zpk);
+  r.ltag = reinterpret_cast<uint32_t*>(p + l.ltag);
+  r.ctag = reinterpret_cast<uint32_t*>(p + l.ctag);
+  r.ztag = reinterpret_cast<uint32_t*>(p + l.ztag);
   r.xrot = reinterpret_cast<float*>(p + l.xrot);
   r.sel = reinterpret_cast<uint8_t*>(p + l.sel);
   r.ghat = reinterpret_cast<float*>(p + l.ghat);
@@ -284,7 +293,7 @@ int cfr_reader_decode_stage(cfr_reader* r, int32_t stage, const float* x, const 
                             const float* gw, int32_t batch, int32_t k, float* y, void* stream) {
   int rc = check_decode_args(r, x, ids, gw, batch, k, y);
   if (rc) return rc;
-  if (stage < 0 || stage >= CFR_NUM_STAGES) return fail(CFR_EINVAL, "stage out of range");
+  if (stage < 0 || stage > CFR_NUM_STAGES) return fail(CFR_EINVAL, "stage out of range");
   DeviceGuard guard(r->cfg.device);
   return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr,
                        nullptr, stage);

@@ -68,8 +68,13 @@ struct cfr_reader {
   float* var = nullptr;        // [B][2][ncp] sketch-error variances of g_hat, v_hat' (expected-error ranking)
   float* rlog = nullptr;       // [B][E] router logits (cfr_reader_route)
   int32_t* rarr = nullptr;     // [B] workgroups of the route that have finished; zero between calls
-  float* ypart = nullptr;      // [B][kMaxGatherWgs][H]  partial outputs of the gather workgroups
-  float* zpart = nullptr;      // [B][kMaxRecoverWgs][rank]  partial recovery vectors
+  // hand-over words of the select kernel ((launch tag << 32) | payload)
+  unsigned long long* rowid = nullptr;  // [B][ncand]  kept channel row of each rank
+  unsigned long long* coef = nullptr;   // [B][ncand]  w a_j of each rank
+  unsigned long long* zpk = nullptr;    // [B][kMaxRecoverWgs][rank]  partial recovery vectors
+  uint32_t* ltag = nullptr;             // [B][kMaxGatherWgs]  rows published (launch tag)
+  uint32_t* ctag = nullptr;             // [B][kMaxGatherWgs]  coefficients published
+  uint32_t* ztag = nullptr;             // [B][kMaxRecoverWgs]  recovery partial published
   float* xrot = nullptr;       // [B][H]   H_128 (sigma x) per block (debug copy only)
   uint8_t* sel = nullptr;      // [B][nblk][n_screen] (debug copy only)
   float* ghat = nullptr;       // [B][ncand] (debug copy only)
