@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <memory>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -31,14 +32,13 @@ struct DeviceGuard {
   }
 };
 
-// Workspace, sized for max_batch (see the field comments on cfr_reader).
+// The reader's own workspace: the decode's buffers for max_batch tokens (with
+// the debug copies), then the router's logits and arrival counters and the
+// status word.
 struct WorkspaceLayout {
-  size_t acc, var, rlog, rarr, rowid, coef, zpk, ltag, ctag, ztag, xrot, sel, ghat, vhat, score, kept, status,
-      total;
+  size_t decode, rlog, rarr, status, total;
   explicit WorkspaceLayout(const cfr_reader& r) {
     const cfr_config& c = r.cfg;
-    const size_t B = c.max_batch, H = c.hidden, nc = r.ncand;
-    const size_t R = c.rank > 0 ? c.rank : 1;
     auto rnd = [](size_t n) { return (n + 255) / 256 * 256; };
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -46,22 +46,9 @@ struct WorkspaceLayout {
       o += rnd(bytes);
       return at;
     };
-    acc = take(sizeof(unsigned long long) * B * 2 * r.ncp);
-    var = take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0);
-    rlog = take(sizeof(float) * B * c.n_experts);
-    rarr = take(sizeof(int32_t) * B);
-    rowid = take(sizeof(unsigned long long) * B * nc);
-    coef = take(sizeof(unsigned long long) * B * nc);
-    zpk = take(sizeof(unsigned long long) * B * kMaxRecoverWgs * R);
-    ltag = take(sizeof(uint32_t) * B * kMaxGatherWgs);
-    ctag = take(sizeof(uint32_t) * B * kMaxGatherWgs);
-    ztag = take(sizeof(uint32_t) * B * kMaxRecoverWgs);
-    xrot = take(sizeof(float) * B * H);
-    sel = take(B * r.nblk * c.n_screen);
-    ghat = take(sizeof(float) * B * nc);
-    vhat = take(sizeof(float) * B * nc);
-    score = take(sizeof(float) * B * nc);
-    kept = take(sizeof(int32_t) * B * nc);
+    decode = take(carve_decode_workspace(r, c.max_batch, true, nullptr, nullptr));
+    rlog = take(sizeof(float) * c.max_batch * c.n_experts);
+    rarr = take(sizeof(int32_t) * c.max_batch);
     status = take(sizeof(int32_t));
     total = o;
   }
@@ -72,22 +59,9 @@ size_t workspace_bytes(const cfr_reader& r) { return WorkspaceLayout(r).total; }
 void carve_workspace(cfr_reader& r) {
   const WorkspaceLayout l(r);
   char* p = static_cast<char*>(r.ws);
-  r.acc = reinterpret_cast<unsigned long long*>(p + l.acc);
-  r.var = reinterpret_cast<float*>(p + l.var);
+  carve_decode_workspace(r, r.cfg.max_batch, true, p + l.decode, &r.wk);
   r.rlog = reinterpret_cast<float*>(p + l.rlog);
   r.rarr = reinterpret_cast<int32_t*>(p + l.rarr);
-  r.rowid = reinterpret_cast<unsigned long long*>(p + l.rowid);
-  r.coef = reinterpret_cast<unsigned long long*>(p + l.coef);
-  r.zpk = reinterpret_cast<unsigned long long*>(p + l.zpk);
-  r.ltag = reinterpret_cast<uint32_t*>(p + l.ltag);
-  r.ctag = reinterpret_cast<uint32_t*>(p + l.ctag);
-  r.ztag = reinterpret_cast<uint32_t*>(p + l.ztag);
-  r.xrot = reinterpret_cast<float*>(p + l.xrot);
-  r.sel = reinterpret_cast<uint8_t*>(p + l.sel);
-  r.ghat = reinterpret_cast<float*>(p + l.ghat);
-  r.vhat = reinterpret_cast<float*>(p + l.vhat);
-  r.score = reinterpret_cast<float*>(p + l.score);
-  r.kept = reinterpret_cast<int32_t*>(p + l.kept);
   r.status = reinterpret_cast<int32_t*>(p + l.status);
 }
 
@@ -170,9 +144,76 @@ int check_decode_args(cfr_reader* r, const void* x, const void* ids, const void*
   return CFR_OK;
 }
 
+// Scratch of the allocation-free decode: the decode's per-call buffers
+// live in this file-scope array (each device holds its own copy, for as long
+// as the library stays loaded).  Host code must not pass the array's name to
+// a kernel: it is a host-side stand-in.  Its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchDevices {
+  std::mutex m;
+  void* ptr[kMaxDevices] = {};
+  // leading bytes of the array known to be zero: the screen accumulates its
+  // sums into the start of the array, whose extent depends on the call's
+  // shape, and a previous call may have left hand-over words past its own sums
+  size_t zero_upto[kMaxDevices] = {};
+};
+ScratchDevices g_scratch;
+
+// This device's copy of scratch, with its first `sums` bytes zero: the part
+// not known to be zero is cleared by a fill kernel on `st` first (the whole
+// array, the first time a device is used).
+int scratch_on_device(int dev, size_t sums, hipStream_t st, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(CFR_EUNSUPPORTED, "device ordinal above the scratch table");
+  if (!g_scratch.ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hipf(e, "scratch address");
+    g_scratch.ptr[dev] = p;
+    g_scratch.zero_upto[dev] = 0;
+    sums = kScratchBytes;
+  }
+  const size_t z = g_scratch.zero_upto[dev];
+  if (sums > z) {
+    const hipError_t e = launch_zero(static_cast<char*>(g_scratch.ptr[dev]) + z, sums - z, st);
+    if (e != hipSuccess) return hipf(e, "scratch clear");
+  }
+  *out = g_scratch.ptr[dev];
+  return CFR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int cfr_reader_decode_noalloc(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                              int32_t batch, int32_t k, float* y, void* stream) {
+  int rc = check_decode_args(r, x, ids, gw, batch, k, y);
+  if (rc) return rc;
+  const size_t need = carve_decode_workspace(*r, batch, false, nullptr, nullptr);
+  if (need > kScratchBytes)
+    return fail(CFR_EUNSUPPORTED, "this call needs " + std::to_string(need) +
+                                      " bytes of decode scratch, above the " + std::to_string(kScratchBytes) +
+                                      " bytes of the allocation-free entry point: use cfr_reader_decode or a "
+                                      "smaller batch");
+  DeviceGuard guard(r->cfg.device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the screen sums come first in the carve: their extent must start zero
+  const size_t acc_bytes = decode_sums_bytes(*r, batch);
+  std::lock_guard<std::mutex> lock(g_scratch.m);
+  void* base = nullptr;
+  rc = scratch_on_device(r->cfg.device, acc_bytes, st, &base);
+  if (rc) return rc;
+  Workspace w;
+  carve_decode_workspace(*r, batch, false, static_cast<char*>(base), &w);
+  rc = launch_decode(r, x, ids, gw, batch, k, y, st, nullptr, nullptr, -1, nullptr, &w);
+  // a decode leaves its sums zero and its hand-over words after them; a
+  // failed one may have left partial sums
+  g_scratch.zero_upto[r->cfg.device] = rc ? 0 : acc_bytes;
+  return rc;
+}
 
 int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t* up,
                      const uint16_t* down, const uint16_t* router, cfr_reader** out) {

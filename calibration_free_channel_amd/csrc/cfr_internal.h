@@ -17,6 +17,8 @@ constexpr int kMaxTop = 16;
 constexpr int kMaxRank = 64;
 constexpr int kMaxBatch = 64;
 constexpr int kMaxHidden = 4096;
+constexpr int kMaxGatherWgs = 256;  // gather + recovery workgroups per call, summed over the batch
+constexpr int kMaxRecoverWgs = 16;  // recovery workgroups per token
 
 // Error reporting (thread-local message).
 int fail(int code, const std::string& msg);
@@ -43,6 +45,27 @@ void sign_vector(uint64_t seed, int hidden, float* out);
 uint16_t f64_to_f16_rne(double v);
 double f16_to_f64(uint16_t h);
 
+// The decode's per-call device buffers (views into one block of device
+// memory: the reader's workspace, or the allocation-free entry point's
+// static array).
+struct Workspace {
+  unsigned long long* acc = nullptr;  // [B][2][ncp] fixed-point screen sums (gate, up); zero between calls
+  float* var = nullptr;               // [B][2][ncp] sketch-error variances (expected-error ranking)
+  // hand-over words of the select kernel ((launch tag << 32) | payload)
+  unsigned long long* rowid = nullptr;  // [B][ncand]  kept channel row of each rank
+  unsigned long long* coef = nullptr;   // [B][ncand]  w a_j of each rank
+  unsigned long long* zpk = nullptr;    // [B][kMaxRecoverWgs][rank]  partial recovery vectors
+  uint32_t* ltag = nullptr;             // [B][kMaxGatherWgs]  rows published (launch tag)
+  uint32_t* ctag = nullptr;             // [B][kMaxGatherWgs]  coefficients published
+  uint32_t* ztag = nullptr;             // [B][kMaxRecoverWgs]  recovery partial published
+  float* xrot = nullptr;    // [B][H]   H_128 (sigma x) per block (debug copy only)
+  uint8_t* sel = nullptr;   // [B][nblk][n_screen] (debug copy only)
+  float* ghat = nullptr;    // [B][ncand] (debug copy only)
+  float* vhat = nullptr;    // [B][ncand] (debug copy only)
+  float* score = nullptr;   // [B][ncand] (debug copy only)
+  int32_t* kept = nullptr;  // [B][ncand]  kept candidates by rank (debug copy only)
+};
+
 }  // namespace cfr
 
 // The reader object.  All pointers are device memory on cfg.device unless
@@ -64,22 +87,8 @@ struct cfr_reader {
   // workspace (sized for cfg.max_batch); one allocation, zeroed once
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  unsigned long long* acc = nullptr;  // [B][2][ncp] fixed-point screen sums (gate, up); zero between calls
-  float* var = nullptr;        // [B][2][ncp] sketch-error variances of g_hat, v_hat' (expected-error ranking)
   float* rlog = nullptr;       // [B][E] router logits (cfr_reader_route)
   int32_t* rarr = nullptr;     // [B] workgroups of the route that have finished; zero between calls
-  // hand-over words of the select kernel ((launch tag << 32) | payload)
-  unsigned long long* rowid = nullptr;  // [B][ncand]  kept channel row of each rank
-  unsigned long long* coef = nullptr;   // [B][ncand]  w a_j of each rank
-  unsigned long long* zpk = nullptr;    // [B][kMaxRecoverWgs][rank]  partial recovery vectors
-  uint32_t* ltag = nullptr;             // [B][kMaxGatherWgs]  rows published (launch tag)
-  uint32_t* ctag = nullptr;             // [B][kMaxGatherWgs]  coefficients published
-  uint32_t* ztag = nullptr;             // [B][kMaxRecoverWgs]  recovery partial published
-  float* xrot = nullptr;       // [B][H]   H_128 (sigma x) per block (debug copy only)
-  uint8_t* sel = nullptr;      // [B][nblk][n_screen] (debug copy only)
-  float* ghat = nullptr;       // [B][ncand] (debug copy only)
-  float* vhat = nullptr;       // [B][ncand] (debug copy only)
-  float* score = nullptr;      // [B][ncand] (debug copy only)
-  int32_t* kept = nullptr;     // [B][ncand]  kept candidates by rank (debug copy only)
+  cfr::Workspace wk;           // the decode's buffers, views into ws
   int32_t* status = nullptr;   // [1]
 };

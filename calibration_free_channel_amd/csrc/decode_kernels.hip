@@ -36,6 +36,7 @@
 // serialise), so no kernel waits for another workgroup.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -1525,6 +1526,55 @@ static int hip_fail(hipError_t e, const char* what) {
   return fail(CFR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// Zero fill of a device buffer (a kernel rather than a memset node, so that
+// a caller may capture it in a graph)
+__global__ void k_zero(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  const int blocks = (int)std::min<size_t>((n16 + 255) / 256, 1024);
+  if (blocks > 0) k_zero<<<blocks, 256, 0, st>>>(static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+size_t decode_sums_bytes(const cfr_reader& r, int batch) {
+  return (sizeof(unsigned long long) * batch * 2 * r.ncp + 255) / 256 * 256;
+}
+
+size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w) {
+  const cfr_config& c = r.cfg;
+  const size_t B = batch, H = c.hidden, nc = r.ncand, R = c.rank > 0 ? c.rank : 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += (bytes + 255) / 256 * 256;
+    return base ? base + at : nullptr;
+  };
+  Workspace v;
+  v.acc = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * 2 * r.ncp));
+  v.var = reinterpret_cast<float*>(
+      take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0));
+  v.rowid = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * nc));
+  v.coef = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * nc));
+  v.zpk = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * kMaxRecoverWgs * R));
+  v.ltag = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kMaxGatherWgs));
+  v.ctag = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kMaxGatherWgs));
+  v.ztag = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kMaxRecoverWgs));
+  if (debug) {
+    v.xrot = reinterpret_cast<float*>(take(sizeof(float) * B * H));
+    v.sel = reinterpret_cast<uint8_t*>(take(B * r.nblk * c.n_screen));
+    v.ghat = reinterpret_cast<float*>(take(sizeof(float) * B * nc));
+    v.vhat = reinterpret_cast<float*>(take(sizeof(float) * B * nc));
+    v.score = reinterpret_cast<float*>(take(sizeof(float) * B * nc));
+    v.kept = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * nc));
+  }
+  if (w) *w = v;
+  return o;
+}
+
 Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
   Plan p;
   const int nblk = c.hidden / kBlock, nbytes = (c.inter + 4) / 5, nc = c.top * c.inter;
@@ -1651,8 +1701,9 @@ static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t 
 
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev, int only,
-                  const float* resid) {
+                  const float* resid, const Workspace* wsp) {
   const cfr_config& c = r->cfg;
+  const Workspace& W = wsp ? *wsp : r->wk;
   const Plan p = make_plan(c, batch, k, false);
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], st);
@@ -1660,17 +1711,17 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   hipError_t e;
   mark(0);
   // the sketch-error variances, with the expected-error ranking only
-  float* var = c.ranking == CFR_RANK_EXPECTED_ERROR ? r->var : nullptr;
-  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->rho, r->acc, var, r->xrot,
-               r->sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
+  float* var = c.ranking == CFR_RANK_EXPECTED_ERROR ? W.var : nullptr;
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->rho, W.acc, var, W.xrot,
+               W.sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
                c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, dbg != nullptr};
   if (only < 0 || only == 0)
     if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
   // the select kernel clears the screen sums after reading them, except
   // when it is launched alone for timing without its screen (only == 2)
-  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->u, resid, y, r->rowid, r->coef, r->zpk,
-               r->ltag, r->ctag, r->ztag, r->ghat, r->vhat, r->score, r->kept, r->status, c.hidden,
+  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, r->u, resid, y, W.rowid, W.coef, W.zpk,
+               W.ltag, W.ctag, W.ztag, W.ghat, W.vhat, W.score, W.kept, r->status, c.hidden,
                c.n_experts, c.inter, c.top, r->ncand, r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0,
                dbg != nullptr, 1.0f / (float)c.inter, cps_mul(c.inter), var, batch, p.S, only == 2 ? 0 : 1};
   if (only < 0 || only >= 1)
@@ -1681,14 +1732,14 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
     auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
       return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
     };
-    if ((e = cp(dbg->xrot, r->xrot, sizeof(float) * batch * H)) != hipSuccess ||
-        (e = cp(dbg->sel, r->sel, (size_t)batch * nblk * c.n_screen)) != hipSuccess ||
-        (e = cp(dbg->ghat, r->ghat, sizeof(float) * nsc)) != hipSuccess ||
-        (e = cp(dbg->vhat, r->vhat, sizeof(float) * nsc)) != hipSuccess ||
-        (e = cp(dbg->score, r->score, sizeof(float) * nsc)) != hipSuccess)
+    if ((e = cp(dbg->xrot, W.xrot, sizeof(float) * batch * H)) != hipSuccess ||
+        (e = cp(dbg->sel, W.sel, (size_t)batch * nblk * c.n_screen)) != hipSuccess ||
+        (e = cp(dbg->ghat, W.ghat, sizeof(float) * nsc)) != hipSuccess ||
+        (e = cp(dbg->vhat, W.vhat, sizeof(float) * nsc)) != hipSuccess ||
+        (e = cp(dbg->score, W.score, sizeof(float) * nsc)) != hipSuccess)
       return hip_fail(e, "debug copy");
     if (dbg->kept && k > 0) {
-      e = hipMemcpy2DAsync(dbg->kept, sizeof(int32_t) * k, r->kept, sizeof(int32_t) * r->ncand,
+      e = hipMemcpy2DAsync(dbg->kept, sizeof(int32_t) * k, W.kept, sizeof(int32_t) * r->ncand,
                            sizeof(int32_t) * k, batch, hipMemcpyDeviceToDevice, st);
       if (e != hipSuccess) return hip_fail(e, "debug copy kept");
     }
@@ -1701,8 +1752,9 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   const cfr_config& c = r->cfg;
   const int nc = r->ncand;
   const Plan p = make_plan(c, batch, nc, true);
-  SelectArgs B{x, ids, gw, r->w3, r->b, r->acc, r->norms, r->u, resid, y, r->rowid, r->coef, r->zpk,
-               r->ltag, r->ctag, r->ztag, nullptr, nullptr, nullptr, nullptr, r->status, c.hidden,
+  const Workspace& W = r->wk;
+  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, r->u, resid, y, W.rowid, W.coef, W.zpk,
+               W.ltag, W.ctag, W.ztag, nullptr, nullptr, nullptr, nullptr, r->status, c.hidden,
                c.n_experts, c.inter, c.top, nc, r->ncp, nc, 0, p.G, 0, p.cpw, p.chan, 1, 0,
                1.0f / (float)c.inter, cps_mul(c.inter), nullptr, batch, p.S, 0};
   hipError_t e;

@@ -11,8 +11,6 @@ namespace cfr {
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kScreenThreads = 512;     // screen workgroup size
-constexpr int kMaxGatherWgs = 256;      // gather + recovery workgroups per call, summed over the batch
-constexpr int kMaxRecoverWgs = 16;      // recovery workgroups per token
 constexpr int kDownSlice = 32;          // hidden units per down workgroup
 
 __host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 16; }
@@ -111,7 +109,16 @@ struct DebugOut {
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t stream, const DebugOut* dbg,
                   hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1,
-                  const float* resid = nullptr /* non-null: y = resid + output */);
+                  const float* resid = nullptr /* non-null: y = resid + output */,
+                  const Workspace* ws = nullptr /* null: the reader's own workspace */);
+// Zero a device buffer (a multiple of 16 bytes) with a fill kernel on st.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+// The decode's buffers for `batch` tokens carved from base (any size when
+// base is null); returns the bytes they take.  debug: also the copies the
+// debug entry point reads.
+size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w);
+// Bytes of the screen sums at the start of that carve (rounded as carved).
+size_t decode_sums_bytes(const cfr_reader& r, int batch);
 // Kernel attributes (hipFuncSetAttribute) apply to the current device: a
 // launcher sets them once per device, the first time it runs there.  Setting
 // them twice (two threads at once) is harmless.

@@ -187,6 +187,17 @@ class Reader:
                                                     self._stream(stream)))
         return out
 
+    def decode_noalloc(self, x, expert_ids, gate_w, k: int, out, stream=None):
+        """cfr_reader_decode_noalloc: the decode with its per-call buffers in
+        the library's static device array (no allocation in the call); `out`
+        [batch, hidden] float32 is required.  Calls overlapping on one device
+        race (they share the array)."""
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
+        check(load().cfr_reader_decode_noalloc(self._h, px, pi, pw, B, int(k), py, self._stream(stream)))
+        return out
+
     def decode_debug(self, x, expert_ids, gate_w, k: int, stream=None) -> dict:
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)

@@ -185,6 +185,25 @@ int cfr_reader_decode_residual(cfr_reader* r, const float* x, const int32_t* exp
                                float* y, void* stream);
 
 /*
+ * cfr_reader_decode for callers that cannot allocate device memory during
+ * the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it): the same kernels and result, bit for bit, with the
+ * decode's per-call buffers (screen sums, hand-over words) in a static
+ * device array of the library, 8 MiB per device (kept until the process
+ * ends), instead of the reader's workspace.  The call allocates nothing; the
+ * first call on a device also clears the array with a fill kernel on
+ * `stream`.  Every call on a device shares that device's array: calls that
+ * overlap in time on one device (two streams, or two readers) race and
+ * their outputs are unspecified; order them.  The array keeps the last
+ * call's contents; the decode leaves its screen sums zero for the next call.
+ * Errors: those of cfr_reader_decode, and CFR_EUNSUPPORTED when the call
+ * would need more than the 8 MiB (for example batch 64 at 16384 candidates
+ * per token); the message says how much it needs.
+ */
+int cfr_reader_decode_noalloc(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                              const float* gate_w, int32_t batch, int32_t k, float* y, void* stream);
+
+/*
  * Same computation as cfr_reader_decode, also copying the intermediates to
  * the caller's device buffers (any may be NULL):
  *   xrot  fp32  [batch][H]              H_128 (sigma * x) per block, before the 1/sqrt(128)
