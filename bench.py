@@ -140,7 +140,7 @@ def profile_summary(d):
                          f"moved -> scale {scale:.4f}")
             traffic[c + "_scale"] = round(scale, 4)
         for (k, c), (tot, n, _) in acc.items():
-            name = {"k_screen": "screen", "k_select": "select"}.get(k.split("<")[0].split()[-1])
+            name = {"k_screen": "screen", "k_select": "select", "k_reduce": "reduce"}.get(k.split("<")[0].split()[-1])
             if name:
                 traffic.setdefault("kernels", {}).setdefault(name, {})[
                     "fetch_kib" if c == "FETCH_SIZE" else "write_kib"] = round(tot / n, 1)
@@ -215,13 +215,13 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None,
 def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
     """Average duration of each decode kernel: the kernel launched alone, back
     to back over all layer copies in one HIP graph, timed with HIP events on
-    the replay stream; returns {stage: microseconds per launch}.  The screen
-    is timed first (its sums pile up, in range and meaningless); a real
-    decode pass then leaves fresh sums, and the select kernel is timed in its
-    timing mode, which reads them without clearing them."""
+    the replay stream; returns {stage: microseconds per launch}.  Stage order
+    keeps every launch meaningful: the screen is timed first (its sums pile
+    up), a reduce pass clears them, a real screen pass fills them, then the
+    select (which only reads them) and the reduce (which clears them)."""
     L = len(readers)
     s = torch.cuda.Stream()
-    Y = torch.empty((L, X.shape[1], X.shape[-1]), dtype=torch.float32, device=X.device)
+    Y = torch.empty((L, 1, X.shape[-1]), dtype=torch.float32, device=X.device)
 
     def one_pass(stage):
         for i, r in enumerate(readers):
@@ -249,13 +249,11 @@ def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
 
     out = {"screen": timed(0)}
     with torch.cuda.stream(s):
-        one_pass(1)  # clears the piled-up sums
-        one_pass(0)  # fresh sums of these inputs
+        one_pass(2)
+        one_pass(0)
     torch.cuda.synchronize()
-    out["select"] = timed(readers[0].STAGE_SELECT_KEEP_SUMS)
-    with torch.cuda.stream(s):
-        one_pass(1)  # clears them for the next decode
-    torch.cuda.synchronize()
+    out["select"] = timed(1)
+    out["reduce"] = timed(2)
     return out
 
 
@@ -606,7 +604,8 @@ def main():
     # algorithmic bytes of each kernel per launch (one token)
     stage_bytes = {
         "screen": rb["codes"] + rb["scales"] + rb["norms"],
-        "select": rb["exact"] + rb["b"] + rb["u"],
+        "select": rb["exact"] + rb["b"],
+        "reduce": rb["u"],
     }
     dom = max(stage_bytes, key=lambda n: main_r["stages"].get(n, 0.0))
     dom_us = main_r["stages"][dom]

@@ -334,7 +334,7 @@ int cfr_reader_decode_stage(cfr_reader* r, int32_t stage, const float* x, const 
                             const float* gw, int32_t batch, int32_t k, float* y, void* stream) {
   int rc = check_decode_args(r, x, ids, gw, batch, k, y);
   if (rc) return rc;
-  if (stage < 0 || stage > CFR_NUM_STAGES) return fail(CFR_EINVAL, "stage out of range");
+  if (stage < 0 || stage >= CFR_NUM_STAGES) return fail(CFR_EINVAL, "stage out of range");
   DeviceGuard guard(r->cfg.device);
   return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr,
                        nullptr, stage);

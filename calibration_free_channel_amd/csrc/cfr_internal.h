@@ -17,8 +17,6 @@ constexpr int kMaxTop = 16;
 constexpr int kMaxRank = 64;
 constexpr int kMaxBatch = 64;
 constexpr int kMaxHidden = 4096;
-constexpr int kMaxGatherWgs = 256;  // gather + recovery workgroups per call, summed over the batch
-constexpr int kMaxRecoverWgs = 16;  // recovery workgroups per token
 
 // Error reporting (thread-local message).
 int fail(int code, const std::string& msg);
@@ -51,13 +49,8 @@ double f16_to_f64(uint16_t h);
 struct Workspace {
   unsigned long long* acc = nullptr;  // [B][2][ncp] fixed-point screen sums (gate, up); zero between calls
   float* var = nullptr;               // [B][2][ncp] sketch-error variances (expected-error ranking)
-  // hand-over words of the select kernel ((launch tag << 32) | payload)
-  unsigned long long* rowid = nullptr;  // [B][ncand]  kept channel row of each rank
-  unsigned long long* coef = nullptr;   // [B][ncand]  w a_j of each rank
-  unsigned long long* zpk = nullptr;    // [B][kMaxRecoverWgs][rank]  partial recovery vectors
-  uint32_t* ltag = nullptr;             // [B][kMaxGatherWgs]  rows published (launch tag)
-  uint32_t* ctag = nullptr;             // [B][kMaxGatherWgs]  coefficients published
-  uint32_t* ztag = nullptr;             // [B][kMaxRecoverWgs]  recovery partial published
+  float* ypart = nullptr;             // [kMaxGatherWgs][H] partial outputs of the gather workgroups
+  float* zpart = nullptr;             // [B][kMaxRecoverWgs][rank] partial recovery vectors
   float* xrot = nullptr;    // [B][H]   H_128 (sigma x) per block (debug copy only)
   uint8_t* sel = nullptr;   // [B][nblk][n_screen] (debug copy only)
   float* ghat = nullptr;    // [B][ncand] (debug copy only)

@@ -298,7 +298,6 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   __shared__ uint4 lut[256];
   __shared__ int2 rec[128];
   __shared__ float qn2[VAR ? kMaxHidden / 128 : 1];  // ||x_b||^2 of every block (VAR)
-  __shared__ int sh_e;                               // the routed expert
   CFR_TRACE_PHASE(0, 0);
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
@@ -309,29 +308,71 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   const int s = ts % a.top, t = ts / a.top;
   const int tid = threadIdx.x, lane = tid & 63;
   const int H = a.H, I = a.I, NS = a.ns;
-  // Wave 0 loads the token block, its signs and the routed expert; it rotates
-  // the block and picks the screened coordinates, then hands the expert to
-  // the workgroup through LDS at the barrier.  Every load that depends on the
-  // expert is issued after the barrier, the code words first: loads complete
-  // in issue order, so no wait of the rotation or of the decode covers a load
-  // it does not need.
+  // token block and signs (wave 0) first: the rotation waits on them; then
+  // the routed expert and everything that depends on it
   float x0 = 0.f, x1 = 0.f, g0 = 0.f, g1 = 0.f;
-  int eraw = 0;
   if (tid < 64) {
     const float* xb = a.x + (size_t)t * H + b * 128;
     x0 = xb[lane];
     x1 = xb[lane + 64];
     g0 = a.sigma[b * 128 + lane];
     g1 = a.sigma[b * 128 + 64 + lane];
-    eraw = a.ids[ts];
   }
-  // VAR: the token, four coordinates per thread and chunk, for the block norms
+  // VAR: the token, four coordinates per thread and chunk, for the block
+  // norms (before the loads that wait on the routed expert)
   float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0;
   if constexpr (VAR) {
     const float* xt = a.x + (size_t)t * H;
     const int h0 = 4 * tid, h1 = 4 * (tid + NT);
     q0 = *reinterpret_cast<const float4*>(xt + (h0 < H ? h0 : H - 4));
     q1 = *reinterpret_cast<const float4*>(xt + (h1 < H ? h1 : H - 4));
+  }
+  const int e = clamp_expert(a.ids[ts], a.E, a.status);
+  CFR_TRACE_PHASE(0, 5);
+  // thread (d, g) = tid: code word d (channels 20d .. 20d+19 of the half),
+  // lane g of the NG consecutive lanes that share it; after the decode, lane g
+  // finalises channels 20d + g + NG r (r < RPL): their scales, loaded now
+  constexpr int RPL = (20 + NG - 1) / NG;
+  const int d = tid / NG, g = tid & (NG - 1);
+  const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
+  uint16_t al[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int j = 20 * d + g + NG * r;
+    al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
+  }
+  // VAR: this workgroup owns channels [b vper, (b + 1) vper) of the half;
+  // thread tid < vper loads channel b vper + tid's rho in every block and
+  // ||d_j|| now, as buffer loads that the other threads point past the end
+  // (issued by every thread: no wait depends on which path a thread took);
+  // channels past NT of the share, if any, are done at the end
+  constexpr int VB = VAR ? kMaxHidden / 128 : 1;
+  const int vper = (I + a.nblk - 1) / a.nblk;
+  const bool vown = VAR && tid < vper && b * vper + tid < I;
+  uint16_t vrho[VB];
+  float vdn = 1.f;
+  if constexpr (VAR) {
+    const __amdgpu_buffer_rsrc_t rrs = buffer_rsrc(a.rho + (size_t)e * a.nblk * 2 * I, (uint32_t)(a.nblk * 2 * I * 2));
+    const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(a.norms + (size_t)e * I, (uint32_t)I * 4u);
+    const uint32_t jb = (uint32_t)(m * I + b * vper + tid) * 2u;
+#pragma unroll
+    for (int q = 0; q < VB; ++q)
+      vrho[q] = __builtin_amdgcn_raw_buffer_load_b16(rrs, vown && q < a.nblk ? jb + (uint32_t)q * 4u * I : kNoLoad,
+                                                     0, 0);
+    vdn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        drs, vown ? (uint32_t)(b * vper + tid) * 4u : kNoLoad, 0, 0));
+  }
+  // the up half carries ||d_j|| into its sums (v_hat' = ||d_j|| v_hat), so the
+  // score needs no per-candidate norm read later: those norms, loaded now
+  float nrm[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) nrm[r] = 1.f;
+  if (m == 1) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int j = 20 * d + g + NG * r;
+      nrm[r] = a.norms[(size_t)e * I + (j < I ? j : I - 1)];
+    }
   }
   // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
   // 243..255 never occur in a packed unit and decode to zero)
@@ -340,10 +381,10 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     if (tid < 243) {
       int q = tid;
 #pragma unroll
-      for (int dd = 0; dd < 5; ++dd) {
+      for (int d = 0; d < 5; ++d) {
         const int dig = q % 3;
         q /= 3;
-        h[dd] = dig == 0 ? 0xBC00u : (dig == 2 ? 0x3C00u : 0u);
+        h[d] = dig == 0 ? 0xBC00u : (dig == 2 ? 0x3C00u : 0u);
       }
     }
     lut[tid] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u);
@@ -354,7 +395,6 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
     rotate_select(x0 * g0, x1 * g1, NS, a.unit, rec,
                   writer ? a.sel + ((size_t)t * a.nblk + b) * NS : nullptr,
                   writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
-    if (tid == 0) sh_e = clamp_expert(eraw, a.E, a.status);
   }
   if constexpr (VAR) {
     // ||x_b||^2 of every block: 32 lanes hold one block's 128 coordinates
@@ -380,80 +420,28 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   CFR_TRACE_PHASE(0, 6);
   lds_barrier();
   CFR_TRACE_PHASE(0, 1);
-  const int e = sh_e;
-  CFR_TRACE_PHASE(0, 5);
 
-  // screen: thread (d, g) = tid decodes code word d (channels 20d .. 20d+19
-  // of the half) at screened coordinates g, g + NG, g + 2 NG, ..., CPB of its
-  // words in flight together; after the decode, lane g finalises channels
-  // 20d + g + NG r (r < RPL)
-  constexpr int RPL = (20 + NG - 1) / NG;
-  const int d = tid / NG, g = tid & (NG - 1);
+  // screen: thread (d, g) decodes code word d at screened coordinates
+  // g, g + NG, g + 2 NG, ..., all its words in flight together (CPB at a time)
   const int ND = a.nd;
   const bool active = d < ND;
-  // uniform base of this (expert, block) and 32-bit per-coordinate offsets
-  const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit;
-  const uint32_t col = (uint32_t)(m * a.lp + 4 * d);
-  uint32_t wv[CPB];
-  float xv[CPB];
-  auto load_words = [&](int c0) {
-#pragma unroll
-    for (int u = 0; u < CPB; ++u) {
-      const int c = c0 + u * NG;
-      const int2 rc = rec[c < NS ? c : NS - 1];  // clamped; past the list x = 0
-      wv[u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
-      xv[u] = c < NS ? __int_as_float(rc.y) : 0.f;
-    }
-  };
-  // the routed expert's scales of this block and half, and the norms the up
-  // half carries into its sums (v_hat' = ||d_j|| v_hat, so the score needs no
-  // per-candidate norm read later), issued just before the code words:
-  // unconditional (clamped) loads, so no branch waits on them
-  const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
-  uint16_t al[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int j = 20 * d + g + NG * r;
-    al[r] = sp[j < I ? j : I - 1];
-  }
-  float nrm[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) nrm[r] = 1.f;
-  if (m == 1) {
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int j = 20 * d + g + NG * r;
-      nrm[r] = a.norms[(size_t)e * I + (j < I ? j : I - 1)];
-    }
-  }
-  // VAR: this workgroup owns channels [b vper, (b + 1) vper) of the half;
-  // thread tid < vper loads channel b vper + tid's rho in every block and
-  // ||d_j||, as buffer loads that the other threads point past the end
-  // (issued by every thread: no wait depends on which path a thread took);
-  // channels past NT of the share, if any, are done at the end
-  constexpr int VB = VAR ? kMaxHidden / 128 : 1;
-  const int vper = (I + a.nblk - 1) / a.nblk;
-  const bool vown = VAR && tid < vper && b * vper + tid < I;
-  uint16_t vrho[VB];
-  float vdn = 1.f;
-  if constexpr (VAR) {
-    const __amdgpu_buffer_rsrc_t rrs = buffer_rsrc(a.rho + (size_t)e * a.nblk * 2 * I, (uint32_t)(a.nblk * 2 * I * 2));
-    const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(a.norms + (size_t)e * I, (uint32_t)I * 4u);
-    const uint32_t jb = (uint32_t)(m * I + b * vper + tid) * 2u;
-#pragma unroll
-    for (int q = 0; q < VB; ++q)
-      vrho[q] = __builtin_amdgcn_raw_buffer_load_b16(rrs, vown && q < a.nblk ? jb + (uint32_t)q * 4u * I : kNoLoad,
-                                                     0, 0);
-    vdn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        drs, vown ? (uint32_t)(b * vper + tid) * 4u : kNoLoad, 0, 0));
-  }
-  if (active) load_words(g);
   float acc[20];
 #pragma unroll
   for (int q = 0; q < 20; ++q) acc[q] = 0.f;
   if (active) {
+    // uniform base of this (expert, block) and 32-bit per-coordinate offsets
+    const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit;
+    const uint32_t col = (uint32_t)(m * a.lp + 4 * d);
     for (int c0 = g; c0 < NS; c0 += NG * CPB) {
-      if (c0 != g) load_words(c0);
+      uint32_t wv[CPB];
+      float xv[CPB];
+#pragma unroll
+      for (int u = 0; u < CPB; ++u) {
+        const int c = c0 + u * NG;
+        const int2 rc = rec[c < NS ? c : NS - 1];  // clamped; past the list x = 0
+        wv[u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
+        xv[u] = c < NS ? __int_as_float(rc.y) : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < CPB; ++u) {
 #pragma unroll
@@ -538,19 +526,10 @@ struct SelectArgs {
   const float* gw;
   const uint16_t* w3;
   const uint16_t* bmat;
-  unsigned long long* acc;  // read by gather and recovery workgroups, cleared by down workgroups
-  const float* norms;       // ||d_j|| [E][I]
-  const uint16_t* U;        // [H][rank] fp16
-  const float* resid;       // non-null: y = resid + output (resid may be y)
-  float* y;
-  // hand-over words, each (launch tag << 32) | payload, written with
-  // device-scope stores and valid only when the tag is this launch's
-  unsigned long long* rowid;  // [B][nc] the kept channel of each rank: its row e * I + j
-  unsigned long long* coef;   // [B][nc] w a_j of each rank
-  unsigned long long* zpk;    // [B][kMaxRecoverWgs][rank] partial recovery vectors
-  uint32_t* ltag;             // [B][kMaxGatherWgs] a gather workgroup's rows are published
-  uint32_t* ctag;             // [B][kMaxGatherWgs] a gather workgroup's coefficients are published
-  uint32_t* ztag;             // [B][kMaxRecoverWgs] a recovery workgroup's partial is published
+  const unsigned long long* acc;
+  const float* norms;  // ||d_j|| [E][I]
+  float* ypart;
+  float* zpart;
   float* ghat;   // debug outputs (written by workgroup 0 of each token when dbg)
   float* vhat;
   float* score;
@@ -560,64 +539,7 @@ struct SelectArgs {
   float invI;   // 1 / I rounded to float (exact slot division below 2^17)
   int cps_mul;  // I % 128 == 0: ceil(2^16 / (I / 128)), else 0
   const float* var;  // [B][2][ncp] sketch-error variances (expected-error ranking)
-  int B;             // tokens in the call
-  int S;             // down workgroups per token (hidden / kDownSlice)
-  int clear;         // the down workgroups clear the screen accumulators (a full decode)
 };
-
-// The dispatch's id (the packet index in its hardware queue): the same for
-// every workgroup of one launch, different for every launch on the queue,
-// graph replays included.  Its low 32 bits tag the words one launch hands
-// from workgroup to workgroup, so no word needs resetting between launches.
-extern "C" __device__ unsigned long long cfr_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-
-constexpr int kSpinLimit = 1 << 16;  // polls before a hand-over wait gives up (status bit 2)
-
-__device__ __forceinline__ unsigned long long tagged(uint32_t tag, uint32_t payload) {
-  return ((unsigned long long)tag << 32) | payload;
-}
-__device__ __forceinline__ void publish(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish_tag(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long fetch(const unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The payload of a hand-over word already fetched as v: while its tag is not
-// `want` (the producer's store has not landed yet), poll it again, bounded;
-// on time-out the payload is 0 and bit 2 of the status word is set.
-__device__ __forceinline__ uint32_t settle(unsigned long long v, const unsigned long long* p, uint32_t want,
-                                           int32_t* status) {
-  for (int it = 0; (uint32_t)(v >> 32) != want; ++it) {
-    if (it >= kSpinLimit) {
-      atomicOr(status, 4);
-      return 0u;
-    }
-    __builtin_amdgcn_s_sleep(1);
-    v = fetch(p);
-  }
-  return (uint32_t)v;
-}
-// One wave polls tags[lo, hi) with device-scope loads until every one is
-// `want` (bounded; bit 2 of the status word on time-out).  The caller's
-// other waves wait for it at a barrier.
-__device__ __forceinline__ void wait_tags(const uint32_t* tags, int lo, int hi, uint32_t want, int32_t* status) {
-  const int lane = threadIdx.x & 63;
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    for (int it = 0;; ++it) {
-      const bool ready = i >= hi || __hip_atomic_load(tags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
-      if (__ballot(!ready) == 0ull) break;
-      if (it >= kSpinLimit) {
-        if (lane == 0) atomicOr(status, 4);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-}
 
 // misc slots
 constexpr int kMiscDigit = 16, kMiscNeed = 17, kMiscCount = 18, kMiscSlot = 19, kMiscDT = 20,
@@ -751,150 +673,6 @@ __device__ __forceinline__ void write_kept_debug(const bool (&f)[PER], int* wc, 
   }
 }
 
-// A down workgroup: y over hidden units [h0, h0 + kDownSlice) of token t.
-// Once the gather workgroups have published the kept rows, it loads the
-// kept channels' transposed down rows over its slice (kDownSlice / 8 lanes
-// per channel, 16 bytes each; kDownSteps steps of NT / that many channels in
-// flight) and U's rows of the slice; once they have published the
-// coefficients w a_j, it forms sum_K w a_j d_j over the slice in rank order,
-// adds U z (z = the recovery workgroups' partials, in order) and the
-// residual, and writes y.  Finally it clears its share of the token's screen
-// accumulators, which every gather and recovery workgroup has read by then.
-constexpr int kDownSteps = 8;
-
-template <int NT>
-__device__ __forceinline__ void down_slice(const SelectArgs& a, unsigned char* smem, int q) {
-  constexpr int NW = NT / 64;
-  constexpr int LPC = kDownSlice / 8;  // lanes per channel
-  constexpr int CPS = NT / LPC;        // channels per step
-  static_assert(kDownSlice % 8 == 0 && LPC <= 64 && (64 % LPC) == 0, "whole channels per wave");
-  const int t = q / a.S, sl = q - t * a.S;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = a.H;
-  const uint32_t want = (uint32_t)cfr_dispatch_id();
-  const bool all = a.dense || a.k == a.nc;
-  const int kk = all ? a.nc : a.k;
-  const int h0 = sl * kDownSlice;
-  const int piece = tid % LPC, cs = tid / LPC;
-  float* red = reinterpret_cast<float*>(smem);  // [NW][kDownSlice]
-  float* zs = red + NW * kDownSlice;             // [kMaxRank]
-  const bool rec = a.Z > 0 && a.rank > 0;
-  // U rows of the slice and the residual first (their own loads)
-  uint4 uq[kMaxRank / 8];
-  const int hu = h0 + (tid < kDownSlice ? tid : 0);
-#pragma unroll
-  for (int r8 = 0; r8 < kMaxRank / 8; ++r8)
-    uq[r8] = (rec && r8 * 8 < a.rank) ? *reinterpret_cast<const uint4*>(a.U + (size_t)hu * a.rank + r8 * 8)
-                                      : make_uint4(0u, 0u, 0u, 0u);
-  const float rv = a.resid ? a.resid[(size_t)t * H + hu] : 0.f;
-  const uint16_t* dbase = a.w3 + 2 * H + h0 + piece * 8;
-  const unsigned long long* rowp = a.rowid + (size_t)t * a.nc;
-  const unsigned long long* coefp = a.coef + (size_t)t * a.nc;
-  const uint32_t* lt = a.ltag + t * kMaxGatherWgs;
-  const uint32_t* ct = a.ctag + t * kMaxGatherWgs;
-  const uint32_t nrows = (uint32_t)(a.E * a.I);
-  float y8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y8[i] = 0.f;
-  if (kk > 0) {
-    if (wave == 0) wait_tags(lt, 0, a.G, want, a.status);
-    lds_barrier();
-  }
-  for (int base = 0; base < kk; base += CPS * kDownSteps) {
-    // the rows of this round's ranks, then their down slices, all in flight
-    unsigned long long rw[kDownSteps];
-#pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) rw[u] = fetch(rowp + min(base + u * CPS + cs, kk - 1));
-    uint4 dq[kDownSteps];
-#pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) {
-      const uint32_t row = min(settle(rw[u], rowp + min(base + u * CPS + cs, kk - 1), want, a.status), nrows - 1u);
-      dq[u] = *reinterpret_cast<const uint4*>(dbase + (size_t)row * 3 * H);
-    }
-    // the coefficients of these ranks: the gather workgroups that own them
-    const int r_hi = min(base + CPS * kDownSteps, kk);
-    if (wave == 0) wait_tags(ct, base / a.chan, (r_hi - 1) / a.chan + 1, want, a.status);
-    lds_barrier();
-    unsigned long long cw[kDownSteps];
-#pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) cw[u] = fetch(coefp + min(base + u * CPS + cs, kk - 1));
-#pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) {
-      const int r = base + u * CPS + cs;
-      const float c = __uint_as_float(settle(cw[u], coefp + min(r, kk - 1), want, a.status));
-      if (r < kk) {
-        const uint32_t dw[4] = {dq[u].x, dq[u].y, dq[u].z, dq[u].w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          y8[2 * p] = fmaf(c, bf_lo(dw[p]), y8[2 * p]);
-          y8[2 * p + 1] = fmaf(c, bf_hi(dw[p]), y8[2 * p + 1]);
-        }
-      }
-    }
-  }
-  // the recovery vector: the recovery workgroups' partials, summed in order
-  if (rec) {
-    if (wave == 0) wait_tags(a.ztag + t * kMaxRecoverWgs, 0, a.Z, want, a.status);
-    lds_barrier();
-    if (tid < a.rank) {
-      const unsigned long long* zp = a.zpk + (size_t)t * kMaxRecoverWgs * a.rank + tid;
-      unsigned long long zw[kMaxRecoverWgs];
-#pragma unroll
-      for (int v = 0; v < kMaxRecoverWgs; ++v) zw[v] = v < a.Z ? fetch(zp + (size_t)v * a.rank) : 0ull;
-      float z = 0.f;
-#pragma unroll
-      for (int v = 0; v < kMaxRecoverWgs; ++v)
-        if (v < a.Z) z += __uint_as_float(settle(zw[v], zp + (size_t)v * a.rank, want, a.status));
-      zs[tid] = z;
-    }
-  }
-  // over the lanes of a wave that hold the same piece, then over the waves
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if constexpr (LPC < 2) y8[i] += xor_lane_f<1>(y8[i]);
-    if constexpr (LPC < 4) y8[i] += xor_lane_f<2>(y8[i]);
-    if constexpr (LPC < 8) y8[i] += xor_lane_f<4>(y8[i]);
-    if constexpr (LPC < 16) y8[i] += xor_lane_f<8>(y8[i]);
-    if constexpr (LPC < 32) y8[i] += xor_lane_f<16>(y8[i]);
-    if constexpr (LPC < 64) y8[i] += xor_lane_f<32>(y8[i]);
-  }
-  if (lane < LPC) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[wave * kDownSlice + lane * 8 + i] = y8[i];
-  }
-  lds_barrier();
-  if (tid < kDownSlice) {
-    float o = 0.f;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) o += red[v * kDownSlice + tid];
-    if (rec) {
-#pragma unroll
-      for (int r8 = 0; r8 < kMaxRank / 8; ++r8)
-        if (r8 * 8 < a.rank) {
-          const uint32_t uw[4] = {uq[r8].x, uq[r8].y, uq[r8].z, uq[r8].w};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            o = fmaf(lo16(uw[d]), zs[r8 * 8 + 2 * d], o);
-            o = fmaf(hi16(uw[d]), zs[r8 * 8 + 2 * d + 1], o);
-          }
-        }
-    }
-    // the residual is added to the finished output, as a separate add would
-    a.y[(size_t)t * H + h0 + tid] = a.resid ? rv + o : o;
-  }
-  if (a.clear) {
-    // every gather workgroup of the token has published (so has read the
-    // screen sums); the recovery ones were waited for above
-    if (wave == 0) wait_tags(ct, 0, a.G, want, a.status);
-    lds_barrier();
-    const int n = 2 * a.ncp;
-    const int per = (n / 2 + a.S - 1) / a.S;
-    ulonglong2* ap = reinterpret_cast<ulonglong2*>(a.acc + (size_t)t * n);
-    for (int i = sl * per + tid; i < min((sl + 1) * per, n / 2); i += NT) ap[i] = make_ulonglong2(0ull, 0ull);
-  }
-}
-
 // VAR: rank by the expected squared error of skipping (error_key) instead of
 // the output-unit score.
 template <int NT, int PER, int NCH, bool VAR>
@@ -905,11 +683,6 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   static_assert(P2 * NW <= 128, "two wave counts per lane");
   CFR_TRACE_PHASE(1, 0);
   const int wgs = a.G + a.Z;
-  // the down workgroups come last, after every workgroup they wait for
-  if ((int)blockIdx.x >= a.B * wgs) {
-    down_slice<NT>(a, smem, (int)blockIdx.x - a.B * wgs);
-    return;
-  }
   const int t = blockIdx.x / wgs, w = blockIdx.x - t * wgs;
   const bool recover = w >= a.G;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -920,6 +693,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   float* pvl = reinterpret_cast<float*>(smem + L.pv);
   uint8_t* flags = smem + L.flags;
   uint32_t* dl = reinterpret_cast<uint32_t*>(smem + L.dl);
+  float* yred = reinterpret_cast<float*>(smem + L.yred);
   int* hist = reinterpret_cast<int*>(smem + L.hist);
   int* list = reinterpret_cast<int*>(smem + L.list);
   int* misc = reinterpret_cast<int*>(smem + L.misc);
@@ -1356,23 +1130,16 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   }
   CFR_TRACE_PHASE(1, 3);
 
-  const uint32_t want = (uint32_t)cfr_dispatch_id();
   if (!recover) {
-    // ---- publish the rows of this workgroup's kept ranks [r0, r1) (wave 0),
-    // so the down workgroups can start loading their transposed down rows ----
+    // ---- decode step (3): exact kept channels from native BF16 rows ----
+    // wave v takes list entries [v cpw, (v+1) cpw), two channels at a time
+    // when registers allow, all rows in flight together
+    float yv[NCH][8];
+#pragma unroll
+    for (int q = 0; q < NCH; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yv[q][i] = 0.f;
     const int nmine = r1 - r0;
-    if (wave == 0) {
-      for (int q = lane; q < nmine; q += 64) {
-        const int c = list[q];
-        const int sr = slot_of(c);
-        publish(a.rowid + (size_t)t * nc + r0 + q, tagged(want, (uint32_t)(sl_e[sr] * I + (c - sr * I))));
-      }
-      if (lane == 0) publish_tag(a.ltag + t * kMaxGatherWgs + w, want);
-    }
-    // ---- decode step (3): a_j = silu(g_j.x)(v_j.x) from the native gate and
-    // up rows of the kept channels; wave v takes list entries
-    // [v cpw, (v+1) cpw), two channels at a time when registers allow, all
-    // rows in flight together; lane 0 publishes w a_j of each ----
     constexpr bool kPair = NCH <= 4;
     constexpr int NR = kPair ? 2 : 1;
     const int qend = min((wave + 1) * a.cpw, nmine);
@@ -1381,7 +1148,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       int cc[NR];
       cc[0] = list[q0];
       if constexpr (kPair) cc[NR - 1] = two ? list[q0 + 1] : cc[0];
-      uint4 gq2[NR][NCH], uq2[NR][NCH];
+      uint4 gq2[NR][NCH], uq2[NR][NCH], dq2[NR][NCH];
       int sr[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -1393,10 +1160,11 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
             const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
             gq2[r][ch] = *reinterpret_cast<const uint4*>(row + h);
             uq2[r][ch] = *reinterpret_cast<const uint4*>(row + H + h);
+            dq2[r][ch] = *reinterpret_cast<const uint4*>(row + 2 * H + h);
           }
         } else {
 #pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) gq2[r][ch] = uq2[r][ch] = make_uint4(0u, 0u, 0u, 0u);
+          for (int ch = 0; ch < NCH; ++ch) gq2[r][ch] = uq2[r][ch] = dq2[r][ch] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
       float gs[NR], vs[NR];
@@ -1423,19 +1191,78 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
           }
         }
       }
-      const float cf0 = sl_w[sr[0]] * silu(wave_sum(gs[0])) * wave_sum(vs[0]);
-      if (lane == 0) publish(a.coef + (size_t)t * nc + r0 + q0, tagged(want, __float_as_uint(cf0)));
-      if constexpr (kPair) {
-        if (two) {
-          const float cf1 = sl_w[sr[NR - 1]] * silu(wave_sum(gs[NR - 1])) * wave_sum(vs[NR - 1]);
-          if (lane == 0) publish(a.coef + (size_t)t * nc + r0 + q0 + 1, tagged(want, __float_as_uint(cf1)));
+      float cf[NR];
+      cf[0] = sl_w[sr[0]] * silu(wave_sum(gs[0])) * wave_sum(vs[0]);
+      if constexpr (kPair) cf[NR - 1] = two ? sl_w[sr[NR - 1]] * silu(wave_sum(gs[NR - 1])) * wave_sum(vs[NR - 1]) : 0.f;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const uint32_t dw[4] = {dq2[r][ch].x, dq2[r][ch].y, dq2[r][ch].z, dq2[r][ch].w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            yv[ch][2 * p] = fmaf(cf[r], bf_lo(dw[p]), yv[ch][2 * p]);
+            yv[ch][2 * p + 1] = fmaf(cf[r], bf_hi(dw[p]), yv[ch][2 * p + 1]);
+          }
+        }
+    }
+    CFR_TRACE_PHASE(1, 4);
+    // ---- partial output: only waves that took channels contribute ----
+    // With one LDS slot per wave (rows up to 2048 wide) each such wave stores
+    // its rows in its slot; otherwise waves [0, NW/2) store and the others
+    // add theirs.  The slots are then summed in a fixed order.
+    constexpr int SL = NCH <= 4 ? NW : NW / 2;
+    const int used = min(NW, (nmine + a.cpw - 1) / a.cpw);  // waves holding channels
+    const int slot = wave % SL;
+    if (wave < SL && (SL == NW ? wave < used : true)) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int h = ch * 512 + lane * 8;
+        if (h < H) {
+          float* o = yred + (size_t)slot * H + h;
+          *reinterpret_cast<float4*>(o) = make_float4(yv[ch][0], yv[ch][1], yv[ch][2], yv[ch][3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(yv[ch][4], yv[ch][5], yv[ch][6], yv[ch][7]);
         }
       }
     }
-    CFR_TRACE_PHASE(1, 4);
-    // every wave's coefficients are issued: the workgroup's tag
+    if constexpr (SL < NW) {
+      lds_barrier();
+      if (wave >= SL && wave < used) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+          const int h = ch * 512 + lane * 8;
+          if (h < H) {
+            float* o = yred + (size_t)slot * H + h;
+            float4 p0 = *reinterpret_cast<float4*>(o);
+            float4 p1 = *reinterpret_cast<float4*>(o + 4);
+            p0.x += yv[ch][0];
+            p0.y += yv[ch][1];
+            p0.z += yv[ch][2];
+            p0.w += yv[ch][3];
+            p1.x += yv[ch][4];
+            p1.y += yv[ch][5];
+            p1.z += yv[ch][6];
+            p1.w += yv[ch][7];
+            *reinterpret_cast<float4*>(o) = p0;
+            *reinterpret_cast<float4*>(o + 4) = p1;
+          }
+        }
+      }
+    }
     lds_barrier();
-    if (tid == 0) publish_tag(a.ctag + t * kMaxGatherWgs + w, want);
+    const int nsl = min(SL, used);  // slots that received rows
+    float* yp = a.ypart + ((size_t)t * a.G + w) * H;
+    for (int h = tid * 4; h < H; h += NT * 4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int q = 0; q < nsl; ++q) {
+        const float4 u = *reinterpret_cast<const float4*>(yred + (size_t)q * H + h);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+      *reinterpret_cast<float4*>(yp + h) = v;
+    }
     CFR_TRACE_PHASE(1, 5);
     return;
   }
@@ -1498,17 +1325,108 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   }
   lds_barrier();
   CFR_TRACE_PHASE(1, 5);
-  // wave 0 (rank <= 64 lanes) publishes the partial, then the workgroup's tag
-  if (wave == 0) {
-    if (lane < a.rank) {
-      float z = 0.f;
+  if (tid < a.rank) {
+    float z = 0.f;
 #pragma unroll
-      for (int v = 0; v < NW; ++v) z += zw[v * 64 + lane];
-      publish(a.zpk + ((size_t)t * kMaxRecoverWgs + (w - a.G)) * a.rank + lane, tagged(want, __float_as_uint(z)));
-    }
-    if (lane == 0) publish_tag(a.ztag + t * kMaxRecoverWgs + (w - a.G), want);
+    for (int v = 0; v < NW; ++v) z += zw[v * 64 + tid];
+    a.zpart[((size_t)t * a.Z + (w - a.G)) * a.rank + tid] = z;
   }
   CFR_TRACE_PHASE(1, 6);
+}
+
+// ===========================================================================
+// 3: y = sum of the partial outputs + U z; clear the screen accumulators
+// ===========================================================================
+struct ReduceArgs {
+  const float* ypart;
+  const float* zpart;
+  const uint16_t* U;
+  float* y;
+  unsigned long long* acc;
+  int H, G, Z, rank, ncp, nslices, clear;
+  const float* resid = nullptr;  // non-null: y = resid + output (resid may be y)
+};
+
+constexpr int kReduceThreads = 256;
+constexpr int kReduceParts = kReduceThreads / kReduceSlice;  // 8
+constexpr int kReducePer = kMaxGatherWgs / kReduceParts;     // partial rows per thread, at most
+
+__global__ __launch_bounds__(kReduceThreads) void k_reduce(ReduceArgs a) {
+  __shared__ float part[kReduceParts][kReduceSlice];
+  __shared__ float zs[64];
+  CFR_TRACE_PHASE(2, 0);
+  const int t = blockIdx.x / a.nslices, sl = blockIdx.x - t * a.nslices;
+  const int tid = threadIdx.x;
+  const int H = a.H, h0 = sl * kReduceSlice;
+  const int hl = tid % kReduceSlice, pt = tid / kReduceSlice;
+  // U rows of this slice, the recovery partials and the output partials:
+  // all issued before any is summed
+  uint4 uq[8];
+  const bool rec = a.Z > 0;
+  if (rec && tid < kReduceSlice) {
+    const uint4* up = reinterpret_cast<const uint4*>(a.U + (size_t)(h0 + tid) * a.rank);
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) uq[r8] = up[r8 * 8 < a.rank ? r8 : 0];
+  }
+  float zv[kMaxRecoverWgs];
+  if (rec && tid < a.rank) {
+    const float* zp = a.zpart + (size_t)t * a.Z * a.rank + tid;
+#pragma unroll
+    for (int q = 0; q < kMaxRecoverWgs; ++q) zv[q] = zp[(size_t)(q < a.Z ? q : 0) * a.rank];
+  }
+  const float* yp = a.ypart + (size_t)t * a.G * H + h0 + hl;
+  float pv[kReducePer];
+#pragma unroll
+  for (int u = 0; u < kReducePer; ++u) {
+    const int wq = pt + u * kReduceParts;
+    pv[u] = yp[(size_t)(wq < a.G ? wq : 0) * H];
+  }
+  // the residual last: the waits above do not wait for it
+  float rv = 0.f;
+  if (a.resid && tid < kReduceSlice) rv = a.resid[(size_t)t * H + h0 + tid];
+  float v = 0.f;
+#pragma unroll
+  for (int u = 0; u < kReducePer; ++u) v += pt + u * kReduceParts < a.G ? pv[u] : 0.f;
+  CFR_TRACE_PHASE(2, 1);
+  part[pt][hl] = v;
+  if (tid < 64) {
+    float z = 0.f;
+    if (rec && tid < a.rank)
+#pragma unroll
+      for (int q = 0; q < kMaxRecoverWgs; ++q) z += q < a.Z ? zv[q] : 0.f;
+    zs[tid] = z;
+  }
+  lds_barrier();
+  if (tid < kReduceSlice) {
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < kReduceParts; ++q) o += part[q][tid];
+    if (rec) {
+#pragma unroll
+      for (int r8 = 0; r8 < 8; ++r8)
+        if (r8 * 8 < a.rank) {
+          const uint32_t uw[4] = {uq[r8].x, uq[r8].y, uq[r8].z, uq[r8].w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            o = fmaf(lo16(uw[d]), zs[r8 * 8 + 2 * d], o);
+            o = fmaf(hi16(uw[d]), zs[r8 * 8 + 2 * d + 1], o);
+          }
+        }
+    }
+    // the residual is added to the finished output, as a separate add would
+    a.y[(size_t)t * H + h0 + tid] = a.resid ? rv + o : o;
+  }
+  CFR_TRACE_PHASE(2, 2);
+  if (a.clear) {
+    // the screen accumulators of this token (gate then up, ncp each), split
+    // over its slices
+    const int n = 2 * a.ncp;
+    const int per = (n + a.nslices - 1) / a.nslices;
+    const int b0 = sl * per, b1 = min(b0 + per, n);
+    ulonglong2* ap = reinterpret_cast<ulonglong2*>(a.acc + (size_t)t * n);
+    for (int q = b0 / 2 + tid; q < b1 / 2; q += kReduceThreads) ap[q] = make_ulonglong2(0ull, 0ull);
+  }
+  CFR_TRACE_PHASE(2, 3);
 }
 
 // ===========================================================================
@@ -1554,15 +1472,14 @@ size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* 
     return base ? base + at : nullptr;
   };
   Workspace v;
+  // the screen sums first: they must be zero when a decode starts, and the
+  // reduce kernel leaves them zero
   v.acc = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * 2 * r.ncp));
   v.var = reinterpret_cast<float*>(
       take(c.ranking == CFR_RANK_EXPECTED_ERROR ? sizeof(float) * B * 2 * r.ncp : 0));
-  v.rowid = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * nc));
-  v.coef = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * nc));
-  v.zpk = reinterpret_cast<unsigned long long*>(take(sizeof(unsigned long long) * B * kMaxRecoverWgs * R));
-  v.ltag = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kMaxGatherWgs));
-  v.ctag = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kMaxGatherWgs));
-  v.ztag = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kMaxRecoverWgs));
+  // the gather workgroups of the whole call number at most kMaxGatherWgs
+  v.ypart = reinterpret_cast<float*>(take(sizeof(float) * (size_t)kMaxGatherWgs * H));
+  v.zpart = reinterpret_cast<float*>(take(sizeof(float) * B * kMaxRecoverWgs * R));
   if (debug) {
     v.xrot = reinterpret_cast<float*>(take(sizeof(float) * B * H));
     v.sel = reinterpret_cast<uint8_t*>(take(B * r.nblk * c.n_screen));
@@ -1585,31 +1502,30 @@ Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
   p.items1 = batch * c.top * nblk * 2;
   p.per_xcd1 = (p.items1 + 7) / 8;
   p.lds1 = 0;
-  // select: per token, G gather workgroups (one kept channel per wave, up to
-  // kMaxGatherWgs summed over the batch less the recovery workgroups), Z
-  // recovery workgroups, then hidden / kDownSlice down workgroups
+  // select/gather: about 240 gather workgroups over the batch plus 16
+  // recovery workgroups, so the whole grid fits one workgroup per CU
   const SelectGeom g = select_geom(nc);
   p.nt2 = g.nt;
   p.per = g.per;
   p.ncp = g.nt * g.per;
   const int NW = p.nt2 / 64;
   const int kk = dense ? nc : k;
-  int z = kMaxRecoverWgs / batch;
-  if (z < 1) z = 1;
-  p.Z = (!dense && c.rank > 0 && k < nc) ? z : 0;
-  if (p.Z > nc) p.Z = nc;
-  int gmax = kMaxGatherWgs / batch - p.Z;
+  int gmax = (kMaxGatherWgs - kMaxRecoverWgs) / batch;
   if (gmax < 1) gmax = 1;
-  p.chan = NW;  // one channel per wave
-  if ((kk + p.chan - 1) / p.chan > gmax) p.chan = (kk + gmax - 1) / gmax;
+  p.chan = (kk + gmax - 1) / gmax;
   if (p.chan < 1) p.chan = 1;
   p.cpw = (p.chan + NW - 1) / NW;
   p.G = (kk + p.chan - 1) / p.chan;
   if (p.G < 1) p.G = 1;
+  int z = kMaxRecoverWgs / batch;
+  if (z < 1) z = 1;
+  p.Z = (!dense && c.rank > 0 && k < nc) ? z : 0;
+  if (p.Z > nc) p.Z = nc;
   p.nch = 1;
   while (p.nch * 512 < c.hidden) p.nch *= 2;
-  p.S = c.hidden / kDownSlice;
   p.lds2 = GatherLds(c.hidden, p.ncp, p.nt2, p.chan).total;
+  // reduce
+  p.nslices = c.hidden / kReduceSlice;
   return p;
 }
 
@@ -1643,7 +1559,7 @@ template <int NT, int PER, int NCH, bool VAR>
 static hipError_t launch_select_t(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   static OncePerDevice attr;
   attr([] { allow_lds(k_select<NT, PER, NCH, VAR>); });
-  k_select<NT, PER, NCH, VAR><<<batch * (p.G + p.Z + p.S), NT, p.lds2, st>>>(a);
+  k_select<NT, PER, NCH, VAR><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1699,6 +1615,11 @@ static hipError_t launch_screen(const ScreenArgs& a, const Plan& p, hipStream_t 
   return a.var ? launch_screen_v<true>(a, p, st) : launch_screen_v<false>(a, p, st);
 }
 
+static hipError_t launch_reduce(const ReduceArgs& a, int batch, hipStream_t st) {
+  k_reduce<<<batch * a.nslices, kReduceThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t st, const DebugOut* dbg, hipEvent_t* ev, int only,
                   const float* resid, const Workspace* wsp) {
@@ -1718,15 +1639,18 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   if (only < 0 || only == 0)
     if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
   mark(1);
-  // the select kernel clears the screen sums after reading them, except
-  // when it is launched alone for timing without its screen (only == 2)
-  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, r->u, resid, y, W.rowid, W.coef, W.zpk,
-               W.ltag, W.ctag, W.ztag, W.ghat, W.vhat, W.score, W.kept, r->status, c.hidden,
-               c.n_experts, c.inter, c.top, r->ncand, r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0,
-               dbg != nullptr, 1.0f / (float)c.inter, cps_mul(c.inter), var, batch, p.S, only == 2 ? 0 : 1};
-  if (only < 0 || only >= 1)
+  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, W.ypart, W.zpart, W.ghat, W.vhat,
+               W.score, W.kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
+               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter,
+               cps_mul(c.inter), var};
+  if (only < 0 || only == 1)
     if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
+  ReduceArgs C{W.ypart, W.zpart, r->u, y, W.acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
+               p.nslices, 1, resid};
+  if (only < 0 || only == 2)
+    if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
+  mark(3);
   if (dbg) {
     const int H = c.hidden, nblk = r->nblk, nsc = batch * r->ncand;
     auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
@@ -1753,12 +1677,14 @@ int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float*
   const int nc = r->ncand;
   const Plan p = make_plan(c, batch, nc, true);
   const Workspace& W = r->wk;
-  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, r->u, resid, y, W.rowid, W.coef, W.zpk,
-               W.ltag, W.ctag, W.ztag, nullptr, nullptr, nullptr, nullptr, r->status, c.hidden,
-               c.n_experts, c.inter, c.top, nc, r->ncp, nc, 0, p.G, 0, p.cpw, p.chan, 1, 0,
-               1.0f / (float)c.inter, cps_mul(c.inter), nullptr, batch, p.S, 0};
+  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, W.ypart, W.zpart, nullptr, nullptr,
+               nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
+               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter), nullptr};
   hipError_t e;
   if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
+  ReduceArgs C{W.ypart, W.zpart, r->u, y, W.acc, c.hidden, p.G, 0, c.rank, r->ncp,
+               p.nslices, 0, resid};
+  if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "dense reduce launch");
   return CFR_OK;
 }
 

@@ -11,7 +11,9 @@ namespace cfr {
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kScreenThreads = 512;     // screen workgroup size
-constexpr int kDownSlice = 32;          // hidden units per down workgroup
+constexpr int kMaxGatherWgs = 256;      // gather workgroups per call, summed over the batch
+constexpr int kMaxRecoverWgs = 16;      // recovery workgroups per token
+constexpr int kReduceSlice = 32;        // hidden units per reduce workgroup
 
 __host__ __device__ inline size_t lds_align(size_t v) { return (v + 15) / 16 * 16; }
 
@@ -35,11 +37,14 @@ __host__ __device__ inline SelectGeom select_geom(int nc) {
   return {nt, per};
 }
 
-// LDS layout of the select kernel (bytes); host and device share it.
+// LDS layout of the select/gather kernel (bytes); host and device share it.
 //   xs     fp32 [H]          the token (gather workgroups)
 //   pv     fp32 [ncp]        p of every candidate (recovery workgroups)
 //   dl     u32 [ncp]         key distance d of every candidate (recovery)
 //   flags  u8 [ncp]          kept flag of every candidate (recovery, debug)
+//   yred   fp32 [S][H]       partial outputs, S = NT/64 slots for H <= 2048
+//                            else NT/128 (gather workgroups; shares the
+//                            space of pv, dl and flags)
 //   hist   int [2048]        selection histogram
 //   list   int [chan]        this workgroup's kept candidates, by rank
 //   misc   int [64]          scan scratch and broadcast values
@@ -47,19 +52,19 @@ __host__ __device__ inline SelectGeom select_geom(int nc) {
 //   wcnt   int [256]         per-wave counts of the ordered prefix sums
 //   slot   int [16] + fp32 [16]  routed expert and weight per slot
 //   zred   fp32 [NT/64][64]  per-wave recovery sums
-// A down workgroup uses the start of the space for its own sums.
 struct GatherLds {
-  size_t xs, pv, dl, flags, hist, list, misc, bmem, wcnt, slot_e, slot_w, zred, total;
+  size_t xs, pv, dl, flags, yred, hist, list, misc, bmem, wcnt, slot_e, slot_w, zred, total;
   __host__ __device__ GatherLds(int H, int ncp, int nt, int chan) {
     size_t o = 0;
     xs = o;
     o += lds_align((size_t)H * 4);
+    const size_t rec = 2 * lds_align((size_t)ncp * 4) + lds_align((size_t)ncp);
+    const size_t red = (size_t)(H <= 2048 ? nt / 64 : nt / 128) * H * 4;
     pv = o;
-    o += lds_align((size_t)ncp * 4);
-    dl = o;
-    o += lds_align((size_t)ncp * 4);
-    flags = o;
-    o += lds_align((size_t)ncp);
+    dl = o + lds_align((size_t)ncp * 4);
+    flags = o + 2 * lds_align((size_t)ncp * 4);
+    yred = o;
+    o += rec > red ? rec : red;
     hist = o;
     o += 2048 * 4;
     list = o;
@@ -87,9 +92,11 @@ struct Plan {
   int nd = 0;  // 32-bit code words per half-unit that hold codes
   int ng = 0;  // screened-coordinate groups per workgroup
   size_t lds1 = 0;
-  // select: gather, recovery and down workgroups
-  int nt2 = 512, per = 4, ncp = 0, nch = 1, cpw = 1, chan = 1, G = 1, Z = 0, S = 0;
+  // select/gather
+  int nt2 = 512, per = 4, ncp = 0, nch = 1, cpw = 1, chan = 1, G = 1, Z = 0;
   size_t lds2 = 0;
+  // reduce
+  int nslices = 0;
 };
 Plan make_plan(const cfr_config& c, int batch, int k, bool dense);
 size_t max_lds_needed(const cfr_config& c);  // over every batch and k the config allows
@@ -104,8 +111,7 @@ struct DebugOut {
   int32_t* kept = nullptr;
 };
 
-// only: -1 launches every stage; 0 or 1 launches that stage's kernel alone;
-// 2 launches the select kernel alone without clearing the screen sums
+// only: -1 launches every stage; 0, 1 or 2 launches that stage's kernel alone
 int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                   int k, float* y, hipStream_t stream, const DebugOut* dbg,
                   hipEvent_t* stage_events = nullptr /* CFR_NUM_STAGES + 1 or null */, int only = -1,
@@ -117,7 +123,8 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 // base is null); returns the bytes they take.  debug: also the copies the
 // debug entry point reads.
 size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w);
-// Bytes of the screen sums at the start of that carve (rounded as carved).
+// Bytes at the start of that carve that must be zero when a decode starts
+// (the screen sums; a decode leaves them zero).
 size_t decode_sums_bytes(const cfr_reader& r, int batch);
 // Kernel attributes (hipFuncSetAttribute) apply to the current device: a
 // launcher sets them once per device, the first time it runs there.  Setting

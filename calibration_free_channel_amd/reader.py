@@ -219,8 +219,7 @@ class Reader:
         o["kept"] = o["kept"][:, :int(k)]
         return o
 
-    STAGES = ("screen", "select")
-    STAGE_SELECT_KEEP_SUMS = 2  # the select kernel alone, screen sums left in place (timing)
+    STAGES = ("screen", "select", "reduce")
 
     def decode_profile(self, x, expert_ids, gate_w, k: int, out=None, stream=None) -> dict:
         """Decode with an event after every stage; returns {stage: microseconds}.
@@ -237,10 +236,9 @@ class Reader:
         return dict(zip(self.STAGES, list(us)))
 
     def decode_stage(self, stage: int, x, expert_ids, gate_w, k: int, out=None, stream=None):
-        """Launch one decode stage's kernel alone (0 screen, 1 select, or
-        STAGE_SELECT_KEEP_SUMS: the select kernel without clearing the screen
-        sums); for timing a kernel in isolation.  y is the decode's only when
-        stages 0 and 1 run in order for the same inputs."""
+        """Launch one decode stage's kernel alone (0 screen, 1 select, 2 reduce);
+        for timing a kernel in isolation.  y is the decode's only when the three
+        stages run in order for the same inputs."""
         torch = _torch()
         B, px, pi, pw = self._args(x, expert_ids, gate_w)
         if out is None:

@@ -188,7 +188,7 @@ int cfr_reader_decode_residual(cfr_reader* r, const float* x, const int32_t* exp
  * cfr_reader_decode for callers that cannot allocate device memory during
  * the call (code under HIP graph capture, tight serving loops, harnesses
  * that forbid it): the same kernels and result, bit for bit, with the
- * decode's per-call buffers (screen sums, hand-over words) in a static
+ * decode's per-call buffers (screen sums, partial outputs) in a static
  * device array of the library, 8 MiB per device (kept until the process
  * ends), instead of the reader's workspace.  The call allocates nothing; the
  * first call on a device also clears the array with a fill kernel on
@@ -197,7 +197,7 @@ int cfr_reader_decode_residual(cfr_reader* r, const float* x, const int32_t* exp
  * their outputs are unspecified; order them.  The array keeps the last
  * call's contents; the decode leaves its screen sums zero for the next call.
  * Errors: those of cfr_reader_decode, and CFR_EUNSUPPORTED when the call
- * would need more than the 8 MiB (for example batch 64 at 16384 candidates
+ * would need more than the 8 MiB (for example batch 64 at 8192 candidates
  * per token); the message says how much it needs.
  */
 int cfr_reader_decode_noalloc(cfr_reader* r, const float* x, const int32_t* expert_ids,
@@ -264,15 +264,11 @@ int cfr_dense_decode_residual(cfr_reader* r, const float* x, const int32_t* expe
 
 /* Stages of the decode path, in launch order; cfr_reader_decode_profile
  * reports one duration per stage. */
-#define CFR_NUM_STAGES 2
+#define CFR_NUM_STAGES 3
 /* 0 screen: rotate, partial screen, sketch screen sums (k_screen);
- * 1 select: scores, exact top-k, the kept channels' activations from their
- *   gate and up rows, the recovery projection of the skipped ones, and y
- *   over hidden slices from the kept channels' transposed down rows plus
- *   U z (k_select); it clears the screen sums for the next call */
-#define CFR_STAGE_SELECT_KEEP_SUMS 2
-/* the select kernel without clearing the screen sums, so that it can be
- * launched any number of times after one screen pass (timing only) */
+ * 1 select: scores, exact top-k, exact gather of the kept channels and the
+ *   recovery projection of the skipped ones (k_select);
+ * 2 reduce: sum of the partial outputs plus U z (k_reduce) */
 
 /*
  * Measurement entry: the same computation as cfr_reader_decode with a HIP
@@ -287,16 +283,13 @@ int cfr_reader_decode_profile(cfr_reader* r, const float* x, const int32_t* expe
 
 /*
  * Measurement entry: launches the kernel of one decode stage alone on
- * `stream` (stage 0 or 1 as listed above, or CFR_STAGE_SELECT_KEEP_SUMS),
- * with the arguments cfr_reader_decode would give it; no host
- * synchronisation.  A stage reads what the previous stage left in the
- * reader's workspace, so y is the decode's result only when stages 0 and 1
- * run in that order for the same inputs; any other order reads stale but
- * in-range workspace contents.  Stage 0 adds to the screen sums that stage 1
- * clears: run stage 0 alone more than once and the sums pile up (in range,
- * meaningless).  For timing one kernel in isolation (for example many
- * launches in a HIP graph).  Errors as cfr_reader_decode, plus CFR_EINVAL
- * for a stage out of range.
+ * `stream` (stage 0, 1 or 2, as listed above), with the arguments
+ * cfr_reader_decode would give it; no host synchronisation.  A stage reads
+ * what the previous stage left in the reader's workspace, so y is the
+ * decode's result only when stages 0, 1, 2 run in that order for the same
+ * inputs; any other order reads stale but in-range workspace contents.  For
+ * timing one kernel in isolation (for example many launches in a HIP graph).
+ * Errors as cfr_reader_decode, plus CFR_EINVAL for a stage out of range.
  */
 int cfr_reader_decode_stage(cfr_reader* r, int32_t stage, const float* x, const int32_t* expert_ids,
                             const float* gate_w, int32_t batch, int32_t k, float* y, void* stream);
@@ -327,10 +320,7 @@ int cfr_reader_config(const cfr_reader* r, cfr_config* out);
 
 /* Read (and clear) the reader's device status word: bit 0 = an expert id
  * was out of range and clamped; bit 1 = a router logit was not finite
- * (cfr_reader_route); bit 2 = a wait of the select kernel for a value
- * another workgroup of the same launch publishes gave up after its bound
- * (the output of that call is then unspecified; it cannot happen while the
- * launch's workgroups all make progress).  Synchronises the reader's device. */
+ * (cfr_reader_route).  Synchronises the reader's device. */
 int cfr_reader_status(cfr_reader* r, int32_t* flags);
 
 /* Release the reader and all its device memory.  NULL-safe. */

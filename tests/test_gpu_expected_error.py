@@ -83,7 +83,7 @@ def test_tiny_expected_error_deterministic_and_staged(tiny):
     y1 = r.decode(x, i, ww, 23)
     d = r.decode_debug(x, i, ww, 23)
     y2 = torch.empty_like(y1)
-    for stage in range(2):
+    for stage in range(3):
         r.decode_stage(stage, x, i, ww, 23, out=y2)
     torch.cuda.synchronize()
     assert torch.equal(y1, d["y"]) and torch.equal(y1, y2)

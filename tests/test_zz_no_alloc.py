@@ -3,9 +3,10 @@ the C ABI: its output equals cfr_reader_decode's bit for bit (the same
 kernels on the same inputs; stricter than the 2e-3 relative L2 bar), on two
 calls in a row where the second is smaller (fewer tokens, another k), on
 the tiny layer and on the Qwen3-30B-A3B-shaped layer, with the ordinary
-entry point's calls interleaved; a call needing more scratch than the static
-array holds is refused with CFR_EUNSUPPORTED and leaves the next call
-correct."""
+entry point's calls interleaved, and calls of two readers of different
+shapes interleaved (each carves the shared array differently); a call
+needing more scratch than the static array holds is refused with
+CFR_EUNSUPPORTED and leaves the next call correct."""
 import numpy as np
 import pytest
 
@@ -60,23 +61,23 @@ def test_noalloc_equals_decode_on_two_calls(name, calls):
 
 
 def test_noalloc_refuses_calls_beyond_its_scratch():
-    # 8 routed experts x 768 channels: 6144 candidates per token; at 64 tokens
-    # the screen sums and hand-over words take about 12.6 MB
-    shape = LayerShape(hidden=128, n_experts=16, inter=768, top=8)
+    # 8 routed experts x 1024 channels: 8192 candidates per token; at 64
+    # tokens the screen sums alone take 8 MiB
+    shape = LayerShape(hidden=128, n_experts=16, inter=1024, top=8)
     wl = workload("tiny", shape=shape)
     layer = make_layer(wl)
-    r = Reader.build(Config(hidden=128, n_experts=16, inter=768, top=8, rot_seed=wl.rot_seed, max_batch=64),
+    r = Reader.build(Config(hidden=128, n_experts=16, inter=1024, top=8, rot_seed=wl.rot_seed, max_batch=64),
                      layer["gate"], layer["up"], layer["down"], layer["router"])
     try:
         x, i, w = _inputs(layer, wl, 64, seed_offset=3)
         y = torch.empty((64, 128), dtype=torch.float32, device="cuda")
         with pytest.raises(CfrError) as err:
-            r.decode_noalloc(x, i, w, 700, out=y)
+            r.decode_noalloc(x, i, w, 900, out=y)
         assert err.value.code == CFR_EUNSUPPORTED
         # a call that fits still equals the ordinary decode
-        y_ref = r.decode(x[:2], i[:2], w[:2], 700)
+        y_ref = r.decode(x[:2], i[:2], w[:2], 900)
         y2 = torch.empty_like(y_ref)
-        r.decode_noalloc(x[:2], i[:2], w[:2], 700, out=y2)
+        r.decode_noalloc(x[:2], i[:2], w[:2], 900, out=y2)
         torch.cuda.synchronize()
         assert torch.equal(y2, y_ref)
     finally:
@@ -85,8 +86,8 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
 
 def test_noalloc_interleaved_readers_of_different_shapes():
     # readers whose calls carve the shared array differently: a larger call's
-    # screen sums cover bytes where a smaller call left its hand-over words,
-    # and the other way round
+    # screen sums cover bytes where a smaller call left partial outputs, and
+    # the other way round
     built = []
     for name, mb in (("tiny", 8), ("qwen3-30b-a3b", 4)):
         wl = workload(name)
