@@ -36,7 +36,12 @@ Readings of open points (each also listed in the design notes):
 
 Test-only modes (never used by the library): ``storage="fp64"`` keeps U and b
 unrounded; ``sketch="exact"`` replaces alpha*c by the true rotated row values,
-so a full screen (n_screen = 128) reproduces g^T x exactly.
+so a full screen (n_screen = 128) reproduces g^T x exactly; ``experts=`` (a
+list of expert ids) runs load steps (1) and (2) for those experts only, so a
+128-expert layer can be checked on the experts a few tokens route to: their
+codes, scales, rho and norms are the ones the full build gives, and load step
+(3) still stacks the down columns of every expert (decoding a token routed
+elsewhere is an error).
 
 Pins (tests/test_oracle_reader.py): k = all channels reproduces the dense
 gated MLP; rank = H recovery equals the exact skipped contribution; full
@@ -44,6 +49,9 @@ screen with exact sketch gives g_hat = g^T x; k = 0 gives y = U z; one expert
 may take every kept channel.  The y values at the real layer sizes have no
 printed worked example: beyond those identities they are parity unpinned.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .numerics import bf16_to_f64, f64_to_f16_bits, f16_bits_to_f64
@@ -58,10 +66,17 @@ from .expected_error import block_norms2, sketch_variance, expected_error_score
 DEFAULT_ROT_SEED = 0x5EED_0000_CAFE_F00D
 
 
+def _threads():
+    try:
+        return max(1, min(8, len(os.sched_getaffinity(0))))
+    except (AttributeError, OSError):
+        return max(1, min(8, os.cpu_count() or 1))
+
+
 class OracleReader:
     def __init__(self, hidden, n_experts, inter, top, gate, up, down, router=None, *,
                  rank=32, n_screen=80, rot_seed=DEFAULT_ROT_SEED, storage="fp16",
-                 sketch="ternary", block=128):
+                 sketch="ternary", block=128, experts=None):
         assert hidden % block == 0
         self.H, self.E, self.I, self.top = hidden, n_experts, inter, top
         self.rank, self.n_screen, self.block = rank, n_screen, block
@@ -70,33 +85,46 @@ class OracleReader:
         self.gate, self.up, self.down, self.router = gate, up, down, router
         self.sigma = sign_vector(rot_seed, hidden)
         nb, E, I = self.nblk, n_experts, inter
+        # the sketched experts, and where each one's arrays sit (-1: not built)
+        self.experts = (np.arange(E) if experts is None
+                        else np.unique(np.asarray(experts, dtype=np.int64)))
+        assert self.experts.size and self.experts[0] >= 0 and self.experts[-1] < E
+        self.eix = np.full(E, -1, dtype=np.int64)
+        self.eix[self.experts] = np.arange(self.experts.size)
+        nE = self.experts.size
 
         # load step (1): rotation + ternary sketch
-        self.codes = np.empty((E, 2, nb, block, I), dtype=np.int8)
-        self.alpha_bits = np.empty((E, nb, 2, I), dtype=np.uint16)
-        self.rho_bits = np.empty((E, nb, 2, I), dtype=np.uint16)
-        self.rot_rows = np.empty((E, 2, nb, block, I)) if sketch == "exact" else None
-        for e in range(E):
+        self.codes = np.empty((nE, 2, nb, block, I), dtype=np.int8)
+        self.alpha_bits = np.empty((nE, nb, 2, I), dtype=np.uint16)
+        self.rho_bits = np.empty((nE, nb, 2, I), dtype=np.uint16)
+        self.rot_rows = np.empty((nE, 2, nb, block, I)) if sketch == "exact" else None
+        def sketch_expert(i):
+            e = int(self.experts[i])
             for m, w in enumerate((gate, up)):
                 u = rotate_rows(bf16_to_f64(w[e]), self.sigma, block)  # [I][nb][128]
                 c, a, r = ternarize_blocks(u)
-                self.codes[e, m] = c.transpose(1, 2, 0)
-                self.alpha_bits[e, :, m, :] = a.T
-                self.rho_bits[e, :, m, :] = r.T
+                self.codes[i, m] = c.transpose(1, 2, 0)
+                self.alpha_bits[i, :, m, :] = a.T
+                self.rho_bits[i, :, m, :] = r.T
                 if self.rot_rows is not None:
-                    self.rot_rows[e, m] = (u / np.sqrt(128.0)).transpose(1, 2, 0)
+                    self.rot_rows[i, m] = (u / np.sqrt(128.0)).transpose(1, 2, 0)
+
+        # experts are independent: a few at a time on host threads (numpy
+        # releases the GIL in its array loops); each writes only its own slice
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(sketch_expert, range(nE)))
         self.alpha = f16_bits_to_f64(self.alpha_bits)
         self.rho = f16_bits_to_f64(self.rho_bits)
         self.units = pack_units(self.codes[:, 0], self.codes[:, 1])  # [E][nb][128][unit]
 
         # load step (2): down-column norms, summed over h in index order
-        self.norms = np.empty((E, I), dtype=np.float32)
-        for e0 in range(0, E, 16):
-            d = bf16_to_f64(down[e0:e0 + 16])  # [e][H][I]
+        self.norms = np.empty((nE, I), dtype=np.float32)
+        for i0 in range(0, nE, 16):
+            d = bf16_to_f64(down[self.experts[i0:i0 + 16]])  # [e][H][I]
             acc = np.zeros((d.shape[0], I))
             for h in range(hidden):
                 acc = acc + d[:, h, :] * d[:, h, :]
-            self.norms[e0:e0 + 16] = np.sqrt(acc).astype(np.float32)
+            self.norms[i0:i0 + 16] = np.sqrt(acc).astype(np.float32)
 
         # load step (3): recovery basis
         u64, b64 = recovery_basis(down, rank)
@@ -107,6 +135,13 @@ class OracleReader:
         else:
             self.U_bits = self.b_bits = None
             self.U, self.b = u64, b64
+
+    def ix(self, ids):
+        """Positions of expert ids in the sketched experts' arrays."""
+        i = self.eix[np.asarray(ids, dtype=np.int64)]
+        if np.any(i < 0):
+            raise ValueError("expert not sketched by this oracle (built with experts=)")
+        return i
 
     # -- decode -------------------------------------------------------------
     def select(self, x):
@@ -123,7 +158,7 @@ class OracleReader:
     def screen(self, x, ids, sel):
         xr = rotate_x_f64(np.asarray(x, dtype=np.float32).astype(np.float64), self.sigma, self.block)
         est = np.zeros((2, self.top, self.I))
-        for s, e in enumerate(np.asarray(ids).tolist()):
+        for s, e in enumerate(self.ix(ids).tolist()):
             for m in range(2):
                 acc = np.zeros(self.I)
                 for b in range(self.nblk):
@@ -152,14 +187,14 @@ class OracleReader:
         sel = own_sel if sel is None else np.sort(np.asarray(sel, dtype=np.int64), axis=-1)
         ghat, vhat = self.screen(x, ids, sel)
         p = silu(ghat) * vhat
-        dn = self.norms[ids].astype(np.float64)
+        dn = self.norms[self.ix(ids)].astype(np.float64)
         if ranking == "score":
             score = w[:, None] * dn * np.abs(p)
         elif ranking == "expected_error":
             assert self.n_screen == self.block, "expected-error ranking reads the whole sketch"
             xb2 = block_norms2(x, self.block)
-            var_g = sketch_variance(self.rho[ids, :, 0, :].transpose(0, 2, 1), xb2)
-            var_v = sketch_variance(self.rho[ids, :, 1, :].transpose(0, 2, 1), xb2)
+            var_g = sketch_variance(self.rho[self.ix(ids), :, 0, :].transpose(0, 2, 1), xb2)
+            var_v = sketch_variance(self.rho[self.ix(ids), :, 1, :].transpose(0, 2, 1), xb2)
             score = expected_error_score(ghat, vhat, var_g, var_v, w[:, None], dn)
         else:
             raise ValueError(f"unknown ranking {ranking!r}")

@@ -48,26 +48,30 @@ def ternarize_blocks(u: np.ndarray):
     """
     u = np.asarray(u, dtype=np.float64)
     nblk = u.shape[-1]
-    au = np.abs(u)
+    # coordinate-major copies, so that each index-ordered sum below walks
+    # contiguous slices (the same additions in the same order)
+    uT = np.ascontiguousarray(np.moveaxis(u, -1, 0))
+    auT = np.abs(uT)
     s = np.zeros(u.shape[:-1])
     for i in range(nblk):
-        s = s + au[..., i]
-    keep = 1280.0 * au > 7.0 * s[..., None]
-    codes = (np.sign(u) * keep).astype(np.int8)
-    n = keep.sum(axis=-1)
+        s = s + auT[i]
+    keepT = 1280.0 * auT > 7.0 * s
+    codesT = (np.sign(uT) * keepT).astype(np.int8)
+    n = keepT.sum(axis=0)
     a = np.zeros(u.shape[:-1])
     for i in range(nblk):
-        a = a + np.where(keep[..., i], au[..., i], 0.0)
+        a = a + np.where(keepT[i], auT[i], 0.0)
     with np.errstate(divide="ignore", invalid="ignore"):
         alpha64 = np.where(n > 0, a / (n * SQRT128), 0.0)
     alpha_bits = f64_to_f16_bits(alpha64)
     alpha = f16_bits_to_f64(alpha_bits)
-    r = u / SQRT128
+    rT = uT / SQRT128
     acc = np.zeros(u.shape[:-1])
     for i in range(nblk):
-        d = r[..., i] - alpha * codes[..., i]
+        d = rT[i] - alpha * codesT[i]
         acc = acc + d * d
     rho_bits = f64_to_f16_bits(acc / 128.0)
+    codes = np.ascontiguousarray(np.moveaxis(codesT, 0, -1))
     return codes, alpha_bits, rho_bits
 
 

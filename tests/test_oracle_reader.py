@@ -255,3 +255,23 @@ def test_pack_matches_codes(tiny_reader):
     assert np.array_equal(g, tiny_reader.codes[:, 0])
     assert np.array_equal(u, tiny_reader.codes[:, 1])
     assert tiny_reader.units.shape == (S.n_experts, S.n_blocks, 128, 32)
+
+
+def test_expert_subset_build_decodes_like_the_full_build(tiny_layer, tiny_reader):
+    """An oracle built for the routed experts only (load steps (1)-(2) on those,
+    the recovery basis over every expert) decodes those tokens bit for bit like
+    the full build, and refuses a token routed elsewhere."""
+    X = _tokens(4)
+    routes = [route(tiny_layer["router"], x, S.top)[:2] for x in X]
+    used = sorted({int(e) for ids, _ in routes for e in ids})
+    sub = _reader(tiny_layer, experts=used)
+    assert np.array_equal(sub.U_bits, tiny_reader.U_bits) and np.array_equal(sub.b_bits, tiny_reader.b_bits)
+    for x, (ids, w) in zip(X, routes):
+        a = tiny_reader.decode(x, ids, w, 23)
+        b = sub.decode(x, ids, w, 23)
+        for key in ("ghat", "vhat", "score", "kept", "y"):
+            assert np.array_equal(a[key], b[key]), key
+    other = next(e for e in range(S.n_experts) if e not in used)
+    ids = np.array([other] + list(routes[0][0][1:]))
+    with pytest.raises(ValueError):
+        sub.decode(X[0], ids, routes[0][1], 23)
