@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "device_util.h"
 #include "kernels.h"
 
 // Optional device-side phase trace: a build that defines CFR_TRACE_PHASE(k, i)
@@ -52,116 +53,6 @@
 namespace cfr {
 
 namespace {
-
-constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
-constexpr float kTwo32 = 4294967296.0f;                // 2^32: fixed-point scale of the screen sums
-
-__device__ __forceinline__ float f16f(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-__device__ __forceinline__ float lo16(uint32_t w) { return f16f((uint16_t)(w & 0xFFFFu)); }
-__device__ __forceinline__ float hi16(uint32_t w) { return f16f((uint16_t)(w >> 16)); }
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// silu(z) = z / (1 + e^-z) through the hardware exp2 and reciprocal (about
-// one ulp each; the method's tolerances are far wider).
-__device__ __forceinline__ float silu(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-}
-
-// float -> 64-bit two's complement fixed point with 32 fraction bits, rounded
-// to nearest; exact in float32 arithmetic for |v| < 2^31: v = fl + fr with
-// fl = floor(v) and fr in [0, 1), and fr * 2^32 is an exact float.
-__device__ __forceinline__ unsigned long long to_fix(float v) {
-  const float fl = floorf(v);
-  const float fr = v - fl;
-  const uint32_t hi = (uint32_t)(int)fl;
-  const uint32_t lo = (uint32_t)rintf(fr * kTwo32);
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-// fixed point -> float (one rounding)
-__device__ __forceinline__ float from_fix(unsigned long long x) {
-  return fmaf((float)(int)(x >> 32), kTwo32, (float)(uint32_t)x) * (1.0f / kTwo32);
-}
-
-__device__ __forceinline__ int clamp_expert(int e, int E, int32_t* status) {
-  if (e < 0 || e >= E) {
-    atomicOr(status, 1);
-    e = e < 0 ? 0 : E - 1;
-  }
-  return e;
-}
-
-// Order-preserving map of a float to an unsigned key: a larger float gives a
-// larger key (negative values below positive ones).
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Value of lane (lane ^ H) in a wave64, through register-level exchanges:
-// DPP quad permutes for H = 1, 2, DPP row shifts for H = 4, 8 and the gfx950
-// permlane swaps for H = 16, 32 (no trip through the LDS crossbar).
-template <int H>
-__device__ __forceinline__ int xor_lane(int v) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (H == 1) {
-    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-  } else if constexpr (H == 2) {
-    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-  } else if constexpr (H == 4 || H == 8) {
-    const int up = __builtin_amdgcn_update_dpp(0, v, 0x100 + H, 0xF, 0xF, false);  // row_shl:H
-    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x110 + H, 0xF, 0xF, false);  // row_shr:H
-    return (lane & H) ? dn : up;
-  } else if constexpr (H == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
-
-template <int H>
-__device__ __forceinline__ float xor_lane_f(float v) {
-  return __int_as_float(xor_lane<H>(__float_as_int(v)));
-}
-
-// Butterfly sum over the wave; every lane ends with the same total.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += xor_lane_f<1>(v);
-  v += xor_lane_f<2>(v);
-  v += xor_lane_f<4>(v);
-  v += xor_lane_f<8>(v);
-  v += xor_lane_f<16>(v);
-  v += xor_lane_f<32>(v);
-  return v;
-}
-
-// Inclusive prefix sum over a wave64 (DPP row shifts and row broadcasts).
-__device__ __forceinline__ int wave_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return v;
-}
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
-// every outstanding global load of the wave; these kernels exchange data
-// through LDS alone, so loads issued early stay in flight across barriers.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  // compiler-only barrier: global loads issued before stay before (nothing
-  // waits for them here), so they remain in flight across the barrier
-  asm volatile("" ::: "memory");
-}
 
 // Inclusive prefix sum over the NT threads of a workgroup.  sh: NT/64 ints
 // that nobody else uses between the two barriers inside.
@@ -535,7 +426,7 @@ struct SelectArgs {
   float* score;
   int32_t* kept;
   int32_t* status;
-  int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dense, dbg;
+  int H, E, I, top, nc, ncp, k, rank, G, Z, cpw, chan, dbg;
   float invI;   // 1 / I rounded to float (exact slot division below 2^17)
   int cps_mul;  // I % 128 == 0: ceil(2^16 / (I / 128)), else 0
   const float* var;  // [B][2][ncp] sketch-error variances (expected-error ranking)
@@ -703,7 +594,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   float* sl_w = reinterpret_cast<float*>(smem + L.slot_w);
   float* zw = reinterpret_cast<float*>(smem + L.zred);
 
-  const bool all = a.dense || k == nc;
+  const bool all = k == nc;
   const bool partial = !all && k > 0;
   const int kk = all ? nc : k;  // kept candidates
   const int r0 = recover ? 0 : min(w * a.chan, kk);
@@ -721,9 +612,6 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   // scores): loads complete in issue order, so waiting for these must not
   // wait for the screen sums issued after them
   const float gwl = a.gw[t * a.top + min(lane, a.top - 1)];
-  // (issued on every path, as buffer loads that the dense mode points past
-  // the end: a load on one path only would make every later wait on the
-  // other path conservative)
   ulonglong2 gq[P2], vq[P2];
   float2 gvq[VAR ? P2 : 1], vvq[VAR ? P2 : 1];
   float2 wq[P2];
@@ -732,9 +620,9 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
     const uint32_t vofs = (uint32_t)a.ncp * 8u;
 #pragma unroll
     for (int i = 0; i < P2; ++i) {
-      const uint32_t o = a.dense ? kNoLoad : (uint32_t)(i * NT + tid) * 16u;
+      const uint32_t o = (uint32_t)(i * NT + tid) * 16u;
       const auto g4 = __builtin_amdgcn_raw_buffer_load_b128(ars, o, 0, 0);
-      const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(ars, a.dense ? kNoLoad : o + vofs, 0, 0);
+      const auto v4 = __builtin_amdgcn_raw_buffer_load_b128(ars, o + vofs, 0, 0);
       gq[i] = make_ulonglong2(((unsigned long long)g4[1] << 32) | g4[0], ((unsigned long long)g4[3] << 32) | g4[2]);
       vq[i] = make_ulonglong2(((unsigned long long)v4[1] << 32) | v4[0], ((unsigned long long)v4[3] << 32) | v4[2]);
     }
@@ -766,7 +654,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   uint32_t key[PER];
   float pr[PER];
   uint32_t kmax = 0u;
-  if (!a.dense) {
+  {
 #pragma unroll
     for (int i = 0; i < P2; ++i) {
       if (a.cps_mul) {
@@ -808,7 +696,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   if (tid == 0) misc[kMiscSlot] = 0;
   lds_barrier();
   CFR_TRACE_PHASE(1, 1);
-  if (dbgw && !a.dense) {
+  if (dbgw) {
     // debug copies of g_hat, v_hat and the scores: a separate pass that reads
     // the sums again (kept out of the loop above, whose loads it would stall)
     for (int c = tid; c < nc; c += NT) {
@@ -1492,7 +1380,7 @@ size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* 
   return o;
 }
 
-Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
+Plan make_plan(const cfr_config& c, int batch, int k) {
   Plan p;
   const int nblk = c.hidden / kBlock, nbytes = (c.inter + 4) / 5, nc = c.top * c.inter;
   // screen
@@ -1509,7 +1397,7 @@ Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
   p.per = g.per;
   p.ncp = g.nt * g.per;
   const int NW = p.nt2 / 64;
-  const int kk = dense ? nc : k;
+  const int kk = k;
   int gmax = (kMaxGatherWgs - kMaxRecoverWgs) / batch;
   if (gmax < 1) gmax = 1;
   p.chan = (kk + gmax - 1) / gmax;
@@ -1519,7 +1407,7 @@ Plan make_plan(const cfr_config& c, int batch, int k, bool dense) {
   if (p.G < 1) p.G = 1;
   int z = kMaxRecoverWgs / batch;
   if (z < 1) z = 1;
-  p.Z = (!dense && c.rank > 0 && k < nc) ? z : 0;
+  p.Z = (c.rank > 0 && k < nc) ? z : 0;
   if (p.Z > nc) p.Z = nc;
   p.nch = 1;
   while (p.nch * 512 < c.hidden) p.nch *= 2;
@@ -1534,12 +1422,12 @@ size_t max_lds_needed(const cfr_config& c) {
   const int nc = c.top * c.inter;
   for (int b = 1; b <= c.max_batch; ++b)
     for (int kk : {0, 1, nc / 2, nc}) {
-      const Plan p = make_plan(c, b, kk, false);
+      const Plan p = make_plan(c, b, kk);
       if (p.lds1 + 8192 > m) m = p.lds1 + 8192;  // + the screen kernel's static LDS
       if (p.lds2 > m) m = p.lds2;
     }
-  const Plan d = make_plan(c, 1, nc, true);
-  if (d.lds2 > m) m = d.lds2;
+  const DensePlan d = make_dense_plan(c, 1);
+  if (d.lds > m) m = d.lds;
   return m;
 }
 
@@ -1588,7 +1476,7 @@ static hipError_t launch_select_v(const SelectArgs& a, const Plan& p, int batch,
 }
 
 static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  return a.var && !a.dense ? launch_select_v<true>(a, p, batch, st) : launch_select_v<false>(a, p, batch, st);
+  return a.var ? launch_select_v<true>(a, p, batch, st) : launch_select_v<false>(a, p, batch, st);
 }
 
 // CPB: coordinates per thread batch, the n_screen = 80 share of one thread in
@@ -1625,7 +1513,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
                   const float* resid, const Workspace* wsp) {
   const cfr_config& c = r->cfg;
   const Workspace& W = wsp ? *wsp : r->wk;
-  const Plan p = make_plan(c, batch, k, false);
+  const Plan p = make_plan(c, batch, k);
   auto mark = [&](int i) {
     if (ev) (void)hipEventRecord(ev[i], st);
   };
@@ -1641,7 +1529,7 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
   mark(1);
   SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, W.ypart, W.zpart, W.ghat, W.vhat,
                W.score, W.kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
-               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, 0, dbg != nullptr, 1.0f / (float)c.inter,
+               r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, dbg != nullptr, 1.0f / (float)c.inter,
                cps_mul(c.inter), var};
   if (only < 0 || only == 1)
     if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
@@ -1674,16 +1562,13 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t st, const float* resid) {
   const cfr_config& c = r->cfg;
-  const int nc = r->ncand;
-  const Plan p = make_plan(c, batch, nc, true);
+  const DensePlan p = make_dense_plan(c, batch);
   const Workspace& W = r->wk;
-  SelectArgs B{x, ids, gw, r->w3, r->b, W.acc, r->norms, W.ypart, W.zpart, nullptr, nullptr,
-               nullptr, nullptr, r->status, c.hidden, c.n_experts, c.inter, c.top, nc, r->ncp,
-               nc, 0, p.G, 0, p.cpw, p.chan, 1, 0, 1.0f / (float)c.inter, cps_mul(c.inter), nullptr};
   hipError_t e;
-  if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "dense launch");
+  if ((e = launch_dense_block(x, ids, gw, r->w3, W.ypart, r->status, c, batch, p, st)) != hipSuccess)
+    return hip_fail(e, "dense launch");
   ReduceArgs C{W.ypart, W.zpart, r->u, y, W.acc, c.hidden, p.G, 0, c.rank, r->ncp,
-               p.nslices, 0, resid};
+               c.hidden / kReduceSlice, 0, resid};
   if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "dense reduce launch");
   return CFR_OK;
 }

@@ -1,0 +1,122 @@
+// Device helpers shared by the decode and dense kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace cfr {
+namespace {
+
+constexpr float kInvSqrt128f = 0.08838834764831845f;  // 1/sqrt(128) rounded to float
+constexpr float kTwo32 = 4294967296.0f;                // 2^32: fixed-point scale of the screen sums
+
+__device__ __forceinline__ float f16f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float lo16(uint32_t w) { return f16f((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi16(uint32_t w) { return f16f((uint16_t)(w >> 16)); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// silu(z) = z / (1 + e^-z) through the hardware exp2 and reciprocal (about
+// one ulp each; the method's tolerances are far wider).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// float -> 64-bit two's complement fixed point with 32 fraction bits, rounded
+// to nearest; exact in float32 arithmetic for |v| < 2^31: v = fl + fr with
+// fl = floor(v) and fr in [0, 1), and fr * 2^32 is an exact float.
+__device__ __forceinline__ unsigned long long to_fix(float v) {
+  const float fl = floorf(v);
+  const float fr = v - fl;
+  const uint32_t hi = (uint32_t)(int)fl;
+  const uint32_t lo = (uint32_t)rintf(fr * kTwo32);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// fixed point -> float (one rounding)
+__device__ __forceinline__ float from_fix(unsigned long long x) {
+  return fmaf((float)(int)(x >> 32), kTwo32, (float)(uint32_t)x) * (1.0f / kTwo32);
+}
+
+__device__ __forceinline__ int clamp_expert(int e, int E, int32_t* status) {
+  if (e < 0 || e >= E) {
+    atomicOr(status, 1);
+    e = e < 0 ? 0 : E - 1;
+  }
+  return e;
+}
+
+// Order-preserving map of a float to an unsigned key: a larger float gives a
+// larger key (negative values below positive ones).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Value of lane (lane ^ H) in a wave64, through register-level exchanges:
+// DPP quad permutes for H = 1, 2, DPP row shifts for H = 4, 8 and the gfx950
+// permlane swaps for H = 16, 32 (no trip through the LDS crossbar).
+template <int H>
+__device__ __forceinline__ int xor_lane(int v) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (H == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (H == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (H == 4 || H == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x100 + H, 0xF, 0xF, false);  // row_shl:H
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x110 + H, 0xF, 0xF, false);  // row_shr:H
+    return (lane & H) ? dn : up;
+  } else if constexpr (H == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+template <int H>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  return __int_as_float(xor_lane<H>(__float_as_int(v)));
+}
+
+// Butterfly sum over the wave; every lane ends with the same total.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += xor_lane_f<1>(v);
+  v += xor_lane_f<2>(v);
+  v += xor_lane_f<4>(v);
+  v += xor_lane_f<8>(v);
+  v += xor_lane_f<16>(v);
+  v += xor_lane_f<32>(v);
+  return v;
+}
+
+// Inclusive prefix sum over a wave64 (DPP row shifts and row broadcasts).
+__device__ __forceinline__ int wave_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load of the wave; these kernels exchange data
+// through LDS alone, so loads issued early stay in flight across barriers.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  // compiler-only barrier: global loads issued before stay before (nothing
+  // waits for them here), so they remain in flight across the barrier
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace
+}  // namespace cfr

@@ -98,7 +98,7 @@ struct Plan {
   // reduce
   int nslices = 0;
 };
-Plan make_plan(const cfr_config& c, int batch, int k, bool dense);
+Plan make_plan(const cfr_config& c, int batch, int k);
 size_t max_lds_needed(const cfr_config& c);  // over every batch and k the config allows
 
 // Intermediates copied out by the debug entry point (any may be null).
@@ -152,6 +152,18 @@ hipError_t launch_route(const float* x, const uint16_t* router, const cfr_config
                         hipStream_t st);
 int launch_dense(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
                  float* y, hipStream_t stream, const float* resid = nullptr);
+
+// The dense block's streaming kernel (dense_kernel.hip): G workgroups per
+// token over `chan` channels each, `cpw` per wave, u in flight per wave,
+// writing G partial outputs per token into ypart[batch][G][H].
+struct DensePlan {
+  int G = 1, chan = 1, cpw = 1, nch = 1, u = 1;
+  size_t lds = 0;
+};
+DensePlan make_dense_plan(const cfr_config& c, int batch);
+hipError_t launch_dense_block(const float* x, const int32_t* ids, const float* gw, const uint16_t* w3,
+                              float* ypart, int32_t* status, const cfr_config& c, int batch,
+                              const DensePlan& p, hipStream_t st);
 
 // Load step (3) on the device: U (fp16 [H][rank]) and b (fp16 [E][I][rank])
 // from the resident down rows.  Synchronous.
