@@ -27,7 +27,10 @@ Method:
     routing of RMSNorm(x) with the fused pre-norm, then the decode of the
     normed token with its output added to the residual stream x in the
     decode's last kernel; the same with the dense block, and the routing
-    alone (the 48-layer stack is `--stack`);
+    alone;
+  * the 48-layer stack (`stack_48l`, independent weights per layer): one
+    batch-1 step of route + decode + residual per layer as one HIP graph,
+    beside the same chain with the dense block (`--stack` times it alone);
   * the 28.7% budget is timed the same way on a second set of layer copies
     built for the ranking the method uses from that budget on (whole sketch,
     expected squared error with rho), k chosen by the read accounting;
@@ -50,6 +53,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MIN_PASSES = 5      # graph passes per timed figure, at least
+MIN_DECODES = 200   # decodes per timed figure, at least
 METRIC = "MoE-block µs/token and achieved HBM GB/s at 17.8% reads, batch 1"
 
 
@@ -64,7 +69,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--layers", type=int, default=40, help="layer copies cycled per graph pass")
     ap.add_argument("--workload", default="qwen3-30b-a3b")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--main-budget-only", action="store_true",
@@ -79,8 +84,10 @@ def parse():
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="summarise rocprofv3 CSV output under DIR as text and exit")
     ap.add_argument("--stack", action="store_true",
-                    help="time the 48-layer batch-1 decode step instead (route, decode, residual "
+                    help="time only the 48-layer batch-1 decode step (route, decode, residual "
                          "per layer, captured as one HIP graph); prints its own JSON line")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 48-layer batch-1 decode step in the main line")
     return ap.parse_args()
 
 
@@ -190,7 +197,8 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None,
     with torch.cuda.graph(g, stream=s):
         one_pass()
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // L))
+    # at least MIN_PASSES passes and MIN_DECODES decodes, whatever --steps says
+    reps = max(MIN_PASSES, -(-steps // L), -(-MIN_DECODES // L))
     wreps = max(1, -(-warmup // L))
     with torch.cuda.stream(s):
         for _ in range(wreps):
@@ -233,7 +241,7 @@ def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
         with torch.cuda.graph(g, stream=s):
             one_pass(stage)
         torch.cuda.synchronize()
-        reps = max(1, -(-steps // L))
+        reps = max(MIN_PASSES, -(-steps // L), -(-MIN_DECODES // L))
         with torch.cuda.stream(s):
             for _ in range(max(1, -(-warmup // L))):
                 g.replay()
@@ -283,6 +291,7 @@ def traffic_bytes(kernel):
 
 
 def _cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo, else lscpu."""
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
@@ -290,26 +299,42 @@ def _cpu_model():
                     return line.split(":", 1)[1].strip()
     except OSError:
         pass
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
     return None
 
 
-def cpu_baseline(wl, layer, X, IDS, W, k, seconds):
-    """The oracle's float64 decode on the host: on every BLAS thread it uses,
-    then on one thread (a shorter sample), per token."""
+def _host_cpus():
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, layer, X, IDS, W, ks, seconds):
+    """The oracle's float64 decode on the host, per token, at each budget in
+    ks (the sample split evenly between them): on every BLAS thread it uses,
+    then on one thread (a shorter sample) at the first budget."""
     from oracle import OracleReader
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threadpool_limits = None
-        threads = os.cpu_count() or 1
+        threads = _host_cpus()
     s = wl.shape
     t = time.time()
     o = OracleReader(s.hidden, s.n_experts, s.inter, s.top, layer["gate"], layer["up"],
                      layer["down"], rot_seed=wl.rot_seed)
     log(f"oracle built in {time.time() - t:.1f}s (not timed)")
 
-    def run(budget):
+    def run(k, budget):
         n = 0
         t0 = time.perf_counter()
         while True:
@@ -320,20 +345,25 @@ def cpu_baseline(wl, layer, X, IDS, W, k, seconds):
             if (el >= budget and n >= 8) or n >= 4096:
                 return n, el
 
-    n, el = run(seconds)
+    by_k = {}
+    for k in ks:
+        n, el = run(k, seconds / len(ks))
+        by_k[f"k={k}"] = {"value": round(1e6 * el / n, 1), "tokens": n, "seconds": round(el, 1)}
     one = None
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            n1, el1 = run(seconds / 2)
-        one = {"value": round(1e6 * el1 / n1, 1), "tokens": n1, "seconds": round(el1, 1)}
-    return {"value": round(1e6 * el / n, 1), "unit": "us/token", "cores": int(threads),
+            n1, el1 = run(ks[0], seconds / 4)
+        one = {"value": round(1e6 * el1 / n1, 1), "k": ks[0], "tokens": n1, "seconds": round(el1, 1)}
+    main = by_k[f"k={ks[0]}"]
+    return {"value": main["value"], "unit": "us/token", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n} batch-1 tokens of the {wl.name} layer at k={k}, float64 numpy "
-                      f"decode only (load-time build excluded), {el:.1f}s of CPU work",
-            "single_core": one, "cpu_model": _cpu_model()}
+            "sample": f"{main['tokens']} batch-1 tokens of the {wl.name} layer at k={ks[0]}, float64 "
+                      f"numpy decode only (load-time build excluded), {main['seconds']}s of CPU work; "
+                      "the other budgets on samples of the same length",
+            "by_k": by_k, "single_core": one, "cpu_model": _cpu_model(), "host_cpus": _host_cpus()}
 
 
-def stack_step(args):
+def stack_48l(steps, warmup):
     """The 48-layer stack of Qwen3-30B-A3B-shaped layers (independent weights
     per layer) as one batch-1 decode step: per layer h = RMSNorm(x) (unit
     weights, fused into the library's routing), the library routes h and
@@ -354,7 +384,7 @@ def stack_step(args):
     readers = []
     t = time.time()
     for l in range(wl.n_layers):
-        L = make_layer(wl, layer=l)
+        L = make_layer(wl, layer=l)  # independent weights per layer
         readers.append(Reader.build(cfg, L["gate"], L["up"], L["down"], L["router"]))
         del L
         if l % 8 == 7:
@@ -378,7 +408,7 @@ def stack_step(args):
             else:
                 r.decode(h, ids, w, k, out=x, residual=x)
 
-    def timed(mode, steps, warmup):
+    def timed(mode, steps, warmup, spread=None):
         st.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(st):
             one_step(mode)
@@ -390,19 +420,24 @@ def stack_step(args):
         with torch.cuda.stream(st):
             for _ in range(warmup):
                 g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            ev[0].record(st)
+            for i in range(steps):
                 g.replay()
-            e1.record(st)
+                ev[i + 1].record(st)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        ms = ev[0].elapsed_time(ev[-1])
+        if spread is not None:
+            per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+            spread["median"] = round(per[len(per) // 2], 2)
+            spread["p90"] = round(per[min(steps - 1, int(0.9 * steps))], 2)
         del g
         return 1000.0 * ms / steps
 
-    steps = min(args.steps, 200)
-    warm = max(2, min(args.warmup, 20))
-    us = timed("reader", steps, warm)
+    steps = max(MIN_PASSES, min(steps, 200))
+    warm = max(2, min(warmup, 20))
+    spread = {}
+    us = timed("reader", steps, warm, spread)
     xr = x.clone()
     dense_us = timed("dense", steps, warm)
     route_us = timed("route", steps, warm)
@@ -416,6 +451,7 @@ def stack_step(args):
                                "pre-norm (RMSNorm, unit weights) and residual",
                    "layers": wl.n_layers, "timing": "one hip graph per step, replayed"},
         "us_per_layer": round(us / wl.n_layers, 3),
+        "per_step_median_us": spread["median"], "per_step_p90_us": spread["p90"],
         "bytes_per_step": per_layer * wl.n_layers,
         "achieved_GBps": round(per_layer * wl.n_layers / us / 1e3, 1),
         "dense_bf16_us_per_step": round(dense_us, 2),
@@ -423,9 +459,10 @@ def stack_step(args):
         "speedup_vs_dense": round(dense_us / us, 3),
         "final_x_finite": bool(torch.isfinite(xr).all().item()),
     }
-    print(json.dumps(out), flush=True)
     for r in readers:
         r.close()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -437,7 +474,7 @@ def main():
         if args.gpus != 1:
             print("bench.py --stack runs on one GPU only.", file=sys.stderr)
             sys.exit(2)
-        stack_step(args)
+        print(json.dumps(stack_48l(args.steps, args.warmup)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs the single-GPU reader only; --gpus {args.gpus} is not supported "
@@ -595,6 +632,18 @@ def main():
         for r in r5:
             r.close()
 
+    # the 48-layer stack (independent weights per layer) as one batch-1 step
+    stack = None
+    if not args.main_budget_only and not args.no_stack:
+        for r in readers[1:]:
+            r.close()
+        readers = readers[:1]
+        torch.cuda.empty_cache()
+        t = time.time()
+        stack = stack_48l(args.steps, args.warmup)
+        log(f"48-layer step: {stack['value']} us/step (median {stack['per_step_median_us']}, "
+            f"dense {stack['dense_bf16_us_per_step']}), {time.time() - t:.0f}s with the build")
+
     if args.copy_calibration:
         copy_calibration(torch)
         log(f"copy calibration: {COPY_BYTES >> 20} MiB read and written 4 times")
@@ -616,8 +665,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, layer, Xh, IDh.reshape(L, 1, s.top), Wh.reshape(L, 1, s.top),
-                           k_main, args.cpu_seconds)
-        log(f"cpu baseline: {cpu['value']} us/token on {cpu['cores']} threads"
+                           [k_main] + ([k_low] if k_low else []), args.cpu_seconds)
+        log(f"cpu baseline: {cpu['by_k']} us/token on {cpu['cores']} threads ({cpu['cpu_model']})"
             + (f", {cpu['single_core']['value']} us/token on one" if cpu["single_core"] else ""))
 
     out = {
@@ -669,6 +718,10 @@ def main():
                                    "with the dense block; route: the routing alone")
                               if layer_step else None),
         "qwen3_235b_a22b_batch8": c5,
+        "stack_48l": None if stack is None else {
+            kk: stack[kk] for kk in ("value", "unit", "steps", "us_per_layer", "per_step_median_us",
+                                     "per_step_p90_us", "achieved_GBps", "dense_bf16_us_per_step",
+                                     "norm_and_route_us_per_step", "speedup_vs_dense", "final_x_finite")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -21,11 +21,13 @@ Value recipe (no trained weights exist here):
     dimensions multiplied by ``x_outlier_mult`` (the same dimensions for
     every token of a workload).
 
-Every array comes from its own numpy ``default_rng([seed, stream])`` stream,
-so one array can be regenerated without the others.
+Every array comes from its own numpy ``default_rng([seed, stream, ...])``
+streams, so one array can be regenerated without the others.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
 import numpy as np
@@ -142,22 +144,44 @@ def x_outlier_dims(wl: Workload) -> np.ndarray:
     return np.sort(rng.choice(wl.shape.hidden, size=wl.x_outlier_dims, replace=False)).astype(np.int64)
 
 
-def _normal_bf16(seed, stream, shape, std, col_scale=None, chunk_rows=4096):
-    """N(0, std) float32 rounded to bf16, generated in row chunks to bound memory.
+_CHUNK_ROWS = 4096
 
-    ``shape`` is (..., H); ``col_scale`` multiplies the last axis before rounding.
+
+def _pool_size() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except (AttributeError, OSError):
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def _normal_bf16(seed, stream, shape, std, col_scale=None):
+    """N(0, std) float32 rounded to bf16.
+
+    ``shape`` is (..., H); ``col_scale`` multiplies the last axis before
+    rounding.  Rows come in chunks of 4096, chunk c from its own stream
+    ``default_rng([seed, stream, 1 + c])``, so the result does not depend on
+    how many threads fill it (numpy's generators release the GIL while they
+    fill an array).
     """
     rows = int(np.prod(shape[:-1]))
     cols = shape[-1]
     out = np.empty((rows, cols), dtype=np.uint16)
-    rng = _rng(seed, stream)
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        a = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+
+    def fill(c):
+        r0 = c * _CHUNK_ROWS
+        r1 = min(rows, r0 + _CHUNK_ROWS)
+        a = _rng(seed, stream, 1 + c).standard_normal((r1 - r0, cols), dtype=np.float32)
         a *= np.float32(std)
         if col_scale is not None:
             a *= col_scale
         out[r0:r1] = f32_to_bf16_bits(a)
+
+    n = -(-rows // _CHUNK_ROWS)
+    if n == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_pool_size()) as ex:
+            list(ex.map(fill, range(n)))
     return out.reshape(shape)
 
 
