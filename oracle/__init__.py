@@ -33,8 +33,10 @@ from .accounting import read_bytes, resident_bytes
 from .expected_error import (silu_grad, block_norms2, sketch_variance, activation_variance,
                              expected_error_score)
 from .reader import OracleReader
+from .shared import decode_shared
 
 __all__ = [
+    "decode_shared",
     "bf16_to_f64", "f64_to_f16_bits", "f16_bits_to_f64", "splitmix64_stream",
     "sign_vector", "sylvester_hadamard", "rotate_rows", "rotate_x_f64",
     "rotation_matrix", "SQRT128", "ternarize_blocks",
