@@ -35,7 +35,10 @@ Method:
     built for the ranking the method uses from that budget on (whole sketch,
     expected squared error with rho), k chosen by the read accounting;
   * the Qwen3-235B-A22B-shaped layer (hidden 4096, 128 experts, intermediate
-    1536) at batch 8 and k = 1511, on 8 copies, beside its dense block.
+    1536) at batch 8 and k = 1511, on 8 copies, beside its dense block;
+  * batch-shared selection (one top-k per call over the call's distinct
+    routed experts, k = the per-token budget times distinct experts / top)
+    at batch 4 and on the Qwen3-235B-A22B layer at batch 8.
 
 Prints ONE JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
@@ -164,7 +167,8 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None,
     With spread (a dict), also the median and 90th percentile of the per-pass
     averages (an event after every replay).  fn: "decode", "dense", or a
     layer step on copies built with router weights, on the residual stream
-    x = Y[i]: "route" (routing of RMSNorm(x) alone), "layer" (that routing,
+    x = Y[i]: "shared" (the batch-shared decode, k a list with one budget
+    per copy), "route" (routing of RMSNorm(x) alone), "layer" (that routing,
     then the decode of the normed token, its output added to x in the
     decode's last kernel), "layer_dense" (the same with the dense block); IDS
     and W are then the routing's outputs."""
@@ -178,6 +182,8 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None,
         for i, r in enumerate(readers):
             if fn == "decode":
                 r.decode(X[i], IDS[i], W[i], k, out=Y[i])
+            elif fn == "shared":
+                r.decode_shared(X[i], IDS[i], W[i], k[i], out=Y[i])  # k: one budget per copy
             elif fn == "dense":
                 r.dense(X[i], IDS[i], W[i], out=Y[i])
             else:
@@ -218,6 +224,24 @@ def graph_time(torch, readers, X, IDS, W, k, steps, warmup, fn="decode", Y=None,
         spread["passes"] = reps
     del g
     return 1000.0 * total_ms / (reps * L), reps * L, wreps * L
+
+
+def shared_leg(torch, cfg, readers, X, IDS, W, ids_host, k_token, shape, args):
+    """The batch-shared decode on every copy's batch, each at k = k_token
+    times (distinct experts of the batch) / top: microseconds per token, the
+    library's count of the bytes one call reads (averaged over the first
+    eight copies) and its rate."""
+    from calibration_free_channel_amd import read_bytes_shared
+    B = X.shape[1]
+    ks = [int(round(k_token * np.unique(ids_host[i]).size / shape.top)) for i in range(len(readers))]
+    us, _, _ = graph_time(torch, readers, X, IDS, W, ks, min(args.steps, 400), args.warmup, fn="shared")
+    nb = []
+    for i in range(min(8, len(readers))):
+        dbg = readers[i].decode_debug(X[i], IDS[i], W[i], 0)  # the screened coordinates
+        nb.append(read_bytes_shared(cfg, ids_host[i], dbg["sel"].cpu().numpy(), ks[i])["total"])
+    bytes_call = float(np.mean(nb))
+    return {"k_mean": round(float(np.mean(ks)), 1), "us_per_token": round(us / B, 3),
+            "bytes_per_call": int(bytes_call), "GBps": round(bytes_call / us / 1e3, 1)}
 
 
 def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
@@ -559,6 +583,11 @@ def main():
             us4, _, _ = graph_time(torch, readers, X4, I4, W4, 0, min(args.steps, 400), args.warmup,
                                    fn="dense")
             batch4["dense"] = round(us4 / 4, 3)
+        # batch-shared selection: one top-k per call over the call's distinct
+        # experts, at the per-token budget's share of the union
+        for k in [k_main] + ([k_low] if k_low else []):
+            sh = shared_leg(torch, cfg, readers, X4, I4, W4, I4h.reshape(L, 4, s.top), k, s, args)
+            batch4[f"shared_k={k}"] = sh
         log("batch 4, us/token: " + ", ".join(f"{n}={v}" for n, v in batch4.items()))
 
     # 28.7% and up: the whole sketch with the expected-error ranking, on copies
@@ -615,6 +644,7 @@ def main():
         ud5 = None
         if not args.no_dense:
             ud5, _, _ = graph_time(torch, r5, X5, I5, W5, 0, min(args.steps, 200), args.warmup, fn="dense")
+        sh5 = shared_leg(torch, cfg5, r5, X5, I5, W5, i5.reshape(L5, 8, s5.top), k5, s5, args)
         rb5 = read_bytes(cfg5, k5)
         dbg = {n: v.cpu().numpy() for n, v in r5[0].decode_debug(X5[0], I5[0], W5[0], k5).items()}
         ub5 = read_bytes_batch(cfg5, I5[0].cpu().numpy(), dbg["sel"], dbg["kept"], k5)["total"]
@@ -626,7 +656,8 @@ def main():
               # distinct bytes)
               "sum_of_token_bytes_GBps": round(8 * rb5["total"] / us5 / 1e3, 1),
               "dense_us_per_token": None if ud5 is None else round(ud5 / 8, 3),
-              "speedup_vs_dense": None if ud5 is None else round(ud5 / us5, 3)}
+              "speedup_vs_dense": None if ud5 is None else round(ud5 / us5, 3),
+              "shared": sh5}
         log(f"qwen3-235b-a22b batch 8, k={k5}: {us5 / 8:.2f} us/token"
             + ("" if ud5 is None else f", dense {ud5 / 8:.2f} us/token"))
         for r in r5:

@@ -37,10 +37,12 @@ SIGNATURES = {
     "cfr_read_bytes": (c_int32, [POINTER(CfrConfig), c_int32, POINTER(CfrReadStats)]),
     "cfr_read_bytes_batch": (c_int32, [POINTER(CfrConfig), c_int32, c_int32, _P, _P, _P,
                                        POINTER(CfrReadStats)]),
+    "cfr_read_bytes_shared": (c_int32, [POINTER(CfrConfig), c_int32, _P, _P, c_int32, POINTER(CfrReadStats)]),
     "cfr_build_reader": (c_int32, [POINTER(CfrConfig), _P, _P, _P, _P, POINTER(c_void_p)]),
     "cfr_reader_decode": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P]),
     "cfr_reader_decode_residual": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),
     "cfr_reader_decode_noalloc": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P]),
+    "cfr_reader_decode_shared": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P, _P, _P]),
     "cfr_reader_decode_debug": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P, _P, _P,
                                           _P, _P, _P]),
     "cfr_reader_decode_profile": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libcfr.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HOST_SRCS = ["common.cpp", "pack_host.cpp"]
-HIP_SRCS = ["api.hip", "decode_kernels.hip", "dense_kernel.hip", "build_device.hip", "route_kernel.hip"]
+HIP_SRCS = ["api.hip", "decode_kernels.hip", "dense_kernel.hip", "shared_kernels.hip", "build_device.hip", "route_kernel.hip"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-pthread", "-Wall"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

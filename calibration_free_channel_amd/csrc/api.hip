@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <memory>
 #include <mutex>
 #include <new>
@@ -46,7 +47,7 @@ struct WorkspaceLayout {
       o += rnd(bytes);
       return at;
     };
-    decode = take(carve_decode_workspace(r, c.max_batch, true, nullptr, nullptr));
+    decode = take(carve_decode_workspace(r, c.max_batch, true, nullptr, nullptr, true));
     rlog = take(sizeof(float) * c.max_batch * c.n_experts);
     rarr = take(sizeof(int32_t) * c.max_batch);
     status = take(sizeof(int32_t));
@@ -59,7 +60,7 @@ size_t workspace_bytes(const cfr_reader& r) { return WorkspaceLayout(r).total; }
 void carve_workspace(cfr_reader& r) {
   const WorkspaceLayout l(r);
   char* p = static_cast<char*>(r.ws);
-  carve_decode_workspace(r, r.cfg.max_batch, true, p + l.decode, &r.wk);
+  carve_decode_workspace(r, r.cfg.max_batch, true, p + l.decode, &r.wk, true);
   r.rlog = reinterpret_cast<float*>(p + l.rlog);
   r.rarr = reinterpret_cast<int32_t*>(p + l.rarr);
   r.status = reinterpret_cast<int32_t*>(p + l.status);
@@ -286,6 +287,24 @@ int cfr_reader_decode_residual(cfr_reader* r, const float* x, const int32_t* ids
   DeviceGuard guard(r->cfg.device);
   return launch_decode(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr, nullptr, -1,
                        resid);
+}
+
+int cfr_reader_decode_shared(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,
+                             int32_t batch, int32_t k, float* y, float* bscore, int32_t* kept,
+                             int32_t* experts, void* stream) {
+  clear_error();
+  if (!r) return fail(CFR_EINVAL, "reader is NULL");
+  if (!x || !ids || !gw || !y) return fail(CFR_EINVAL, "x, expert_ids, gate_w and y must be non-NULL");
+  if (batch < 1 || batch > r->cfg.max_batch) return fail(CFR_EINVAL, "batch must be in 1..max_batch");
+  if (batch > kMaxSharedBatch)
+    return fail(CFR_EUNSUPPORTED, "the batch-shared decode takes at most 8 tokens per call");
+  if (r->cfg.ranking != CFR_RANK_SCORE)
+    return fail(CFR_EUNSUPPORTED, "the batch-shared decode ranks by the output-unit score only");
+  const int64_t nmax = (int64_t)std::min(r->cfg.n_experts, batch * r->cfg.top) * r->cfg.inter;
+  if (k < 0 || k > nmax) return fail(CFR_EINVAL, "k must be in 0..min(n_experts, batch*top)*inter");
+  DeviceGuard guard(r->cfg.device);
+  return launch_decode_shared(r, x, ids, gw, batch, k, y, static_cast<hipStream_t>(stream), nullptr, bscore,
+                              kept, experts);
 }
 
 int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* ids, const float* gw,

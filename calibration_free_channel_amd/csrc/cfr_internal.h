@@ -17,6 +17,7 @@ constexpr int kMaxTop = 16;
 constexpr int kMaxRank = 64;
 constexpr int kMaxBatch = 64;
 constexpr int kMaxHidden = 4096;
+constexpr int kMaxSharedBatch = 8;  // tokens of one batch-shared decode
 
 // Error reporting (thread-local message).
 int fail(int code, const std::string& msg);
@@ -57,6 +58,14 @@ struct Workspace {
   float* vhat = nullptr;    // [B][ncand] (debug copy only)
   float* score = nullptr;   // [B][ncand] (debug copy only)
   int32_t* kept = nullptr;  // [B][ncand]  kept candidates by rank (debug copy only)
+  // batch-shared selection (the reader's own workspace only)
+  float* bscore = nullptr;  // [B top I] batch scores of the union candidates
+  int32_t* meta = nullptr;  // [1 + B top] union size, then the union's experts ascending
+  int32_t* klist = nullptr; // [B top I] kept union candidates, ascending
+  uint8_t* kflag = nullptr; // [B top I] kept flag per union candidate
+  float* coef = nullptr;    // [B top I][B] w a_j of each kept channel per token
+  int32_t* krow = nullptr;  // [B top I] row e I + j of each kept union candidate
+  int32_t* ghist = nullptr; // [4096] histogram of the batch scores' keys; zero between calls
 };
 
 }  // namespace cfr

@@ -147,6 +147,44 @@ int cfr_read_bytes_batch(const cfr_config* c, int32_t batch, int32_t k, const in
   return CFR_OK;
 }
 
+int cfr_read_bytes_shared(const cfr_config* c, int32_t batch, const int32_t* ids, const uint8_t* sel,
+                          int32_t n_kept, cfr_read_stats* out) {
+  int rc = validate_config(c);
+  if (rc) return rc;
+  if (!out || !ids || !sel) return fail(CFR_EINVAL, "null argument");
+  const int64_t E = c->n_experts, I = c->inter, H = c->hidden, top = c->top, nblk = H / kBlock;
+  const int64_t ns = c->n_screen;
+  if (batch < 1) return fail(CFR_EINVAL, "batch must be at least 1");
+  std::vector<uint8_t> unit_seen(E * nblk * kBlock, 0), block_seen(E * nblk, 0), expert_seen(E, 0);
+  int64_t n_unit = 0, n_block = 0, n_expert = 0;
+  for (int64_t t = 0; t < batch; ++t)
+    for (int64_t s = 0; s < top; ++s) {
+      const int32_t e = ids[t * top + s];
+      if (e < 0 || e >= E) return fail(CFR_EINVAL, "expert id out of range");
+      if (!expert_seen[e]) expert_seen[e] = 1, ++n_expert;
+      for (int64_t b = 0; b < nblk; ++b) {
+        if (!block_seen[e * nblk + b]) block_seen[e * nblk + b] = 1, ++n_block;
+        const uint8_t* sb = sel + (t * nblk + b) * ns;
+        for (int64_t q = 0; q < ns; ++q) {
+          if (sb[q] >= kBlock) return fail(CFR_EINVAL, "screened coordinate out of range");
+          uint8_t& u = unit_seen[(e * nblk + b) * kBlock + sb[q]];
+          if (!u) u = 1, ++n_unit;
+        }
+      }
+    }
+  if (n_kept < 0 || n_kept > n_expert * I) return fail(CFR_EINVAL, "n_kept must be in 0..u*inter");
+  out->codes = n_unit * sect(unit_bytes(c->inter));
+  out->scales = n_block * sect(2 * I * 2);
+  out->norms = n_expert * sect(I * 4);
+  out->rho = 0;
+  out->exact = (int64_t)n_kept * sect(3 * H * 2);
+  out->b = (n_expert * I - n_kept) * sect((int64_t)c->rank * 2);
+  out->u = sect(H * (int64_t)c->rank * 2);
+  out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
+  out->dense = n_expert * 3 * I * H * 2;
+  return CFR_OK;
+}
+
 int cfr_pack_host(const cfr_config* c, const uint16_t* gate, const uint16_t* up,
                   const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
                   float* norms) {

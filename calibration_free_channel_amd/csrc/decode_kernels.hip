@@ -54,27 +54,6 @@ namespace cfr {
 
 namespace {
 
-// Inclusive prefix sum over the NT threads of a workgroup.  sh: NT/64 ints
-// that nobody else uses between the two barriers inside.
-template <int NT>
-__device__ __forceinline__ int block_scan(int v, int* sh) {
-  static_assert(NT % 256 == 0 && NT <= 1024, "whole groups of four waves");
-  constexpr int NQ = NT / 256;  // int4 groups of wave totals
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = wave_scan(v);
-  if (lane == 63) sh[w] = v;
-  lds_barrier();
-  int add = 0;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int4 p = reinterpret_cast<const int4*>(sh)[q];
-    add += (4 * q < w ? p.x : 0) + (4 * q + 1 < w ? p.y : 0) + (4 * q + 2 < w ? p.z : 0) +
-           (4 * q + 3 < w ? p.w : 0);
-  }
-  lds_barrier();
-  return v + add;
-}
-
 // Buffer resource over `bytes` bytes at p (gfx9 layout): a raw buffer load at
 // an offset past the end returns zeros without a memory access.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
@@ -454,19 +433,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Output-unit score of one candidate from its fixed-point screen sums (the
-// up sum carries ||d_j||) and routing weight w: sets g_hat, v_hat' = ||d_j||
-// v_hat, p' = silu(g_hat) v_hat' = ||d_j|| p and s = w |p'| = w ||d_j|| |p|,
-// and returns the order-preserving key of s.
-__device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned long long v, float w,
-                                              float& gh, float& vh, float& p, float& sc) {
-  gh = from_fix(g) * kInvSqrt128f;
-  vh = from_fix(v) * kInvSqrt128f;
-  p = silu(gh) * vh;
-  sc = w * fabsf(p);
-  return order_key(sc);
 }
 
 // The expected-error ranking ([zh §方法步骤详情] decode step (2), budgets from
@@ -1350,7 +1316,8 @@ size_t decode_sums_bytes(const cfr_reader& r, int batch) {
   return (sizeof(unsigned long long) * batch * 2 * r.ncp + 255) / 256 * 256;
 }
 
-size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w) {
+size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w,
+                              bool shared) {
   const cfr_config& c = r.cfg;
   const size_t B = batch, H = c.hidden, nc = r.ncand, R = c.rank > 0 ? c.rank : 1;
   size_t o = 0;
@@ -1375,6 +1342,16 @@ size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* 
     v.vhat = reinterpret_cast<float*>(take(sizeof(float) * B * nc));
     v.score = reinterpret_cast<float*>(take(sizeof(float) * B * nc));
     v.kept = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * nc));
+  }
+  if (shared) {
+    const size_t nb = std::min<size_t>(B, kMaxSharedBatch) * nc;  // union candidates, at most
+    v.bscore = reinterpret_cast<float*>(take(sizeof(float) * nb));
+    v.meta = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (1 + std::min<size_t>(B, kMaxSharedBatch) * c.top)));
+    v.klist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nb));
+    v.kflag = reinterpret_cast<uint8_t*>(take(nb));
+    v.coef = reinterpret_cast<float*>(take(sizeof(float) * nb * std::min<size_t>(B, kMaxSharedBatch)));
+    v.krow = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nb));
+    v.ghist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4096));
   }
   if (w) *w = v;
   return o;
@@ -1556,6 +1533,34 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
       if (e != hipSuccess) return hip_fail(e, "debug copy kept");
     }
   }
+  return CFR_OK;
+}
+
+int launch_decode_shared(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
+                         int k, float* y, hipStream_t st, const float* resid, float* bscore_out,
+                         int32_t* kept_out, int32_t* meta_out) {
+  const cfr_config& c = r->cfg;
+  const Workspace& W = r->wk;
+  const Plan p = make_plan(c, batch, k);
+  hipError_t e;
+  ScreenArgs A{x, ids, gw, r->sigma, r->codes, r->scales, r->norms, r->rho, W.acc, nullptr, W.xrot,
+               W.sel, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncp, r->nblk,
+               c.n_screen, r->lp, r->unit, p.nd, p.ng, p.items1, p.per_xcd1, 0};
+  if ((e = launch_screen(A, p, st)) != hipSuccess) return hip_fail(e, "screen launch");
+  const SharedPlan sp = make_shared_plan(c, batch, k);
+  if ((e = launch_shared_select(*r, x, ids, gw, batch, k, W, sp, st)) != hipSuccess)
+    return hip_fail(e, "shared selection launch");
+  ReduceArgs C{W.ypart, W.zpart, r->u, y, W.acc, c.hidden, sp.G, sp.Z, c.rank, r->ncp,
+               c.hidden / kReduceSlice, 1, resid};
+  if ((e = launch_reduce(C, batch, st)) != hipSuccess) return hip_fail(e, "reduce launch");
+  const size_t nb = (size_t)batch * r->ncand;
+  auto cp = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+    return dst ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
+  };
+  if ((e = cp(bscore_out, W.bscore, sizeof(float) * nb)) != hipSuccess ||
+      (e = cp(kept_out, W.klist, sizeof(int32_t) * k)) != hipSuccess ||
+      (e = cp(meta_out, W.meta, sizeof(int32_t) * (1 + (size_t)batch * c.top))) != hipSuccess)
+    return hip_fail(e, "debug copy");
   return CFR_OK;
 }
 

@@ -118,5 +118,39 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Inclusive prefix sum over the NT threads of a workgroup.  sh: NT/64 ints
+// that nobody else uses between the two barriers inside.
+template <int NT>
+__device__ __forceinline__ int block_scan(int v, int* sh) {
+  static_assert(NT % 256 == 0 && NT <= 1024, "whole groups of four waves");
+  constexpr int NQ = NT / 256;  // int4 groups of wave totals
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_scan(v);
+  if (lane == 63) sh[w] = v;
+  lds_barrier();
+  int add = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int4 p = reinterpret_cast<const int4*>(sh)[q];
+    add += (4 * q < w ? p.x : 0) + (4 * q + 1 < w ? p.y : 0) + (4 * q + 2 < w ? p.z : 0) +
+           (4 * q + 3 < w ? p.w : 0);
+  }
+  lds_barrier();
+  return v + add;
+}
+
+// Output-unit score of one candidate from its fixed-point screen sums (the
+// up sum carries ||d_j||) and routing weight w: sets g_hat, v_hat' = ||d_j||
+// v_hat, p' = silu(g_hat) v_hat' = ||d_j|| p and s = w |p'| = w ||d_j|| |p|,
+// and returns the order-preserving key of s.
+__device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned long long v, float w,
+                                              float& gh, float& vh, float& p, float& sc) {
+  gh = from_fix(g) * kInvSqrt128f;
+  vh = from_fix(v) * kInvSqrt128f;
+  p = silu(gh) * vh;
+  sc = w * fabsf(p);
+  return order_key(sc);
+}
+
 }  // namespace
 }  // namespace cfr

@@ -122,7 +122,9 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 // The decode's buffers for `batch` tokens carved from base (any size when
 // base is null); returns the bytes they take.  debug: also the copies the
 // debug entry point reads.
-size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w);
+// shared: also the buffers of the batch-shared decode.
+size_t carve_decode_workspace(const cfr_reader& r, int batch, bool debug, char* base, Workspace* w,
+                              bool shared = false);
 // Bytes at the start of that carve that must be zero when a decode starts
 // (the screen sums; a decode leaves them zero).
 size_t decode_sums_bytes(const cfr_reader& r, int batch);
@@ -164,6 +166,24 @@ DensePlan make_dense_plan(const cfr_config& c, int batch);
 hipError_t launch_dense_block(const float* x, const int32_t* ids, const float* gw, const uint16_t* w3,
                               float* ypart, int32_t* status, const cfr_config& c, int batch,
                               const DensePlan& p, hipStream_t st);
+
+// Batch-shared selection (shared_kernels.hip): after the screen kernel, the
+// batch scores (nscore workgroups), the batch top-k (one workgroup), the
+// kept channels' coefficients (Ga workgroups) with batch * Z recovery
+// workgroups writing zpart [batch][Z][rank], then G ranges of qc kept
+// channels times nhs hidden slices writing ypart [batch][G][H], for the
+// reduce kernel.
+struct SharedPlan {
+  int nscore = 1, Ga = 1, Z = 0, qc = 64, G = 1, nhs = 1, nch = 1;
+};
+SharedPlan make_shared_plan(const cfr_config& c, int batch, int k);
+hipError_t launch_shared_select(const cfr_reader& r, const float* x, const int32_t* ids, const float* gw,
+                                int batch, int k, const Workspace& W, const SharedPlan& p, hipStream_t st);
+// Batch-shared decode (screen, shared selection, reduce); debug copies of the
+// batch scores, kept list and union when the pointers are non-null.
+int launch_decode_shared(cfr_reader* r, const float* x, const int32_t* ids, const float* gw, int batch,
+                         int k, float* y, hipStream_t st, const float* resid, float* bscore_out,
+                         int32_t* kept_out, int32_t* meta_out);
 
 // Load step (3) on the device: U (fp16 [H][rank]) and b (fp16 [E][I][rank])
 // from the resident down rows.  Synchronous.

@@ -68,6 +68,21 @@ def read_bytes_batch(cfg: Config, expert_ids, sel, kept, k: int) -> dict:
     return {f: getattr(s, f) for f, _ in CfrReadStats._fields_}
 
 
+def read_bytes_shared(cfg: Config, expert_ids, sel, n_kept: int) -> dict:
+    """Distinct 32-byte sectors one batch-shared decode call reads, from the
+    call's expert ids [B][top], screened coordinates [B][nblk][n_screen]
+    (host arrays) and the number of kept union candidates."""
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    sel = np.ascontiguousarray(sel, dtype=np.uint8)
+    B = ids.shape[0]
+    if ids.shape != (B, cfg.top) or sel.shape != (B, cfg.hidden // 128, cfg.n_screen):
+        raise ValueError("expert_ids [B][top] and sel [B][nblk][n_screen] expected")
+    s = CfrReadStats()
+    check(load().cfr_read_bytes_shared(ctypes.byref(cfg.c()), B, _ptr(ids), _ptr(sel), int(n_kept),
+                                       ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in CfrReadStats._fields_}
+
+
 def _u16(a, shape, name):
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16 or a.shape != tuple(shape):
@@ -197,6 +212,33 @@ class Reader:
         py = _dev_tensor(out, torch.float32, (B, self.cfg.hidden), "out", self.cfg.device)
         check(load().cfr_reader_decode_noalloc(self._h, px, pi, pw, B, int(k), py, self._stream(stream)))
         return out
+
+    def decode_shared(self, x, expert_ids, gate_w, k: int, out=None, stream=None, debug=False):
+        """cfr_reader_decode_shared: one top-k of k channels for the whole
+        batch over its distinct routed experts (at most 8 tokens).  Returns y
+        [batch, hidden]; with debug=True a dict with y, the batch scores
+        "bscore" [u * inter], the kept union candidates "kept" and the union's
+        experts "experts" (ascending), u = their number."""
+        torch = _torch()
+        B, px, pi, pw = self._args(x, expert_ids, gate_w)
+        c, dev = self.cfg, x.device
+        if out is None:
+            out = torch.empty((B, c.hidden), dtype=torch.float32, device=dev)
+        py = _dev_tensor(out, torch.float32, (B, c.hidden), "out", c.device)
+        if not debug:
+            check(load().cfr_reader_decode_shared(self._h, px, pi, pw, B, int(k), py, None, None, None,
+                                                  self._stream(stream)))
+            return out
+        bs = torch.empty((B * c.top * c.inter,), dtype=torch.float32, device=dev)
+        kp = torch.empty((max(int(k), 1),), dtype=torch.int32, device=dev)
+        ex = torch.empty((1 + B * c.top,), dtype=torch.int32, device=dev)
+        check(load().cfr_reader_decode_shared(self._h, px, pi, pw, B, int(k), py,
+                                              ctypes.c_void_p(bs.data_ptr()), ctypes.c_void_p(kp.data_ptr()),
+                                              ctypes.c_void_p(ex.data_ptr()), self._stream(stream)))
+        torch.cuda.synchronize(dev)
+        u = int(ex[0].item())
+        return {"y": out, "bscore": bs[:u * c.inter], "kept": kp[:min(int(k), u * c.inter)],
+                "experts": ex[1:1 + u]}
 
     def decode_debug(self, x, expert_ids, gate_w, k: int, stream=None) -> dict:
         torch = _torch()

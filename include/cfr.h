@@ -131,6 +131,18 @@ int cfr_read_bytes_batch(const cfr_config* cfg, int32_t batch, int32_t k, const 
                          const uint8_t* sel, const int32_t* kept, cfr_read_stats* out);
 
 /*
+ * Bytes a batch-shared decode (cfr_reader_decode_shared) reads, counted as
+ * cfr_read_bytes_batch does: the sketch units, scales and norms of the
+ * batch's distinct routed experts at the coordinates any token screened,
+ * the exact rows of the n_kept kept union candidates once, the b rows of
+ * the other union candidates once, and U once.  ids int32 [batch][top] and
+ * sel uint8 [batch][nblk][n_screen] (host memory, as for
+ * cfr_read_bytes_batch); n_kept in 0 .. u * inter (u = distinct experts).
+ */
+int cfr_read_bytes_shared(const cfr_config* cfg, int32_t batch, const int32_t* expert_ids,
+                          const uint8_t* sel, int32_t n_kept, cfr_read_stats* out);
+
+/*
  * Load-time work for one layer ([zh §方法步骤详情] load steps (1)-(4);
  * [ko §어떻게 쓰나]):
  *   (1) rotate every gate/up row per 128-block and store TWN ternary codes,
@@ -216,6 +228,35 @@ int cfr_reader_decode_debug(cfr_reader* r, const float* x, const int32_t* expert
                             const float* gate_w, int32_t batch, int32_t k, float* y,
                             float* xrot, uint8_t* sel, float* ghat, float* vhat,
                             float* score, int32_t* kept, void* stream);
+
+/*
+ * Batch-shared channel selection: one exact top-k for the whole batch
+ * (the pages leave selecting channels jointly for the batch as the route to
+ * larger-batch gains, [zh §未来方向] direction (1); [ko §전제와 한계]).
+ * Candidates are the channels of the batch's distinct routed experts, union
+ * candidate u * inter + j for the u-th distinct expert in ascending id
+ * order; a candidate's batch score is the sum, over the (token, slot) pairs
+ * routed to its expert (token-major, slot order), of the per-token score
+ * w ||d_j|| |silu(g_hat_j) v_hat_j|; the k largest are kept (ties to the
+ * lower union candidate).  Each kept channel's native rows are read once and
+ * give the exact a_j of every token routed to its expert; each token
+ * recovers its own skipped channels with its own p_j (rank-32 term).
+ *   x, expert_ids, gate_w, y   as cfr_reader_decode; batch <= max_batch and
+ *                              at most 8 (CFR_EUNSUPPORTED above)
+ *   k        0 .. min(n_experts, batch * top) * inter; above the batch's
+ *            union size u * inter every union candidate is kept
+ *   bscore   fp32 [batch * top * inter] device or NULL: the batch scores of
+ *            the union candidates (the first u * inter entries)
+ *   kept     int32 [k] device or NULL: the kept union candidates, ascending
+ *            (the first min(k, u * inter) entries)
+ *   experts  int32 [1 + batch * top] device or NULL: u, then the union's
+ *            experts ascending
+ * Readers built for the expected-error ranking are refused
+ * (CFR_EUNSUPPORTED).  Asynchronous on `stream`; allocates nothing.
+ */
+int cfr_reader_decode_shared(cfr_reader* r, const float* x, const int32_t* expert_ids,
+                             const float* gate_w, int32_t batch, int32_t k, float* y,
+                             float* bscore, int32_t* kept, int32_t* experts, void* stream);
 
 /*
  * The experts a token activates and their weights, from the router weights

@@ -38,11 +38,13 @@ from .numerics import bf16_to_f64
 from .topk import topk_desc
 
 
-def decode_shared(oracle, X, IDS, W, k):
+def decode_shared(oracle, X, IDS, W, k, kept=None):
     """Batch-shared decode with an OracleReader.  X [B][H], IDS [B][top],
     W [B][top], k kept union candidates.  Returns a dict: "experts" (the
     union, ascending), "bscore" [u][I], "kept" (union candidates, ascending),
-    and per token "y", "y_exact", "y_rec", "p"."""
+    and per token "y", "y_exact", "y_rec", "p".  kept, when given, replaces
+    the top-k (for comparisons where neighbouring batch scores tie within
+    rounding)."""
     X = np.asarray(X, dtype=np.float32)
     IDS = np.asarray(IDS, dtype=np.int64)
     W = np.asarray(W, dtype=np.float32).astype(np.float64)
@@ -63,7 +65,10 @@ def decode_shared(oracle, X, IDS, W, k):
             e = int(IDS[t, s])
             dn = oracle.norms[oracle.ix([e])[0]].astype(np.float64)
             bscore[uix[e]] = bscore[uix[e]] + W[t, s] * dn * np.abs(P[t][s])
-    kept = topk_desc(bscore.reshape(-1), min(int(k), bscore.size))
+    if kept is None:
+        kept = topk_desc(bscore.reshape(-1), min(int(k), bscore.size))
+    else:
+        kept = np.sort(np.asarray(kept, dtype=np.int64))
     kmask = np.zeros(bscore.size, dtype=bool)
     kmask[kept] = True
     kmask = kmask.reshape(experts.size, I)

@@ -84,3 +84,35 @@ def test_rejects_out_of_range():
     bad[0] = 6144
     with pytest.raises(CfrError):
         read_bytes_batch(CFG, ids[None], sel[None], bad[None], 3)
+
+
+def test_shared_accounting_counts_the_union_once():
+    """The batch-shared count: sketch, scales and norms of the distinct
+    experts at the coordinates any token screened, n_kept exact rows and the
+    rest of the union's b rows, each once, and U once."""
+    from calibration_free_channel_amd import read_bytes_shared
+    B, nblk = 3, 16
+    ids = np.array([[0, 1, 2, 3, 4, 5, 6, 7], [4, 5, 6, 7, 8, 9, 10, 11], [0, 1, 2, 3, 8, 9, 10, 11]],
+                   dtype=np.int32)
+    u = 12
+    sel = np.tile(np.arange(80, dtype=np.uint8), (B, nblk, 1))  # every token screens the same 80
+    for n_kept in (0, 5, 756, u * 768):
+        st = read_bytes_shared(CFG, ids, sel, n_kept)
+        assert st["codes"] == u * nblk * 80 * 320
+        assert st["scales"] == u * nblk * 2 * 768 * 2
+        assert st["norms"] == u * 768 * 4
+        assert st["exact"] == n_kept * 3 * 2048 * 2
+        assert st["b"] == (u * 768 - n_kept) * 32 * 2
+        assert st["u"] == 2048 * 32 * 2
+        assert st["dense"] == u * 3 * 768 * 2048 * 2
+    # one token: the per-token count at k = n_kept
+    one = read_bytes_shared(CFG, ids[:1], sel[:1], 756)
+    assert one == read_bytes(CFG, 756)
+    # a second token screening other coordinates adds their units only
+    sel2 = sel.copy()
+    sel2[1] = np.arange(48, 128, dtype=np.uint8)
+    st = read_bytes_shared(CFG, ids[:2], sel2[:2], 0)
+    # experts 0-3 and 8-11: one token each; 4-7: both, the union of 0..79 and 48..127
+    assert st["codes"] == (4 * 80 + 4 * 128 + 4 * 80) * nblk * 320
+    with pytest.raises(CfrError):
+        read_bytes_shared(CFG, ids, sel, u * 768 + 1)
