@@ -38,7 +38,11 @@ Method:
     1536) at batch 8 and k = 1511, on 8 copies, beside its dense block;
   * batch-shared selection (one top-k per call over the call's distinct
     routed experts, k = the per-token budget times distinct experts / top)
-    at batch 4 and on the Qwen3-235B-A22B layer at batch 8.
+    at batch 4 and on the Qwen3-235B-A22B layer at batch 8;
+  * the reader over a synthetic 4-bit checkpoint of the batch-1 layer
+    (`int4_exact_rows`: exact rows in 4 bits with fp16 group scales, sketch
+    unchanged) at k = 756 and at the k reading 18.9% of the BF16 routed
+    bytes, beside the 4-bit dense block.
 
 Prints ONE JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
@@ -89,6 +93,8 @@ def parse():
     ap.add_argument("--stack", action="store_true",
                     help="time only the 48-layer batch-1 decode step (route, decode, residual "
                          "per layer, captured as one HIP graph); prints its own JSON line")
+    ap.add_argument("--no-q4", action="store_true",
+                    help="skip the reader over the layer's 4-bit checkpoint")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 48-layer batch-1 decode step in the main line")
     return ap.parse_args()
@@ -663,6 +669,44 @@ def main():
         for r in r5:
             r.close()
 
+    # a 4-bit checkpoint of the same layer (exact rows in 4 bits, sketch
+    # unchanged): the reader at k = 756 and at the k whose counted reads are
+    # 18.9% of the BF16 routed bytes, beside the 4-bit dense block
+    q4 = None
+    if not args.main_budget_only and not args.no_q4:
+        for r in readers[1:]:
+            r.close()
+        readers = readers[:1]
+        torch.cuda.empty_cache()
+        from synth import make_layer_q4
+        t = time.time()
+        lq = make_layer_q4(wl)
+        cfg_q = Config(hidden=s.hidden, n_experts=s.n_experts, inter=s.inter, top=s.top, rank=s.rank,
+                       n_screen=s.n_screen, max_batch=4, rot_seed=wl.rot_seed, exact_bits=4)
+        bq = Reader.build_q4(cfg_q, lq["rows"])
+        del lq
+        rq = [bq] + [bq.clone() for _ in range(L - 1)]
+        torch.cuda.synchronize()
+        log(f"4-bit layer built and copied in {time.time() - t:.1f}s")
+        bf16_dense = read_bytes(cfg, 0)["dense"]
+        k189 = min(range(s.top * s.inter + 1),
+                   key=lambda kk: abs(read_bytes(cfg_q, kk)["total"] / bf16_dense - 0.189))
+        q4 = {}
+        for kq in (k_main, k189):
+            us_q, _, _ = graph_time(torch, rq, X, IDS, W, kq, min(args.steps, 400), args.warmup)
+            rbq = read_bytes(cfg_q, kq)
+            q4[f"k={kq}"] = {"us_per_token": round(us_q, 3), "read_bytes_per_token": rbq["total"],
+                             "read_pct_of_bf16_dense": round(100.0 * rbq["total"] / bf16_dense, 2),
+                             "achieved_GBps": round(rbq["total"] / us_q / 1e3, 1)}
+        udq, _, _ = graph_time(torch, rq, X, IDS, W, 0, min(args.steps, 400), args.warmup, fn="dense")
+        q4["dense_q4_us_per_token"] = round(udq, 3)
+        q4["dense_q4_GBps"] = round(read_bytes(cfg_q, 0)["dense"] / udq / 1e3, 1)
+        for kk in (k_main, k189):
+            q4[f"k={kk}"]["speedup_vs_dense_q4"] = round(udq / q4[f"k={kk}"]["us_per_token"], 3)
+        log("4-bit rows: " + json.dumps(q4))
+        for r in rq:
+            r.close()
+
     # the 48-layer stack (independent weights per layer) as one batch-1 step
     stack = None
     if not args.main_budget_only and not args.no_stack:
@@ -749,6 +793,7 @@ def main():
                                    "with the dense block; route: the routing alone")
                               if layer_step else None),
         "qwen3_235b_a22b_batch8": c5,
+        "int4_exact_rows": q4,
         "stack_48l": None if stack is None else {
             kk: stack[kk] for kk in ("value", "unit", "steps", "us_per_layer", "per_step_median_us",
                                      "per_step_p90_us", "achieved_GBps", "dense_bf16_us_per_step",

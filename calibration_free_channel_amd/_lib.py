@@ -14,7 +14,8 @@ CFR_OK, CFR_EINVAL, CFR_ENOMEM, CFR_EHIP, CFR_EUNSUPPORTED, CFR_ESOLVER = 0, -1,
 class CfrConfig(ctypes.Structure):
     _fields_ = [("hidden", c_int32), ("n_experts", c_int32), ("inter", c_int32), ("top", c_int32),
                 ("rank", c_int32), ("n_screen", c_int32), ("max_batch", c_int32),
-                ("device", c_int32), ("rot_seed", c_uint64), ("ranking", c_int32)]
+                ("device", c_int32), ("rot_seed", c_uint64), ("ranking", c_int32),
+                ("exact_bits", c_int32)]
 
 
 class CfrSizes(ctypes.Structure):
@@ -39,6 +40,7 @@ SIGNATURES = {
                                        POINTER(CfrReadStats)]),
     "cfr_read_bytes_shared": (c_int32, [POINTER(CfrConfig), c_int32, _P, _P, c_int32, POINTER(CfrReadStats)]),
     "cfr_build_reader": (c_int32, [POINTER(CfrConfig), _P, _P, _P, _P, POINTER(c_void_p)]),
+    "cfr_build_reader_q4": (c_int32, [POINTER(CfrConfig), _P, _P, POINTER(c_void_p)]),
     "cfr_reader_decode": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P]),
     "cfr_reader_decode_residual": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P, _P]),
     "cfr_reader_decode_noalloc": (c_int32, [_P, _P, _P, _P, c_int32, c_int32, _P, _P]),

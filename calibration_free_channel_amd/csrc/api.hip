@@ -94,7 +94,7 @@ ResidentSizes resident_sizes(const cfr_reader& r) {
   const cfr_config& c = r.cfg;
   const size_t E = c.n_experts, I = c.inter, H = c.hidden;
   ResidentSizes s;
-  s.w3 = E * I * 3 * H * 2;
+  s.w3 = E * I * 3 * (size_t)row_bytes((int)H, q4_rows(c));
   s.codes = E * r.nblk * kBlock * r.unit;
   s.scales = E * r.nblk * 2 * I * 2;
   s.norms = E * I * 4;
@@ -223,6 +223,7 @@ int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t
   *out = nullptr;
   int rc = validate_config(cfg);
   if (rc) return rc;
+  if (q4_rows(*cfg)) return fail(CFR_EINVAL, "exact_bits 4: build with cfr_build_reader_q4");
   if (!gate || !up || !down) return fail(CFR_EINVAL, "gate, up and down must be non-NULL");
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev)
@@ -239,7 +240,7 @@ int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t
   ResidentSizes s = resident_sizes(*r);
 
   // load steps (1), (2), (4) on the host
-  auto w3 = host_array<uint16_t>(s.w3 / 2);
+  auto w3 = host_array<uint16_t>(s.w3 / 2);  // BF16 rows
   auto codes = host_array<uint8_t>(s.codes);
   auto scales = host_array<uint16_t>(s.scales / 2);
   auto rho = host_array<uint16_t>(s.scales / 2);
@@ -264,6 +265,73 @@ int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t
     return hipf(e, "upload");
   // load step (3) on the device
   rc = device_lowrank(r.get());
+  if (rc) return rc;
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "build");
+  *out = r.release();
+  return CFR_OK;
+}
+
+int cfr_build_reader_q4(const cfr_config* cfg, const uint8_t* rows, const uint16_t* router, cfr_reader** out) {
+  clear_error();
+  if (!out) return fail(CFR_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!q4_rows(*cfg)) return fail(CFR_EINVAL, "cfr_build_reader_q4 takes a config with exact_bits 4");
+  if (!rows) return fail(CFR_EINVAL, "rows must be non-NULL");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev)
+    return fail(CFR_EINVAL, "device ordinal not available");
+  DeviceGuard guard(cfg->device);
+  if (!guard.ok) return fail(CFR_EHIP, "cannot select device");
+
+  std::unique_ptr<cfr_reader, void (*)(cfr_reader*)> r(new (std::nothrow) cfr_reader(), free_reader);
+  if (!r) return fail(CFR_ENOMEM, "host allocation");
+  r->cfg = *cfg;
+  init_geometry(*r);
+  if (max_lds_needed(*cfg) > kMaxLds)
+    return fail(CFR_EUNSUPPORTED, "hidden, inter and top too large for one workgroup's LDS");
+  ResidentSizes s = resident_sizes(*r);
+  const size_t E = cfg->n_experts, I = cfg->inter, H = cfg->hidden, rq = row_bytes((int)H, true);
+
+  // the weights the checkpoint holds: the sketch, the norms and the recovery
+  // basis are built from them, as from BF16 weights
+  auto gate = host_array<float>(E * I * H);
+  auto up = host_array<float>(E * I * H);
+  auto down = host_array<float>(E * H * I);
+  auto codes = host_array<uint8_t>(s.codes);
+  auto scales = host_array<uint16_t>(s.scales / 2);
+  auto rho = host_array<uint16_t>(s.scales / 2);
+  auto norms = host_array<float>(s.norms / 4);
+  auto sigma = host_array<float>(s.sigma / 4);
+  auto drow = host_array<float>(H);
+  if (!gate || !up || !down || !codes || !scales || !rho || !norms || !sigma || !drow)
+    return fail(CFR_ENOMEM, "host staging allocation");
+  for (size_t e = 0; e < E; ++e)
+    for (size_t j = 0; j < I; ++j) {
+      const uint8_t* rec = rows + (e * I + j) * 3 * rq;
+      if ((rc = dequant_q4_record(rec, (int)H, gate.get() + (e * I + j) * H)) ||
+          (rc = dequant_q4_record(rec + rq, (int)H, up.get() + (e * I + j) * H)) ||
+          (rc = dequant_q4_record(rec + 2 * rq, (int)H, drow.get())))
+        return rc;
+      for (size_t h = 0; h < H; ++h) down[(e * H + h) * I + j] = drow[h];
+    }
+  rc = pack_host_f32(*cfg, gate.get(), up.get(), down.get(), codes.get(), scales.get(), rho.get(), norms.get(),
+                     sigma.get());
+  if (rc) return rc;
+
+  rc = alloc_resident(*r, router != nullptr);
+  if (rc) return rc;
+  hipError_t e;
+  if ((e = hipMemcpy(r->w3, rows, s.w3, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->codes, codes.get(), s.codes, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->scales, scales.get(), s.scales, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->rho, rho.get(), s.scales, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->norms, norms.get(), s.norms, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(r->sigma, sigma.get(), s.sigma, hipMemcpyHostToDevice)) != hipSuccess ||
+      (router && (e = hipMemcpy(r->router, router, s.router, hipMemcpyHostToDevice)) != hipSuccess))
+    return hipf(e, "upload");
+  rc = device_lowrank(r.get());  // load step (3) from the 4-bit down rows
   if (rc) return rc;
   if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "build");
   *out = r.release();
@@ -300,6 +368,7 @@ int cfr_reader_decode_shared(cfr_reader* r, const float* x, const int32_t* ids, 
     return fail(CFR_EUNSUPPORTED, "the batch-shared decode takes at most 8 tokens per call");
   if (r->cfg.ranking != CFR_RANK_SCORE)
     return fail(CFR_EUNSUPPORTED, "the batch-shared decode ranks by the output-unit score only");
+  if (q4_rows(r->cfg)) return fail(CFR_EUNSUPPORTED, "the batch-shared decode reads BF16 rows only");
   const int64_t nmax = (int64_t)std::min(r->cfg.n_experts, batch * r->cfg.top) * r->cfg.inter;
   if (k < 0 || k > nmax) return fail(CFR_EINVAL, "k must be in 0..min(n_experts, batch*top)*inter");
   DeviceGuard guard(r->cfg.device);

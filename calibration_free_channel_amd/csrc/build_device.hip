@@ -31,10 +31,26 @@ __device__ __forceinline__ double bf16d(uint16_t b) {
   return (double)__uint_as_float((uint32_t)b << 16);
 }
 
+// Weight h of the down row of channel n in the [N][3] row layout (rows of
+// rowq bytes): BF16, or a 4-bit record, scale (q - zero) (exact in double).
+template <bool Q4>
+__device__ __forceinline__ double down_w(const uint8_t* w3, size_t n, int h, int H, int rowq) {
+  const uint8_t* row = w3 + (n * 3 + 2) * (size_t)rowq;
+  if constexpr (Q4) {
+    const int q = (row[h >> 1] >> (4 * (h & 1))) & 15;
+    const uint16_t sb = *reinterpret_cast<const uint16_t*>(row + (H >> 1) + 2 * (h >> 7));
+    const int z = row[(H >> 1) + (H >> 6) + (h >> 7)];
+    return (double)__builtin_bit_cast(_Float16, sb) * (double)(q - z);
+  } else {
+    return bf16d(reinterpret_cast<const uint16_t*>(row)[h]);
+  }
+}
+
 // G[i][j] = sum_n d_n[i] d_n[j] over all N channels, upper tiles only, mirrored.
 // d_n is the transposed-down row of channel n inside the [N][3][H] layout.
-__global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ w3,
-                                              double* __restrict__ G, int H, int N) {
+template <bool Q4>
+__global__ __launch_bounds__(256) void k_gram(const uint8_t* __restrict__ w3,
+                                              double* __restrict__ G, int H, int N, int rowq) {
   const int tc = blockIdx.x, tr = blockIdx.y;
   if (tr > tc) return;
   __shared__ double A[kNC][kT];
@@ -44,9 +60,8 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ w3,
   for (int n0 = 0; n0 < N; n0 += kNC) {
     for (int q = tid; q < kNC * kT; q += 256) {
       const int nn = q / kT, h = q % kT, n = n0 + nn;
-      const uint16_t* d = w3 + ((size_t)n * 3 + 2) * H;
-      A[nn][h] = n < N ? bf16d(d[tr * kT + h]) : 0.0;
-      B[nn][h] = n < N ? bf16d(d[tc * kT + h]) : 0.0;
+      A[nn][h] = n < N ? down_w<Q4>(w3, n, tr * kT + h, H, rowq) : 0.0;
+      B[nn][h] = n < N ? down_w<Q4>(w3, n, tc * kT + h, H, rowq) : 0.0;
     }
     __syncthreads();
     for (int nn = 0; nn < kNC; ++nn) {
@@ -75,16 +90,17 @@ __global__ __launch_bounds__(256) void k_gram(const uint16_t* __restrict__ w3,
 
 // b[n][r] = sum_h U[h][r] d_n[h]; eig holds eigenvectors as contiguous
 // columns (column-major), ascending eigenvalue; column H-1-r is the r-th largest.
-__global__ __launch_bounds__(256) void k_coeffs(const uint16_t* __restrict__ w3,
+template <bool Q4>
+__global__ __launch_bounds__(256) void k_coeffs(const uint8_t* __restrict__ w3,
                                                 const double* __restrict__ eig,
-                                                double* __restrict__ bout, int H, int N, int rank) {
+                                                double* __restrict__ bout, int H, int N, int rank,
+                                                int rowq) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)N * rank) return;
   const int n = (int)(idx / rank), r = (int)(idx % rank);
-  const uint16_t* d = w3 + ((size_t)n * 3 + 2) * H;
   const double* u = eig + (size_t)(H - 1 - r) * H;
   double acc = 0.0;
-  for (int h = 0; h < H; ++h) acc += u[h] * bf16d(d[h]);
+  for (int h = 0; h < H; ++h) acc += u[h] * down_w<Q4>(w3, n, h, H, rowq);
   bout[idx] = acc;
 }
 
@@ -114,7 +130,12 @@ int device_lowrank(cfr_reader* r) {
       (e = hipMalloc(&Bb.p, sizeof(double) * N * rank)) != hipSuccess)
     return fail(CFR_ENOMEM, std::string("lowrank workspace: ") + hipGetErrorString(e));
   const int nt = H / kT;
-  k_gram<<<dim3(nt, nt), 256>>>(r->w3, (double*)G.p, H, N);
+  const bool q4 = q4_rows(r->cfg);
+  const int rowq = row_bytes(H, q4);
+  if (q4)
+    k_gram<true><<<dim3(nt, nt), 256>>>(r->w3, (double*)G.p, H, N, rowq);
+  else
+    k_gram<false><<<dim3(nt, nt), 256>>>(r->w3, (double*)G.p, H, N, rowq);
   if ((e = hipGetLastError()) != hipSuccess) return hipf(e, "gram launch");
   if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "gram");
 
@@ -133,8 +154,12 @@ int device_lowrank(cfr_reader* r) {
   if (info != 0) return fail(CFR_ESOLVER, "eigensolver did not converge (info != 0)");
 
   const long nb = (long)N * rank;
-  k_coeffs<<<(unsigned)((nb + 255) / 256), 256>>>(r->w3, (const double*)G.p, (double*)Bb.p, H, N,
-                                                   rank);
+  if (q4)
+    k_coeffs<true><<<(unsigned)((nb + 255) / 256), 256>>>(r->w3, (const double*)G.p, (double*)Bb.p, H, N,
+                                                   rank, rowq);
+  else
+    k_coeffs<false><<<(unsigned)((nb + 255) / 256), 256>>>(r->w3, (const double*)G.p, (double*)Bb.p, H, N,
+                                                   rank, rowq);
   if ((e = hipGetLastError()) != hipSuccess) return hipf(e, "coeffs launch");
   if ((e = hipDeviceSynchronize()) != hipSuccess) return hipf(e, "coeffs");
 

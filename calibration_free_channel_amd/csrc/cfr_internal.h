@@ -34,11 +34,25 @@ inline int unit_bytes(int inter) { return (2 * half_bytes(inter) + 31) / 32 * 32
 
 int validate_config(const cfr_config* c);
 
+// Exact rows in 4 bits (cfr_config.exact_bits == 4) rather than BF16.
+inline bool q4_rows(const cfr_config& c) { return c.exact_bits == 4; }
+// Bytes of one resident row of H weights: BF16, or the 4-bit record (H/2
+// bytes of codes, H/128 fp16 group scales, H/128 byte zero points) padded to
+// a multiple of 16 bytes.
+inline int row_bytes(int H, bool q4) { return q4 ? ((H / 2 + 3 * (H / 128)) + 15) / 16 * 16 : 2 * H; }
+
 // Host pack (load steps 1, 2 and 4).  Writes into caller buffers; any may be null.
 //   w3: [E][I][3][H] bf16 (gate row, up row, down column) — the resident layout.
 int pack_host(const cfr_config& c, const uint16_t* gate, const uint16_t* up,
               const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
               float* norms, uint16_t* w3, float* sigma);
+
+// The same from real-valued weights (a dequantized 4-bit checkpoint; no
+// resident BF16 layout).
+int pack_host_f32(const cfr_config& c, const float* gate, const float* up, const float* down,
+                  uint8_t* codes, uint16_t* scales, uint16_t* rho, float* norms, float* sigma_out);
+// Weights of one 4-bit row record of H weights (see row_bytes).
+int dequant_q4_record(const uint8_t* rec, int H, float* out);
 
 void sign_vector(uint64_t seed, int hidden, float* out);
 uint16_t f64_to_f16_rne(double v);
@@ -77,7 +91,7 @@ struct cfr_reader {
   int nblk, lp, unit, ncand;
   int ncp = 0;  // candidates per token padded for the select kernel (select_geom)
   // resident state
-  uint16_t* w3 = nullptr;      // [E][I][3][H] bf16
+  uint8_t* w3 = nullptr;       // [E][I][3] rows of row_bytes(H) bytes: BF16, or 4-bit records
   uint8_t* codes = nullptr;    // [E][nblk][128][unit]
   uint16_t* scales = nullptr;  // [E][nblk][2][I] fp16
   uint16_t* rho = nullptr;     // [E][nblk][2][I] fp16

@@ -42,6 +42,10 @@ int validate_config(const cfr_config* c) {
     return fail(CFR_EINVAL, "ranking must be CFR_RANK_SCORE or CFR_RANK_EXPECTED_ERROR");
   if (c->ranking == CFR_RANK_EXPECTED_ERROR && c->n_screen != kBlock)
     return fail(CFR_EINVAL, "the expected-error ranking reads the whole sketch: n_screen must be 128");
+  if (c->exact_bits != 0 && c->exact_bits != 16 && c->exact_bits != 4)
+    return fail(CFR_EINVAL, "exact_bits must be 16 (or 0) or 4");
+  if (c->exact_bits == 4 && c->ranking != CFR_RANK_SCORE)
+    return fail(CFR_EUNSUPPORTED, "4-bit exact rows are read with the output-unit score ranking only");
   return CFR_OK;
 }
 
@@ -69,7 +73,7 @@ int cfr_sizes_of(const cfr_config* c, cfr_sizes* out) {
   out->norms_count = E * I;
   out->u_count = H * c->rank;
   out->b_count = E * I * c->rank;
-  out->weights_bytes = E * I * 3 * H * 2;
+  out->weights_bytes = E * I * 3 * (int64_t)row_bytes((int)H, q4_rows(*c));
   return CFR_OK;
 }
 
@@ -83,11 +87,11 @@ int cfr_read_bytes(const cfr_config* c, int32_t k, cfr_read_stats* out) {
   out->scales = top * nblk * sect(2 * I * 2);
   out->norms = top * sect(I * 4);
   out->rho = c->ranking == CFR_RANK_EXPECTED_ERROR ? top * nblk * sect(2 * I * 2) : 0;
-  out->exact = (int64_t)k * sect(3 * H * 2);
+  out->exact = (int64_t)k * sect(3 * (int64_t)row_bytes((int)H, q4_rows(*c)));
   out->b = (top * I - k) * sect((int64_t)c->rank * 2);
   out->u = sect(H * (int64_t)c->rank * 2);
   out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
-  out->dense = top * 3 * I * H * 2;
+  out->dense = top * 3 * I * (int64_t)row_bytes((int)H, q4_rows(*c));
   return CFR_OK;
 }
 
@@ -139,11 +143,11 @@ int cfr_read_bytes_batch(const cfr_config* c, int32_t batch, int32_t k, const in
   out->scales = n_block * sect(2 * I * 2);
   out->norms = n_expert * sect(I * 4);
   out->rho = c->ranking == CFR_RANK_EXPECTED_ERROR ? n_block * sect(2 * I * 2) : 0;
-  out->exact = n_exact * sect(3 * H * 2);
+  out->exact = n_exact * sect(3 * (int64_t)row_bytes((int)H, q4_rows(*c)));
   out->b = n_skip * sect((int64_t)c->rank * 2);
   out->u = sect(H * (int64_t)c->rank * 2);
   out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
-  out->dense = n_expert * 3 * I * H * 2;
+  out->dense = n_expert * 3 * I * (int64_t)row_bytes((int)H, q4_rows(*c));
   return CFR_OK;
 }
 
@@ -177,11 +181,11 @@ int cfr_read_bytes_shared(const cfr_config* c, int32_t batch, const int32_t* ids
   out->scales = n_block * sect(2 * I * 2);
   out->norms = n_expert * sect(I * 4);
   out->rho = 0;
-  out->exact = (int64_t)n_kept * sect(3 * H * 2);
+  out->exact = (int64_t)n_kept * sect(3 * (int64_t)row_bytes((int)H, q4_rows(*c)));
   out->b = (n_expert * I - n_kept) * sect((int64_t)c->rank * 2);
   out->u = sect(H * (int64_t)c->rank * 2);
   out->total = out->codes + out->scales + out->norms + out->rho + out->exact + out->b + out->u;
-  out->dense = n_expert * 3 * I * H * 2;
+  out->dense = n_expert * 3 * I * (int64_t)row_bytes((int)H, q4_rows(*c));
   return CFR_OK;
 }
 

@@ -394,7 +394,7 @@ struct SelectArgs {
   const float* x;
   const int32_t* ids;
   const float* gw;
-  const uint16_t* w3;
+  const uint8_t* w3;  // [E][I][3] rows of rowq bytes (BF16, or 4-bit records)
   const uint16_t* bmat;
   const unsigned long long* acc;
   const float* norms;  // ||d_j|| [E][I]
@@ -409,6 +409,7 @@ struct SelectArgs {
   float invI;   // 1 / I rounded to float (exact slot division below 2^17)
   int cps_mul;  // I % 128 == 0: ceil(2^16 / (I / 128)), else 0
   const float* var;  // [B][2][ncp] sketch-error variances (expected-error ranking)
+  int rowq = 0;      // bytes of one resident row
 };
 
 // misc slots
@@ -532,7 +533,7 @@ __device__ __forceinline__ void write_kept_debug(const bool (&f)[PER], int* wc, 
 
 // VAR: rank by the expected squared error of skipping (error_key) instead of
 // the output-unit score.
-template <int NT, int PER, int NCH, bool VAR>
+template <int NT, int PER, int NCH, bool VAR, bool Q4>
 __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NW = NT / 64, P2 = PER / 2;
@@ -985,7 +986,8 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   CFR_TRACE_PHASE(1, 3);
 
   if (!recover) {
-    // ---- decode step (3): exact kept channels from native BF16 rows ----
+    // ---- decode step (3): exact kept channels from the resident rows
+    // (native BF16, or 4-bit records dequantized on the fly) ----
     // wave v takes list entries [v cpw, (v+1) cpw), two channels at a time
     // when registers allow, all rows in flight together
     float yv[NCH][8];
@@ -1002,23 +1004,23 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       int cc[NR];
       cc[0] = list[q0];
       if constexpr (kPair) cc[NR - 1] = two ? list[q0 + 1] : cc[0];
-      uint4 gq2[NR][NCH], uq2[NR][NCH], dq2[NR][NCH];
+      Chunk8<Q4> gq2[NR][NCH], uq2[NR][NCH], dq2[NR][NCH];
       int sr[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         sr[r] = slot_of(cc[r]);
-        const uint16_t* row = a.w3 + ((size_t)sl_e[sr[r]] * I + (cc[r] - sr[r] * I)) * 3 * H;
+        const uint8_t* row = a.w3 + ((size_t)sl_e[sr[r]] * I + (cc[r] - sr[r] * I)) * 3 * a.rowq;
         if (r == 0 || two) {  // wave-uniform
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch) {
             const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
-            gq2[r][ch] = *reinterpret_cast<const uint4*>(row + h);
-            uq2[r][ch] = *reinterpret_cast<const uint4*>(row + H + h);
-            dq2[r][ch] = *reinterpret_cast<const uint4*>(row + 2 * H + h);
+            gq2[r][ch].load(row, H, h);
+            uq2[r][ch].load(row + a.rowq, H, h);
+            dq2[r][ch].load(row + 2 * a.rowq, H, h);
           }
         } else {
 #pragma unroll
-          for (int ch = 0; ch < NCH; ++ch) gq2[r][ch] = uq2[r][ch] = dq2[r][ch] = make_uint4(0u, 0u, 0u, 0u);
+          for (int ch = 0; ch < NCH; ++ch) gq2[r][ch].clear(), uq2[r][ch].clear(), dq2[r][ch].clear();
         }
       }
       float gs[NR], vs[NR];
@@ -1033,14 +1035,13 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
           const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
-            const uint32_t gw4[4] = {gq2[r][ch].x, gq2[r][ch].y, gq2[r][ch].z, gq2[r][ch].w};
-            const uint32_t uw4[4] = {uq2[r][ch].x, uq2[r][ch].y, uq2[r][ch].z, uq2[r][ch].w};
+            float gv[8], uv[8];
+            gq2[r][ch].vals(gv);
+            uq2[r][ch].vals(uv);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              gs[r] = fmaf(bf_lo(gw4[p]), xv[2 * p], gs[r]);
-              gs[r] = fmaf(bf_hi(gw4[p]), xv[2 * p + 1], gs[r]);
-              vs[r] = fmaf(bf_lo(uw4[p]), xv[2 * p], vs[r]);
-              vs[r] = fmaf(bf_hi(uw4[p]), xv[2 * p + 1], vs[r]);
+            for (int i = 0; i < 8; ++i) {
+              gs[r] = fmaf(gv[i], xv[i], gs[r]);
+              vs[r] = fmaf(uv[i], xv[i], vs[r]);
             }
           }
         }
@@ -1052,12 +1053,10 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
       for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const uint32_t dw[4] = {dq2[r][ch].x, dq2[r][ch].y, dq2[r][ch].z, dq2[r][ch].w};
+          float dv[8];
+          dq2[r][ch].vals(dv);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            yv[ch][2 * p] = fmaf(cf[r], bf_lo(dw[p]), yv[ch][2 * p]);
-            yv[ch][2 * p + 1] = fmaf(cf[r], bf_hi(dw[p]), yv[ch][2 * p + 1]);
-          }
+          for (int i = 0; i < 8; ++i) yv[ch][i] = fmaf(cf[r], dv[i], yv[ch][i]);
         }
     }
     CFR_TRACE_PHASE(1, 4);
@@ -1420,40 +1419,43 @@ static void allow_lds(K kernel) {
   (void)hipGetLastError();
 }
 
-template <int NT, int PER, int NCH, bool VAR>
+template <int NT, int PER, int NCH, bool VAR, bool Q4>
 static hipError_t launch_select_t(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   static OncePerDevice attr;
-  attr([] { allow_lds(k_select<NT, PER, NCH, VAR>); });
-  k_select<NT, PER, NCH, VAR><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
+  attr([] { allow_lds(k_select<NT, PER, NCH, VAR, Q4>); });
+  k_select<NT, PER, NCH, VAR, Q4><<<batch * (p.G + p.Z), NT, p.lds2, st>>>(a);
   return hipGetLastError();
 }
 
-template <int PER, bool VAR>
+template <int PER, bool VAR, bool Q4>
 static hipError_t launch_select_n(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   switch (p.nch) {
-    case 1: return launch_select_t<512, PER, 1, VAR>(a, p, batch, st);
-    case 2: return launch_select_t<512, PER, 2, VAR>(a, p, batch, st);
-    case 4: return launch_select_t<512, PER, 4, VAR>(a, p, batch, st);
-    default: return launch_select_t<512, PER, 8, VAR>(a, p, batch, st);
+    case 1: return launch_select_t<512, PER, 1, VAR, Q4>(a, p, batch, st);
+    case 2: return launch_select_t<512, PER, 2, VAR, Q4>(a, p, batch, st);
+    case 4: return launch_select_t<512, PER, 4, VAR, Q4>(a, p, batch, st);
+    default: return launch_select_t<512, PER, 8, VAR, Q4>(a, p, batch, st);
   }
 }
 
-template <bool VAR>
+template <bool VAR, bool Q4>
 static hipError_t launch_select_v(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
   switch (p.per) {  // select_geom: 512 threads, 2..32 candidates each
-    case 2: return launch_select_n<2, VAR>(a, p, batch, st);
-    case 4: return launch_select_n<4, VAR>(a, p, batch, st);
-    case 6: return launch_select_n<6, VAR>(a, p, batch, st);
-    case 8: return launch_select_n<8, VAR>(a, p, batch, st);
-    case 12: return launch_select_n<12, VAR>(a, p, batch, st);
-    case 16: return launch_select_n<16, VAR>(a, p, batch, st);
-    case 24: return launch_select_n<24, VAR>(a, p, batch, st);
-    default: return launch_select_n<32, VAR>(a, p, batch, st);
+    case 2: return launch_select_n<2, VAR, Q4>(a, p, batch, st);
+    case 4: return launch_select_n<4, VAR, Q4>(a, p, batch, st);
+    case 6: return launch_select_n<6, VAR, Q4>(a, p, batch, st);
+    case 8: return launch_select_n<8, VAR, Q4>(a, p, batch, st);
+    case 12: return launch_select_n<12, VAR, Q4>(a, p, batch, st);
+    case 16: return launch_select_n<16, VAR, Q4>(a, p, batch, st);
+    case 24: return launch_select_n<24, VAR, Q4>(a, p, batch, st);
+    default: return launch_select_n<32, VAR, Q4>(a, p, batch, st);
   }
 }
 
-static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, hipStream_t st) {
-  return a.var ? launch_select_v<true>(a, p, batch, st) : launch_select_v<false>(a, p, batch, st);
+// 4-bit rows are read with the output-unit score only (the configuration
+// refuses them with the expected-error ranking)
+static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, bool q4, hipStream_t st) {
+  if (q4) return launch_select_v<false, true>(a, p, batch, st);
+  return a.var ? launch_select_v<true, false>(a, p, batch, st) : launch_select_v<false, false>(a, p, batch, st);
 }
 
 // CPB: coordinates per thread batch, the n_screen = 80 share of one thread in
@@ -1508,8 +1510,9 @@ int launch_decode(cfr_reader* r, const float* x, const int32_t* ids, const float
                W.score, W.kept, r->status, c.hidden, c.n_experts, c.inter, c.top, r->ncand,
                r->ncp, k, c.rank, p.G, p.Z, p.cpw, p.chan, dbg != nullptr, 1.0f / (float)c.inter,
                cps_mul(c.inter), var};
+  B.rowq = row_bytes(c.hidden, q4_rows(c));
   if (only < 0 || only == 1)
-    if ((e = launch_select(B, p, batch, st)) != hipSuccess) return hip_fail(e, "select launch");
+    if ((e = launch_select(B, p, batch, q4_rows(c), st)) != hipSuccess) return hip_fail(e, "select launch");
   mark(2);
   ReduceArgs C{W.ypart, W.zpart, r->u, y, W.acc, c.hidden, p.G, p.Z, c.rank, r->ncp,
                p.nslices, 1, resid};

@@ -7,8 +7,9 @@
 // Calibration Data"): a_j = silu(g_j . x)(v_j . x), y = sum_j w_j a_j d_j.
 //
 // The block is a pure HBM stream: every routed channel's gate, up and
-// (transposed) down rows are read once, 3 H BF16 values that lie next to each
-// other in the [E][I][3][H] layout.  One launch of G workgroups per token,
+// (transposed) down rows are read once, three rows that lie next to each
+// other in the [E][I][3] row layout (native BF16, or 4-bit records
+// dequantized on the fly).  One launch of G workgroups per token,
 // each over a contiguous range of the token's top * inter channels; a wave
 // takes its channels U at a time with every row of the U in flight together
 // (one memory latency per U channels; the CU's other waves hide it), and the
@@ -27,10 +28,10 @@ struct DenseArgs {
   const float* x;       // [B][H]
   const int32_t* ids;   // [B][top]
   const float* gw;      // [B][top]
-  const uint16_t* w3;   // [E][I][3][H] bf16
+  const uint8_t* w3;    // [E][I][3] rows of rowq bytes (BF16, or 4-bit records)
   float* ypart;         // [B][G][H]
   int32_t* status;
-  int H, E, I, top, nc, G, chan, cpw;
+  int H, E, I, top, nc, G, chan, cpw, rowq;
 };
 
 constexpr int kDenseThreads = 512;
@@ -38,7 +39,7 @@ constexpr int kDenseWaves = kDenseThreads / 64;
 
 // NCH: 512-wide chunks covering a row (H <= 512 NCH); U: channels a wave has
 // in flight at once.
-template <int NCH, int U>
+template <int NCH, int U, bool Q4>
 __global__ __launch_bounds__(kDenseThreads) void k_dense(DenseArgs a) {
   extern __shared__ float4 dense_lds[];
   float* xs = reinterpret_cast<float*>(dense_lds);  // [H]
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense(DenseArgs a) {
     for (int i = 0; i < 8; ++i) yv[ch][i] = 0.f;
 
   for (int q = q0; q < q1; q += U) {
-    uint4 gq[U][NCH], uq[U][NCH], dq[U][NCH];
+    Chunk8<Q4> gq[U][NCH], uq[U][NCH], dq[U][NCH];
     int sr[U];
     // every row of the U channels issued before any is used; a channel past
     // the wave's range re-reads the last one and gets coefficient 0
@@ -73,13 +74,13 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense(DenseArgs a) {
     for (int r = 0; r < U; ++r) {
       const int cc = min(q + r, q1 - 1);
       sr[r] = cc / I;
-      const uint16_t* row = a.w3 + ((size_t)sl_e[sr[r]] * I + (cc - sr[r] * I)) * 3 * H;
+      const uint8_t* row = a.w3 + ((size_t)sl_e[sr[r]] * I + (cc - sr[r] * I)) * 3 * a.rowq;
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
-        gq[r][ch] = *reinterpret_cast<const uint4*>(row + h);
-        uq[r][ch] = *reinterpret_cast<const uint4*>(row + H + h);
-        dq[r][ch] = *reinterpret_cast<const uint4*>(row + 2 * H + h);
+        gq[r][ch].load(row, H, h);
+        uq[r][ch].load(row + a.rowq, H, h);
+        dq[r][ch].load(row + 2 * a.rowq, H, h);
       }
     }
     float gs[U], vs[U];
@@ -94,14 +95,13 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense(DenseArgs a) {
         const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
         for (int r = 0; r < U; ++r) {
-          const uint32_t g4[4] = {gq[r][ch].x, gq[r][ch].y, gq[r][ch].z, gq[r][ch].w};
-          const uint32_t u4[4] = {uq[r][ch].x, uq[r][ch].y, uq[r][ch].z, uq[r][ch].w};
+          float gv[8], uv[8];
+          gq[r][ch].vals(gv);
+          uq[r][ch].vals(uv);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            gs[r] = fmaf(bf_lo(g4[p]), xv[2 * p], gs[r]);
-            gs[r] = fmaf(bf_hi(g4[p]), xv[2 * p + 1], gs[r]);
-            vs[r] = fmaf(bf_lo(u4[p]), xv[2 * p], vs[r]);
-            vs[r] = fmaf(bf_hi(u4[p]), xv[2 * p + 1], vs[r]);
+          for (int i = 0; i < 8; ++i) {
+            gs[r] = fmaf(gv[i], xv[i], gs[r]);
+            vs[r] = fmaf(uv[i], xv[i], vs[r]);
           }
         }
       }
@@ -116,12 +116,10 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense(DenseArgs a) {
     for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
       for (int r = 0; r < U; ++r) {
-        const uint32_t d4[4] = {dq[r][ch].x, dq[r][ch].y, dq[r][ch].z, dq[r][ch].w};
+        float dv[8];
+        dq[r][ch].vals(dv);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          yv[ch][2 * p] = fmaf(cf[r], bf_lo(d4[p]), yv[ch][2 * p]);
-          yv[ch][2 * p + 1] = fmaf(cf[r], bf_hi(d4[p]), yv[ch][2 * p + 1]);
-        }
+        for (int i = 0; i < 8; ++i) yv[ch][i] = fmaf(cf[r], dv[i], yv[ch][i]);
       }
   }
 
@@ -163,28 +161,38 @@ __global__ __launch_bounds__(kDenseThreads) void k_dense(DenseArgs a) {
   }
 }
 
-template <int NCH, int U>
+template <int NCH, int U, bool Q4>
 hipError_t launch_dense_t(const DenseArgs& a, int batch, size_t lds, hipStream_t st) {
   static OncePerDevice attr;
   attr([] {
-    (void)hipFuncSetAttribute((const void*)k_dense<NCH, U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)k_dense<NCH, U, Q4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)(kMaxLds - 1024));
     (void)hipGetLastError();
   });
-  k_dense<NCH, U><<<batch * a.G, kDenseThreads, lds, st>>>(a);
+  k_dense<NCH, U, Q4><<<batch * a.G, kDenseThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 
-template <int NCH>
+template <int NCH, bool Q4>
 hipError_t launch_dense_u(const DenseArgs& a, int u, int batch, size_t lds, hipStream_t st) {
   if constexpr (NCH >= 8) {
-    return launch_dense_t<NCH, 1>(a, batch, lds, st);
+    return launch_dense_t<NCH, 1, Q4>(a, batch, lds, st);
   } else {
     switch (u) {
-      case 1: return launch_dense_t<NCH, 1>(a, batch, lds, st);
-      case 2: return launch_dense_t<NCH, 2>(a, batch, lds, st);
-      default: return launch_dense_t<NCH, 3>(a, batch, lds, st);
+      case 1: return launch_dense_t<NCH, 1, Q4>(a, batch, lds, st);
+      case 2: return launch_dense_t<NCH, 2, Q4>(a, batch, lds, st);
+      default: return launch_dense_t<NCH, 3, Q4>(a, batch, lds, st);
     }
+  }
+}
+
+template <bool Q4>
+hipError_t launch_dense_q(const DenseArgs& a, int nch, int u, int batch, size_t lds, hipStream_t st) {
+  switch (nch) {
+    case 1: return launch_dense_u<1, Q4>(a, u, batch, lds, st);
+    case 2: return launch_dense_u<2, Q4>(a, u, batch, lds, st);
+    case 4: return launch_dense_u<4, Q4>(a, u, batch, lds, st);
+    default: return launch_dense_u<8, Q4>(a, u, batch, lds, st);
   }
 }
 
@@ -205,17 +213,14 @@ DensePlan make_dense_plan(const cfr_config& c, int batch) {
   return p;
 }
 
-hipError_t launch_dense_block(const float* x, const int32_t* ids, const float* gw, const uint16_t* w3,
+hipError_t launch_dense_block(const float* x, const int32_t* ids, const float* gw, const uint8_t* w3,
                               float* ypart, int32_t* status, const cfr_config& c, int batch,
                               const DensePlan& p, hipStream_t st) {
+  const bool q4 = q4_rows(c);
   DenseArgs a{x, ids, gw, w3, ypart, status, c.hidden, c.n_experts, c.inter, c.top,
-              c.top * c.inter, p.G, p.chan, p.cpw};
-  switch (p.nch) {
-    case 1: return launch_dense_u<1>(a, p.u, batch, p.lds, st);
-    case 2: return launch_dense_u<2>(a, p.u, batch, p.lds, st);
-    case 4: return launch_dense_u<4>(a, p.u, batch, p.lds, st);
-    default: return launch_dense_u<8>(a, p.u, batch, p.lds, st);
-  }
+              c.top * c.inter, p.G, p.chan, p.cpw, row_bytes(c.hidden, q4)};
+  return q4 ? launch_dense_q<true>(a, p.nch, p.u, batch, p.lds, st)
+            : launch_dense_q<false>(a, p.nch, p.u, batch, p.lds, st);
 }
 
 }  // namespace cfr

@@ -152,5 +152,46 @@ __device__ __forceinline__ uint32_t score_key(unsigned long long g, unsigned lon
   return order_key(sc);
 }
 
+// Eight consecutive weights h .. h + 7 (h a multiple of 8) of one resident
+// row, as one lane holds them.  BF16 rows: 16 bytes.  4-bit rows (a row
+// record of H/2 bytes of codes, value h in byte h/2, even h in the low
+// nibble, then H/128 fp16 group scales, then H/128 byte zero points):
+// w = scale (q - zero), the eight in one group of 128.
+template <bool Q4>
+struct Chunk8;
+
+template <>
+struct Chunk8<false> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint8_t* row, int H, int h) {
+    (void)H;
+    w = *reinterpret_cast<const uint4*>(row + 2 * (size_t)h);
+  }
+  __device__ __forceinline__ void clear() { w = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void vals(float* v) const {
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) v[2 * p] = bf_lo(q[p]), v[2 * p + 1] = bf_hi(q[p]);
+  }
+};
+
+template <>
+struct Chunk8<true> {
+  uint32_t q;
+  uint16_t s;
+  uint8_t z;
+  __device__ __forceinline__ void load(const uint8_t* row, int H, int h) {
+    q = *reinterpret_cast<const uint32_t*>(row + (h >> 1));
+    s = *reinterpret_cast<const uint16_t*>(row + (H >> 1) + 2 * (h >> 7));
+    z = row[(H >> 1) + (H >> 6) + (h >> 7)];
+  }
+  __device__ __forceinline__ void clear() { q = 0u, s = 0, z = 0; }
+  __device__ __forceinline__ void vals(float* v) const {
+    const float sc = f16f(s), zf = (float)z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ((float)((q >> (4 * i)) & 15u) - zf) * sc;
+  }
+};
+
 }  // namespace
 }  // namespace cfr

@@ -163,7 +163,7 @@ struct DensePlan {
   size_t lds = 0;
 };
 DensePlan make_dense_plan(const cfr_config& c, int batch);
-hipError_t launch_dense_block(const float* x, const int32_t* ids, const float* gw, const uint16_t* w3,
+hipError_t launch_dense_block(const float* x, const int32_t* ids, const float* gw, const uint8_t* w3,
                               float* ypart, int32_t* status, const cfr_config& c, int batch,
                               const DensePlan& p, hipStream_t st);
 

@@ -17,6 +17,8 @@
 //   rho    = fp16_rne( sum_i (u_i / sqrt128 - alpha c_i)^2 / 128 )
 //   ||d_j|| = (float) sqrt( sum_h d_hj^2 )   (h in order)
 #include <math.h>
+
+#include <cmath>
 #include <string.h>
 
 #include <algorithm>
@@ -94,9 +96,14 @@ static void fwht128(double* v) {
 
 namespace {
 
+static inline double w_f64(uint16_t b) { return bf16_to_f64(b); }
+static inline double w_f64(float f) { return (double)f; }
+
+// T: uint16_t (BF16 bit patterns) or float (a dequantized 4-bit checkpoint)
+template <typename T>
 struct PackJob {
   const cfr_config* c;
-  const uint16_t *gate, *up, *down;
+  const T *gate, *up, *down;
   uint8_t* codes;
   uint16_t *scales, *rho, *w3;
   float* norms;
@@ -104,19 +111,20 @@ struct PackJob {
   int nblk, lp, unit;
 };
 
-// One expert: sketch of gate and up, norms, resident layout.
-void pack_expert(const PackJob& J, int e, std::vector<int8_t>& trits) {
+// One expert: sketch of gate and up, norms, resident layout (BF16 only).
+template <typename T>
+void pack_expert(const PackJob<T>& J, int e, std::vector<int8_t>& trits) {
   const int H = J.c->hidden, I = J.c->inter, nblk = J.nblk;
   const size_t row_stride = (size_t)H;
   double u[kBlock];
   for (int m = 0; m < 2; ++m) {
-    const uint16_t* W = (m == 0 ? J.gate : J.up) + (size_t)e * I * H;
+    const T* W = (m == 0 ? J.gate : J.up) + (size_t)e * I * H;
     // trits[b][i][j], coordinate-major like the units
     for (int j = 0; j < I; ++j) {
-      const uint16_t* row = W + (size_t)j * row_stride;
+      const T* row = W + (size_t)j * row_stride;
       for (int b = 0; b < nblk; ++b) {
         for (int i = 0; i < kBlock; ++i)
-          u[i] = (double)J.sigma[b * kBlock + i] * bf16_to_f64(row[b * kBlock + i]);
+          u[i] = (double)J.sigma[b * kBlock + i] * w_f64(row[b * kBlock + i]);
         fwht128(u);
         double S = 0.0;
         for (int i = 0; i < kBlock; ++i) S = S + fabs(u[i]);
@@ -171,17 +179,18 @@ void pack_expert(const PackJob& J, int e, std::vector<int8_t>& trits) {
     }
   }
   // down norms and the resident layout
-  const uint16_t* D = J.down + (size_t)e * H * I;
+  const T* D = J.down + (size_t)e * H * I;
   if (J.norms) {
     std::vector<double> acc(I, 0.0);
     for (int h = 0; h < H; ++h)
       for (int j = 0; j < I; ++j) {
-        double d = bf16_to_f64(D[(size_t)h * I + j]);
+        double d = w_f64(D[(size_t)h * I + j]);
         acc[j] = acc[j] + d * d;
       }
     for (int j = 0; j < I; ++j) J.norms[(size_t)e * I + j] = (float)sqrt(acc[j]);
   }
-  if (J.w3) {
+  if constexpr (sizeof(T) == 2) {
+    if (!J.w3) return;
     for (int j = 0; j < I; ++j) {
       uint16_t* dst = J.w3 + ((size_t)e * I + j) * 3 * H;
       memcpy(dst, J.gate + ((size_t)e * I + j) * H, (size_t)H * 2);
@@ -193,25 +202,28 @@ void pack_expert(const PackJob& J, int e, std::vector<int8_t>& trits) {
   }
 }
 
-// True when any of n BF16 bit patterns is an infinity or a NaN (exponent
+// True when any of n weights is an infinity or a NaN (for BF16: exponent
 // field all ones).
-static bool any_nonfinite_bf16(const uint16_t* a, size_t n) {
+static bool any_nonfinite(const uint16_t* a, size_t n) {
   for (size_t i = 0; i < n; ++i)
     if ((a[i] & 0x7F80u) == 0x7F80u) return true;
   return false;
 }
+static bool any_nonfinite(const float* a, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(a[i])) return true;
+  return false;
+}
 
-}  // namespace
-
-int pack_host(const cfr_config& c, const uint16_t* gate, const uint16_t* up,
-              const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
-              float* norms, uint16_t* w3, float* sigma_out) {
+template <typename T>
+int pack_host_t(const cfr_config& c, const T* gate, const T* up, const T* down, uint8_t* codes,
+                uint16_t* scales, uint16_t* rho, float* norms, uint16_t* w3, float* sigma_out) {
   // the sketch, the norms and the recovery basis are only defined for finite
   // weights: a NaN or an infinity is rejected before any work
   const size_t nw = (size_t)c.n_experts * c.inter * c.hidden;
-  if (any_nonfinite_bf16(gate, nw) || any_nonfinite_bf16(up, nw) || any_nonfinite_bf16(down, nw))
+  if (any_nonfinite(gate, nw) || any_nonfinite(up, nw) || any_nonfinite(down, nw))
     return fail(CFR_EINVAL, "weights contain NaN or infinity");
-  PackJob J;
+  PackJob<T> J;
   J.c = &c;
   J.gate = gate;
   J.up = up;
@@ -246,6 +258,38 @@ int pack_host(const cfr_config& c, const uint16_t* gate, const uint16_t* up,
   for (auto& th : pool) th.join();
   for (int e : errs)
     if (e) return fail(CFR_ENOMEM, "pack_host: host allocation failed");
+  return CFR_OK;
+}
+
+}  // namespace
+
+int pack_host(const cfr_config& c, const uint16_t* gate, const uint16_t* up,
+              const uint16_t* down, uint8_t* codes, uint16_t* scales, uint16_t* rho,
+              float* norms, uint16_t* w3, float* sigma_out) {
+  return pack_host_t<uint16_t>(c, gate, up, down, codes, scales, rho, norms, w3, sigma_out);
+}
+
+int pack_host_f32(const cfr_config& c, const float* gate, const float* up, const float* down,
+                  uint8_t* codes, uint16_t* scales, uint16_t* rho, float* norms, float* sigma_out) {
+  return pack_host_t<float>(c, gate, up, down, codes, scales, rho, norms, nullptr, sigma_out);
+}
+
+// A 4-bit row record (cfr_build_reader_q4): weight h = scale_g (q_h - z_g),
+// g = h / 128; every product is exact in float.  Zero points above 15 or
+// non-finite scales are reported.
+int dequant_q4_record(const uint8_t* rec, int H, float* out) {
+  const int G = H / kBlock;
+  for (int g = 0; g < G; ++g) {
+    const uint16_t sb = (uint16_t)(rec[H / 2 + 2 * g] | (rec[H / 2 + 2 * g + 1] << 8));
+    const double sc = f16_to_f64(sb);
+    const int z = rec[H / 2 + 2 * G + g];
+    if (z > 15 || !std::isfinite(sc)) return fail(CFR_EINVAL, "4-bit record: zero point above 15 or scale not finite");
+    for (int i = 0; i < kBlock; ++i) {
+      const int h = g * kBlock + i;
+      const int q = (rec[h / 2] >> (4 * (h & 1))) & 15;
+      out[h] = (float)(sc * (double)(q - z));
+    }
+  }
   return CFR_OK;
 }
 

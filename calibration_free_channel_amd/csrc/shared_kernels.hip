@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kBActThreads) void k_bact(BActArgs a) {
     for (int r = 0; r < kBActU; ++r) {
       const int c = a.klist[q0 + min(r, nq - 1)];
       ux[r] = c / I;
-      const uint16_t* row = a.w3 + (size_t)a.krow[q0 + min(r, nq - 1)] * 3 * H;
+      const uint16_t* row = a.w3 + (size_t)a.krow[q0 + min(r, nq - 1)] * 3 * H;  // BF16 rows
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
@@ -699,7 +699,8 @@ hipError_t launch_shared_select(const cfr_reader& r, const float* x, const int32
   BTopkArgs t{W.bscore, W.meta, W.ghist, W.klist, W.krow, W.kflag, c.inter, k};
   k_btopk<<<1, kTopkThreads, 0, st>>>(t);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  BActArgs ba{x, ids, gw, r.w3, r.b, r.norms, W.acc, W.klist, W.krow, W.kflag, W.coef, W.zpart, r.status,
+  const uint16_t* w3 = reinterpret_cast<const uint16_t*>(r.w3);  // BF16 rows (the API refuses 4-bit ones)
+  BActArgs ba{x, ids, gw, w3, r.b, r.norms, W.acc, W.klist, W.krow, W.kflag, W.coef, W.zpart, r.status,
               c.hidden, c.n_experts, c.inter, c.top, batch, n, r.ncp, k, c.rank, p.Ga, p.Z};
   const size_t lds = sizeof(float) * (size_t)batch * c.hidden;
   switch (p.nch) {
@@ -709,7 +710,7 @@ hipError_t launch_shared_select(const cfr_reader& r, const float* x, const int32
     default: e = launch_bact_t<8>(ba, lds, st); break;
   }
   if (e != hipSuccess) return e;
-  BDownArgs bd{r.w3, W.krow, W.meta, W.coef, W.ypart, c.hidden, c.inter, batch, k, p.G, p.qc, p.nhs};
+  BDownArgs bd{w3, W.krow, W.meta, W.coef, W.ypart, c.hidden, c.inter, batch, k, p.G, p.qc, p.nhs};
   k_bdown<<<p.G * p.nhs, kBDownThreads, 0, st>>>(bd);
   return hipGetLastError();
 }

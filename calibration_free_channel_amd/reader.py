@@ -32,11 +32,12 @@ class Config:
     device: int = 0
     rot_seed: int = DEFAULT_ROT_SEED
     ranking: int = RANK_SCORE
+    exact_bits: int = 16  # 16: native BF16 exact rows; 4: a 4-bit checkpoint (Reader.build_q4)
 
     def c(self) -> CfrConfig:
         return CfrConfig(self.hidden, self.n_experts, self.inter, self.top, self.rank,
                          self.n_screen, self.max_batch, self.device, self.rot_seed & (2 ** 64 - 1),
-                         self.ranking)
+                         self.ranking, self.exact_bits)
 
 
 def sizes(cfg: Config) -> dict:
@@ -151,6 +152,23 @@ class Reader:
         h = ctypes.c_void_p()
         check(load().cfr_build_reader(ctypes.byref(cfg.c()), _ptr(gate), _ptr(up), _ptr(down),
                                       _ptr(router), ctypes.byref(h)))
+        return cls(h, cfg)
+
+    @classmethod
+    def build_q4(cls, cfg: Config, rows, router=None) -> "Reader":
+        """A reader over a 4-bit checkpoint: rows uint8 [E][I][3][R], each
+        channel's gate row, up row and down column as 4-bit row records of
+        R = roundup(H/2 + 3 H/128, 16) bytes (codes, fp16 group scales, zero
+        points; cfr_build_reader_q4).  cfg.exact_bits must be 4."""
+        E, I, H = cfg.n_experts, cfg.inter, cfg.hidden
+        R = -(-(H // 2 + 3 * (H // 128)) // 16) * 16
+        rows = np.ascontiguousarray(rows)
+        if rows.dtype != np.uint8 or rows.shape != (E, I, 3, R):
+            raise ValueError(f"rows: expected uint8 of shape {(E, I, 3, R)}, got {rows.dtype} {rows.shape}")
+        if router is not None:
+            router = _u16(router, (E, H), "router")
+        h = ctypes.c_void_p()
+        check(load().cfr_build_reader_q4(ctypes.byref(cfg.c()), _ptr(rows), _ptr(router), ctypes.byref(h)))
         return cls(h, cfg)
 
     def clone(self) -> "Reader":

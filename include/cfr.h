@@ -70,6 +70,11 @@ typedef struct cfr_config {
                        *     of the expected squared output error of skipping j,
                        *     with Var[a_j] from the stored rho_b and the block
                        *     norms of x (budgets from 28.7% on).                  */
+  int32_t exact_bits; /* format of the resident exact rows: 16 (or 0) for the native
+                       * BF16 rows given to cfr_build_reader; 4 for a 4-bit
+                       * checkpoint given to cfr_build_reader_q4 (the pages run the
+                       * reader over a GPTQ 4-bit checkpoint, [zh §独立分析的弱点]
+                       * item (2)); 4-bit readers rank by the output-unit score.  */
 } cfr_config;
 
 #define CFR_RANK_SCORE 0
@@ -163,6 +168,28 @@ int cfr_read_bytes_shared(const cfr_config* cfg, int32_t batch, const int32_t* e
  */
 int cfr_build_reader(const cfr_config* cfg, const uint16_t* gate, const uint16_t* up,
                      const uint16_t* down, const uint16_t* router, cfr_reader** out);
+
+/*
+ * Builds a reader over a 4-bit checkpoint of the routed experts (the pages
+ * run the reader over a GPTQ 4-bit checkpoint with the sketch unchanged,
+ * [zh §独立分析的弱点] item (2)).  cfg->exact_bits must be 4.
+ *   rows    uint8 [E][I][3][R] host, read only during the call: for each
+ *           channel j of expert e its gate row g_j, up row v_j and down
+ *           column d_j (over the H hidden units) as row records of
+ *           R = roundup(H/2 + 3 H/128, 16) bytes: H/2 bytes of 4-bit codes
+ *           (weight h in byte h/2, even h in the low nibble), then H/128
+ *           fp16 group scales, then H/128 zero points (bytes, 0..15),
+ *           then zero padding; weight h = scale_g (q_h - zero_g), g = h/128.
+ *   router  bf16 [E][H] host or NULL, as for cfr_build_reader.
+ * The sketch, the down norms and the recovery basis are built from the
+ * dequantized weights (load steps (1)-(3)); the records themselves are the
+ * resident exact rows, which the decode and the dense block dequantize as
+ * they read them.  Errors: CFR_EINVAL for a zero point above 15 or a
+ * non-finite scale, otherwise as cfr_build_reader.  The batch-shared decode
+ * refuses 4-bit readers (CFR_EUNSUPPORTED).
+ */
+int cfr_build_reader_q4(const cfr_config* cfg, const uint8_t* rows, const uint16_t* router,
+                        cfr_reader** out);
 
 /*
  * Decode one batch ([zh §方法步骤详情] decode steps (1)-(4); [zh §核心方法];

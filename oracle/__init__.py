@@ -20,7 +20,7 @@ Citation legend used in this package:
 
 Parity status per function (what pins it) is listed in each module header.
 """
-from .numerics import bf16_to_f64, f64_to_f16_bits, f16_bits_to_f64
+from .numerics import bf16_to_f64, weights_f64, f64_to_f16_bits, f16_bits_to_f64
 from .rotation import (splitmix64_stream, sign_vector, sylvester_hadamard,
                        rotate_rows, rotate_x_f64,
                        rotation_matrix, SQRT128)
@@ -37,7 +37,7 @@ from .shared import decode_shared
 
 __all__ = [
     "decode_shared",
-    "bf16_to_f64", "f64_to_f16_bits", "f16_bits_to_f64", "splitmix64_stream",
+    "bf16_to_f64", "weights_f64", "f64_to_f16_bits", "f16_bits_to_f64", "splitmix64_stream",
     "sign_vector", "sylvester_hadamard", "rotate_rows", "rotate_x_f64",
     "rotation_matrix", "SQRT128", "ternarize_blocks",
     "unit_geometry", "pack_units", "unpack_units", "recovery_basis", "dense_moe",

@@ -13,7 +13,7 @@ per-channel decode at k = all channels equals this function on random data.
 """
 import numpy as np
 
-from .numerics import bf16_to_f64
+from .numerics import weights_f64
 
 
 def silu(z):
@@ -25,7 +25,7 @@ def dense_moe(gate_bits, up_bits, down_bits, x, ids, w):
     x = np.asarray(x, dtype=np.float64)
     y = np.zeros(x.shape[-1])
     for e, ws in zip(np.asarray(ids).tolist(), np.asarray(w, dtype=np.float64).tolist()):
-        g = bf16_to_f64(gate_bits[e]) @ x
-        v = bf16_to_f64(up_bits[e]) @ x
-        y += ws * (bf16_to_f64(down_bits[e]) @ (silu(g) * v))
+        g = weights_f64(gate_bits[e]) @ x
+        v = weights_f64(up_bits[e]) @ x
+        y += ws * (weights_f64(down_bits[e]) @ (silu(g) * v))
     return y

@@ -20,7 +20,7 @@ equals the exact skipped contribution.
 import numpy as np
 from scipy.linalg.blas import dsyrk
 
-from .numerics import bf16_to_f64
+from .numerics import weights_f64
 
 
 def recovery_basis(down_bits: np.ndarray, rank: int):
@@ -30,12 +30,12 @@ def recovery_basis(down_bits: np.ndarray, rank: int):
     # products as D_e @ D_e.T, half of them)
     gram = np.zeros((h, h), order="F")
     for ex in range(e):
-        d = bf16_to_f64(down_bits[ex])  # [H][I]
+        d = weights_f64(down_bits[ex])  # [H][I]
         gram = dsyrk(1.0, d, beta=1.0, c=gram, overwrite_c=True)
     vals, vecs = np.linalg.eigh(gram, UPLO="U")
     order = np.argsort(-vals, kind="stable")[:rank]
     u = vecs[:, order]
     b = np.empty((e, i, rank))
     for ex in range(e):
-        b[ex] = (u.T @ bf16_to_f64(down_bits[ex])).T
+        b[ex] = (u.T @ weights_f64(down_bits[ex])).T
     return u, b

@@ -18,6 +18,14 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def weights_f64(w: np.ndarray) -> np.ndarray:
+    """Weights as float64: BF16 bit patterns (uint16) decoded exactly, or
+    real-valued weights (a dequantized 4-bit checkpoint, oracle/int4.py)
+    taken as they are."""
+    w = np.asarray(w)
+    return bf16_to_f64(w) if w.dtype == np.uint16 else w.astype(np.float64)
+
+
 def f64_to_f16_bits(a) -> np.ndarray:
     """Round float64 to IEEE binary16, nearest-even, in a single rounding."""
     with np.errstate(over="ignore"):

@@ -54,7 +54,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .numerics import bf16_to_f64, f64_to_f16_bits, f16_bits_to_f64
+from .numerics import weights_f64, f64_to_f16_bits, f16_bits_to_f64
 from .rotation import sign_vector, rotate_rows, rotate_x_f64
 from .sketch import ternarize_blocks, pack_units
 from .lowrank import recovery_basis
@@ -101,7 +101,7 @@ class OracleReader:
         def sketch_expert(i):
             e = int(self.experts[i])
             for m, w in enumerate((gate, up)):
-                u = rotate_rows(bf16_to_f64(w[e]), self.sigma, block)  # [I][nb][128]
+                u = rotate_rows(weights_f64(w[e]), self.sigma, block)  # [I][nb][128]
                 c, a, r = ternarize_blocks(u)
                 self.codes[i, m] = c.transpose(1, 2, 0)
                 self.alpha_bits[i, :, m, :] = a.T
@@ -120,7 +120,7 @@ class OracleReader:
         # load step (2): down-column norms, summed over h in index order
         self.norms = np.empty((nE, I), dtype=np.float32)
         for i0 in range(0, nE, 16):
-            d = bf16_to_f64(down[self.experts[i0:i0 + 16]])  # [e][H][I]
+            d = weights_f64(down[self.experts[i0:i0 + 16]])  # [e][H][I]
             acc = np.zeros((d.shape[0], I))
             for h in range(hidden):
                 acc = acc + d[:, h, :] * d[:, h, :]
@@ -205,10 +205,10 @@ class OracleReader:
         slot, j = np.divmod(kk, I)
         e = ids[slot]
         # decode step (3): exact kept channels from native rows
-        g = bf16_to_f64(self.gate[e, j]) @ x64
-        v = bf16_to_f64(self.up[e, j]) @ x64
+        g = weights_f64(self.gate[e, j]) @ x64
+        v = weights_f64(self.up[e, j]) @ x64
         a = silu(g) * v
-        dcols = bf16_to_f64(self.down[e, :, j])  # [k][H]
+        dcols = weights_f64(self.down[e, :, j])  # [k][H]
         y_exact = (w[slot] * a) @ dcols if kk.size else np.zeros(H)
         # decode step (4): recovery of skipped channels
         sk = np.nonzero(~mask)[0]

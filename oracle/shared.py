@@ -34,7 +34,7 @@ all k-subsets on a tiny batch maximises the summed batch score.
 import numpy as np
 
 from .dense import silu
-from .numerics import bf16_to_f64
+from .numerics import weights_f64
 from .topk import topk_desc
 
 
@@ -82,8 +82,8 @@ def decode_shared(oracle, X, IDS, W, k, kept=None):
             km = kmask[uix[e]]
             j = np.nonzero(km)[0]
             if j.size:
-                a = silu(bf16_to_f64(oracle.gate[e, j]) @ x64) * (bf16_to_f64(oracle.up[e, j]) @ x64)
-                y_exact = y_exact + (W[t, s] * a) @ bf16_to_f64(oracle.down[e][:, j]).T
+                a = silu(weights_f64(oracle.gate[e, j]) @ x64) * (weights_f64(oracle.up[e, j]) @ x64)
+                y_exact = y_exact + (W[t, s] * a) @ weights_f64(oracle.down[e][:, j]).T
             sk = np.nonzero(~km)[0]
             if sk.size:
                 z = z + (W[t, s] * P[t][s][sk]) @ oracle.b[e, sk]

@@ -34,7 +34,8 @@ import numpy as np
 
 __all__ = [
     "LayerShape", "Workload", "WORKLOADS", "workload", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "make_layer", "make_tokens", "make_routing_inputs",
+    "bf16_bits_to_f32", "make_layer", "make_layer_q4", "q4_row_bytes", "make_tokens",
+    "make_routing_inputs",
 ]
 
 
@@ -201,6 +202,49 @@ def make_layer(wl: Workload, layer: int = 0) -> dict:
     down = _normal_bf16(seed, _STREAM_DOWN, (s.n_experts, s.hidden, s.inter), wl.w_std)
     router = _normal_bf16(seed, _STREAM_ROUTER, (s.n_experts, s.hidden), wl.w_std)
     return {"gate": gate, "up": up, "down": down, "router": router}
+
+
+def q4_row_bytes(hidden: int) -> int:
+    """Bytes of one 4-bit row record of `hidden` weights (see make_layer_q4)."""
+    return -(-(hidden // 2 + 3 * (hidden // 128)) // 16) * 16
+
+
+def _quantize_rows_q4(rows: np.ndarray, group: int = 128) -> np.ndarray:
+    """Round-to-nearest asymmetric 4-bit quantisation of float32 rows [n][H],
+    one fp16 scale and one zero point per group of 128: scale = (max - min)
+    / 15 rounded to fp16 (1 when a group is constant), zero = round(-min /
+    scale) clamped to 0..15, q = round(w / scale) + zero clamped to 0..15.
+    Returns the row records [n][q4_row_bytes(H)] (codes two per byte, even
+    index in the low nibble; then the fp16 scales; then the zero points)."""
+    n, H = rows.shape
+    g = rows.reshape(n, H // group, group).astype(np.float32)
+    mn, mx = g.min(axis=2), g.max(axis=2)
+    scale = ((mx - mn) / np.float32(15)).astype(np.float16)
+    scale[scale == 0] = np.float16(1)
+    sc = scale.astype(np.float32)
+    zero = np.clip(np.rint(-mn / sc), 0, 15).astype(np.uint8)
+    q = np.clip(np.rint(g / sc[..., None]) + zero[..., None], 0, 15).astype(np.uint8).reshape(n, H)
+    rec = np.zeros((n, q4_row_bytes(H)), dtype=np.uint8)
+    rec[:, :H // 2] = q[:, 0::2] | (q[:, 1::2] << 4)
+    rec[:, H // 2:H // 2 + 2 * (H // group)] = scale.view(np.uint8).reshape(n, -1)
+    rec[:, H // 2 + 2 * (H // group):H // 2 + 3 * (H // group)] = zero
+    return rec
+
+
+def make_layer_q4(wl: Workload, layer: int = 0) -> dict:
+    """A synthetic 4-bit (GPTQ-like storage) checkpoint of the layer
+    make_layer draws: every channel's gate row, up row and down column
+    (over the hidden units) quantised per group of 128 hidden units
+    (_quantize_rows_q4).  Returns {"rows": uint8 [E][I][3][q4_row_bytes(H)]
+    (gate, up, down record of each channel), "router": bf16 [E][H]}."""
+    L = make_layer(wl, layer)
+    s = wl.shape
+    rows = np.empty((s.n_experts, s.inter, 3, q4_row_bytes(s.hidden)), dtype=np.uint8)
+    for e in range(s.n_experts):
+        rows[e, :, 0] = _quantize_rows_q4(bf16_bits_to_f32(L["gate"][e]))
+        rows[e, :, 1] = _quantize_rows_q4(bf16_bits_to_f32(L["up"][e]))
+        rows[e, :, 2] = _quantize_rows_q4(np.ascontiguousarray(bf16_bits_to_f32(L["down"][e]).T))
+    return {"rows": rows, "router": L["router"]}
 
 
 def make_tokens(wl: Workload, n: int | None = None, seed_offset: int = 0) -> np.ndarray:

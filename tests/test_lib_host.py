@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _declared_symbols():
     txt = open(os.path.join(ROOT, "include", "cfr.h")).read()
-    return sorted(set(re.findall(r"^(?:int|void|const char\*)\s+(cfr_[a-z_]+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^(?:int|void|const char\*)\s+(cfr_[a-z0-9_]+)\s*\(", txt, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -136,3 +136,23 @@ def test_host_pack_bit_exact_qwen3_30b_shape_subset():
 @pytest.mark.slow
 def test_host_pack_bit_exact_qwen3_235b_shape_subset():
     _compare_pack(workload("qwen3-235b-a22b"), n_experts=2)
+
+
+def test_exact_bits_rules_and_4bit_accounting():
+    from calibration_free_channel_amd import Config, RANK_EXPECTED_ERROR, read_bytes
+    from calibration_free_channel_amd._lib import CfrError
+    base = dict(hidden=2048, n_experts=128, inter=768, top=8)
+    with pytest.raises(CfrError):
+        read_bytes(Config(**base, exact_bits=8), 10)
+    with pytest.raises(CfrError):
+        read_bytes(Config(**base, exact_bits=4, n_screen=128, ranking=RANK_EXPECTED_ERROR), 10)
+    b16 = read_bytes(Config(**base), 756)
+    b4 = read_bytes(Config(**base, exact_bits=4), 756)
+    # a 4-bit row of 2048 weights: 1024 code bytes, 16 fp16 scales, 16 zero
+    # points (1072 bytes); a kept channel's three rows, 3216 bytes, touch 101
+    # 32-byte sectors
+    assert b4["exact"] == 756 * 3232
+    assert b4["dense"] == 8 * 3 * 768 * 1072
+    for f in ("codes", "scales", "norms", "b", "u"):
+        assert b4[f] == b16[f]
+    assert read_bytes(Config(**base, exact_bits=0), 756) == b16
