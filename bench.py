@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--leg", choices=["k756", "k445", "dense", "b4", "shared4", "high", "c5", "q4"],
+                    help="time one leg only and print its figures (profiling runs: one configuration "
+                         "per counter pass)")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="summarise rocprofv3 CSV output under DIR as text and exit")
     ap.add_argument("--stack", action="store_true",
@@ -123,6 +126,13 @@ def profile_summary(d):
         name = name.replace("(anonymous namespace)::", "").replace("cfr::", "")
         return name.split("(")[0]
 
+    names = {"k_screen": "screen", "k_select": "select", "k_reduce": "reduce", "k_dense": "dense",
+             "k_bscore": "bscore", "k_btopk": "btopk", "k_bact": "bact", "k_bdown": "bdown",
+             "k_route": "route"}
+
+    def ours(k):  # the decode-time kernels of the library
+        return k.split("<")[0].split()[-1] in names
+
     lines = []
     traffic = {}
     for f in sorted(set(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))):
@@ -130,6 +140,8 @@ def profile_summary(d):
         lines.append(f"{'kernel':<44} {'calls':>7} {'avg us':>9} {'min us':>9} {'max us':>9} {'% time':>7}")
         with open(f) as fh:
             for r in csv.DictReader(fh):
+                if not ours(short(r["Name"])):
+                    continue
                 lines.append(f"{short(r['Name'])[:44]:<44} {int(r['Calls']):>7} "
                              f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['MinNs']) / 1e3:>9.2f} "
                              f"{float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>7.2f}")
@@ -137,29 +149,35 @@ def profile_summary(d):
         acc = {}
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                key = (short(r["Kernel_Name"]), r["Counter_Name"])
-                a = acc.setdefault(key, [0.0, 0, r["Grid_Size"]])
+                key = (short(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])
+                a = acc.setdefault(key, [0.0, 0])
                 a[0] += float(r["Counter_Value"])
                 a[1] += 1
         lines.append(f"counters: {os.path.relpath(f, d)} (average per dispatch; FETCH_SIZE and "
-                     "WRITE_SIZE in KiB)")
-        for (k, c), (tot, n, grid) in sorted(acc.items()):
-            lines.append(f"  {k[:44]:<44} {c:<12} dispatches {n:>6}  avg {tot / n:>14.1f}")
+                     "WRITE_SIZE in KiB; one line per kernel and grid size in threads)")
+        for (k, g, c), (tot, n) in sorted(acc.items()):
+            if ours(k):
+                lines.append(f"  {k[:44]:<44} grid {g:>8} {c:<12} dispatches {n:>6}  avg {tot / n:>14.1f}")
         # the copy reference is the largest elementwise kernel of the run
-        copy = [(k, c, tot / n) for (k, c), (tot, n, _) in acc.items()
+        copy = [(k, c, tot / n) for (k, g, c), (tot, n) in acc.items()
                 if "elementwise" in k.lower() and tot / n > 0.25 * (COPY_BYTES >> 10)]
         for k, c, v in copy:
-            bytes_kib = v
-            ratio = bytes_kib * 1024 / COPY_BYTES
+            ratio = v * 1024 / COPY_BYTES
             scale = 1 / ratio if ratio else float("nan")
-            lines.append(f"  copy reference {k[:40]} {c}: {bytes_kib:.0f} KiB for {COPY_BYTES >> 10} KiB "
+            lines.append(f"  copy reference {k[:40]} {c}: {v:.0f} KiB for {COPY_BYTES >> 10} KiB "
                          f"moved -> scale {scale:.4f}")
             traffic[c + "_scale"] = round(scale, 4)
-        for (k, c), (tot, n, _) in acc.items():
-            name = {"k_screen": "screen", "k_select": "select", "k_reduce": "reduce"}.get(k.split("<")[0].split()[-1])
-            if name:
-                traffic.setdefault("kernels", {}).setdefault(name, {})[
-                    "fetch_kib" if c == "FETCH_SIZE" else "write_kib"] = round(tot / n, 1)
+        best = {}
+        for (k, g, c), (tot, n) in acc.items():
+            name = names.get(k.split("<")[0].split()[-1])
+            if not name:
+                continue
+            ent = traffic.setdefault("kernels", {}).setdefault(name, {})
+            # the grid launched most often stands for the kernel
+            if best.get((name, c), (0, 0))[0] < n:
+                best[(name, c)] = (n, g)
+                ent["grid"] = g
+                ent["fetch_kib" if c == "FETCH_SIZE" else "write_kib"] = round(tot / n, 1)
     print("\n".join(lines))
     traffic = {"source_sha256": source_digest(),
                "fetch_scale": traffic.get("FETCH_SIZE_scale"), "write_scale": traffic.get("WRITE_SIZE_scale"),
@@ -296,13 +314,20 @@ def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen3-30b-a3b_k756.json")
-KERNEL_SOURCE = os.path.join(ROOT, "calibration_free_channel_amd", "csrc", "decode_kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "calibration_free_channel_amd", "csrc")
 
 
 def source_digest():
+    """SHA-256 over the device sources (every .hip and .h of the library, by
+    name), so that counters taken on other kernels are not used."""
+    import glob
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(KERNEL_DIR, "*.hip")) + glob.glob(os.path.join(KERNEL_DIR, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def traffic_bytes(kernel):
@@ -540,8 +565,14 @@ def main():
     IDS = torch.from_numpy(IDh.reshape(L, 1, s.top)).cuda()
     W = torch.from_numpy(Wh.reshape(L, 1, s.top)).cuda()
 
+    def on(name):  # this leg runs: every leg by default, else the one asked for
+        return args.leg is None or args.leg == name
+
+    full = args.leg is None and not args.main_budget_only
     res = {}
-    for k in [k_main] + ([k_low] if k_low and not args.main_budget_only else []):
+    ks = ([k_main] if on("k756") else []) + \
+        ([k_low] if k_low and ((args.leg is None and not args.main_budget_only) or args.leg == "k445") else [])
+    for k in ks:
         spread = {}
         us, nsteps, nwarm = graph_time(torch, readers, X, IDS, W, k, args.steps, args.warmup, spread=spread)
         rb = read_bytes(cfg, k)
@@ -550,7 +581,7 @@ def main():
         log(f"k={k}: {us:.2f} us/token, {rb['total'] / us / 1e3:.1f} GB/s counted; stages "
             + ", ".join(f"{n}={v:.1f}" for n, v in stages.items()))
     dense_us = None
-    if not args.no_dense:
+    if not args.no_dense and on("dense"):
         dense_us, _, _ = graph_time(torch, readers, X, IDS, W, 0, min(args.steps, 400),
                                     args.warmup, fn="dense")
         log(f"dense BF16 block: {dense_us:.2f} us/token")
@@ -559,7 +590,7 @@ def main():
     # pre-norm), decode the normed token with the residual added in the
     # decode's last kernel; the dense block the same way; the routing alone
     layer_step = {}
-    if not args.main_budget_only:
+    if full:
         IDr = torch.empty_like(IDS)
         Wr = torch.empty_like(W)
         Xr = X.clone()  # the residual stream, carried on over the replays
@@ -574,24 +605,24 @@ def main():
     # batch 4 (per-token routing and top-k), the configuration's batched case:
     # µs per token = µs per call / 4
     batch4 = {}
-    if not args.main_budget_only:
+    if full or args.leg in ("b4", "shared4"):
         X4 = torch.from_numpy(make_tokens(wl, 4 * L, seed_offset=7).reshape(L, 4, s.hidden)).cuda()
         I4h, W4h = make_routing_inputs(wl, 4 * L, seed_offset=7)
         I4 = torch.from_numpy(I4h.reshape(L, 4, s.top)).cuda()
         W4 = torch.from_numpy(W4h.reshape(L, 4, s.top)).cuda()
-        for k in [k_main] + ([k_low] if k_low else []):
+        for k in ([k_main] + ([k_low] if k_low else [])) if args.leg != "shared4" else []:
             us4, _, _ = graph_time(torch, readers, X4, I4, W4, k, min(args.steps, 400), args.warmup)
             batch4[f"k={k}"] = round(us4 / 4, 3)
             dbg = {n: v.cpu().numpy() for n, v in readers[0].decode_debug(X4[0], I4[0], W4[0], k).items()}
             ub4 = read_bytes_batch(cfg, I4[0].cpu().numpy(), dbg["sel"], dbg["kept"], k)["total"]
             batch4[f"k={k}_union_GBps"] = round(ub4 / us4 / 1e3, 1)
-        if not args.no_dense:
+        if not args.no_dense and args.leg != "shared4":
             us4, _, _ = graph_time(torch, readers, X4, I4, W4, 0, min(args.steps, 400), args.warmup,
                                    fn="dense")
             batch4["dense"] = round(us4 / 4, 3)
         # batch-shared selection: one top-k per call over the call's distinct
         # experts, at the per-token budget's share of the union
-        for k in [k_main] + ([k_low] if k_low else []):
+        for k in ([k_main] + ([k_low] if k_low else [])) if args.leg != "b4" else []:
             sh = shared_leg(torch, cfg, readers, X4, I4, W4, I4h.reshape(L, 4, s.top), k, s, args)
             batch4[f"shared_k={k}"] = sh
         log("batch 4, us/token: " + ", ".join(f"{n}={v}" for n, v in batch4.items()))
@@ -599,7 +630,7 @@ def main():
     # 28.7% and up: the whole sketch with the expected-error ranking, on copies
     # of a reader built for it (the resident bytes are the same layout)
     high = None
-    if not args.main_budget_only and not args.no_high_budget:
+    if (full and not args.no_high_budget) or args.leg == "high":
         for r in readers[1:]:
             r.close()
         readers = readers[:1]
@@ -624,7 +655,7 @@ def main():
 
     # the Qwen3-235B-A22B-shaped layer at batch 8 (per-token routing and top-k)
     c5 = None
-    if not args.main_budget_only and not args.no_c5:
+    if (full and not args.no_c5) or args.leg == "c5":
         for r in readers[1:]:
             r.close()
         readers = readers[:1]
@@ -673,7 +704,7 @@ def main():
     # unchanged): the reader at k = 756 and at the k whose counted reads are
     # 18.9% of the BF16 routed bytes, beside the 4-bit dense block
     q4 = None
-    if not args.main_budget_only and not args.no_q4:
+    if (full and not args.no_q4) or args.leg == "q4":
         for r in readers[1:]:
             r.close()
         readers = readers[:1]
@@ -709,7 +740,7 @@ def main():
 
     # the 48-layer stack (independent weights per layer) as one batch-1 step
     stack = None
-    if not args.main_budget_only and not args.no_stack:
+    if full and not args.no_stack:
         for r in readers[1:]:
             r.close()
         readers = readers[:1]
@@ -722,6 +753,16 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         log(f"copy calibration: {COPY_BYTES >> 20} MiB read and written 4 times")
+    if args.leg is not None:
+        figures = {"k756": res, "k445": res, "dense": dense_us, "b4": batch4, "shared4": batch4,
+                   "high": high, "c5": c5, "q4": q4}[args.leg]
+        if args.leg in ("k756", "k445"):
+            figures = {f"k={kk}": {"us_per_token": round(r["us"], 3), "stages_us": r["stages"]}
+                       for kk, r in res.items()}
+        print(json.dumps({"leg": args.leg, "figures": figures}), flush=True)
+        for r in readers:
+            r.close()
+        return
 
     main_r = res[k_main]
     rb = main_r["bytes"]
@@ -738,7 +779,7 @@ def main():
     path_gbps = rb["total"] / main_r["us"] / 1e3
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.leg is None:
         cpu = cpu_baseline(wl, layer, Xh, IDh.reshape(L, 1, s.top), Wh.reshape(L, 1, s.top),
                            [k_main] + ([k_low] if k_low else []), args.cpu_seconds)
         log(f"cpu baseline: {cpu['by_k']} us/token on {cpu['cores']} threads ({cpu['cpu_model']})"
