@@ -277,7 +277,7 @@ def stage_times(torch, readers, X, IDS, W, k, steps, warmup):
     select (which only reads them) and the reduce (which clears them)."""
     L = len(readers)
     s = torch.cuda.Stream()
-    Y = torch.empty((L, 1, X.shape[-1]), dtype=torch.float32, device=X.device)
+    Y = torch.empty((L, X.shape[1], X.shape[-1]), dtype=torch.float32, device=X.device)
 
     def one_pass(stage):
         for i, r in enumerate(readers):
@@ -616,6 +616,9 @@ def main():
             dbg = {n: v.cpu().numpy() for n, v in readers[0].decode_debug(X4[0], I4[0], W4[0], k).items()}
             ub4 = read_bytes_batch(cfg, I4[0].cpu().numpy(), dbg["sel"], dbg["kept"], k)["total"]
             batch4[f"k={k}_union_GBps"] = round(ub4 / us4 / 1e3, 1)
+            batch4[f"k={k}_stages_us_per_call"] = {
+                n: round(v, 2) for n, v in stage_times(torch, readers, X4, I4, W4, k, min(args.steps, 400),
+                                                       args.warmup).items()}
         if not args.no_dense and args.leg != "shared4":
             us4, _, _ = graph_time(torch, readers, X4, I4, W4, 0, min(args.steps, 400), args.warmup,
                                    fn="dense")
@@ -678,6 +681,7 @@ def main():
         W5 = torch.from_numpy(g5.reshape(L5, 8, s5.top).astype(np.float32)).cuda()
         k5 = w5.ks[0]
         us5, _, _ = graph_time(torch, r5, X5, I5, W5, k5, min(args.steps, 200), args.warmup)
+        st5 = stage_times(torch, r5, X5, I5, W5, k5, min(args.steps, 200), args.warmup)
         ud5 = None
         if not args.no_dense:
             ud5, _, _ = graph_time(torch, r5, X5, I5, W5, 0, min(args.steps, 200), args.warmup, fn="dense")
@@ -687,6 +691,7 @@ def main():
         ub5 = read_bytes_batch(cfg5, I5[0].cpu().numpy(), dbg["sel"], dbg["kept"], k5)["total"]
         c5 = {"k": k5, "batch": 8, "us_per_token": round(us5 / 8, 3),
               "union_bytes_per_call": ub5, "union_GBps": round(ub5 / us5 / 1e3, 1),
+              "stages_us_per_call": {n: round(v, 2) for n, v in st5.items()},
               "read_pct_of_dense": round(100.0 * rb5["total"] / rb5["dense"], 2),
               # per-token counted bytes summed over the batch (experts routed by
               # several tokens are counted once per token: an upper bound on the

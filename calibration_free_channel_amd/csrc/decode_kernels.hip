@@ -5,16 +5,19 @@
 // Selection for Mixture-of-Experts Decoding Needs No Calibration Data"), three
 // kernels; a kernel boundary is the only grid-wide synchronisation:
 //
-//   1 k_screen   one workgroup per (token, routed slot, 128-block, half):
-//                rotate the block of x (float32 butterfly of H_128 sigma x),
-//                pick its n_screen coordinates of largest |value| (ties to the
-//                lower index), read the whole half-units of those coordinates
-//                (coalesced: every sketch byte is fetched by exactly one
-//                workgroup), decode the base-3 codes through an LDS table and
-//                add alpha_b * sum_i c_i x_i for every channel of the half into
-//                a 64-bit fixed-point accumulator.  Integer addition is
-//                associative, so the sum over blocks is bit-reproducible
-//                whatever the order the workgroups finish in.
+//   1 k_screen   one workgroup per (token, routed slot, group of bg
+//                128-blocks, half): rotate each block of x (float32
+//                butterfly of H_128 sigma x), pick its n_screen coordinates of
+//                largest |value| (ties to the lower index), read the whole
+//                half-units of those coordinates (coalesced: every sketch
+//                byte is fetched by exactly one workgroup), decode the base-3
+//                codes through an LDS table of digits and add
+//                sum_b alpha_b sum_i c_i x_i over the group's blocks for every
+//                channel of the half into a 64-bit fixed-point accumulator.
+//                Integer addition is associative, so the sum over groups is
+//                bit-reproducible whatever the order the workgroups finish in.
+//                bg = 1 at batch 1 (most workgroups, shortest chains); at
+//                larger batches groups of 2-8 blocks cut the atomics.
 //   2 k_select   per token, G gather workgroups and Z recovery workgroups.
 //                Each finalises g_hat, v_hat, p = silu(g_hat) v_hat and the
 //                output-unit score s = w ||d|| |p| of every candidate,
@@ -162,31 +165,39 @@ __device__ __forceinline__ void rotate_select(float v0, float v1, int NS, int un
 // sum_b rho_b ||x_b||^2 (times ||d_j||^2 for the up half: the variance of
 // v_hat'), every term from stored values, so no accumulation across
 // workgroups is needed.
-template <int NT, int NG, int CPB, bool VAR>
+template <int NT, int NG, int CPB, bool VAR, int BG, int BC>
 __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   static_assert(NG >= 1 && NG <= 16 && (NG & (NG - 1)) == 0, "word groups within a row of lanes");
-  __shared__ uint4 lut[256];
-  __shared__ int2 rec[128];
+  static_assert(BG == 1 || (!VAR && BG <= NT / 64), "block groups: score ranking, one wave per block");
+  static_assert(BG % BC == 0 && (BG > 1 || BC == 1), "blocks of a group in whole chunks");
+  __shared__ uint2 lut[256];
+  __shared__ int2 rec[BG][128];
   __shared__ float qn2[VAR ? kMaxHidden / 128 : 1];  // ||x_b||^2 of every block (VAR)
   CFR_TRACE_PHASE(0, 0);
   const int item = xcd_item(blockIdx.x, a.per_xcd);
   if (item >= a.items) return;
+  // a workgroup screens the BG blocks [b, b + nbh) of one half (BG > 1 at
+  // batch sizes where the atomics' count, not latency, bounds the kernel:
+  // the blocks are summed in registers before one atomic per channel)
+  const int nbg = (a.nblk + BG - 1) / BG;
   const int m = item & 1;          // 0 gate, 1 up
   const int rb = item >> 1;
-  const int b = rb % a.nblk;       // block
-  const int ts = rb / a.nblk;      // token * top + slot
+  const int b = (rb % nbg) * BG;   // first block
+  const int nbh = min(BG, a.nblk - b);
+  const int ts = rb / nbg;         // token * top + slot
   const int s = ts % a.top, t = ts / a.top;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wvi = tid >> 6;
   const int H = a.H, I = a.I, NS = a.ns;
-  // token block and signs (wave 0) first: the rotation waits on them; then
-  // the routed expert and everything that depends on it
+  // token block and signs (wave v: block b + v) first: the rotation waits on
+  // them; then the routed expert and everything that depends on it
   float x0 = 0.f, x1 = 0.f, g0 = 0.f, g1 = 0.f;
-  if (tid < 64) {
-    const float* xb = a.x + (size_t)t * H + b * 128;
+  if (wvi < nbh) {
+    const int bb = b + wvi;
+    const float* xb = a.x + (size_t)t * H + bb * 128;
     x0 = xb[lane];
     x1 = xb[lane + 64];
-    g0 = a.sigma[b * 128 + lane];
-    g1 = a.sigma[b * 128 + 64 + lane];
+    g0 = a.sigma[bb * 128 + lane];
+    g1 = a.sigma[bb * 128 + 64 + lane];
   }
   // VAR: the token, four coordinates per thread and chunk, for the block
   // norms (before the loads that wait on the routed expert)
@@ -204,13 +215,17 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   // finalises channels 20d + g + NG r (r < RPL): their scales, loaded now
   constexpr int RPL = (20 + NG - 1) / NG;
   const int d = tid / NG, g = tid & (NG - 1);
-  const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b) * 2 + m) * I;
-  uint16_t al[RPL];
+  // (a block group loads each chunk's scales with its words)
+  auto load_scales = [&](int bi, uint16_t* al) {
+    const uint16_t* sp = a.scales + (((size_t)e * a.nblk + b + bi) * 2 + m) * I;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    const int j = 20 * d + g + NG * r;
-    al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
-  }
+    for (int r = 0; r < RPL; ++r) {
+      const int j = 20 * d + g + NG * r;
+      al[r] = sp[j < I ? j : I - 1];  // unconditional (clamped): no branch waits on it
+    }
+  };
+  uint16_t al[RPL];
+  if constexpr (BG == 1) load_scales(0, al);
   // VAR: this workgroup owns channels [b vper, (b + 1) vper) of the half;
   // thread tid < vper loads channel b vper + tid's rho in every block and
   // ||d_j|| now, as buffer loads that the other threads point past the end
@@ -244,27 +259,26 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
       nrm[r] = a.norms[(size_t)e * I + (j < I ? j : I - 1)];
     }
   }
-  // code table: byte q -> its five codes c_t = digit_t - 1 as fp16 (entries
-  // 243..255 never occur in a packed unit and decode to zero)
+  // code table: byte q -> its five base-3 digits d_t = c_t + 1, one byte each
+  // (entries 243..255 never occur in a packed unit and decode to codes 0)
   if (tid < 256) {
-    uint32_t h[5] = {0u, 0u, 0u, 0u, 0u};
+    uint32_t dg[5] = {1u, 1u, 1u, 1u, 1u};
     if (tid < 243) {
       int q = tid;
 #pragma unroll
       for (int d = 0; d < 5; ++d) {
-        const int dig = q % 3;
+        dg[d] = (uint32_t)(q % 3);
         q /= 3;
-        h[d] = dig == 0 ? 0xBC00u : (dig == 2 ? 0x3C00u : 0u);
       }
     }
-    lut[tid] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u);
+    lut[tid] = make_uint2(dg[0] | (dg[1] << 8) | (dg[2] << 16) | (dg[3] << 24), dg[4]);
   }
   // decode step (1): rotation and the partial-screen coordinates
   const bool writer = a.dbg && s == 0 && m == 0;
-  if (tid < 64) {
-    rotate_select(x0 * g0, x1 * g1, NS, a.unit, rec,
-                  writer ? a.sel + ((size_t)t * a.nblk + b) * NS : nullptr,
-                  writer ? a.xrot + (size_t)t * H + b * 128 : nullptr);
+  if (wvi < nbh) {
+    rotate_select(x0 * g0, x1 * g1, NS, a.unit, rec[wvi],
+                  writer ? a.sel + ((size_t)t * a.nblk + b + wvi) * NS : nullptr,
+                  writer ? a.xrot + (size_t)t * H + (b + wvi) * 128 : nullptr);
   }
   if constexpr (VAR) {
     // ||x_b||^2 of every block: 32 lanes hold one block's 128 coordinates
@@ -295,57 +309,140 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   // g, g + NG, g + 2 NG, ..., all its words in flight together (CPB at a time)
   const int ND = a.nd;
   const bool active = d < ND;
-  float acc[20];
+  const uint32_t col = (uint32_t)(m * a.lp + 4 * d);
+  constexpr int NA = 21;  // sums per thread
+  // thread's codes decoded into its word's 20 channels, x-weighted: the
+  // table gives the digits d = c + 1, so the sums are sum d x and acc[20]
+  // carries sum x, taken off at the end (each digit is one byte-to-float
+  // conversion; measured faster than fp16 codes, whose table reads take
+  // twice the LDS bandwidth, and than digits computed from the byte)
+  auto decode_words = [&](const uint32_t* wq, const float* xq, float* acc) {
 #pragma unroll
-  for (int q = 0; q < 20; ++q) acc[q] = 0.f;
-  if (active) {
-    // uniform base of this (expert, block) and 32-bit per-coordinate offsets
-    const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit;
-    const uint32_t col = (uint32_t)(m * a.lp + 4 * d);
-    for (int c0 = g; c0 < NS; c0 += NG * CPB) {
-      uint32_t wv[CPB];
-      float xv[CPB];
+    for (int u = 0; u < CPB; ++u) {
+      acc[20] += xq[u];
 #pragma unroll
-      for (int u = 0; u < CPB; ++u) {
-        const int c = c0 + u * NG;
-        const int2 rc = rec[c < NS ? c : NS - 1];  // clamped; past the list x = 0
-        wv[u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
-        xv[u] = c < NS ? __int_as_float(rc.y) : 0.f;
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint2 cw = lut[(wq[u] >> (8 * kb)) & 0xFFu];
+        acc[5 * kb + 0] = fmaf((float)(cw.x & 0xFFu), xq[u], acc[5 * kb + 0]);
+        acc[5 * kb + 1] = fmaf((float)((cw.x >> 8) & 0xFFu), xq[u], acc[5 * kb + 1]);
+        acc[5 * kb + 2] = fmaf((float)((cw.x >> 16) & 0xFFu), xq[u], acc[5 * kb + 2]);
+        acc[5 * kb + 3] = fmaf((float)(cw.x >> 24), xq[u], acc[5 * kb + 3]);
+        acc[5 * kb + 4] = fmaf((float)(cw.y & 0xFFu), xq[u], acc[5 * kb + 4]);
       }
+    }
+  };
+  // sum over the NG lanes of each word (register butterfly, every lane ends
+  // with the totals)
+  auto word_sums = [&](float* acc) {
 #pragma unroll
-      for (int u = 0; u < CPB; ++u) {
+    for (int q = 0; q < NA; ++q) {
+      if constexpr (NG > 1) acc[q] += xor_lane_f<1>(acc[q]);
+      if constexpr (NG > 2) acc[q] += xor_lane_f<2>(acc[q]);
+      if constexpr (NG > 4) acc[q] += xor_lane_f<4>(acc[q]);
+      if constexpr (NG > 8) acc[q] += xor_lane_f<8>(acc[q]);
+    }
+  };
+  // lane g's value of its r-th channel 20 d + g + NG r
+  auto lane_value = [&](const float* acc, int r) {
+    float v = acc[(NG * r < 20) ? NG * r : 19];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint4 cw = lut[(wv[u] >> (8 * kb)) & 0xFFu];
-          acc[5 * kb + 0] = fmaf(lo16(cw.x), xv[u], acc[5 * kb + 0]);
-          acc[5 * kb + 1] = fmaf(hi16(cw.x), xv[u], acc[5 * kb + 1]);
-          acc[5 * kb + 2] = fmaf(lo16(cw.y), xv[u], acc[5 * kb + 2]);
-          acc[5 * kb + 3] = fmaf(hi16(cw.y), xv[u], acc[5 * kb + 3]);
-          acc[5 * kb + 4] = fmaf(lo16(cw.z), xv[u], acc[5 * kb + 4]);
+    for (int q = 1; q < NG; ++q)
+      if (NG * r + q < 20) v = g == q ? acc[NG * r + q] : v;
+    v -= acc[20];
+    return v;
+  };
+  // per lane channel: alpha-scaled sum over the workgroup's blocks (the
+  // up half times ||d_j||), before the fixed-point accumulator
+  float tot[RPL];
+  if constexpr (BG == 1) {
+    // screen: thread (d, g) decodes code word d at screened coordinates
+    // g, g + NG, g + 2 NG, ..., all its words in flight together (CPB at a time)
+    float acc[NA];
+#pragma unroll
+    for (int q = 0; q < NA; ++q) acc[q] = 0.f;
+    if (active) {
+      // uniform base of this (expert, block) and 32-bit per-coordinate offsets
+      const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b) * 128 * a.unit;
+      for (int c0 = g; c0 < NS; c0 += NG * CPB) {
+        uint32_t wq[CPB];
+        float xq[CPB];
+#pragma unroll
+        for (int u = 0; u < CPB; ++u) {
+          const int c = c0 + u * NG;
+          const int2 rc = rec[0][c < NS ? c : NS - 1];  // clamped; past the list x = 0
+          wq[u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
+          xq[u] = c < NS ? __int_as_float(rc.y) : 0.f;
+        }
+        decode_words(wq, xq, acc);
+      }
+    }
+    CFR_TRACE_PHASE(0, 2);
+    word_sums(acc);
+    CFR_TRACE_PHASE(0, 3);
+    // Every loaded value is consumed before the first atomic or store: on this
+    // target the in-order memory counter also counts stores and atomics, so a
+    // wait for a load placed after them would wait for them as well.
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      tot[r] = f16f(al[r]) * nrm[r] * lane_value(acc, r);
+      asm volatile("" ::"v"(tot[r]));
+    }
+  } else {
+    // the group's blocks BC at a time (the host picks BG only when one batch
+    // of CPB coordinates covers n_screen), every word of the BC blocks in
+    // flight together; each block's sums scaled by its alpha and added up
+    float sum[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) sum[r] = 0.f;
+    // chunk by chunk: the chunk's words and scales, then its decode (a
+    // prefetch of the next chunk measured slower: the registers it holds
+    // cost a wave per SIMD).  Blocks past a group cut short by nblk re-read
+    // the group's last block and get x = 0, so every load is in bounds and
+    // an active thread issues the same loads on every path (threads past the
+    // half's words skip the whole loop)
+    if (active) {
+#pragma unroll 1
+      for (int i0 = 0; i0 < BG; i0 += BC) {
+        uint32_t wq[BC][CPB];
+        uint16_t aq[BC][RPL];
+#pragma unroll
+        for (int i = 0; i < BC; ++i) {
+          const int bi = min(i0 + i, nbh - 1);
+          const uint8_t* ub = a.codes + ((size_t)e * a.nblk + b + bi) * 128 * a.unit;
+#pragma unroll
+          for (int u = 0; u < CPB; ++u) {
+            const int c = g + u * NG;
+            const int2 rc = rec[bi][c < NS ? c : NS - 1];  // clamped; past the list x = 0
+            wq[i][u] = *reinterpret_cast<const uint32_t*>(ub + ((uint32_t)rc.x + col));
+          }
+          load_scales(bi, aq[i]);
+        }
+        CFR_TRACE_PHASE(0, 2);
+#pragma unroll
+        for (int i = 0; i < BC; ++i) {
+          const int bi = min(i0 + i, nbh - 1);
+          float xq[CPB];
+#pragma unroll
+          for (int u = 0; u < CPB; ++u) {
+            const int c = g + u * NG;
+            xq[u] = (c < NS && i0 + i < nbh) ? __int_as_float(rec[bi][c < NS ? c : NS - 1].y) : 0.f;
+          }
+          float acc[NA];
+#pragma unroll
+          for (int q = 0; q < NA; ++q) acc[q] = 0.f;
+          decode_words(wq[i], xq, acc);
+          word_sums(acc);
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) sum[r] = fmaf(f16f(aq[i][r]), lane_value(acc, r), sum[r]);
         }
       }
     }
-  }
-  CFR_TRACE_PHASE(0, 2);
-  // sum over the NG lanes of each word (register butterfly, every lane ends
-  // with the totals), then lane g scales channel 20d + g + NG r by alpha_b
-  // and adds it to the fixed-point accumulator
+    CFR_TRACE_PHASE(0, 3);
 #pragma unroll
-  for (int q = 0; q < 20; ++q) {
-    if constexpr (NG > 1) acc[q] += xor_lane_f<1>(acc[q]);
-    if constexpr (NG > 2) acc[q] += xor_lane_f<2>(acc[q]);
-    if constexpr (NG > 4) acc[q] += xor_lane_f<4>(acc[q]);
-    if constexpr (NG > 8) acc[q] += xor_lane_f<8>(acc[q]);
-  }
-  CFR_TRACE_PHASE(0, 3);
-  // Every loaded value is consumed before the first atomic or store: on this
-  // target the in-order memory counter also counts stores and atomics, so a
-  // wait for a load placed after them would wait for them as well.
-  float alf[RPL];
-#pragma unroll
-  for (int r = 0; r < RPL; ++r) {
-    alf[r] = f16f(al[r]) * nrm[r];
-    asm volatile("" ::"v"(alf[r]));
+    for (int r = 0; r < RPL; ++r) {
+      tot[r] = nrm[r] * sum[r];
+      asm volatile("" ::"v"(tot[r]));
+    }
   }
   float vsum = 0.f;
   if constexpr (VAR) {
@@ -359,12 +456,8 @@ __global__ __launch_bounds__(NT) void k_screen(ScreenArgs a) {
   if (active) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
-      float v = acc[(NG * r < 20) ? NG * r : 19];
-#pragma unroll
-      for (int q = 1; q < NG; ++q)
-        if (NG * r + q < 20) v = g == q ? acc[NG * r + q] : v;
       const int i = g + NG * r, j = 20 * d + i;
-      if (i < 20 && j < I) atomicAdd(ap + j, to_fix(alf[r] * v));
+      if (i < 20 && j < I) atomicAdd(ap + j, to_fix(tot[r]));
     }
   }
   if constexpr (VAR) {
@@ -1363,7 +1456,18 @@ Plan make_plan(const cfr_config& c, int batch, int k) {
   p.nd = (nbytes + 3) / 4;
   p.ng = 16;  // threads per code word: a power of two with ng * nd <= threads
   while (p.ng > 1 && p.ng * p.nd > kScreenThreads) p.ng /= 2;
-  p.items1 = batch * c.top * nblk * 2;
+  // several blocks per workgroup when the batch makes the screen's atomics
+  // count (the score ranking, one batch of CPB coordinates per thread
+  // covering n_screen; CPB 5, 10, 20 for ng 16, 8, 4): the largest group of
+  // 2, 4 or 8 blocks that leaves kScreenMinWgs workgroups (measured best at
+  // the Qwen3-30B-A3B layer, batch 4, and the Qwen3-235B-A22B layer, batch 8)
+  p.bg = 1;
+  if (batch >= 2 && c.ranking == CFR_RANK_SCORE && p.ng >= 4) {
+    const int cpb = p.ng == 16 ? 5 : (p.ng == 8 ? 10 : 20);
+    if (c.n_screen <= p.ng * cpb)
+      while (p.bg < 8 && batch * c.top * 2 * ((nblk + 2 * p.bg - 1) / (2 * p.bg)) >= kScreenMinWgs) p.bg *= 2;
+  }
+  p.items1 = batch * c.top * ((nblk + p.bg - 1) / p.bg) * 2;
   p.per_xcd1 = (p.items1 + 7) / 8;
   p.lds1 = 0;
   // select/gather: about 240 gather workgroups over the batch plus 16
@@ -1399,7 +1503,10 @@ size_t max_lds_needed(const cfr_config& c) {
   for (int b = 1; b <= c.max_batch; ++b)
     for (int kk : {0, 1, nc / 2, nc}) {
       const Plan p = make_plan(c, b, kk);
-      if (p.lds1 + 8192 > m) m = p.lds1 + 8192;  // + the screen kernel's static LDS
+      // + the screen kernel's static LDS: code table, bg blocks' coordinate
+      // lists, block norms
+      const size_t st1 = 2048 + 1024 * (size_t)p.bg + 4 * (kMaxHidden / 128);
+      if (p.lds1 + st1 > m) m = p.lds1 + st1;
       if (p.lds2 > m) m = p.lds2;
     }
   const DensePlan d = make_dense_plan(c, 1);
@@ -1460,21 +1567,42 @@ static hipError_t launch_select(const SelectArgs& a, const Plan& p, int batch, b
 
 // CPB: coordinates per thread batch, the n_screen = 80 share of one thread in
 // one batch
-template <int NG, int CPB, bool VAR>
+// blocks of a group whose words are in flight together (at most 40 words
+// per thread)
+constexpr int screen_chunk(int ng, int bg) { return ng >= 8 ? 2 : (bg == 2 ? 2 : 1); }
+
+template <int NG, int CPB, bool VAR, int BG, int BC>
 static hipError_t launch_screen_t(const ScreenArgs& a, const Plan& p, hipStream_t st) {
-  k_screen<kScreenThreads, NG, CPB, VAR><<<8 * p.per_xcd1, kScreenThreads, 0, st>>>(a);
+  k_screen<kScreenThreads, NG, CPB, VAR, BG, BC><<<8 * p.per_xcd1, kScreenThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
 // (the whole sketch, VAR: a thread's share of all 128 coordinates in one batch)
 template <bool VAR>
 static hipError_t launch_screen_v(const ScreenArgs& a, const Plan& p, hipStream_t st) {
+  if constexpr (!VAR) {
+    if (p.bg > 1) {  // the (ng, bg) pairs make_plan can choose
+      switch (p.ng * 16 + p.bg) {
+        case 16 * 16 + 2: return launch_screen_t<16, 5, false, 2, screen_chunk(16, 2)>(a, p, st);
+        case 16 * 16 + 4: return launch_screen_t<16, 5, false, 4, screen_chunk(16, 4)>(a, p, st);
+        case 16 * 16 + 8: return launch_screen_t<16, 5, false, 8, screen_chunk(16, 8)>(a, p, st);
+        case 8 * 16 + 2: return launch_screen_t<8, 10, false, 2, screen_chunk(8, 2)>(a, p, st);
+        case 8 * 16 + 4: return launch_screen_t<8, 10, false, 4, screen_chunk(8, 4)>(a, p, st);
+        case 8 * 16 + 8: return launch_screen_t<8, 10, false, 8, screen_chunk(8, 8)>(a, p, st);
+        case 4 * 16 + 2: return launch_screen_t<4, 20, false, 2, screen_chunk(4, 2)>(a, p, st);
+        case 4 * 16 + 4: return launch_screen_t<4, 20, false, 4, screen_chunk(4, 4)>(a, p, st);
+        case 4 * 16 + 8: return launch_screen_t<4, 20, false, 8, screen_chunk(4, 8)>(a, p, st);
+        default: return hipErrorInvalidConfiguration;
+      }
+    }
+  }
+  if (p.bg != 1) return hipErrorInvalidConfiguration;
   switch (p.ng) {
-    case 16: return launch_screen_t<16, VAR ? 8 : 5, VAR>(a, p, st);
-    case 8: return launch_screen_t<8, VAR ? 16 : 10, VAR>(a, p, st);
-    case 4: return launch_screen_t<4, 20, VAR>(a, p, st);
-    case 2: return launch_screen_t<2, 20, VAR>(a, p, st);
-    default: return launch_screen_t<1, 20, VAR>(a, p, st);
+    case 16: return launch_screen_t<16, VAR ? 8 : 5, VAR, 1, 1>(a, p, st);
+    case 8: return launch_screen_t<8, VAR ? 16 : 10, VAR, 1, 1>(a, p, st);
+    case 4: return launch_screen_t<4, 20, VAR, 1, 1>(a, p, st);
+    case 2: return launch_screen_t<2, 20, VAR, 1, 1>(a, p, st);
+    default: return launch_screen_t<1, 20, VAR, 1, 1>(a, p, st);
   }
 }
 

@@ -11,6 +11,7 @@ namespace cfr {
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kScreenThreads = 512;     // screen workgroup size
+constexpr int kScreenMinWgs = 512;     // screen workgroups a block group may leave at batch >= 2
 constexpr int kMaxGatherWgs = 256;      // gather workgroups per call, summed over the batch
 constexpr int kMaxRecoverWgs = 16;      // recovery workgroups per token
 constexpr int kReduceSlice = 32;        // hidden units per reduce workgroup
@@ -87,8 +88,8 @@ struct GatherLds {
 
 // Launch geometry of one decode call.
 struct Plan {
-  // screen: one workgroup per (token, routed slot, block, half)
-  int items1 = 0, per_xcd1 = 0;
+  // screen: one workgroup per (token, routed slot, group of bg blocks, half)
+  int items1 = 0, per_xcd1 = 0, bg = 1;
   int nd = 0;  // 32-bit code words per half-unit that hold codes
   int ng = 0;  // screened-coordinate groups per workgroup
   size_t lds1 = 0;
