@@ -106,6 +106,19 @@ def test_tiny_shared_experts_and_k_above_the_union(tiny):
     assert rel_l2(y, yd) < 1e-5
 
 
+@pytest.mark.parametrize("k", [1, 37, 100])
+def test_tiny_all_scores_tied(tiny, k):
+    # x = 0: every batch score is 0, so the kept candidates are the k lowest
+    # union candidates (ties to the lower index) and every y is 0
+    L, r, o = tiny
+    X = np.zeros((5, TS.hidden), np.float32)
+    ids, w = make_routing_inputs(TINY, 5, seed_offset=5)
+    _, nd, nu = _check(r, o, X, ids, w, k)
+    lib = r.decode_shared(_dev(X), _dev(ids), _dev(w), k, debug=True)
+    assert nd == 0
+    assert np.array_equal(lib["kept"].cpu().numpy(), np.arange(min(k, nu * TS.inter)))
+
+
 def test_argument_rules(tiny):
     L, r, o = tiny
     X = _dev(make_tokens(TINY, 2))
