@@ -1,5 +1,6 @@
 """GPU parity at edge shapes: every select geometry (2..32 candidates per
-thread), every hidden-chunk count of the gather, one and an odd number of
+thread), every hidden-chunk count of the gather (with 8 chunks, up to two
+channels per wave, one after the other), one and an odd number of
 128-blocks, intermediate sizes that leave a ragged last code byte or are not
 a multiple of 128, top = 1 and the largest top * inter, rank 0 (no recovery),
 a rank that is not a power of two and the largest rank, partial screens of
@@ -29,6 +30,7 @@ CASES = [
     (640, 8, 96, 8, 24, 77, (3, 100, 767)),          # 5 blocks, rank 24, odd screen
     (256, 8, 640, 4, 32, 80, (300,)),                # 6 per thread
     (256, 8, 1000, 8, 32, 80, (1234,)),              # 16 per thread
+    (4096, 8, 200, 4, 32, 80, (0, 7, 650, 800)),     # 8 hidden chunks, 2 channels a wave in turn
 ]
 
 
