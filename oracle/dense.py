@@ -17,7 +17,10 @@ from .numerics import weights_f64
 
 
 def silu(z):
-    return z / (1.0 + np.exp(-z))
+    # exp(-z) overflows to inf for z below about -709, where z / inf = -0 is
+    # the right limit: the overflow is expected, not an error
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def dense_moe(gate_bits, up_bits, down_bits, x, ids, w):
