@@ -1,7 +1,7 @@
 """GPU parity on the Qwen3-30B-A3B-shaped layer (hidden 2048, 128 experts,
 intermediate 768, top-8: 6144 candidates per token), batch 1 as timed by
 bench.py and batch 4 with per-token routing and top-k, at the 17.8% (k = 756)
-and 12.8% (k = 445) read budgets."""
+and 12.8% (k = 445) read budgets; batches 2, 5 and 8 at k = 756."""
 import sys
 import time
 
@@ -50,7 +50,7 @@ def oracle(layer):
 def reader(layer):
     t = time.time()
     r = Reader.build(Config(hidden=S.hidden, n_experts=S.n_experts, inter=S.inter, top=S.top,
-                            rot_seed=WL.rot_seed, max_batch=4),
+                            rot_seed=WL.rot_seed, max_batch=8),
                      layer["gate"], layer["up"], layer["down"], layer["router"])
     _log(f"library reader built in {time.time() - t:.1f}s")
     yield r
@@ -113,6 +113,20 @@ def test_batch4_parity(reader, oracle, layer, k):
             g = b0 + t
             ref = oracle.decode(X[g], ids[g], w[g], k)
             check_token(lib, ref, oracle, X[g], ids[g], w[g], k, t)
+
+
+@pytest.mark.parametrize("batch", [2, 5, 8])
+def test_other_batch_sizes(reader, oracle, layer, batch):
+    # the screen's block groups by batch at this layer: 1 block per
+    # workgroup at batch 2, 2 at batch 5, 4 at batch 8 (512 workgroups)
+    X = make_tokens(WL4, batch, seed_offset=20 + batch)
+    ids, w = _routed(layer, X)
+    lib = _np(reader.decode_debug(_dev(X), _dev(ids), _dev(w), 756))
+    y_fast = reader.decode(_dev(X), _dev(ids), _dev(w), 756).cpu().numpy()
+    assert np.array_equal(y_fast, lib["y"]), "fast path differs from the debug path"
+    for t in range(batch):
+        ref = oracle.decode(X[t], ids[t], w[t], 756)
+        check_token(lib, ref, oracle, X[t], ids[t], w[t], 756, t)
 
 
 def test_batch1_fast_path_matches_debug(reader, layer):
