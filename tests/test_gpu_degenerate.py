@@ -9,6 +9,9 @@ the Qwen3-30B-A3B-shaped layer:
     zero, and k beyond one expert's channels keeps zero-score channels by
     index;
   * x scaled by 1000 (the screen's fixed-point range);
+  * a NaN coordinate in one token of a batch: that token's y is NaN and the
+    other tokens are untouched (every index the kernels use comes from
+    ranges, never from the token's values);
   * a sweep over random routings and k = 1 .. top*I - 1."""
 import numpy as np
 import pytest
@@ -104,3 +107,22 @@ def test_random_sweep(c2):
         k = int(rng.integers(1, S.n_cand))
         sl = slice(b0, b0 + 4)
         _run(o, r, X[sl], ids[sl], w[sl], k)
+
+
+@pytest.mark.parametrize("k", [1, 756])
+def test_nan_token_is_isolated(c2, k):
+    o, r = c2
+    X = make_tokens(WL, 3, seed_offset=41)
+    X[1, 5] = np.nan
+    ids, w = _routing(3, 41)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    lib = {n: v.cpu().numpy() for n, v in r.decode_debug(d(X), d(ids), d(w), k).items()}
+    y = r.decode(d(X), d(ids), d(w), k).cpu().numpy()
+    assert np.array_equal(y, lib["y"], equal_nan=True)
+    assert np.isnan(y[1]).all()
+    for t in (0, 2):
+        ref = o.decode(X[t], ids[t], w[t], k)
+        check_token(lib, ref, o, X[t], ids[t], w[t], k, t)
+    # the next call on the same reader is exact again (the accumulators
+    # were cleared, whatever the NaN token left in them)
+    _run(o, r, X[[0, 2]], ids[[0, 2]], w[[0, 2]], k)
