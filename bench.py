@@ -133,7 +133,7 @@ def profile_summary(d):
     def ours(k):  # the decode-time kernels of the library
         return k.split("<")[0].split()[-1] in names
 
-    lines = []
+    lines = [f"device sources (csrc/*.hip, csrc/*.h) SHA-256: {source_digest()}"]
     traffic = {}
     for f in sorted(set(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))):
         lines.append(f"kernel stats: {os.path.relpath(f, d)}")
