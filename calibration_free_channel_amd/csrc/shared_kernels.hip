@@ -464,8 +464,11 @@ __global__ __launch_bounds__(kBActThreads) void k_bact(BActArgs a) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         const int h = min(ch * 512 + lane * 8, H - 8);  // clamped; the tail is masked below
-        gq[r][ch] = *reinterpret_cast<const uint4*>(row + h);
-        uq[r][ch] = *reinterpret_cast<const uint4*>(row + H + h);
+        // streamed, like the row chunks of the per-token gather
+        const u32x4_t g4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + h));
+        const u32x4_t u4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + H + h));
+        gq[r][ch] = make_uint4(g4.x, g4.y, g4.z, g4.w);
+        uq[r][ch] = make_uint4(u4.x, u4.y, u4.z, u4.w);
       }
     }
 #pragma unroll
@@ -618,7 +621,8 @@ __global__ __launch_bounds__(kBDownThreads) void k_bdown(BDownArgs a) {
 #pragma unroll
     for (int u = 0; u < kBDownRows; ++u) {
       const int q = min(q0 + u * kBDownWaves, r1 - 1);
-      dq[u] = *reinterpret_cast<const uint4*>(dbase + (size_t)a.krow[q] * 3 * H);
+      const u32x4_t d4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dbase + (size_t)a.krow[q] * 3 * H));
+      dq[u] = make_uint4(d4.x, d4.y, d4.z, d4.w);  // streamed
 #pragma unroll
       for (int t = 0; t < kMaxSharedBatch; ++t)
         cf[u][t] = (t < B && q0 + u * kBDownWaves < r1) ? a.coef[(size_t)q * B + t] : 0.f;
